@@ -1,0 +1,141 @@
+"""fp64 CPU oracle for the Attention Residuals operator -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never imports it, and the two share no code.
+
+The arithmetic lives in ``attnres_oracle.c`` (plain double-precision loops, one
+token at a time).  It follows the formula box of the architecture figure in
+"Kimi K3 模型结构（10）：RL 与服务中的状态管理": softmax over the sources of the
+pseudo-query w_l dotted with each RMS-normalised source, then the softmax-
+weighted sum of the raw sources.  The backward pass is the chain rule of that
+formula.  Inputs are the exact bf16 / fp32 values widened to double; outputs
+stay in double.
+
+Every function here is pinned by ``tests/test_oracle.py`` against finite
+differences, an independent PyTorch fp64 autograd route, hand-derived closed
+forms (``tests/golden/``) and invariants of the formula.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+MAX_SOURCES = 16
+
+class Oracle:
+    """ctypes view of one build of the oracle library (the default one, or a
+    deliberately mutated copy that the pin tests compile to prove the pins
+    catch mistakes)."""
+
+    def __init__(self, lib_path: str = _LIB_PATH):
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(lib_path)
+        i32, i64, f64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        for name in ("oracle_fwd", "oracle_bwd", "oracle_fwd_f64", "oracle_bwd_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [i32, i64, i64, vp, vp, f64, vp, vp, vp]
+            f.restype = None
+        self.lib = lib
+        self.path = lib_path
+
+    def fwd(self, src_bits: np.ndarray, w: np.ndarray, eps: float):
+        """Forward on bf16 bit patterns src [N][T][D] (uint16) and fp32 w [D].
+
+        Returns (out [T][D], rstd [T][N], alpha [T][N]) in float64.
+        """
+        src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        N, T, D = _shape(src_bits)
+        assert w.shape == (D,)
+        out = np.empty((T, D))
+        rstd = np.empty((T, N))
+        alpha = np.empty((T, N))
+        self.lib.oracle_fwd(N, T, D, _p(src_bits), _p(w), float(eps), _p(out), _p(rstd), _p(alpha))
+        return out, rstd, alpha
+
+    def bwd(self, src_bits: np.ndarray, w: np.ndarray, eps: float, dout_bits: np.ndarray, want_dsrc: bool = True):
+        """Backward on bf16 bit patterns; returns (dsrc [N][T][D] or None, dw [D]) in float64."""
+        src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        dout_bits = np.ascontiguousarray(dout_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        N, T, D = _shape(src_bits)
+        assert w.shape == (D,) and dout_bits.shape == (T, D)
+        dsrc = np.empty((N, T, D)) if want_dsrc else None
+        dw = np.empty(D)
+        self.lib.oracle_bwd(N, T, D, _p(src_bits), _p(w), float(eps), _p(dout_bits), _p(dsrc), _p(dw))
+        return dsrc, dw
+
+    def fwd_f64(self, x: np.ndarray, w: np.ndarray, eps: float):
+        """Forward on float64 sources x [N][T][D] and float64 w [D]."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        N, T, D = _shape(x)
+        assert w.shape == (D,)
+        out = np.empty((T, D))
+        rstd = np.empty((T, N))
+        alpha = np.empty((T, N))
+        self.lib.oracle_fwd_f64(N, T, D, _p(x), _p(w), float(eps), _p(out), _p(rstd), _p(alpha))
+        return out, rstd, alpha
+
+    def bwd_f64(self, x: np.ndarray, w: np.ndarray, eps: float, g: np.ndarray):
+        """Backward on float64 inputs; returns (dx [N][T][D], dw [D])."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        g = np.ascontiguousarray(g, dtype=np.float64)
+        N, T, D = _shape(x)
+        assert w.shape == (D,) and g.shape == (T, D)
+        dx = np.empty((N, T, D))
+        dw = np.empty(D)
+        self.lib.oracle_bwd_f64(N, T, D, _p(x), _p(w), float(eps), _p(g), _p(dx), _p(dw))
+        return dx, dw
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _shape(src):
+    assert src.ndim == 3, "sources are [N][T][D]"
+    N, T, D = src.shape
+    assert 1 <= N <= MAX_SOURCES
+    return N, T, D
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def fwd(src_bits, w, eps):
+    return default().fwd(src_bits, w, eps)
+
+
+def bwd(src_bits, w, eps, dout_bits, want_dsrc=True):
+    return default().bwd(src_bits, w, eps, dout_bits, want_dsrc)
+
+
+def fwd_f64(x, w, eps):
+    return default().fwd_f64(x, w, eps)
+
+
+def bwd_f64(x, w, eps, g):
+    return default().bwd_f64(x, w, eps, g)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float64."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,209 @@
+/*
+ * fp64 CPU oracle for the Attention Residuals operator -- TEST INFRASTRUCTURE.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  The HIP library never calls it and shares no code with
+ * it.  It is plain on purpose: one token at a time, straight loops in double,
+ * no blocking, no fusion and no reordering beyond what the formula states.
+ *
+ * What it computes (the formula box of the architecture figure in "Kimi K3
+ * 模型结构（10）：RL 与服务中的状态管理": the weights over the depth sources are
+ * softmax(w_l . RMSNorm(sources)), and the operator returns the weighted sum of
+ * the sources, scored with the sub-layer's pseudo-query w_l).  For one token
+ * with sources x_0 .. x_{N-1} (each of length D):
+ *
+ *   ms_i    = (1/D) sum_d x_id^2
+ *   r_i     = 1 / sqrt(ms_i + eps)                 RMSNorm, no gain
+ *   z_i     = sum_d w_d (r_i x_id)                 score of source i
+ *   alpha_i = exp(z_i - max_j z_j) / sum_k exp(z_k - max_j z_j)
+ *   out_d   = sum_i alpha_i x_id                   raw (un-normalised) sources
+ *
+ * The backward pass is the chain rule of the above for the loss
+ * L = sum_d g_d out_d (g = dout):
+ *
+ *   da_i  = sum_d g_d x_id
+ *   s     = sum_i alpha_i da_i
+ *   dz_i  = alpha_i (da_i - s)                     softmax Jacobian
+ *   dx_id = alpha_i g_d + dz_i r_i (w_d - z_i r_i x_id / D)
+ *   dw_d  = sum over tokens and sources of dz_i r_i x_id
+ *
+ * Readings where the pages are silent: the normalisation has no learnable
+ * gain, eps sits inside the square root and the mean is over D, the score has
+ * no temperature, and the weighted sum uses the raw sources.
+ *
+ * Layout: sources are source-major [N][T][D]; out, dout are [T][D]; rstd and
+ * alpha are token-major [T][N]; dx is [N][T][D]; dw is [D].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Tokens whose dw contributions are summed together before the chunks are
+ * added in chunk order; fixed, so dw does not depend on the thread count. */
+#define DW_CHUNK 256
+
+/* ---- one token ---------------------------------------------------------- */
+
+/* x[i] points at source i's row for this token. */
+static void token_forward(int N, int64_t D, const double* const* x, const double* w, double eps, double* out,
+                          double* r, double* z, double* alpha) {
+  for (int i = 0; i < N; ++i) {
+    double ss = 0.0;
+    for (int64_t d = 0; d < D; ++d) ss += x[i][d] * x[i][d];
+    r[i] = 1.0 / sqrt(ss / (double)D + eps);
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += w[d] * (r[i] * x[i][d]);
+    z[i] = dot;
+  }
+  double m = z[0];
+  for (int i = 1; i < N; ++i)
+    if (z[i] > m) m = z[i];
+  double den = 0.0;
+  for (int i = 0; i < N; ++i) den += exp(z[i] - m);
+  for (int i = 0; i < N; ++i) alpha[i] = exp(z[i] - m) / den;
+  for (int64_t d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int i = 0; i < N; ++i) acc += alpha[i] * x[i][d];
+    out[d] = acc;
+  }
+}
+
+static void token_backward(int N, int64_t D, const double* const* x, const double* w, double eps, const double* g,
+                           double* const* dx, double* dw) {
+  double r[16], z[16], alpha[16], da[16], dz[16];
+  double* out = (double*)malloc(sizeof(double) * (size_t)D);
+  token_forward(N, D, x, w, eps, out, r, z, alpha);
+  free(out);
+  for (int i = 0; i < N; ++i) {
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += g[d] * x[i][d];
+    da[i] = acc;
+  }
+  double s = 0.0;
+  for (int i = 0; i < N; ++i) s += alpha[i] * da[i];
+  for (int i = 0; i < N; ++i) dz[i] = alpha[i] * (da[i] - s);
+  for (int i = 0; i < N; ++i)
+    for (int64_t d = 0; d < D; ++d)
+      dx[i][d] = alpha[i] * g[d] + dz[i] * r[i] * (w[d] - z[i] * r[i] * x[i][d] / (double)D);
+  for (int i = 0; i < N; ++i)
+    for (int64_t d = 0; d < D; ++d) dw[d] += dz[i] * r[i] * x[i][d];
+}
+
+/* ---- fp64 inputs -------------------------------------------------------- */
+
+/* x: [N][T][D]; out: [T][D]; rstd, alpha: [T][N] (either may be NULL). */
+void oracle_fwd_f64(int N, int64_t T, int64_t D, const double* x, const double* w, double eps, double* out,
+                    double* rstd, double* alpha) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    const double* rows[16];
+    double r[16], z[16], a[16];
+    for (int i = 0; i < N; ++i) rows[i] = x + ((int64_t)i * T + t) * D;
+    token_forward(N, D, rows, w, eps, out + t * D, r, z, a);
+    for (int i = 0; i < N; ++i) {
+      if (rstd) rstd[t * N + i] = r[i];
+      if (alpha) alpha[t * N + i] = a[i];
+    }
+  }
+}
+
+/* x, dx: [N][T][D]; g: [T][D]; dw: [D] (overwritten with the sum over all T tokens). */
+void oracle_bwd_f64(int N, int64_t T, int64_t D, const double* x, const double* w, double eps, const double* g,
+                    double* dx, double* dw) {
+  const int64_t nchunk = (T + DW_CHUNK - 1) / DW_CHUNK;
+  double* part = (double*)calloc((size_t)(nchunk > 0 ? nchunk : 1) * (size_t)D, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < nchunk; ++c) {
+    const int64_t t1 = (c + 1) * DW_CHUNK < T ? (c + 1) * DW_CHUNK : T;
+    for (int64_t t = c * DW_CHUNK; t < t1; ++t) {
+      const double* rows[16];
+      double* drows[16];
+      for (int i = 0; i < N; ++i) {
+        rows[i] = x + ((int64_t)i * T + t) * D;
+        drows[i] = dx + ((int64_t)i * T + t) * D;
+      }
+      token_backward(N, D, rows, w, eps, g + t * D, drows, part + c * D);
+    }
+  }
+  for (int64_t d = 0; d < D; ++d) dw[d] = 0.0;
+  for (int64_t c = 0; c < nchunk; ++c)
+    for (int64_t d = 0; d < D; ++d) dw[d] += part[c * D + d];
+  free(part);
+}
+
+/* ---- bf16 / fp32 inputs, widened exactly to fp64 ------------------------ */
+
+static double bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static void widen_token(int N, int64_t T, int64_t D, const uint16_t* src, int64_t t, double* buf, double** rows) {
+  for (int i = 0; i < N; ++i) {
+    rows[i] = buf + (int64_t)i * D;
+    const uint16_t* s = src + ((int64_t)i * T + t) * D;
+    for (int64_t d = 0; d < D; ++d) rows[i][d] = bf16_to_f64(s[d]);
+  }
+}
+
+/* src: bf16 bits [N][T][D]; w: fp32 [D].  Outputs as in oracle_fwd_f64. */
+void oracle_fwd(int N, int64_t T, int64_t D, const uint16_t* src, const float* w, double eps, double* out,
+                double* rstd, double* alpha) {
+  double* wd = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int64_t d = 0; d < D; ++d) wd[d] = (double)w[d];
+#pragma omp parallel
+  {
+    double* buf = (double*)malloc(sizeof(double) * (size_t)N * (size_t)D);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+      double* rows[16];
+      double r[16], z[16], a[16];
+      widen_token(N, T, D, src, t, buf, rows);
+      token_forward(N, D, (const double* const*)rows, wd, eps, out + t * D, r, z, a);
+      for (int i = 0; i < N; ++i) {
+        if (rstd) rstd[t * N + i] = r[i];
+        if (alpha) alpha[t * N + i] = a[i];
+      }
+    }
+    free(buf);
+  }
+  free(wd);
+}
+
+/* src: bf16 bits [N][T][D]; dout: bf16 bits [T][D]; dx: fp64 [N][T][D] (may be
+ * NULL to compute dw only); dw: fp64 [D]. */
+void oracle_bwd(int N, int64_t T, int64_t D, const uint16_t* src, const float* w, double eps, const uint16_t* dout,
+                double* dx, double* dw) {
+  const int64_t nchunk = (T + DW_CHUNK - 1) / DW_CHUNK;
+  double* part = (double*)calloc((size_t)(nchunk > 0 ? nchunk : 1) * (size_t)D, sizeof(double));
+  double* wd = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int64_t d = 0; d < D; ++d) wd[d] = (double)w[d];
+#pragma omp parallel
+  {
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(N + 1) * (size_t)D);
+    double* dbuf = (double*)malloc(sizeof(double) * (size_t)N * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nchunk; ++c) {
+      const int64_t t1 = (c + 1) * DW_CHUNK < T ? (c + 1) * DW_CHUNK : T;
+      for (int64_t t = c * DW_CHUNK; t < t1; ++t) {
+        double* rows[16];
+        double* drows[16];
+        widen_token(N, T, D, src, t, buf, rows);
+        double* g = buf + (int64_t)N * D;
+        for (int64_t d = 0; d < D; ++d) g[d] = bf16_to_f64(dout[t * D + d]);
+        for (int i = 0; i < N; ++i) drows[i] = dx ? dx + ((int64_t)i * T + t) * D : dbuf + (int64_t)i * D;
+        token_backward(N, D, (const double* const*)rows, wd, eps, g, drows, part + c * D);
+      }
+    }
+    free(buf);
+    free(dbuf);
+  }
+  for (int64_t d = 0; d < D; ++d) dw[d] = 0.0;
+  for (int64_t c = 0; c < nchunk; ++c)
+    for (int64_t d = 0; d < D; ++d) dw[d] += part[c * D + d];
+  free(part);
+  free(wd);
+}

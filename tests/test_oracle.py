@@ -1,0 +1,294 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself:
+  * hand-derived closed forms (tests/golden/hand_derived.json),
+  * an independent library route: PyTorch fp64 ``rms_norm`` + ``softmax`` with
+    autograd for the backward,
+  * central finite differences of the oracle's own forward (pins the backward),
+  * invariants of the formula (weights sum to 1, N = 1, w = 0, identical
+    sources, permutation, scale invariance at eps = 0, the Euler identity
+    sum <dx, x> = sum <out, g> at eps = 0, large scores),
+  * bf16-entry vs fp64-entry agreement with torch's own bf16 widening.
+
+``test_pins_catch_planted_mistakes`` compiles mutated copies of the oracle
+source (on the CPU, in a temp dir) and asserts every mutant fails some pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "hand_derived.json")
+ORACLE_SRC = os.path.join(os.path.dirname(HERE), "oracle", "attnres_oracle.c")
+
+_MATH = {"sqrt": math.sqrt, "exp": math.exp, "log": math.log, "e": math.e, "__builtins__": {}}
+
+
+def _ev(x):
+    if isinstance(x, list):
+        return [_ev(v) for v in x]
+    return float(eval(x, _MATH)) if isinstance(x, str) else float(x)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------
+# individual pins; each returns a list of failure strings (empty = pass) so the
+# mutation test can run them against a broken oracle build
+# ----------------------------------------------------------------------------
+
+def pin_golden(orc):
+    fails = []
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        D, N, eps = c["D"], c["N"], c["eps"]
+        x = np.array(c["x"], dtype=np.float64).reshape(N, 1, D)
+        w = np.array(_ev(c["w"]))
+        out, rstd, alpha = orc.fwd_f64(x, w, eps)
+        exp = c["expect"]
+        checks = [("rstd", rstd[0]), ("alpha", alpha[0]), ("out", out[0])]
+        if c["g"] is not None:
+            g = np.array(c["g"], dtype=np.float64).reshape(1, D)
+            dx, dw = orc.bwd_f64(x, w, eps, g)
+            checks += [("dx", dx[:, 0, :]), ("dw", dw)]
+        for key, got in checks:
+            if key not in exp:
+                continue
+            want = np.array(_ev(exp[key]))
+            if not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+                fails.append(f"golden {c['name']} {key}: got {got} want {want}")
+    return fails
+
+
+def _torch_route(x, w, eps, g):
+    """Independent route: library rms_norm, softmax and autograd in fp64."""
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    D = x.shape[-1]
+    xn = torch.nn.functional.rms_norm(xt, (D,), eps=eps)  # [N][T][D]
+    z = (xn * wt).sum(-1)  # [N][T]
+    a = torch.softmax(z, dim=0)  # over sources
+    out = (a.unsqueeze(-1) * xt).sum(0)  # [T][D]
+    loss = (out * torch.tensor(g, dtype=torch.float64)).sum()
+    loss.backward()
+    rstd = torch.rsqrt(xt.detach().pow(2).mean(-1) + eps)
+    return (out.detach().numpy(), rstd.T.numpy(), a.detach().T.numpy(), xt.grad.numpy(), wt.grad.numpy())
+
+
+def _rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def pin_torch_route(orc):
+    fails = []
+    # T = 300 spans more than one of the oracle's fixed dw chunks
+    for seed, (N, T, D, eps) in enumerate([(1, 3, 16, 1e-6), (2, 4, 24, 0.1), (3, 5, 32, 1e-6),
+                                          (5, 300, 16, 1e-6), (9, 6, 64, 1e-3), (9, 2, 8, 0.0)]):
+        r = _rng(100 + seed)
+        x = r.standard_normal((N, T, D)) * (1.0 + np.arange(N))[:, None, None]
+        w = r.standard_normal(D) / math.sqrt(D) * 3.0
+        g = r.standard_normal((T, D))
+        t_out, t_rstd, t_alpha, t_dx, t_dw = _torch_route(x, w, eps, g)
+        out, rstd, alpha = orc.fwd_f64(x, w, eps)
+        dx, dw = orc.bwd_f64(x, w, eps, g)
+        for name, a, b in (("out", out, t_out), ("rstd", rstd, t_rstd), ("alpha", alpha, t_alpha),
+                           ("dx", dx, t_dx), ("dw", dw, t_dw)):
+            e = _rel(a, b)
+            if not e < 1e-11:
+                fails.append(f"torch route N={N} T={T} D={D} eps={eps} {name}: rel {e:.3e}")
+    return fails
+
+
+def pin_finite_differences(orc):
+    fails = []
+    r = _rng(7)
+    N, T, D, eps, h = 3, 2, 16, 1e-6, 1e-6
+    x = r.standard_normal((N, T, D)) * np.array([1.0, 2.0, 0.5])[:, None, None]
+    w = r.standard_normal(D) * 0.5
+    g = r.standard_normal((T, D))
+
+    def loss(xx, ww):
+        return float((orc.fwd_f64(xx, ww, eps)[0] * g).sum())
+
+    dx, dw = orc.bwd_f64(x, w, eps, g)
+    fd_x = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp = x.copy()
+        xp[idx] += h
+        xm = x.copy()
+        xm[idx] -= h
+        fd_x[idx] = (loss(xp, w) - loss(xm, w)) / (2 * h)
+    fd_w = np.zeros_like(w)
+    for d in range(D):
+        wp = w.copy()
+        wp[d] += h
+        wm = w.copy()
+        wm[d] -= h
+        fd_w[d] = (loss(x, wp) - loss(x, wm)) / (2 * h)
+    ex, ew = _rel(dx, fd_x), _rel(dw, fd_w)
+    if not ex < 1e-6:
+        fails.append(f"finite differences dx rel {ex:.3e}")
+    if not ew < 1e-6:
+        fails.append(f"finite differences dw rel {ew:.3e}")
+    return fails
+
+
+def pin_invariants(orc):
+    fails = []
+    r = _rng(11)
+    N, T, D = 5, 7, 32
+    x = r.standard_normal((N, T, D)) * (1.0 + np.arange(N))[:, None, None]
+    w = r.standard_normal(D) / math.sqrt(D) * 4.0
+    g = r.standard_normal((T, D))
+    eps = 1e-6
+    out, rstd, alpha = orc.fwd_f64(x, w, eps)
+    dx, dw = orc.bwd_f64(x, w, eps, g)
+    if not np.allclose(alpha.sum(1), 1.0, atol=1e-14):
+        fails.append("alpha does not sum to 1")
+    # w = 0: uniform weights, mean of sources, dx_i = g / N
+    o0, _, a0 = orc.fwd_f64(x, np.zeros(D), eps)
+    dx0, _ = orc.bwd_f64(x, np.zeros(D), eps, g)
+    if not (np.allclose(a0, 1.0 / N, atol=1e-15) and np.allclose(o0, x.mean(0), atol=1e-13)
+            and np.allclose(dx0, np.broadcast_to(g / N, dx0.shape), atol=1e-13)):
+        fails.append("w = 0 invariant")
+    # identical sources: out = x, dw = 0, dx_i = alpha_i g
+    xi = np.broadcast_to(x[:1], x.shape).copy()
+    oi, _, ai = orc.fwd_f64(xi, w, eps)
+    dxi, dwi = orc.bwd_f64(xi, w, eps, g)
+    if not (np.allclose(oi, x[0], atol=1e-13) and np.allclose(dwi, 0.0, atol=1e-12)
+            and np.allclose(dxi, ai.T[:, :, None] * g[None], atol=1e-13)):
+        fails.append("identical-sources invariant")
+    # permutation of the sources
+    p = np.array([3, 0, 4, 1, 2])
+    op, _, ap = orc.fwd_f64(x[p], w, eps)
+    dxp, dwp = orc.bwd_f64(x[p], w, eps, g)
+    if not (np.allclose(op, out, atol=1e-12) and np.allclose(ap, alpha[:, p], atol=1e-14)
+            and np.allclose(dxp, dx[p], atol=1e-12) and np.allclose(dwp, dw, atol=1e-11)):
+        fails.append("permutation invariant")
+    # eps = 0: scaling a source leaves its weight unchanged; scaling all scales out
+    o_e0, _, a_e0 = orc.fwd_f64(x, w, 0.0)
+    xs = x.copy()
+    xs[2] *= 37.0
+    _, _, a_s = orc.fwd_f64(xs, w, 0.0)
+    o_all, _, a_all = orc.fwd_f64(x * 0.125, w, 0.0)
+    if not (np.allclose(a_s, a_e0, atol=1e-14) and np.allclose(a_all, a_e0, atol=1e-14)
+            and np.allclose(o_all, 0.125 * o_e0, atol=1e-13)):
+        fails.append("scale invariance at eps = 0")
+    # eps = 0: out is 1-homogeneous in x, so sum <dx, x> = sum <out, g>
+    dx_e0, _ = orc.bwd_f64(x, w, 0.0, g)
+    lhs, rhs = float((dx_e0 * x).sum()), float((o_e0 * g).sum())
+    if not abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs)):
+        fails.append(f"Euler identity {lhs} vs {rhs}")
+    # token independence: a token's result does not depend on the other tokens
+    o_sub, r_sub, a_sub = orc.fwd_f64(x[:, 2:5], w, eps)
+    dx_sub, _ = orc.bwd_f64(x[:, 2:5], w, eps, g[2:5])
+    if not (np.array_equal(o_sub, out[2:5]) and np.array_equal(a_sub, alpha[2:5])
+            and np.array_equal(r_sub, rstd[2:5]) and np.array_equal(dx_sub, dx[:, 2:5])):
+        fails.append("token independence")
+    # large scores (|z| ~ 1e3): weights stay finite and sum to 1
+    wl = w * 400.0
+    ol, _, al = orc.fwd_f64(x, wl, eps)
+    if not (np.isfinite(al).all() and np.isfinite(ol).all() and np.allclose(al.sum(1), 1.0, atol=1e-14)):
+        fails.append("large-score softmax not finite")
+    # N = 2 closed form: alpha_0 = sigmoid(z_0 - z_1), with z from torch's rms_norm
+    x2 = x[:2]
+    _, _, a2 = orc.fwd_f64(x2, w, eps)
+    z = (torch.nn.functional.rms_norm(torch.tensor(x2), (D,), eps=eps) * torch.tensor(w)).sum(-1).numpy()
+    if not np.allclose(a2[:, 0], 1.0 / (1.0 + np.exp(-(z[0] - z[1]))), atol=1e-14):
+        fails.append("N = 2 sigmoid closed form")
+    return fails
+
+
+def pin_bf16_entry(orc):
+    """The bf16 entry points widen exactly: compare with torch's own bf16 -> fp64."""
+    fails = []
+    wl = synth.Workload("pin", T=260, N=4, D=64, kind="depth")
+    src = wl.sources()
+    dout = wl.dout()
+    w = wl.w()
+    xs = torch.from_numpy(src.view(np.int16)).view(torch.bfloat16).double().numpy()
+    gs = torch.from_numpy(dout.view(np.int16)).view(torch.bfloat16).double().numpy()
+    out, rstd, alpha = orc.fwd(src, w, wl.eps)
+    dsrc, dw = orc.bwd(src, w, wl.eps, dout)
+    out2, rstd2, alpha2 = orc.fwd_f64(xs, w.astype(np.float64), float(np.float32(wl.eps)))
+    dx2, dw2 = orc.bwd_f64(xs, w.astype(np.float64), float(np.float32(wl.eps)), gs)
+    for name, a, b in (("out", out, out2), ("rstd", rstd, rstd2), ("alpha", alpha, alpha2),
+                       ("dsrc", dsrc, dx2), ("dw", dw, dw2)):
+        if not np.allclose(a, b, rtol=1e-13, atol=1e-13):
+            fails.append(f"bf16 entry {name} differs from fp64 entry")
+    _, dw_only = orc.bwd(src, w, wl.eps, dout, want_dsrc=False)
+    if not np.array_equal(dw_only, dw):
+        fails.append("dw-only backward differs")
+    return fails
+
+
+PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    fails = pin(oracle.default())
+    assert not fails, "\n".join(fails)
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle source must fail at least one pin
+# ----------------------------------------------------------------------------
+
+MUTANTS = {
+    "sum_not_mean": ("r[i] = 1.0 / sqrt(ss / (double)D + eps);", "r[i] = 1.0 / sqrt(ss + eps);"),
+    "eps_outside_sqrt": ("r[i] = 1.0 / sqrt(ss / (double)D + eps);", "r[i] = 1.0 / sqrt(ss / (double)D) + eps;"),
+    "eps_dropped": ("r[i] = 1.0 / sqrt(ss / (double)D + eps);", "r[i] = 1.0 / sqrt(ss / (double)D);"),
+    "score_unnormalised": ("dot += w[d] * (r[i] * x[i][d]);", "dot += w[d] * x[i][d];"),
+    "no_max_subtraction": ("alpha[i] = exp(z[i] - m) / den;", "alpha[i] = exp(z[i]) / den * exp(-m);"),
+    "values_normalised": ("acc += alpha[i] * x[i][d];", "acc += alpha[i] * r[i] * x[i][d];"),
+    "softmax_bwd_sign": ("dz[i] = alpha[i] * (da[i] - s);", "dz[i] = alpha[i] * (s - da[i]);"),
+    "direct_term_dropped": ("dx[i][d] = alpha[i] * g[d] + dz[i]", "dx[i][d] = dz[i]"),
+    "rstd_term_dropped": ("(w[d] - z[i] * r[i] * x[i][d] / (double)D)", "(w[d])"),
+    "dw_missing_rstd": ("dw[d] += dz[i] * r[i] * x[i][d];", "dw[d] += dz[i] * x[i][d];"),
+    "da_uses_w": ("acc += g[d] * x[i][d];", "acc += w[d] * x[i][d];"),
+    "token_major_rows": ("rows[i] = x + ((int64_t)i * T + t) * D;", "rows[i] = x + (t * N + i) * D;"),
+    "alpha_transposed": ("if (alpha) alpha[t * N + i] = a[i];", "if (alpha) alpha[i * T + t] = a[i];"),
+    "dw_chunks_overwrite": ("dw[d] += part[c * D + d];", "dw[d] = part[c * D + d];"),
+    "bf16_widen_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "w_narrowed": ("wd[d] = (double)w[d];", "wd[d] = (double)(int)(w[d] * 64.0) / 64.0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found in the oracle source"
+    mutated = src.replace(old, new)
+    c_path = os.path.join(mutant_dir, f"{name}.c")
+    so_path = os.path.join(mutant_dir, f"{name}.so")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-o", so_path, c_path, "-lm"],
+                   check=True)
+    orc = oracle.Oracle(so_path)
+    caught = []
+    for pin in PINS:
+        with np.errstate(all="ignore"):
+            if pin(orc):
+                caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every pin"
