@@ -1,0 +1,137 @@
+"""Python binding of libattnres (Attention Residuals forward/backward on MI355X).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of ``libattnres.so`` (built from ``csrc/attnres.hip`` for gfx950).  PyTorch
+supplies device memory and the stream; outputs are allocated with torch unless
+the caller passes them in.  There is no fallback path: if the library is
+missing or a call fails, an exception is raised.
+
+The C entry points, declared in ``include/attnres.h``:
+
+    attnres_fwd(src[N][T][D] bf16, w[D] fp32, eps, N, T, D,
+                out[T][D] bf16, rstd[T][N] fp32, alpha[T][N] fp32, stream)
+    attnres_bwd(dout[T][D] bf16, src, w, rstd, alpha, N, T, D,
+                dsrc[N][T][D] bf16, dw[D] fp32, workspace, workspace_bytes, stream)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnres.so")
+
+MAX_SOURCES = 9
+MAX_D = 16384
+DW_PARTIALS = 512
+
+STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARGUMENT", 2: "ATTNRES_ERR_WORKSPACE", 3: "ATTNRES_ERR_HIP"}
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libattnres.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        lib.attnres_fwd.argtypes = [vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd.restype = ctypes.c_int
+        lib.attnres_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
+        lib.attnres_bwd.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def workspace_bytes(D: int) -> int:
+    """Bytes of device workspace attnres_bwd needs (ATTNRES_BWD_WORKSPACE_BYTES)."""
+    return DW_PARTIALS * D * 4
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attnres_fwd(src: torch.Tensor, w: torch.Tensor, eps: float, out=None, rstd=None, alpha=None, stream=None):
+    """Forward.  src [N][T][D] bf16, w [D] fp32 -> (out [T][D] bf16, rstd [T][N] fp32, alpha [T][N] fp32)."""
+    if src.dim() != 3:
+        raise ValueError("src must be [N][T][D]")
+    N, T, D = src.shape
+    _check(src, "src", torch.bfloat16, (N, T, D))
+    _check(w, "w", torch.float32, (D,))
+    dev = src.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if rstd is None:
+        rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    code = library().attnres_fwd(src.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+                                 rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_fwd", code)
+    return out, rstd, alpha
+
+
+def attnres_bwd(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor, alpha: torch.Tensor,
+                dsrc=None, dw=None, workspace=None, stream=None):
+    """Backward.  Returns (dsrc [N][T][D] bf16, dw [D] fp32)."""
+    if src.dim() != 3:
+        raise ValueError("src must be [N][T][D]")
+    N, T, D = src.shape
+    _check(src, "src", torch.bfloat16, (N, T, D))
+    _check(dout, "dout", torch.bfloat16, (T, D))
+    _check(w, "w", torch.float32, (D,))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    dev = src.device
+    if dsrc is None:
+        dsrc = torch.empty((N, T, D), dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty((D,), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    _check(dsrc, "dsrc", torch.bfloat16, (N, T, D))
+    _check(dw, "dw", torch.float32, (D,))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    code = library().attnres_bwd(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(), alpha.data_ptr(),
+                                 N, T, D, dsrc.data_ptr(), dw.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                 _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_bwd", code)
+    return dsrc, dw
+
+
+__all__ = ["attnres_fwd", "attnres_bwd", "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D",
+           "DW_PARTIALS", "LIB_PATH"]

@@ -1,0 +1,766 @@
+// libattnres: Attention Residuals forward and backward for gfx950 (MI355X).
+//
+// The operator mixes a token's depth sources with softmax weights of the
+// sub-layer pseudo-query against each RMS-normalised source and returns the
+// weighted sum of the raw sources (formula box of the architecture figure in
+// "Kimi K3 模型结构（10）：RL 与服务中的状态管理").  The Attention Residuals section
+// of "Kimi K3 on Fireworks: Fast RL at frontier scale" fuses normalisation and
+// weighted sum so that nothing per-source is materialised; here that means:
+//
+//   forward   one kernel, one HBM pass over the sources.  A workgroup owns one
+//             token at a time; each thread keeps a fixed D-slice of all N
+//             source rows in registers, forms its partial sum of squares and
+//             w.x, reduces them across the wave with DPP and across waves
+//             through a few LDS words, computes rstd/softmax redundantly in
+//             every thread, and writes the fp32-accumulated weighted sum from
+//             the same registers.
+//   backward  one kernel re-reads each source row once (plus dout), forms
+//             da_i = g.x_i and w.x_i with the same reduction tree, then writes
+//             dsources from the registers and accumulates this workgroup's
+//             dw partial row; a second small kernel sums the fixed number of
+//             partial rows in index order (deterministic, no atomics).
+//
+// Determinism and batch invariance (the determinism section of the Fireworks
+// report fixes reduction orders so results do not depend on the batch): the
+// per-token reduction tree depends only on (N, D), never on T or the grid, so
+// a token's outputs are bitwise the same whatever batch it sits in.
+//
+// No MFMA: the work is a batched GEMV ([T*N x D] . [D]) bound by HBM bandwidth.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "attnres.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 16;  // 1024 threads
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Unpack the eight bf16 values of a 16-byte vector.
+__device__ __forceinline__ void unpack8(const uint4& q, float (&f)[8]) {
+  f[0] = bf_lo(q.x); f[1] = bf_hi(q.x);
+  f[2] = bf_lo(q.y); f[3] = bf_hi(q.y);
+  f[4] = bf_lo(q.z); f[5] = bf_hi(q.z);
+  f[6] = bf_lo(q.w); f[7] = bf_hi(q.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&d)[8]) {
+  uint4 o;
+  o.x = pack_bf16x2(d[0], d[1]);
+  o.y = pack_bf16x2(d[2], d[3]);
+  o.z = pack_bf16x2(d[4], d[5]);
+  o.w = pack_bf16x2(d[6], d[7]);
+  return o;
+}
+
+// acc + a.b over the four bf16 pairs of two 16-byte vectors, with the pair
+// products formed exactly and added in fp32 (v_dot2_f32_bf16 on gfx950).
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer access
+// ---------------------------------------------------------------------------
+// Every row is addressed through a raw buffer descriptor built in scalar
+// registers (base = the row, size = the row's bytes); a lane supplies only a
+// 32-bit byte offset.  The hardware range check turns loads past the row end
+// into zeros and drops such stores, which masks the row tail for free.
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order reductions
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_masked(float v) {
+  // lanes outside ROW_MASK receive 0.0f, the identity of the sum below
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, complete in lane 63.  Butterfly within each
+// 16-lane row (xor 1, xor 2, half-row mirror, row mirror: every lane of a row
+// ends with the same bits because fp32 addition commutes), then the row sums
+// R0..R3 are combined with the row broadcasts as (R3 + R2) + (R1 + R0).
+// Pure VALU/DPP, fixed order.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v += dpp_f<0xB1>(v);             // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);             // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);            // row_half_mirror
+  v += dpp_f<0x140>(v);            // row_mirror
+  v += dpp_masked<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_masked<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Workgroup-wide sums of K (<= 64) per-thread values, returned wave-uniform.
+// Each wave reduces its values, lane 63 stores them in red[k][wave], one
+// barrier, then lane k adds the kMaxWaves slots of red[k] in slot order (slots
+// of absent waves hold zeros, written once at kernel start) and the K totals
+// are broadcast from lane k with v_readlane.  `red` is double-buffered by the
+// caller (alternating tokens), which makes one barrier per token enough: a
+// wave can only overwrite a buffer after passing the next token's barrier,
+// which every wave reaches only after it finished reading that buffer.
+template <int K>
+__device__ __forceinline__ void block_sums(float (&v)[K], float (*red)[kMaxWaves], int lane, int wave) {
+  static_assert(K <= kWave, "one lane per value");
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = wave_sum_lane63(v[k]);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[k][wave] = v[k];
+  }
+  __syncthreads();
+  float s = 0.f;
+  if (lane < K) {
+    const float4* r4 = reinterpret_cast<const float4*>(red[lane]);
+    float4 q[kMaxWaves / 4];
+#pragma unroll
+    for (int j = 0; j < kMaxWaves / 4; ++j) q[j] = r4[j];
+#pragma unroll
+    for (int j = 0; j < kMaxWaves / 4; ++j) {
+      s += q[j].x;
+      s += q[j].y;
+      s += q[j].z;
+      s += q[j].w;
+    }
+  }
+  const int sb = __builtin_bit_cast(int, s);
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sb, k));
+}
+
+// Zero both reduction buffers once, before the first token.
+template <int K>
+__device__ __forceinline__ void clear_red(float (*red)[K][kMaxWaves]) {
+  float* p = &red[0][0][0];
+  for (int j = threadIdx.x; j < 2 * K * kMaxWaves; j += blockDim.x) p[j] = 0.f;
+  __syncthreads();
+}
+
+// Hide a register's contents from the optimiser so values derived from it
+// (unpacked floats) are recomputed after a barrier instead of being kept live
+// across it: holding 8 unpacked floats per packed vector would double the
+// register footprint of a row group.
+__device__ __forceinline__ void opaque(uint4& q) { asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w)); }
+
+// Move a wave-uniform value into a scalar register (frees a VGPR per value).
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// ---------------------------------------------------------------------------
+// Row-group slices
+// ---------------------------------------------------------------------------
+// Thread j of a workgroup owns the 16-byte vectors j + k*blockDim.x (k < VPT)
+// of every row of the token: eight consecutive channels per vector, so one
+// wave-wide load covers 1 KiB of a row.  off[k] is that vector's byte offset
+// within a bf16 row (past the row end for tail threads: the buffer range
+// check then reads zeros and drops stores).  w and the running dw of the
+// backward pass live in LDS slots private to the thread (slot j + k*blockDim.x
+// holds 8 floats), so they need no barrier and leave the register file to the
+// row group.
+template <int VPT>
+struct Slice {
+  uint32_t off[VPT];  // byte offset in a bf16 row
+  int slot[VPT];      // private LDS slot (8 floats)
+  __device__ __forceinline__ Slice(int tid, int nthreads) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      slot[k] = tid + k * nthreads;
+      off[k] = (uint32_t)slot[k] * 16u;
+    }
+  }
+};
+
+__device__ __forceinline__ void load8(const float4* p, int slot, float (&f)[8]) {
+  const float4 a = p[2 * slot], b = p[2 * slot + 1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(float4* p, int slot, const float (&f)[8]) {
+  p[2 * slot] = make_float4(f[0], f[1], f[2], f[3]);
+  p[2 * slot + 1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// w (fp32, D values) into the thread's LDS slots; zeros past the row end.
+template <int VPT>
+__device__ __forceinline__ void stage_w(const float* __restrict__ w, int32_t D, float4* wl, const Slice<VPT>& sl) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(w, (uint32_t)D * 4u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint4 a = bload(r, 2u * sl.off[k]), b = bload(r, 2u * sl.off[k] + 16u);
+    wl[2 * sl.slot[k]] = __builtin_bit_cast(float4, a);
+    wl[2 * sl.slot[k] + 1] = __builtin_bit_cast(float4, b);
+  }
+}
+
+// This thread's slice of token t's N source rows.  Row (i, t) starts at
+// src + (i*T + t)*D; its descriptor is built in scalar registers.
+template <int N, int VPT>
+__device__ __forceinline__ void load_rows(uint4 (&x)[N][VPT], const uint16_t* __restrict__ src, int64_t T,
+                                          int64_t t, int32_t D, const Slice<VPT>& sl) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((int64_t)i * T + t) * D, (uint32_t)D * 2u);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) x[i][k] = bload(r, sl.off[k]);
+  }
+}
+
+template <int VPT>
+__device__ __forceinline__ void load_row(uint4 (&g)[VPT], const uint16_t* __restrict__ p, int64_t t, int32_t D,
+                                         const Slice<VPT>& sl) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(p + t * D, (uint32_t)D * 2u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) g[k] = bload(r, sl.off[k]);
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+// Persistent: workgroup b handles tokens b, b + G, b + 2G, ... (G = gridDim.x).
+// With PIPE, the next token's row group is loaded into a second register set
+// while the current one is reduced and summed, so HBM latency overlaps the
+// barrier and the arithmetic.  Dynamic LDS holds w.
+template <int N, int VPT, bool PIPE>
+__global__ void __launch_bounds__(1024) fwd_kernel(const uint16_t* __restrict__ src, const float* __restrict__ w,
+                                                   float eps, int64_t T, int32_t D, uint16_t* __restrict__ out,
+                                                   float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
+  __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
+  extern __shared__ float4 dyn_lds[];
+  float4* wl = dyn_lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const Slice<VPT> sl(tid, blockDim.x);
+  stage_w<VPT>(w, D, wl, sl);
+  clear_red<2 * N>(red);
+
+  const int64_t G = gridDim.x;
+  const float inv_d = 1.0f / (float)D;
+  int buf = 0;
+  uint4 xn[N][VPT];
+  if (PIPE && (int64_t)blockIdx.x < T) load_rows<N, VPT>(xn, src, T, blockIdx.x, D, sl);
+  for (int64_t t = blockIdx.x; t < T; t += G) {
+    uint4 x[N][VPT];
+    if (PIPE) {
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) x[i][k] = xn[i][k];
+      if (t + G < T) load_rows<N, VPT>(xn, src, T, t + G, D, sl);
+    } else {
+      load_rows<N, VPT>(x, src, T, t, D, sl);
+    }
+
+    // partial sum of squares (first N) and w.x (last N)
+    float part[2 * N];
+#pragma unroll
+    for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float wr[8];
+      load8(wl, sl.slot[k], wr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        float f[8];
+        unpack8(x[i][k], f);
+        part[i] = dot8_bf16(x[i][k], x[i][k], part[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
+      }
+    }
+    block_sums<2 * N>(part, red[buf], lane, wave);
+    buf ^= 1;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) opaque(x[i][k]);
+
+    // rstd, scores, softmax over the sources (fp32, max-subtracted)
+    float r[N], a[N];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      r[i] = uniform(1.0f / sqrtf(part[i] * inv_d + eps));
+      a[i] = r[i] * part[N + i];  // z_i
+      m = fmaxf(m, a[i]);
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      a[i] = expf(a[i] - m);
+      den += a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = uniform(a[i] / den);
+
+    // weighted sum of the raw sources
+    const __amdgpu_buffer_rsrc_t ro = rsrc(out + t * D, (uint32_t)D * 2u);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float acc[8];
+      {
+        float f[8];
+        unpack8(x[0][k], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = a[0] * f[e];
+      }
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        float f[8];
+        unpack8(x[i][k], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(a[i], f[e], acc[e]);
+      }
+      bstore(ro, sl.off[k], pack8(acc));
+    }
+    if (tid < N) {
+      float rv = r[0], av = a[0];
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        rv = tid == i ? r[i] : rv;
+        av = tid == i ? a[i] : av;
+      }
+      rstd_out[t * N + tid] = rv;
+      alpha_out[t * N + tid] = av;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward: dsources and dw partial rows
+// ---------------------------------------------------------------------------
+// The tokens are cut into P fixed chunks, chunk c = [c*T/P, (c+1)*T/P); each
+// chunk sums its dw contributions in token order into partial row ws[c][:].
+// Workgroup b handles chunks b, b + G, ... (G = gridDim.x <= P), so dw does not
+// depend on the grid.  With PIPE the next token's sources and dout are loaded
+// while the current token is processed.  Dynamic LDS holds w and the running
+// dw of the current chunk, in the thread's private slots.
+template <int N, int VPT, bool PIPE>
+__global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ src,
+                                                   const float* __restrict__ w, const float* __restrict__ rstd,
+                                                   const float* __restrict__ alpha, int64_t T, int32_t D, int32_t P,
+                                                   uint16_t* __restrict__ dsrc, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
+  extern __shared__ float4 dyn_lds[];
+  float4* wl = dyn_lds;
+  float4* dwl = dyn_lds + 2 * VPT * (int)blockDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t G = gridDim.x;
+  const Slice<VPT> sl(tid, blockDim.x);
+  stage_w<VPT>(w, D, wl, sl);
+  const float zero8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) store8(dwl, sl.slot[k], zero8);
+  clear_red<2 * N>(red);
+
+  const float inv_d = 1.0f / (float)D;
+  int buf = 0;
+
+  int64_t c = blockIdx.x;  // host guarantees gridDim.x <= P <= T, so every chunk is non-empty
+  int64_t t = c * T / P;
+  int64_t te = (c + 1) * T / P;
+  uint4 xn[N][VPT], gn[VPT];
+  if (PIPE) {
+    load_row<VPT>(gn, dout, t, D, sl);
+    load_rows<N, VPT>(xn, src, T, t, D, sl);
+  }
+  while (true) {
+    uint4 x[N][VPT], g[VPT];
+    if (PIPE) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        g[k] = gn[k];
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i][k] = xn[i][k];
+      }
+      // the token after t: next in this chunk, else first of chunk c + G
+      int64_t tn = t + 1;
+      bool more = true;
+      if (tn == te) {
+        more = c + G < P;
+        tn = (c + G) * T / P;
+      }
+      if (more) {
+        load_row<VPT>(gn, dout, tn, D, sl);
+        load_rows<N, VPT>(xn, src, T, tn, D, sl);
+      }
+    } else {
+      load_row<VPT>(g, dout, t, D, sl);
+      load_rows<N, VPT>(x, src, T, t, D, sl);
+    }
+
+    // partial g.x_i (first N) and w.x_i (last N)
+    float part[2 * N];
+#pragma unroll
+    for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float wr[8];
+      load8(wl, sl.slot[k], wr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        float f[8];
+        unpack8(x[i][k], f);
+        part[i] = dot8_bf16(g[k], x[i][k], part[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
+      }
+    }
+    block_sums<2 * N>(part, red[buf], lane, wave);
+    buf ^= 1;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      opaque(g[k]);
+#pragma unroll
+      for (int i = 0; i < N; ++i) opaque(x[i][k]);
+    }
+
+    // softmax backward: s = sum_j alpha_j da_j; dz_i = alpha_i (da_i - s)
+    float al[N], c1[N], c2[N];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      al[i] = alpha[t * N + i];
+      s = fmaf(al[i], part[i], s);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float rs = rstd[t * N + i];
+      const float dz = al[i] * (part[i] - s);
+      const float z = rs * part[N + i];
+      c1[i] = uniform(dz * rs);                 // coefficient of w_d in dx and of x_id in dw
+      c2[i] = uniform(c1[i] * z * rs * inv_d);  // coefficient of x_id in dx
+      al[i] = uniform(al[i]);
+    }
+
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float gf[8], wr[8], dwr[8];
+      unpack8(g[k], gf);
+      load8(wl, sl.slot[k], wr);
+      load8(dwl, sl.slot[k], dwr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        float f[8], d[8];
+        unpack8(x[i][k], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          d[e] = fmaf(-c2[i], f[e], fmaf(c1[i], wr[e], al[i] * gf[e]));
+          dwr[e] = fmaf(c1[i], f[e], dwr[e]);
+        }
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dsrc + ((int64_t)i * T + t) * D, (uint32_t)D * 2u);
+        bstore(rd, sl.off[k], pack8(d));
+      }
+      store8(dwl, sl.slot[k], dwr);
+    }
+
+    if (++t == te) {  // chunk done: publish its dw partial row, start the next chunk
+      const __amdgpu_buffer_rsrc_t rw = rsrc(ws + c * D, (uint32_t)D * 4u);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        bstore(rw, 2u * sl.off[k], __builtin_bit_cast(uint4, dwl[2 * sl.slot[k]]));
+        bstore(rw, 2u * sl.off[k] + 16u, __builtin_bit_cast(uint4, dwl[2 * sl.slot[k] + 1]));
+        store8(dwl, sl.slot[k], zero8);
+      }
+      c += G;
+      if (c >= P) break;
+      t = c * T / P;
+      te = (c + 1) * T / P;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dw stage 2: dw[d] = sum_{p<P} ws[p][d], fixed order
+// ---------------------------------------------------------------------------
+// Workgroup of kReduceWaves waves covers 4*64 = 256 consecutive columns (one
+// float4 per lane); wave q sums rows p = q, q + kReduceWaves, ... in increasing
+// order, then thread group 0 adds the wave sums in wave order.
+constexpr int kReduceWaves = 16;
+
+__global__ void __launch_bounds__(kReduceWaves * kWave) dw_reduce_kernel(const float4* __restrict__ ws, int32_t P,
+                                                                          int32_t D4, float4* __restrict__ dw) {
+  __shared__ float4 part[kReduceWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int q = threadIdx.x / kWave;
+  const int c = blockIdx.x * kWave + lane;  // float4 column
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < D4) {
+    for (int p = q; p < P; p += kReduceWaves) {
+      const float4 v = ws[(int64_t)p * D4 + c];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+  }
+  part[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && c < D4) {
+    float4 t = part[0][lane];
+    for (int r = 1; r < kReduceWaves; ++r) {
+      const float4 v = part[r][lane];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    dw[c] = t;
+  }
+}
+
+__global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct LaunchShape {
+  int vpt;      // 16-byte vectors per thread per row
+  int threads;  // workgroup size
+  size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
+};
+
+// Depends only on D: the per-token reduction tree must not change with T.
+// D <= 8192: one vector per thread and a prefetched second register set;
+// D <= 16384: two vectors per thread, no prefetch (registers).
+LaunchShape shape_for(int32_t D) {
+  const int V = D / 8;
+  LaunchShape s;
+  s.vpt = V > 1024 ? 2 : 1;
+  const int need = (V + s.vpt - 1) / s.vpt;
+  s.threads = ((need + kWave - 1) / kWave) * kWave;
+  s.lds = (size_t)s.vpt * (size_t)s.threads * 32;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool sizes_ok(int32_t N, int64_t T, int32_t D) {
+  if (N < 1 || N > ATTNRES_MAX_SOURCES) return false;
+  if (T < 0) return false;
+  if (D < 8 || D > ATTNRES_MAX_D || (D % 8) != 0) return false;
+  // keep every byte offset well inside int64
+  if (T > (INT64_C(1) << 40) / ((int64_t)N * D)) return false;
+  return true;
+}
+
+// Resident workgroups of `fn` on the current device (occupancy x CUs).  The
+// grid only sets how many workgroups share the tokens; results never depend
+// on it.
+hipError_t resident_blocks(const void* fn, int threads, size_t lds, int64_t* out) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  *out = (int64_t)per_cu * cus;
+  return hipSuccess;
+}
+
+struct FwdArgs {
+  const uint16_t* src;
+  const float* w;
+  float eps;
+  int64_t T;
+  int32_t D;
+  uint16_t* out;
+  float* rstd;
+  float* alpha;
+};
+
+struct BwdArgs {
+  const uint16_t* dout;
+  const uint16_t* src;
+  const float* w;
+  const float* rstd;
+  const float* alpha;
+  int64_t T;
+  int32_t D;
+  int32_t P;
+  uint16_t* dsrc;
+  float* ws;
+};
+
+template <int N, int VPT>
+hipError_t launch_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  constexpr bool kPipe = VPT == 1;
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, kPipe>);
+  int64_t res = 0;
+  hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);
+  if (e != hipSuccess) return e;
+  const int64_t grid = a.T < res ? a.T : res;
+  hipLaunchKernelGGL((fwd_kernel<N, VPT, kPipe>), dim3((unsigned)grid), dim3((unsigned)s.threads), s.lds, st,
+                     a.src, a.w, a.eps, a.T, a.D, a.out, a.rstd, a.alpha);
+  return hipGetLastError();
+}
+
+template <int N, int VPT>
+hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
+  constexpr bool kPipe = VPT == 1;
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, kPipe>);
+  int64_t res = 0;
+  hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);
+  if (e != hipSuccess) return e;
+  const int64_t grid = a.P < res ? a.P : res;
+  hipLaunchKernelGGL((bwd_kernel<N, VPT, kPipe>), dim3((unsigned)grid), dim3((unsigned)s.threads), 2 * s.lds, st,
+                     a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
+  return hipGetLastError();
+}
+
+template <int VPT>
+hipError_t dispatch_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  switch (N) {
+    case 1: return launch_fwd_n<1, VPT>(s, st, a);
+    case 2: return launch_fwd_n<2, VPT>(s, st, a);
+    case 3: return launch_fwd_n<3, VPT>(s, st, a);
+    case 4: return launch_fwd_n<4, VPT>(s, st, a);
+    case 5: return launch_fwd_n<5, VPT>(s, st, a);
+    case 6: return launch_fwd_n<6, VPT>(s, st, a);
+    case 7: return launch_fwd_n<7, VPT>(s, st, a);
+    case 8: return launch_fwd_n<8, VPT>(s, st, a);
+    case 9: return launch_fwd_n<9, VPT>(s, st, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int VPT>
+hipError_t dispatch_bwd(int32_t N, const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
+  switch (N) {
+    case 1: return launch_bwd_n<1, VPT>(s, st, a);
+    case 2: return launch_bwd_n<2, VPT>(s, st, a);
+    case 3: return launch_bwd_n<3, VPT>(s, st, a);
+    case 4: return launch_bwd_n<4, VPT>(s, st, a);
+    case 5: return launch_bwd_n<5, VPT>(s, st, a);
+    case 6: return launch_bwd_n<6, VPT>(s, st, a);
+    case 7: return launch_bwd_n<7, VPT>(s, st, a);
+    case 8: return launch_bwd_n<8, VPT>(s, st, a);
+    case 9: return launch_bwd_n<9, VPT>(s, st, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32_t N, int64_t T,
+                                      int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream) {
+  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (w == nullptr || !aligned(w, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (T == 0) return ATTNRES_OK;
+  if (src == nullptr || out == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(src, 16) || !aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4))
+    return ATTNRES_ERR_INVALID_ARGUMENT;
+  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
+  const Range r_src = range_of(src, (size_t)N * nTD * 2), r_w = range_of(w, (size_t)D * 4);
+  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
+  for (int a = 0; a < 3; ++a) {
+    if (overlap(outs[a], r_src) || overlap(outs[a], r_w)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+
+  const LaunchShape s = shape_for(D);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const FwdArgs a{src, w, eps, T, D, out, rstd, alpha};
+  const hipError_t e = s.vpt == 2 ? dispatch_fwd<2>(N, s, st, a) : dispatch_fwd<1>(N, s, st, a);
+  return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
+extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
+                                      const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (w == nullptr || dw == nullptr || !aligned(w, 16) || !aligned(dw, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (overlap(range_of(dw, (size_t)D * 4), range_of(w, (size_t)D * 4))) return ATTNRES_ERR_INVALID_ARGUMENT;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    const int n4 = D / 4;
+    hipLaunchKernelGGL(zero_kernel, dim3((n4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(dw), n4);
+    return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+  }
+  if (dout == nullptr || src == nullptr || rstd == nullptr || alpha == nullptr || dsrc == nullptr)
+    return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(dout, 16) || !aligned(src, 16) || !aligned(dsrc, 16) || !aligned(rstd, 4) || !aligned(alpha, 4))
+    return ATTNRES_ERR_INVALID_ARGUMENT;
+  const size_t need = ATTNRES_BWD_WORKSPACE_BYTES(D);
+  if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+
+  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
+  const Range ins[5] = {range_of(dout, nTD * 2), range_of(src, (size_t)N * nTD * 2), range_of(w, (size_t)D * 4),
+                        range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
+  const Range outs[3] = {range_of(dsrc, (size_t)N * nTD * 2), range_of(dw, (size_t)D * 4),
+                         range_of(workspace, need)};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 5; ++b)
+      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+
+  const LaunchShape s = shape_for(D);
+  const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
+  float* ws = reinterpret_cast<float*>(workspace);
+  const BwdArgs a{dout, src, w, rstd, alpha, T, D, P, dsrc, ws};
+  hipError_t e = s.vpt == 2 ? dispatch_bwd<2>(N, s, st, a) : dispatch_bwd<1>(N, s, st, a);
+  if (e != hipSuccess) return ATTNRES_ERR_HIP;
+  const int D4 = D / 4;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kWave - 1) / kWave), dim3(kReduceWaves * kWave), 0, st,
+                     reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
+  return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}

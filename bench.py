@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark: Attention Residuals forward + backward on one MI355X.
+
+One step = attnres_fwd + attnres_bwd (every kernel of the operator) over one
+batch of synthetic depth sources that are resident in HBM before timing
+starts.  Default workload: T = 4096 tokens, N = 9 sources, D = 7168 (bf16
+storage, fp32 arithmetic).  Prints one JSON line (rank 0, N = 1 GPU):
+
+  value         tokens/s over the K timed steps (whole job, one GPU)
+  roofline      the dominant call (attnres_bwd) against the 8 TB/s HBM peak,
+                timed with HIP events on the stream the kernels run on
+  cpu_baseline  the fp64 oracle on the host cores, same workload
+
+Flags: --gpus (1 only), --steps, --warmup, --sweep (extra per-T / per-N lines
+with fwd and bwd timed separately and caches flushed between reps),
+--no-cpu-baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "AttnRes fwd+bwd tokens/s and achieved HBM GB/s (% of peak), D=7168 N=9"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_T4096_N9_D7168.json")
+KERNEL_SRC = os.path.join(ROOT, "attention_residuals_depth_amd", "csrc", "attnres.hip")
+
+
+def algo_bytes(T: int, N: int, D: int):
+    """Bytes the operator must move (single pass, nothing materialised beyond
+    the outputs): fwd reads sources and writes out + rstd + alpha; bwd reads
+    sources, dout, rstd, alpha and writes dsources.  Per-call extras: w read
+    (4D per call), the dw partial rows written and read back (2 * 4 * P * D)
+    and dw itself (4D)."""
+    fwd = T * (2 * N * D + 2 * D + 8 * N)
+    bwd = T * (4 * N * D + 2 * D + 8 * N)
+    P = min(T, 512)
+    fwd_extra = 4 * D
+    bwd_extra = 4 * D + 8 * P * D + 4 * D
+    return fwd, bwd, fwd_extra, bwd_extra
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per bwd call from the committed rocprofv3 counter runs, only
+    while the kernel source is the one the counters were taken on."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+def make_inputs(wl, torch, dev):
+    import numpy as np
+
+    src = torch.empty((wl.N, wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    src.view(torch.int16).copy_(torch.from_numpy(wl.sources().view(np.int16)))
+    dout = torch.empty((wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    dout.view(torch.int16).copy_(torch.from_numpy(wl.dout().view(np.int16)))
+    w = torch.from_numpy(wl.w()).to(dev)
+    return src, w, dout
+
+
+def cpu_baseline(wl):
+    """The oracle, as it stands, on the host cores: fwd + bwd of the whole
+    workload (T tokens), timed with a monotonic clock."""
+    import ctypes
+
+    import oracle
+
+    src = wl.sources()
+    w = wl.w()
+    dout = wl.dout()
+    try:
+        cores = int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except OSError:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.fwd(src, w, wl.eps)
+    oracle.bwd(src, w, wl.eps, dout)
+    dt = time.perf_counter() - t0
+    return {"value": wl.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload: fwd+bwd of all {wl.T} tokens (N={wl.N}, D={wl.D}) in fp64, {dt:.2f} s"}
+
+
+def copy_probe(torch, dev, nbytes=2 << 30, reps=10):
+    """Plain device-to-device copy of a known size: measured HBM copy rate."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def timed_steps(ar, torch, src, w, dout, eps, bufs, K):
+    out, rstd, alpha, dsrc, dw, ws = bufs
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(K):
+        ev[k][0].record()
+        ar.attnres_fwd(src, w, eps, out=out, rstd=rstd, alpha=alpha)
+        ev[k][1].record()
+        ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws)
+        ev[k][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    return total_ms, wall, fwd_ms, bwd_ms
+
+
+def alloc_buffers(ar, torch, N, T, D, dev):
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dsrc = torch.empty((N, T, D), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((D,), dtype=torch.float32, device=dev)
+    ws = torch.empty((ar.workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    return out, rstd, alpha, dsrc, dw, ws
+
+
+def sweep(ar, torch, dev, reps=20):
+    """Per-T (N=9) and per-N (T=32768) lines, fwd and bwd timed separately,
+    caches flushed (a 512 MiB write) between reps; inputs are device-side
+    random bf16 of the workload's scales (values do not affect timing)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    D = 7168
+    cases = [(9, T) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
+    cases += [(N, 32768) for N in range(2, 9)]
+    for N, T in cases:
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        scale = torch.sqrt(1 + 12 * torch.arange(N, device=dev, dtype=torch.float32)).view(N, 1, 1)
+        src = (torch.randn((N, T, D), device=dev, generator=g) * scale).to(torch.bfloat16)
+        dout = torch.randn((T, D), device=dev, generator=g).to(torch.bfloat16)
+        w = torch.randn(D, device=dev, generator=g) / D ** 0.5
+        bufs = alloc_buffers(ar, torch, N, T, D, dev)
+        out, rstd, alpha, dsrc, dw, ws = bufs
+        f_ms, b_ms = [], []
+        for r in range(reps + 3):
+            flush.zero_()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            ar.attnres_fwd(src, w, 1e-6, out=out, rstd=rstd, alpha=alpha)
+            e[1].record()
+            flush.zero_()
+            e2 = torch.cuda.Event(enable_timing=True)
+            e2.record()
+            ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws)
+            e[2].record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                f_ms.append(e[0].elapsed_time(e[1]))
+                b_ms.append(e2.elapsed_time(e[2]))
+        f = sorted(f_ms)[len(f_ms) // 2]
+        b = sorted(b_ms)[len(b_ms) // 2]
+        fb, bb, fe, be = algo_bytes(T, N, D)
+        line = {"sweep": True, "N": N, "T": T, "D": D, "fwd_ms": f, "bwd_ms": b,
+                "fwd_GBps": (fb + fe) / f / 1e6, "bwd_GBps": (bb + be) / b / 1e6,
+                "fwdbwd_tokens_per_s": T / ((f + b) * 1e-3),
+                "fwdbwd_GBps": (fb + bb + fe + be) / (f + b) / 1e6,
+                "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (f + b) / 1e6 / HBM_PEAK_GBPS}
+        print(json.dumps(line), flush=True)
+        del src, dout, w, bufs, out, rstd, alpha, dsrc, dw, ws
+        torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the operator is token-local and this build has no "
+              "multi-GPU path (--gpus must be 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import attention_residuals_depth_amd as ar
+    import synth
+
+    dev = torch.device("cuda:0")
+    ar.library()
+    wl = synth.workload(1)  # T=4096, N=9, D=7168
+    T, N, D = wl.T, wl.N, wl.D
+    src, w, dout = make_inputs(wl, torch, dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    bufs = alloc_buffers(ar, torch, N, T, D, dev)
+
+    timed_steps(ar, torch, src, w, dout, wl.eps, bufs, max(args.warmup, 1))
+    total_ms, wall, fwd_ms, bwd_ms = timed_steps(ar, torch, src, w, dout, wl.eps, bufs, args.steps)
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+
+    ms_step = total_ms / args.steps
+    fb, bb, fe, be = algo_bytes(T, N, D)
+    step_gbps = (fb + bb + fe + be) / (ms_step * 1e-3) / 1e9
+    bwd_gbps = (bb + be) / (bwd_ms * 1e-3) / 1e9
+    fwd_gbps = (fb + fe) / (fwd_ms * 1e-3) / 1e9
+    traffic = load_traffic()
+    copy_gbps = copy_probe(torch, dev)
+
+    result = {
+        "metric": METRIC,
+        "value": T * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "f32",
+        "data": "synthetic (seeded; sources N(0,1)*sqrt(1+12i), w N(0,1/sqrt(D)), dout N(0,1))",
+        "config": {"workload": wl.name, "T": T, "N": N, "D": D, "eps": wl.eps, "parallelism": "single GPU"},
+        "achieved_GBps": step_gbps,
+        "hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_GBps": fwd_gbps,
+        "wall_s_timed": wall,
+        "peak_alloc_GiB": peak_gib,
+        "copy_probe_GBps": copy_gbps,
+        "roofline": {
+            "kernel": "attnres_bwd (bwd_kernel + dw_reduce_kernel, one call)",
+            "bound": "hbm",
+            "achieved": bwd_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": bwd_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic["bytes_per_call"] if traffic else None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    if args.sweep:
+        del src, dout, bufs
+        torch.cuda.empty_cache()
+        sweep(ar, torch, dev)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+/*
+ * libattnres -- Attention Residuals (depth mixing) forward and backward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator (formula box of the architecture figure in "Kimi K3 模型结构
+ * （10）：RL 与服务中的状态管理"): before each sub-layer, every token mixes up to
+ * nine depth sources -- the token embedding, the sum of each completed
+ * 12-layer block, and the current block's partial sum -- with weights
+ *
+ *     alpha = softmax_i( w_l . RMSNorm(x_i) )
+ *
+ * where w_l is the sub-layer's learnable pseudo-query, and returns
+ * out = sum_i alpha_i x_i.  Per token t and source i (D = hidden size):
+ *
+ *     rstd[t][i]  = 1 / sqrt( (1/D) sum_d x[i][t][d]^2 + eps )
+ *     z_i         = rstd[t][i] * sum_d w[d] x[i][t][d]
+ *     alpha[t][i] = exp(z_i - max_j z_j) / sum_k exp(z_k - max_j z_j)
+ *     out[t][d]   = sum_i alpha[t][i] x[i][t][d]
+ *
+ * The normalisation has no gain and the weighted sum uses the raw sources.
+ * The section on Attention Residuals in "Kimi K3 on Fireworks: Fast RL at
+ * frontier scale" motivates fusing the normalisation and the weighted sum so
+ * that no per-source intermediate reaches memory; these calls materialise
+ * only out, rstd and alpha (forward) and dsources, dw (backward).
+ *
+ * Conventions for both calls
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *   - Layouts are dense and row-major: sources/dsources [N][T][D]
+ *     (source-major), out/dout [T][D], rstd/alpha [T][N] (token-major).
+ *   - Every pointer is a device pointer owned by the caller.  The library
+ *     allocates nothing, frees nothing, never synchronises and keeps no state
+ *     between calls; it is reentrant.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL selects the null stream) and the call returns once
+ *     the work is enqueued.
+ *   - Outputs are overwritten, never accumulated.  Inputs are not modified.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error the call returns a non-zero status and enqueues nothing.
+ *   - Results for one token depend only on that token's inputs (and w): they
+ *     are bitwise independent of T, of the token's position in the batch and
+ *     of the run.  dw is bitwise reproducible for a given (T, N, D).
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTNRES_OK = 0,
+  ATTNRES_ERR_INVALID_ARGUMENT = 1, /* bad size, null/misaligned/overlapping pointer, bad eps */
+  ATTNRES_ERR_WORKSPACE = 2,        /* backward workspace missing or too small */
+  ATTNRES_ERR_HIP = 3               /* the HIP runtime refused a launch */
+} attnres_status;
+
+/* At most nine depth sources per token (architecture figure, same page). */
+#define ATTNRES_MAX_SOURCES 9
+/* Largest hidden size the kernels accept (a row group lives on chip). */
+#define ATTNRES_MAX_D 16384
+/* Rows of per-workgroup dw partial sums in the backward workspace. */
+#define ATTNRES_DW_PARTIALS 512
+/* Bytes of device workspace attnres_bwd needs for hidden size D. */
+#define ATTNRES_BWD_WORKSPACE_BYTES(D) ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float))
+
+/*
+ * Forward.
+ *   src   [N][T][D] bf16   depth sources, row (i, t) at src + (i*T + t)*D
+ *   w     [D]       fp32   pseudo-query of this sub-layer
+ *   eps             fp32   finite, >= 0; added to the mean square inside the root
+ *   N               1 .. ATTNRES_MAX_SOURCES
+ *   T               >= 0 tokens (T == 0 enqueues nothing and returns OK)
+ *   D               8 .. ATTNRES_MAX_D, a multiple of 8
+ *   out   [T][D]    bf16   sum_i alpha_i x_i, fp32-accumulated, rounded to nearest even
+ *   rstd  [T][N]    fp32   saved for the backward pass
+ *   alpha [T][N]    fp32   saved for the backward pass
+ * Alignment: src, w, out 16-byte aligned; rstd, alpha 4-byte aligned.
+ * Pointers other than w may be NULL when T == 0.  Outputs must not overlap
+ * each other or the inputs.
+ */
+attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                           uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
+ * Backward of L = sum_{t,d} dout[t][d] * out[t][d]:
+ *   dsrc[i][t][d] = alpha_i g_d + dz_i rstd_i (w_d - z_i rstd_i x_id / D)
+ *   dw[d]         = sum over t and i of dz_i rstd_i x_id
+ * with g = dout[t], da_i = g . x_i, dz_i = alpha_i (da_i - sum_j alpha_j da_j)
+ * and z_i = rstd_i (w . x_i) recomputed from the sources (eps enters only
+ * through the saved rstd).
+ *   dout  [T][D]    bf16   output gradient
+ *   src, w                 as passed to attnres_fwd
+ *   rstd, alpha [T][N] fp32 as written by attnres_fwd for these inputs
+ *   dsrc  [N][T][D] bf16   gradient of every source (overwritten)
+ *   dw    [D]       fp32   gradient of w summed over all T tokens (overwritten;
+ *                          zero-filled when T == 0)
+ *   workspace              device scratch of at least
+ *                          ATTNRES_BWD_WORKSPACE_BYTES(D) bytes, 16-byte
+ *                          aligned; contents on entry are ignored and on exit
+ *                          unspecified.  May be NULL when T == 0.
+ * Alignment: dout, src, w, dsrc, dw, workspace 16-byte aligned; rstd, alpha
+ * 4-byte aligned.  dsrc, dw and the workspace must not overlap each other or
+ * any input.  Status ATTNRES_ERR_WORKSPACE if the workspace is NULL or
+ * smaller than required while T > 0.
+ */
+attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
+                           const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

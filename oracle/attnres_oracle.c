@@ -41,7 +41,7 @@
 
 /* Tokens whose dw contributions are summed together before the chunks are
  * added in chunk order; fixed, so dw does not depend on the thread count. */
-#define DW_CHUNK 256
+#define DW_CHUNK 32
 
 /* ---- one token ---------------------------------------------------------- */
 

@@ -13,7 +13,9 @@
  *
  * Normal variates: Box-Muller (Box and Muller, 1958) on one 64-bit draw split
  * into two 24-bit uniforms in (0, 1); counter 2p yields the cosine branch and
- * counter 2p+1 the sine branch of pair p.  The variate is formed in double,
+ * counter 2p+1 the sine branch of pair p.  log, sin and cos are short series
+ * in plain double arithmetic (no C library calls), so the bytes do not depend
+ * on the host's libm.  The variate is formed in double,
  * narrowed to fp32, multiplied by the fp32 scale (and, for outlier channels,
  * by the fp32 channel multiplier), then rounded to bf16 with
  * round-to-nearest-even.
@@ -49,15 +51,54 @@ void synth_uniform_f64(double* dst, int64_t n, uint64_t seed, uint64_t stream, i
   for (int64_t k = 0; k < n; ++k) dst[k] = (double)(draw(key, (uint64_t)(c0 + k)) >> 11) * 0x1.0p-53;
 }
 
+/* Natural log of x > 0 (finite, normal): x = m 2^e with m in [sqrt(1/2), sqrt(2)),
+ * log m = 2 atanh(s), s = (m - 1)/(m + 1), |s| <= 0.1716; the odd series to
+ * s^11 leaves a relative error below 1e-11.  Plain arithmetic, so the values do
+ * not depend on the C library. */
+static inline double log_pos(double x) {
+  uint64_t b;
+  memcpy(&b, &x, 8);
+  int e = (int)((b >> 52) & 0x7FF) - 1023;
+  b = (b & 0x000FFFFFFFFFFFFFULL) | 0x3FF0000000000000ULL;
+  double m;
+  memcpy(&m, &b, 8);
+  if (m > 1.4142135623730951) {
+    m *= 0.5;
+    e += 1;
+  }
+  const double s = (m - 1.0) / (m + 1.0), s2 = s * s;
+  const double p =
+      s * (2.0 + s2 * (2.0 / 3 + s2 * (2.0 / 5 + s2 * (2.0 / 7 + s2 * (2.0 / 9 + s2 * (2.0 / 11))))));
+  return p + (double)e * 0.69314718055994530942;
+}
+
+/* cos and sin of 2 pi u for u in [0, 1): quadrant q = round(4u), remainder
+ * r = 2 pi (u - q/4) in [-pi/4, pi/4], Taylor series to r^14 / r^13. */
+static inline void sincos_turn(double u, double* c, double* s) {
+  const int q = (int)(u * 4.0 + 0.5);
+  const double r = 6.283185307179586476925286766559 * (u - 0.25 * (double)q), r2 = r * r;
+  const double sr = r * (1.0 - r2 / 6 * (1.0 - r2 / 20 * (1.0 - r2 / 42 * (1.0 - r2 / 72 * (1.0 - r2 / 110 *
+                                                                                           (1.0 - r2 / 156))))));
+  const double cr = 1.0 - r2 / 2 * (1.0 - r2 / 12 * (1.0 - r2 / 30 * (1.0 - r2 / 56 * (1.0 - r2 / 90 *
+                                                                                        (1.0 - r2 / 132)))));
+  switch (q & 3) {
+    case 0: *c = cr; *s = sr; break;
+    case 1: *c = -sr; *s = cr; break;
+    case 2: *c = -cr; *s = -sr; break;
+    default: *c = sr; *s = -cr; break;
+  }
+}
+
 /* Both normals of pair p (counters 2p and 2p+1), in double. */
 static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
   const uint64_t b = draw(key, p);
   const double u1 = ((double)(b >> 40) + 0.5) * 0x1.0p-24;
   const double u2 = ((double)(b & 0xFFFFFFULL) + 0.5) * 0x1.0p-24;
-  const double r = sqrt(-2.0 * log(u1));
-  const double th = 6.283185307179586476925286766559 * u2;
-  *z0 = r * cos(th);
-  *z1 = r * sin(th);
+  const double r = sqrt(-2.0 * log_pos(u1));
+  double c, sn;
+  sincos_turn(u2, &c, &sn);
+  *z0 = r * c;
+  *z1 = r * sn;
 }
 
 /* Standard normal for counter c, in double. */

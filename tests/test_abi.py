@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports what include/attnres.h
+declares, agrees with the binding's constants, and rejects bad arguments on the
+host before any HIP call (every call here has at least one invalid argument,
+so no device work is ever attempted)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_residuals_depth_amd as ar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+OK, INVALID, WORKSPACE, HIP = 0, 1, 2, 3
+D = 7168
+A = 1 << 20  # fake, 16-byte aligned "device addresses"; never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^attnres_status\s+(attnres_\w+)\s*\(", text, re.M)
+
+
+def _define(name):
+    m = re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_library_loads_and_exports_declared_symbols():
+    lib = ar.library()
+    names = _declared()
+    assert names == ["attnres_fwd", "attnres_bwd"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert not any(s.startswith("oracle_") for s in exported), "the product library must not carry oracle code"
+
+
+def test_library_is_built_for_gfx950():
+    # the offload bundle of a library built here names its target triple
+    blob = open(ar.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_header_constants_match_binding():
+    assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
+    assert _define("ATTNRES_MAX_D") == ar.MAX_D
+    assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
+    assert ar.workspace_bytes(D) == ar.DW_PARTIALS * D * 4
+
+
+def _fwd(src=A, w=2 * A, eps=1e-6, N=9, T=16, D_=D, out=None, rstd=None, alpha=None):
+    base = 1 << 36
+    out = base if out is None else out
+    rstd = base + (1 << 30) if rstd is None else rstd
+    alpha = base + (1 << 31) if alpha is None else alpha
+    return ar.library().attnres_fwd(src, w, eps, N, T, D_, out, rstd, alpha, None)
+
+
+def _bwd(dout=None, src=None, w=None, rstd=None, alpha=None, N=9, T=16, D_=D, dsrc=None, dw=None, ws=None,
+         ws_bytes=None):
+    g = 1 << 30
+    vals = dict(dout=1 * g, src=2 * g, w=3 * g, rstd=4 * g, alpha=5 * g, dsrc=8 * g, dw=12 * g, ws=13 * g)
+    for k, v in dict(dout=dout, src=src, w=w, rstd=rstd, alpha=alpha, dsrc=dsrc, dw=dw, ws=ws).items():
+        if v is not None:
+            vals[k] = v
+    if ws_bytes is None:
+        ws_bytes = ar.workspace_bytes(D_)
+    return ar.library().attnres_bwd(vals["dout"], vals["src"], vals["w"], vals["rstd"], vals["alpha"], N, T, D_,
+                                    vals["dsrc"], vals["dw"], vals["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(N=10), dict(N=-1), dict(T=-1), dict(D_=0), dict(D_=7),
+                                dict(D_=7172), dict(D_=ar.MAX_D + 8), dict(D_=-8), dict(eps=-1e-6),
+                                dict(eps=float("nan")), dict(eps=float("inf")), dict(w=0), dict(src=0),
+                                dict(out=0), dict(rstd=0), dict(alpha=0), dict(src=A + 8), dict(w=2 * A + 4),
+                                dict(out=(1 << 36) + 2), dict(rstd=(1 << 36) + (1 << 30) + 2),
+                                dict(T=1 << 40)],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+def test_fwd_rejects(kw):
+    assert _fwd(**kw) == INVALID
+
+
+def test_fwd_rejects_overlap():
+    # out starting inside src
+    assert _fwd(src=A, out=A + 16 * D) == INVALID
+    # rstd overlapping alpha
+    assert _fwd(rstd=1 << 38, alpha=(1 << 38) + 64) == INVALID
+    # alpha overlapping w
+    assert _fwd(alpha=2 * A) == INVALID
+
+
+def test_fwd_T0_is_a_host_no_op():
+    # nothing to do: returns before touching HIP; per-token pointers may be NULL
+    assert _fwd(T=0, src=0, out=0, rstd=0, alpha=0) == OK
+    # but w must still be valid
+    assert _fwd(T=0, w=0) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(N=10), dict(T=-5), dict(D_=12), dict(D_=ar.MAX_D + 8),
+                                dict(dout=0), dict(src=0), dict(w=0), dict(rstd=0), dict(alpha=0), dict(dsrc=0),
+                                dict(dw=0), dict(dout=(1 << 30) + 8), dict(dsrc=(8 << 30) + 4),
+                                dict(dw=(12 << 30) + 4), dict(ws=(13 << 30) + 8), dict(rstd=(4 << 30) + 1)],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+def test_bwd_rejects(kw):
+    assert _bwd(**kw) == INVALID
+
+
+def test_bwd_workspace_errors():
+    assert _bwd(ws=0) == WORKSPACE
+    assert _bwd(ws_bytes=ar.workspace_bytes(D) - 1) == WORKSPACE
+
+
+def test_bwd_rejects_aliasing():
+    g = 1 << 30
+    assert _bwd(dsrc=2 * g) == INVALID  # dsrc == src
+    assert _bwd(dsrc=g) == INVALID  # dsrc over dout
+    assert _bwd(ws=2 * g + 64) == INVALID  # workspace inside src
+    assert _bwd(dw=3 * g) == INVALID  # dw == w
+    assert _bwd(dw=8 * g + 1024) == INVALID  # dw inside dsrc
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    src = torch.zeros(2, 3, 8, dtype=torch.bfloat16)
+    w = torch.zeros(8)
+    with pytest.raises(ValueError):
+        ar.attnres_fwd(src, w, 1e-6)

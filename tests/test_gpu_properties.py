@@ -1,0 +1,134 @@
+"""GPU properties that need no oracle: bitwise determinism, batch invariance,
+exact special cases, empty batches and error paths through the binding."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import synth
+from parity import DEV, run_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _inputs(wl):
+    return (to_dev_bf16(wl.sources()), torch.from_numpy(wl.w()).to(DEV), to_dev_bf16(wl.dout()))
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
+
+
+def test_bitwise_deterministic():
+    wl = synth.workload(1)
+    src, w, dout = _inputs(wl)
+    a = run_gpu(src, w, wl.eps, dout)
+    b = run_gpu(src, w, wl.eps, dout)
+    for x, y, name in zip(a, b, ["out", "rstd", "alpha", "dsrc", "dw"]):
+        assert torch.equal(_bits(x), _bits(y)), f"{name} differs between runs"
+
+
+def test_batch_invariance():
+    """A token's outputs do not depend on the batch around it or its position."""
+    small = synth.workload(1, T=128)
+    big = synth.workload(1, T=4096)
+    s_src, w, s_dout = _inputs(small)
+    b_src, _, b_dout = _inputs(big)
+    k = 1111  # embed the small batch at an odd offset
+    b_src[:, k:k + 128] = s_src
+    b_dout[k:k + 128] = s_dout
+    so, sr, sa, sd, _ = run_gpu(s_src, w, small.eps, s_dout)
+    bo, br, ba, bd, _ = run_gpu(b_src, w, big.eps, b_dout)
+    assert torch.equal(_bits(so), _bits(bo[k:k + 128]))
+    assert torch.equal(_bits(sr), _bits(br[k:k + 128]))
+    assert torch.equal(_bits(sa), _bits(ba[k:k + 128]))
+    assert torch.equal(_bits(sd), _bits(bd[:, k:k + 128]))
+
+
+def test_zero_query_gives_uniform_weights_and_mean():
+    wl = synth.workload(1, T=64)
+    src, _, dout = _inputs(wl)
+    w0 = torch.zeros(wl.D, device=DEV)
+    out, rstd, alpha, dsrc, dw = run_gpu(src, w0, wl.eps, dout)
+    assert torch.all(alpha == torch.tensor(1.0 / 9.0, dtype=torch.float32))
+    mean = src.float().mean(0)
+    assert torch.allclose(out.float(), mean, rtol=8e-3, atol=1e-2)
+    # z = 0 and w = 0, so each source receives exactly alpha * dout (one fp32 product) before rounding
+    ref = (dout.float() * alpha[:, 3:4]).to(torch.bfloat16)
+    assert torch.equal(_bits(dsrc[3]), _bits(ref))
+
+
+def test_identical_sources_reproduce_the_source():
+    wl = synth.workload(1, T=96)
+    src, w, dout = _inputs(wl)
+    same = src[4:5].expand(9, -1, -1).contiguous()
+    out, rstd, alpha, dsrc, dw = run_gpu(same, w, wl.eps, dout)
+    assert torch.equal(_bits(out), _bits(same[0]))
+    assert torch.allclose(alpha.sum(1), torch.ones(96, device=DEV), atol=1e-6)
+    assert float(dw.abs().max()) < 1e-3 * float(dout.float().abs().max())
+
+
+def test_single_source():
+    wl = synth.workload(1, T=50, N=1)
+    src, w, dout = _inputs(wl)
+    out, rstd, alpha, dsrc, dw = run_gpu(src, w, wl.eps, dout)
+    assert torch.all(alpha == 1.0)
+    assert torch.equal(_bits(out), _bits(src[0]))
+    assert torch.equal(_bits(dsrc[0]), _bits(dout))
+    assert float(dw.abs().max()) == 0.0
+
+
+def test_empty_batch():
+    D = 7168
+    src = torch.empty((9, 0, D), dtype=torch.bfloat16, device=DEV)
+    w = torch.randn(D, device=DEV)
+    dout = torch.empty((0, D), dtype=torch.bfloat16, device=DEV)
+    out, rstd, alpha = ar.attnres_fwd(src, w, 1e-6)
+    assert out.shape == (0, D) and rstd.shape == (0, 9)
+    dw = torch.full((D,), 7.0, device=DEV)
+    dsrc, dw = ar.attnres_bwd(dout, src, w, rstd, alpha, dw=dw)
+    torch.cuda.synchronize()
+    assert float(dw.abs().max()) == 0.0
+
+
+def test_errors_raise_and_write_nothing():
+    D = 7168
+    src = torch.zeros((10, 4, D), dtype=torch.bfloat16, device=DEV)  # N = 10 > 9
+    w = torch.zeros(D, device=DEV)
+    out = torch.full((4, D), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ar.AttnResError) as ei:
+        ar.attnres_fwd(src, w, 1e-6, out=out)
+    assert ei.value.code == 1
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    src9 = torch.zeros((9, 4, D), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ar.AttnResError):
+        ar.attnres_fwd(src9, w, float("nan"))
+    o, r, a = ar.attnres_fwd(src9, w, 1e-6)
+    small_ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ar.AttnResError) as ei:
+        ar.attnres_bwd(torch.zeros((4, D), dtype=torch.bfloat16, device=DEV), src9, w, r, a, workspace=small_ws)
+    assert ei.value.code == 2
+
+
+def test_stream_argument_is_honoured():
+    wl = synth.workload(1, T=256)
+    src, w, dout = _inputs(wl)
+    ref = run_gpu(src, w, wl.eps, dout)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out, rstd, alpha = ar.attnres_fwd(src, w, wl.eps)
+        dsrc, dw = ar.attnres_bwd(dout, src, w, rstd, alpha)
+    s.synchronize()
+    for x, y in zip(ref, (out, rstd, alpha, dsrc, dw)):
+        assert torch.equal(_bits(x), _bits(y))

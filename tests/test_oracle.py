@@ -94,7 +94,7 @@ def _rel(a, b):
 
 def pin_torch_route(orc):
     fails = []
-    # T = 300 spans more than one of the oracle's fixed dw chunks
+    # T = 300 spans several of the oracle's fixed dw chunks
     for seed, (N, T, D, eps) in enumerate([(1, 3, 16, 1e-6), (2, 4, 24, 0.1), (3, 5, 32, 1e-6),
                                           (5, 300, 16, 1e-6), (9, 6, 64, 1e-3), (9, 2, 8, 0.0)]):
         r = _rng(100 + seed)
