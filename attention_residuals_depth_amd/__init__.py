@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libattnres.so")
 
 MAX_SOURCES = 9
 MAX_D = 16384
-DW_PARTIALS = 512
+DW_PARTIALS = 256
 
 STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARGUMENT", 2: "ATTNRES_ERR_WORKSPACE", 3: "ATTNRES_ERR_HIP"}
 

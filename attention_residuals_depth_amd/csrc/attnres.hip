@@ -93,12 +93,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Cache policy of the streaming accesses (sources, dout, out, dsources): each
+// byte is touched once per call, so loads and stores carry the nontemporal
+// hint (aux bit 1, "nt"); small reused data (w, dw rows) uses the default.
+#ifndef ATTNRES_STREAM_LOAD_AUX
+#define ATTNRES_STREAM_LOAD_AUX 2
+#endif
+#ifndef ATTNRES_STREAM_STORE_AUX
+#define ATTNRES_STREAM_STORE_AUX 2
+#endif
+constexpr int kAuxDefault = 0;
+constexpr int kAuxStreamLoad = ATTNRES_STREAM_LOAD_AUX;
+constexpr int kAuxStreamStore = ATTNRES_STREAM_STORE_AUX;
+
+template <int AUX = kAuxDefault>
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
 }
 
+template <int AUX = kAuxDefault>
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, AUX);
 }
 
 // ---------------------------------------------------------------------------
@@ -180,7 +195,16 @@ __device__ __forceinline__ void clear_red(float (*red)[K][kMaxWaves]) {
 // (unpacked floats) are recomputed after a barrier instead of being kept live
 // across it: holding 8 unpacked floats per packed vector would double the
 // register footprint of a row group.
-__device__ __forceinline__ void opaque(uint4& q) { asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w)); }
+__device__ __forceinline__ void opaque(uint4& q) {
+  u32x4_t v = __builtin_bit_cast(u32x4_t, q);
+  asm volatile("" : "+v"(v));  // one 128-bit operand: the register tuple stays whole
+  q = __builtin_bit_cast(uint4, v);
+}
+
+// Keep the scheduler from moving instructions across this point: prefetch
+// loads must stay where they are issued, before the next token's work, or the
+// in-order wait counts would make a token wait for loads issued after it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Move a wave-uniform value into a scalar register (frees a VGPR per value).
 __device__ __forceinline__ float uniform(float v) {
@@ -235,135 +259,213 @@ __device__ __forceinline__ void stage_w(const float* __restrict__ w, int32_t D, 
 }
 
 // This thread's slice of token t's N source rows.  Row (i, t) starts at
-// src + (i*T + t)*D; its descriptor is built in scalar registers.
+// src + (i*T + t)*D; its descriptor is built in scalar registers.  With
+// valid == false the descriptors have size 0: every lane reads zeros and no
+// memory is touched, but the instructions are still issued.  Keeping the
+// number of loads independent of the path lets the compiler's wait counts
+// stay exact (only the oldest outstanding loads are waited for).
 template <int N, int VPT>
 __device__ __forceinline__ void load_rows(uint4 (&x)[N][VPT], const uint16_t* __restrict__ src, int64_t T,
-                                          int64_t t, int32_t D, const Slice<VPT>& sl) {
+                                          int64_t t, int32_t D, const Slice<VPT>& sl, bool valid = true) {
+  const int64_t tt = valid ? t : 0;
+  const uint32_t bytes = valid ? (uint32_t)D * 2u : 0u;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((int64_t)i * T + t) * D, (uint32_t)D * 2u);
+    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((int64_t)i * T + tt) * D, bytes);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) x[i][k] = bload(r, sl.off[k]);
+    for (int k = 0; k < VPT; ++k) x[i][k] = bload<kAuxStreamLoad>(r, sl.off[k]);
   }
 }
 
 template <int VPT>
 __device__ __forceinline__ void load_row(uint4 (&g)[VPT], const uint16_t* __restrict__ p, int64_t t, int32_t D,
-                                         const Slice<VPT>& sl) {
-  const __amdgpu_buffer_rsrc_t r = rsrc(p + t * D, (uint32_t)D * 2u);
+                                         const Slice<VPT>& sl, bool valid = true) {
+  const int64_t tt = valid ? t : 0;
+  const __amdgpu_buffer_rsrc_t r = rsrc(p + tt * D, valid ? (uint32_t)D * 2u : 0u);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) g[k] = bload(r, sl.off[k]);
+  for (int k = 0; k < VPT; ++k) g[k] = bload<kAuxStreamLoad>(r, sl.off[k]);
+}
+
+// Token t's saved softmax weight and rstd, lane i holding source i (lanes >= N
+// read zeros).  Loaded with the row group, so they complete in the same order.
+template <int N>
+__device__ __forceinline__ void load_saved(float& a, float& r, const float* __restrict__ alpha,
+                                           const float* __restrict__ rstd, int64_t t, int lane, bool valid = true) {
+  const int64_t tt = valid ? t : 0;
+  const uint32_t bytes = valid ? (uint32_t)N * 4u : 0u;
+  a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(alpha + tt * N, bytes), lane * 4, 0, 0));
+  r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(rstd + tt * N, bytes), lane * 4, 0, 0));
+}
+
+__device__ __forceinline__ float lane_value(float v, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
 }
 
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
+// Largest workgroup of a kernel variant: a prefetching two-vector variant keeps
+// two row groups per thread, so it is limited to 512 threads (two waves per
+// SIMD, up to 256 VGPRs each); the others take up to 1024 threads.
+template <int VPT, bool PIPE>
+constexpr int max_threads() {
+  return (PIPE && VPT == 2) ? 512 : 1024;
+}
+
+struct FwdCtx {
+  const uint16_t* src;
+  int64_t T;
+  int32_t D;
+  float eps;
+  float inv_d;
+  uint16_t* out;
+  float* rstd_out;
+  float* alpha_out;
+  const float4* wl;
+  float (*red)[kMaxWaves];  // red[buf * 2N + k][wave]
+  int tid, lane, wave;
+};
+
+// Forward of token t whose row group is already in x: partial sums, workgroup
+// reduction, softmax, weighted sum, stores.  Issues no loads of its own.
+template <int N, int VPT>
+__device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& buf, const FwdCtx& c,
+                                          const Slice<VPT>& sl) {
+  // partial sum of squares (first N) and w.x (last N)
+  float part[2 * N];
+#pragma unroll
+  for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float wr[8];
+    load8(c.wl, sl.slot[k], wr);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float f[8];
+      unpack8(x[i][k], f);
+      part[i] = dot8_bf16(x[i][k], x[i][k], part[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
+    }
+  }
+  block_sums<2 * N>(part, c.red + buf * 2 * N, c.lane, c.wave);
+  buf ^= 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) opaque(x[i][k]);
+
+  // rstd, scores, softmax over the sources (fp32, max-subtracted)
+  float r[N], a[N];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    r[i] = uniform(1.0f / sqrtf(part[i] * c.inv_d + c.eps));
+    a[i] = r[i] * part[N + i];  // z_i
+    m = fmaxf(m, a[i]);
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a[i] = expf(a[i] - m);
+    den += a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = uniform(a[i] / den);
+
+  // weighted sum of the raw sources
+  const __amdgpu_buffer_rsrc_t ro = rsrc(c.out + t * c.D, (uint32_t)c.D * 2u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float acc[8];
+    {
+      float f[8];
+      unpack8(x[0][k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = a[0] * f[e];
+    }
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      float f[8];
+      unpack8(x[i][k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(a[i], f[e], acc[e]);
+    }
+    bstore<kAuxStreamStore>(ro, sl.off[k], pack8(acc));
+  }
+  if (c.tid < N) {
+    float rv = r[0], av = a[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      rv = c.tid == i ? r[i] : rv;
+      av = c.tid == i ? a[i] : av;
+    }
+    c.rstd_out[t * N + c.tid] = rv;
+    c.alpha_out[t * N + c.tid] = av;
+  }
+}
+
 // Persistent: workgroup b handles tokens b, b + G, b + 2G, ... (G = gridDim.x).
-// With PIPE, the next token's row group is loaded into a second register set
-// while the current one is reduced and summed, so HBM latency overlaps the
-// barrier and the arithmetic.  Dynamic LDS holds w.
+// With PIPE, two register sets A and B alternate: while the workgroup works on
+// the token in one set, the loads of the next token are in flight in the
+// other, and a set is refilled with the token two steps ahead as soon as its
+// token is done -- so up to two tokens' loads overlap one token's arithmetic.
+// Dynamic LDS holds w.
 template <int N, int VPT, bool PIPE>
-__global__ void __launch_bounds__(1024) fwd_kernel(const uint16_t* __restrict__ src, const float* __restrict__ w,
-                                                   float eps, int64_t T, int32_t D, uint16_t* __restrict__ out,
-                                                   float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
+__global__ void __launch_bounds__((max_threads<VPT, PIPE>())) fwd_kernel(const uint16_t* __restrict__ src,
+                                                                         const float* __restrict__ w, float eps,
+                                                                         int64_t T, int32_t D,
+                                                                         uint16_t* __restrict__ out,
+                                                                         float* __restrict__ rstd_out,
+                                                                         float* __restrict__ alpha_out) {
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
-  float4* wl = dyn_lds;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const Slice<VPT> sl(tid, blockDim.x);
-  stage_w<VPT>(w, D, wl, sl);
+  FwdCtx c;
+  c.src = src;
+  c.T = T;
+  c.D = D;
+  c.eps = eps;
+  c.inv_d = 1.0f / (float)D;
+  c.out = out;
+  c.rstd_out = rstd_out;
+  c.alpha_out = alpha_out;
+  c.wl = dyn_lds;
+  c.red = &red[0][0];
+  c.tid = threadIdx.x;
+  c.lane = c.tid & (kWave - 1);
+  c.wave = c.tid / kWave;
+  const Slice<VPT> sl(c.tid, blockDim.x);
+  stage_w<VPT>(w, D, dyn_lds, sl);
   clear_red<2 * N>(red);
 
   const int64_t G = gridDim.x;
-  const float inv_d = 1.0f / (float)D;
   int buf = 0;
-  uint4 xn[N][VPT];
-  if (PIPE && (int64_t)blockIdx.x < T) load_rows<N, VPT>(xn, src, T, blockIdx.x, D, sl);
-  for (int64_t t = blockIdx.x; t < T; t += G) {
-    uint4 x[N][VPT];
-    if (PIPE) {
-#pragma unroll
-      for (int i = 0; i < N; ++i)
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) x[i][k] = xn[i][k];
-      if (t + G < T) load_rows<N, VPT>(xn, src, T, t + G, D, sl);
-    } else {
+  if (PIPE) {
+    uint4 xa[N][VPT], xb[N][VPT];
+    int64_t t = blockIdx.x;
+    load_rows<N, VPT>(xa, src, T, t, D, sl);  // host guarantees gridDim.x <= T
+    sched_fence();
+    load_rows<N, VPT>(xb, src, T, t + G, D, sl, t + G < T);
+    sched_fence();
+    while (true) {
+      fwd_token<N, VPT>(xa, t, buf, c, sl);
+      sched_fence();
+      load_rows<N, VPT>(xa, src, T, t + 2 * G, D, sl, t + 2 * G < T);
+      sched_fence();
+      t += G;
+      if (t >= T) break;
+      fwd_token<N, VPT>(xb, t, buf, c, sl);
+      sched_fence();
+      load_rows<N, VPT>(xb, src, T, t + 2 * G, D, sl, t + 2 * G < T);
+      sched_fence();
+      t += G;
+      if (t >= T) break;
+    }
+  } else {
+    for (int64_t t = blockIdx.x; t < T; t += G) {
+      uint4 x[N][VPT];
       load_rows<N, VPT>(x, src, T, t, D, sl);
-    }
-
-    // partial sum of squares (first N) and w.x (last N)
-    float part[2 * N];
-#pragma unroll
-    for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float wr[8];
-      load8(wl, sl.slot[k], wr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float f[8];
-        unpack8(x[i][k], f);
-        part[i] = dot8_bf16(x[i][k], x[i][k], part[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
-      }
-    }
-    block_sums<2 * N>(part, red[buf], lane, wave);
-    buf ^= 1;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) opaque(x[i][k]);
-
-    // rstd, scores, softmax over the sources (fp32, max-subtracted)
-    float r[N], a[N];
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      r[i] = uniform(1.0f / sqrtf(part[i] * inv_d + eps));
-      a[i] = r[i] * part[N + i];  // z_i
-      m = fmaxf(m, a[i]);
-    }
-    float den = 0.f;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      a[i] = expf(a[i] - m);
-      den += a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = uniform(a[i] / den);
-
-    // weighted sum of the raw sources
-    const __amdgpu_buffer_rsrc_t ro = rsrc(out + t * D, (uint32_t)D * 2u);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float acc[8];
-      {
-        float f[8];
-        unpack8(x[0][k], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = a[0] * f[e];
-      }
-#pragma unroll
-      for (int i = 1; i < N; ++i) {
-        float f[8];
-        unpack8(x[i][k], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(a[i], f[e], acc[e]);
-      }
-      bstore(ro, sl.off[k], pack8(acc));
-    }
-    if (tid < N) {
-      float rv = r[0], av = a[0];
-#pragma unroll
-      for (int i = 1; i < N; ++i) {
-        rv = tid == i ? r[i] : rv;
-        av = tid == i ? a[i] : av;
-      }
-      rstd_out[t * N + tid] = rv;
-      alpha_out[t * N + tid] = av;
+      fwd_token<N, VPT>(x, t, buf, c, sl);
     }
   }
 }
@@ -371,156 +473,206 @@ __global__ void __launch_bounds__(1024) fwd_kernel(const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Backward: dsources and dw partial rows
 // ---------------------------------------------------------------------------
-// The tokens are cut into P fixed chunks, chunk c = [c*T/P, (c+1)*T/P); each
-// chunk sums its dw contributions in token order into partial row ws[c][:].
-// Workgroup b handles chunks b, b + G, ... (G = gridDim.x <= P), so dw does not
-// depend on the grid.  With PIPE the next token's sources and dout are loaded
-// while the current token is processed.  Dynamic LDS holds w and the running
-// dw of the current chunk, in the thread's private slots.
+// The tokens are cut into P fixed chunks: with q = T / P and r = T % P, chunk
+// c = [begin(c), begin(c + 1)) with begin(c) = c*q + min(c, r) (the first r
+// chunks hold one extra token).  Workgroup c handles chunk c and sums its dw
+// contributions in token order into partial row ws[c][:]; dw therefore does
+// not depend on how many workgroups are resident at once.
+__device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t T, int64_t P) {
+  const int64_t q = T / P, r = T - (T / P) * P;
+  return c * q + (c < r ? c : r);
+}
+
+struct BwdCtx {
+  const uint16_t* dout;
+  const uint16_t* src;
+  const float* rstd;
+  const float* alpha;
+  int64_t T;
+  int32_t D;
+  float inv_d;
+  uint16_t* dsrc;
+  const float4* wl;
+  float4* dwl;
+  float (*red)[kMaxWaves];
+  int lane, wave;
+};
+
+// Backward of token t whose sources and dout are already in x and g:
+// g.x_i and w.x_i, workgroup reduction, softmax backward, dsources stores and
+// this chunk's running dw (LDS).  Issues no loads of the row group.
+template <int N, int VPT>
+__device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], float sa, float sr, int64_t t,
+                                          int& buf, const BwdCtx& c, const Slice<VPT>& sl) {
+  // partial g.x_i (first N) and w.x_i (last N)
+  float part[2 * N];
+#pragma unroll
+  for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float wr[8];
+    load8(c.wl, sl.slot[k], wr);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float f[8];
+      unpack8(x[i][k], f);
+      part[i] = dot8_bf16(g[k], x[i][k], part[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
+    }
+  }
+  block_sums<2 * N>(part, c.red + buf * 2 * N, c.lane, c.wave);
+  buf ^= 1;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    opaque(g[k]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) opaque(x[i][k]);
+  }
+
+  // softmax backward: s = sum_j alpha_j da_j; dz_i = alpha_i (da_i - s)
+  float al[N], c1[N], c2[N];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    al[i] = lane_value(sa, i);
+    s = fmaf(al[i], part[i], s);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float rs = lane_value(sr, i);
+    const float dz = al[i] * (part[i] - s);
+    const float z = rs * part[N + i];
+    c1[i] = uniform(dz * rs);                   // coefficient of w_d in dx and of x_id in dw
+    c2[i] = uniform(c1[i] * z * rs * c.inv_d);  // coefficient of x_id in dx
+    al[i] = uniform(al[i]);
+  }
+
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float gf[8], wr[8], dwr[8];
+    unpack8(g[k], gf);
+    load8(c.wl, sl.slot[k], wr);
+    load8(c.dwl, sl.slot[k], dwr);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float f[8], d[8];
+      unpack8(x[i][k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        d[e] = fmaf(-c2[i], f[e], fmaf(c1[i], wr[e], al[i] * gf[e]));
+        dwr[e] = fmaf(c1[i], f[e], dwr[e]);
+      }
+      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc + ((int64_t)i * c.T + t) * c.D, (uint32_t)c.D * 2u);
+      bstore<kAuxStreamStore>(rd, sl.off[k], pack8(d));
+    }
+    store8(c.dwl, sl.slot[k], dwr);
+  }
+}
+
+// Publish this workgroup's dw partial row (its chunk's sum).
+template <int VPT>
+__device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, int32_t D, const float4* dwl,
+                                           const Slice<VPT>& sl) {
+  const __amdgpu_buffer_rsrc_t rw = rsrc(ws + ch * D, (uint32_t)D * 4u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    bstore(rw, 2u * sl.off[k], __builtin_bit_cast(uint4, dwl[2 * sl.slot[k]]));
+    bstore(rw, 2u * sl.off[k] + 16u, __builtin_bit_cast(uint4, dwl[2 * sl.slot[k] + 1]));
+  }
+}
+
+// With PIPE, register sets A and B alternate as in the forward kernel, each
+// refilled with the token two steps ahead (in workgroup order) once its token
+// is done.  Dynamic LDS holds w and the running dw of the current chunk, in
+// the thread's private slots.
 template <int N, int VPT, bool PIPE>
-__global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ src,
-                                                   const float* __restrict__ w, const float* __restrict__ rstd,
-                                                   const float* __restrict__ alpha, int64_t T, int32_t D, int32_t P,
-                                                   uint16_t* __restrict__ dsrc, float* __restrict__ ws) {
+__global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const uint16_t* __restrict__ dout,
+                                                                         const uint16_t* __restrict__ src,
+                                                                         const float* __restrict__ w,
+                                                                         const float* __restrict__ rstd,
+                                                                         const float* __restrict__ alpha, int64_t T,
+                                                                         int32_t D, int32_t P,
+                                                                         uint16_t* __restrict__ dsrc,
+                                                                         float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
-  float4* wl = dyn_lds;
-  float4* dwl = dyn_lds + 2 * VPT * (int)blockDim.x;
+  BwdCtx c;
+  c.dout = dout;
+  c.src = src;
+  c.rstd = rstd;
+  c.alpha = alpha;
+  c.T = T;
+  c.D = D;
+  c.inv_d = 1.0f / (float)D;
+  c.dsrc = dsrc;
+  c.wl = dyn_lds;
+  c.dwl = dyn_lds + 2 * VPT * (int)blockDim.x;
+  c.red = &red[0][0];
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  c.lane = tid & (kWave - 1);
+  c.wave = tid / kWave;
   const int64_t G = gridDim.x;
   const Slice<VPT> sl(tid, blockDim.x);
-  stage_w<VPT>(w, D, wl, sl);
+  stage_w<VPT>(w, D, dyn_lds, sl);
   const float zero8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) store8(dwl, sl.slot[k], zero8);
+  for (int k = 0; k < VPT; ++k) store8(c.dwl, sl.slot[k], zero8);
   clear_red<2 * N>(red);
 
-  const float inv_d = 1.0f / (float)D;
   int buf = 0;
-
-  int64_t c = blockIdx.x;  // host guarantees gridDim.x <= P <= T, so every chunk is non-empty
-  int64_t t = c * T / P;
-  int64_t te = (c + 1) * T / P;
-  uint4 xn[N][VPT], gn[VPT];
+  const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
+  const int64_t t0 = chunk_begin(ch, T, P), t1 = chunk_begin(ch + 1, T, P);
   if (PIPE) {
-    load_row<VPT>(gn, dout, t, D, sl);
-    load_rows<N, VPT>(xn, src, T, t, D, sl);
-  }
-  while (true) {
-    uint4 x[N][VPT], g[VPT];
-    if (PIPE) {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        g[k] = gn[k];
-#pragma unroll
-        for (int i = 0; i < N; ++i) x[i][k] = xn[i][k];
-      }
-      // the token after t: next in this chunk, else first of chunk c + G
-      int64_t tn = t + 1;
-      bool more = true;
-      if (tn == te) {
-        more = c + G < P;
-        tn = (c + G) * T / P;
-      }
-      if (more) {
-        load_row<VPT>(gn, dout, tn, D, sl);
-        load_rows<N, VPT>(xn, src, T, tn, D, sl);
-      }
-    } else {
+    uint4 xa[N][VPT], xb[N][VPT], ga[VPT], gb[VPT];
+    float saa, sra, sab, srb;
+    int64_t t = t0;
+    load_row<VPT>(ga, dout, t, D, sl);
+    load_rows<N, VPT>(xa, src, T, t, D, sl);
+    load_saved<N>(saa, sra, alpha, rstd, t, c.lane);
+    sched_fence();
+    load_row<VPT>(gb, dout, t + 1, D, sl, t + 1 < t1);
+    load_rows<N, VPT>(xb, src, T, t + 1, D, sl, t + 1 < t1);
+    load_saved<N>(sab, srb, alpha, rstd, t + 1, c.lane, t + 1 < t1);
+    sched_fence();
+    while (true) {
+      bwd_token<N, VPT>(xa, ga, saa, sra, t, buf, c, sl);
+      sched_fence();
+      load_row<VPT>(ga, dout, t + 2, D, sl, t + 2 < t1);
+      load_rows<N, VPT>(xa, src, T, t + 2, D, sl, t + 2 < t1);
+      load_saved<N>(saa, sra, alpha, rstd, t + 2, c.lane, t + 2 < t1);
+      sched_fence();
+      if (++t >= t1) break;
+      bwd_token<N, VPT>(xb, gb, sab, srb, t, buf, c, sl);
+      sched_fence();
+      load_row<VPT>(gb, dout, t + 2, D, sl, t + 2 < t1);
+      load_rows<N, VPT>(xb, src, T, t + 2, D, sl, t + 2 < t1);
+      load_saved<N>(sab, srb, alpha, rstd, t + 2, c.lane, t + 2 < t1);
+      sched_fence();
+      if (++t >= t1) break;
+    }
+  } else {
+    for (int64_t t = t0; t < t1; ++t) {
+      uint4 x[N][VPT], g[VPT];
+      float sa, sr;
       load_row<VPT>(g, dout, t, D, sl);
       load_rows<N, VPT>(x, src, T, t, D, sl);
-    }
-
-    // partial g.x_i (first N) and w.x_i (last N)
-    float part[2 * N];
-#pragma unroll
-    for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float wr[8];
-      load8(wl, sl.slot[k], wr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float f[8];
-        unpack8(x[i][k], f);
-        part[i] = dot8_bf16(g[k], x[i][k], part[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
-      }
-    }
-    block_sums<2 * N>(part, red[buf], lane, wave);
-    buf ^= 1;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      opaque(g[k]);
-#pragma unroll
-      for (int i = 0; i < N; ++i) opaque(x[i][k]);
-    }
-
-    // softmax backward: s = sum_j alpha_j da_j; dz_i = alpha_i (da_i - s)
-    float al[N], c1[N], c2[N];
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      al[i] = alpha[t * N + i];
-      s = fmaf(al[i], part[i], s);
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const float rs = rstd[t * N + i];
-      const float dz = al[i] * (part[i] - s);
-      const float z = rs * part[N + i];
-      c1[i] = uniform(dz * rs);                 // coefficient of w_d in dx and of x_id in dw
-      c2[i] = uniform(c1[i] * z * rs * inv_d);  // coefficient of x_id in dx
-      al[i] = uniform(al[i]);
-    }
-
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float gf[8], wr[8], dwr[8];
-      unpack8(g[k], gf);
-      load8(wl, sl.slot[k], wr);
-      load8(dwl, sl.slot[k], dwr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float f[8], d[8];
-        unpack8(x[i][k], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          d[e] = fmaf(-c2[i], f[e], fmaf(c1[i], wr[e], al[i] * gf[e]));
-          dwr[e] = fmaf(c1[i], f[e], dwr[e]);
-        }
-        const __amdgpu_buffer_rsrc_t rd = rsrc(dsrc + ((int64_t)i * T + t) * D, (uint32_t)D * 2u);
-        bstore(rd, sl.off[k], pack8(d));
-      }
-      store8(dwl, sl.slot[k], dwr);
-    }
-
-    if (++t == te) {  // chunk done: publish its dw partial row, start the next chunk
-      const __amdgpu_buffer_rsrc_t rw = rsrc(ws + c * D, (uint32_t)D * 4u);
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        bstore(rw, 2u * sl.off[k], __builtin_bit_cast(uint4, dwl[2 * sl.slot[k]]));
-        bstore(rw, 2u * sl.off[k] + 16u, __builtin_bit_cast(uint4, dwl[2 * sl.slot[k] + 1]));
-        store8(dwl, sl.slot[k], zero8);
-      }
-      c += G;
-      if (c >= P) break;
-      t = c * T / P;
-      te = (c + 1) * T / P;
+      load_saved<N>(sa, sr, alpha, rstd, t, c.lane);
+      bwd_token<N, VPT>(x, g, sa, sr, t, buf, c, sl);
     }
   }
+  publish_dw<VPT>(ws, ch, D, c.dwl, sl);
 }
 
 // ---------------------------------------------------------------------------
 // dw stage 2: dw[d] = sum_{p<P} ws[p][d], fixed order
 // ---------------------------------------------------------------------------
-// Workgroup of kReduceWaves waves covers 4*64 = 256 consecutive columns (one
-// float4 per lane); wave q sums rows p = q, q + kReduceWaves, ... in increasing
-// order, then thread group 0 adds the wave sums in wave order.
+// A workgroup covers 64 float4 columns (lane = column, 1 KiB per row per
+// wave).  Wave q sums rows q*R .. q*R + R-1 (R = kReduceRows, all loads issued
+// before the adds) in increasing order; wave 0 then adds the kReduceWaves wave
+// sums in wave order.  Requires P <= kReduceWaves * kReduceRows.
 constexpr int kReduceWaves = 16;
+constexpr int kReduceRows = ATTNRES_DW_PARTIALS / kReduceWaves;
 
 __global__ void __launch_bounds__(kReduceWaves * kWave) dw_reduce_kernel(const float4* __restrict__ ws, int32_t P,
                                                                           int32_t D4, float4* __restrict__ dw) {
@@ -528,20 +680,25 @@ __global__ void __launch_bounds__(kReduceWaves * kWave) dw_reduce_kernel(const f
   const int lane = threadIdx.x & (kWave - 1);
   const int q = threadIdx.x / kWave;
   const int c = blockIdx.x * kWave + lane;  // float4 column
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < D4) {
-    for (int p = q; p < P; p += kReduceWaves) {
-      const float4 v = ws[(int64_t)p * D4 + c];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
+  const bool col_ok = c < D4;
+  float4 v[kReduceRows];
+#pragma unroll
+  for (int j = 0; j < kReduceRows; ++j) {
+    const int p = q * kReduceRows + j;
+    v[j] = (col_ok && p < P) ? ws[(int64_t)p * D4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 s = v[0];
+#pragma unroll
+  for (int j = 1; j < kReduceRows; ++j) {
+    s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
   }
   part[q][lane] = s;
   __syncthreads();
-  if (q == 0 && c < D4) {
+  if (q == 0 && col_ok) {
     float4 t = part[0][lane];
     for (int r = 1; r < kReduceWaves; ++r) {
-      const float4 v = part[r][lane];
-      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+      const float4 u = part[r][lane];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
     dw[c] = t;
   }
@@ -557,17 +714,28 @@ __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
 // ---------------------------------------------------------------------------
 struct LaunchShape {
   int vpt;      // 16-byte vectors per thread per row
+  bool pipe;    // prefetch the next token's rows into a second register set
   int threads;  // workgroup size
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
+#ifndef ATTNRES_SMALL_D_VPT
+#define ATTNRES_SMALL_D_VPT 2
+#endif
+
 // Depends only on D: the per-token reduction tree must not change with T.
-// D <= 8192: one vector per thread and a prefetched second register set;
+// D <= 8192: prefetching variant, ATTNRES_SMALL_D_VPT vectors per thread;
 // D <= 16384: two vectors per thread, no prefetch (registers).
 LaunchShape shape_for(int32_t D) {
   const int V = D / 8;
   LaunchShape s;
-  s.vpt = V > 1024 ? 2 : 1;
+  if (V <= 1024) {
+    s.vpt = ATTNRES_SMALL_D_VPT;
+    s.pipe = true;
+  } else {
+    s.vpt = 2;
+    s.pipe = false;
+  }
   const int need = (V + s.vpt - 1) / s.vpt;
   s.threads = ((need + kWave - 1) / kWave) * kWave;
   s.lds = (size_t)s.vpt * (size_t)s.threads * 32;
@@ -636,9 +804,8 @@ struct BwdArgs {
   float* ws;
 };
 
-template <int N, int VPT>
+template <int N, int VPT, bool kPipe>
 hipError_t launch_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  constexpr bool kPipe = VPT == 1;
   const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, kPipe>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);
@@ -649,49 +816,58 @@ hipError_t launch_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) 
   return hipGetLastError();
 }
 
-template <int N, int VPT>
+template <int N, int VPT, bool kPipe>
 hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  constexpr bool kPipe = VPT == 1;
   const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, kPipe>);
   int64_t res = 0;
-  hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);
+  hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
-  const int64_t grid = a.P < res ? a.P : res;
-  hipLaunchKernelGGL((bwd_kernel<N, VPT, kPipe>), dim3((unsigned)grid), dim3((unsigned)s.threads), 2 * s.lds, st,
+  // one workgroup per dw chunk (P = min(T, ATTNRES_DW_PARTIALS))
+  hipLaunchKernelGGL((bwd_kernel<N, VPT, kPipe>), dim3((unsigned)a.P), dim3((unsigned)s.threads), 2 * s.lds, st,
                      a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();
 }
 
-template <int VPT>
+template <int VPT, bool PIPE>
 hipError_t dispatch_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
   switch (N) {
-    case 1: return launch_fwd_n<1, VPT>(s, st, a);
-    case 2: return launch_fwd_n<2, VPT>(s, st, a);
-    case 3: return launch_fwd_n<3, VPT>(s, st, a);
-    case 4: return launch_fwd_n<4, VPT>(s, st, a);
-    case 5: return launch_fwd_n<5, VPT>(s, st, a);
-    case 6: return launch_fwd_n<6, VPT>(s, st, a);
-    case 7: return launch_fwd_n<7, VPT>(s, st, a);
-    case 8: return launch_fwd_n<8, VPT>(s, st, a);
-    case 9: return launch_fwd_n<9, VPT>(s, st, a);
+    case 1: return launch_fwd_n<1, VPT, PIPE>(s, st, a);
+    case 2: return launch_fwd_n<2, VPT, PIPE>(s, st, a);
+    case 3: return launch_fwd_n<3, VPT, PIPE>(s, st, a);
+    case 4: return launch_fwd_n<4, VPT, PIPE>(s, st, a);
+    case 5: return launch_fwd_n<5, VPT, PIPE>(s, st, a);
+    case 6: return launch_fwd_n<6, VPT, PIPE>(s, st, a);
+    case 7: return launch_fwd_n<7, VPT, PIPE>(s, st, a);
+    case 8: return launch_fwd_n<8, VPT, PIPE>(s, st, a);
+    case 9: return launch_fwd_n<9, VPT, PIPE>(s, st, a);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int VPT>
+template <int VPT, bool PIPE>
 hipError_t dispatch_bwd(int32_t N, const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
   switch (N) {
-    case 1: return launch_bwd_n<1, VPT>(s, st, a);
-    case 2: return launch_bwd_n<2, VPT>(s, st, a);
-    case 3: return launch_bwd_n<3, VPT>(s, st, a);
-    case 4: return launch_bwd_n<4, VPT>(s, st, a);
-    case 5: return launch_bwd_n<5, VPT>(s, st, a);
-    case 6: return launch_bwd_n<6, VPT>(s, st, a);
-    case 7: return launch_bwd_n<7, VPT>(s, st, a);
-    case 8: return launch_bwd_n<8, VPT>(s, st, a);
-    case 9: return launch_bwd_n<9, VPT>(s, st, a);
+    case 1: return launch_bwd_n<1, VPT, PIPE>(s, st, a);
+    case 2: return launch_bwd_n<2, VPT, PIPE>(s, st, a);
+    case 3: return launch_bwd_n<3, VPT, PIPE>(s, st, a);
+    case 4: return launch_bwd_n<4, VPT, PIPE>(s, st, a);
+    case 5: return launch_bwd_n<5, VPT, PIPE>(s, st, a);
+    case 6: return launch_bwd_n<6, VPT, PIPE>(s, st, a);
+    case 7: return launch_bwd_n<7, VPT, PIPE>(s, st, a);
+    case 8: return launch_bwd_n<8, VPT, PIPE>(s, st, a);
+    case 9: return launch_bwd_n<9, VPT, PIPE>(s, st, a);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t run_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  if (!s.pipe) return dispatch_fwd<2, false>(N, s, st, a);
+  return s.vpt == 2 ? dispatch_fwd<ATTNRES_SMALL_D_VPT, true>(N, s, st, a) : dispatch_fwd<1, true>(N, s, st, a);
+}
+
+hipError_t run_bwd(int32_t N, const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
+  if (!s.pipe) return dispatch_bwd<2, false>(N, s, st, a);
+  return s.vpt == 2 ? dispatch_bwd<ATTNRES_SMALL_D_VPT, true>(N, s, st, a) : dispatch_bwd<1, true>(N, s, st, a);
 }
 
 }  // namespace
@@ -717,7 +893,7 @@ extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float
   const LaunchShape s = shape_for(D);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const FwdArgs a{src, w, eps, T, D, out, rstd, alpha};
-  const hipError_t e = s.vpt == 2 ? dispatch_fwd<2>(N, s, st, a) : dispatch_fwd<1>(N, s, st, a);
+  const hipError_t e = run_fwd(N, s, st, a);
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
@@ -757,7 +933,7 @@ extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src,
   const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
   float* ws = reinterpret_cast<float*>(workspace);
   const BwdArgs a{dout, src, w, rstd, alpha, T, D, P, dsrc, ws};
-  hipError_t e = s.vpt == 2 ? dispatch_bwd<2>(N, s, st, a) : dispatch_bwd<1>(N, s, st, a);
+  hipError_t e = run_bwd(N, s, st, a);
   if (e != hipSuccess) return ATTNRES_ERR_HIP;
   const int D4 = D / 4;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kWave - 1) / kWave), dim3(kReduceWaves * kWave), 0, st,

@@ -42,7 +42,7 @@ def algo_bytes(T: int, N: int, D: int):
     and dw itself (4D)."""
     fwd = T * (2 * N * D + 2 * D + 8 * N)
     bwd = T * (4 * N * D + 2 * D + 8 * N)
-    P = min(T, 512)
+    P = min(T, 256)
     fwd_extra = 4 * D
     bwd_extra = 4 * D + 8 * P * D + 4 * D
     return fwd, bwd, fwd_extra, bwd_extra

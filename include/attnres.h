@@ -61,7 +61,7 @@ typedef enum {
 /* Largest hidden size the kernels accept (a row group lives on chip). */
 #define ATTNRES_MAX_D 16384
 /* Rows of per-workgroup dw partial sums in the backward workspace. */
-#define ATTNRES_DW_PARTIALS 512
+#define ATTNRES_DW_PARTIALS 256
 /* Bytes of device workspace attnres_bwd needs for hidden size D. */
 #define ATTNRES_BWD_WORKSPACE_BYTES(D) ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float))
 
