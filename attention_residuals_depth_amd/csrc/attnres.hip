@@ -667,24 +667,27 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const u
 // ---------------------------------------------------------------------------
 // dw stage 2: dw[d] = sum_{p<P} ws[p][d], fixed order
 // ---------------------------------------------------------------------------
-// A workgroup covers 64 float4 columns (lane = column, 1 KiB per row per
-// wave).  Wave q sums rows q*R .. q*R + R-1 (R = kReduceRows, all loads issued
-// before the adds) in increasing order; wave 0 then adds the kReduceWaves wave
-// sums in wave order.  Requires P <= kReduceWaves * kReduceRows.
-constexpr int kReduceWaves = 16;
-constexpr int kReduceRows = ATTNRES_DW_PARTIALS / kReduceWaves;
+// A workgroup of kReduceThreads threads covers kReduceCols consecutive float4
+// columns (256 B of each partial row); thread (c, g) = (tid % kReduceCols, tid / kReduceCols) sums rows
+// g, g + kReduceGroups, g + 2*kReduceGroups, ... in increasing order (all loads
+// issued first), then thread group g = 0 adds the kReduceGroups group sums in
+// group order.  Requires P <= kReduceGroups * kReduceRows.
+constexpr int kReduceCols = 16;
+constexpr int kReduceGroups = 16;
+constexpr int kReduceThreads = kReduceCols * kReduceGroups;
+constexpr int kReduceRows = ATTNRES_DW_PARTIALS / kReduceGroups;
 
-__global__ void __launch_bounds__(kReduceWaves * kWave) dw_reduce_kernel(const float4* __restrict__ ws, int32_t P,
-                                                                          int32_t D4, float4* __restrict__ dw) {
-  __shared__ float4 part[kReduceWaves][kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int q = threadIdx.x / kWave;
-  const int c = blockIdx.x * kWave + lane;  // float4 column
+__global__ void __launch_bounds__(kReduceThreads) dw_reduce_kernel(const float4* __restrict__ ws, int32_t P,
+                                                                    int32_t D4, float4* __restrict__ dw) {
+  __shared__ float4 part[kReduceGroups][kReduceCols];
+  const int cl = threadIdx.x % kReduceCols;
+  const int g = threadIdx.x / kReduceCols;
+  const int c = blockIdx.x * kReduceCols + cl;  // float4 column
   const bool col_ok = c < D4;
   float4 v[kReduceRows];
 #pragma unroll
   for (int j = 0; j < kReduceRows; ++j) {
-    const int p = q * kReduceRows + j;
+    const int p = g + j * kReduceGroups;
     v[j] = (col_ok && p < P) ? ws[(int64_t)p * D4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 s = v[0];
@@ -692,12 +695,13 @@ __global__ void __launch_bounds__(kReduceWaves * kWave) dw_reduce_kernel(const f
   for (int j = 1; j < kReduceRows; ++j) {
     s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
   }
-  part[q][lane] = s;
+  part[g][cl] = s;
   __syncthreads();
-  if (q == 0 && col_ok) {
-    float4 t = part[0][lane];
-    for (int r = 1; r < kReduceWaves; ++r) {
-      const float4 u = part[r][lane];
+  if (g == 0 && col_ok) {
+    float4 t = part[0][cl];
+#pragma unroll
+    for (int r = 1; r < kReduceGroups; ++r) {
+      const float4 u = part[r][cl];
       t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
     dw[c] = t;
@@ -936,7 +940,7 @@ extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src,
   hipError_t e = run_bwd(N, s, st, a);
   if (e != hipSuccess) return ATTNRES_ERR_HIP;
   const int D4 = D / 4;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kWave - 1) / kWave), dim3(kReduceWaves * kWave), 0, st,
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
                      reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
   return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
