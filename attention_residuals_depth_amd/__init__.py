@@ -12,6 +12,9 @@ The C entry points, declared in ``include/attnres.h``:
                 out[T][D] bf16, rstd[T][N] fp32, alpha[T][N] fp32, stream)
     attnres_bwd(dout[T][D] bf16, src, w, rstd, alpha, N, T, D,
                 dsrc[N][T][D] bf16, dw[D] fp32, workspace, workspace_bytes, stream)
+    attnres_fwd_sources / attnres_bwd_sources: the same with the N sources
+                (and their gradients) as separate [T][D] tensors, and an
+                accumulate flag for the source gradients.
 """
 from __future__ import annotations
 
@@ -51,6 +54,11 @@ def library() -> ctypes.CDLL:
         lib.attnres_fwd.restype = ctypes.c_int
         lib.attnres_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
         lib.attnres_bwd.restype = ctypes.c_int
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        lib.attnres_fwd_sources.argtypes = [pp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_sources.restype = ctypes.c_int
+        lib.attnres_bwd_sources.argtypes = [vp, pp, vp, vp, vp, i32, i64, i32, pp, i32, vp, vp, sz, vp]
+        lib.attnres_bwd_sources.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -133,5 +141,81 @@ def attnres_bwd(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: to
     return dsrc, dw
 
 
-__all__ = ["attnres_fwd", "attnres_bwd", "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D",
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _sources(srcs, name):
+    srcs = list(srcs)
+    if not 1 <= len(srcs) <= MAX_SOURCES:
+        raise ValueError(f"{name} must hold 1..{MAX_SOURCES} tensors")
+    if srcs[0].dim() != 2:
+        raise ValueError(f"{name}[i] must be [T][D]")
+    T, D = srcs[0].shape
+    for i, t in enumerate(srcs):
+        _check(t, f"{name}[{i}]", torch.bfloat16, (T, D))
+    return srcs, T, D
+
+
+def attnres_fwd_sources(srcs, w: torch.Tensor, eps: float, out=None, rstd=None, alpha=None, stream=None):
+    """Forward on N separate [T][D] bf16 sources (no stacking copy)."""
+    srcs, T, D = _sources(srcs, "srcs")
+    N = len(srcs)
+    _check(w, "w", torch.float32, (D,))
+    dev = srcs[0].device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if rstd is None:
+        rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    code = library().attnres_fwd_sources(_ptr_array(srcs), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+                                         rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_fwd_sources", code)
+    return out, rstd, alpha
+
+
+def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.Tensor, alpha: torch.Tensor,
+                        dsrcs=None, accumulate: bool = False, dw=None, workspace=None, stream=None):
+    """Backward on N separate sources.  dsrcs: N separate [T][D] bf16 gradient
+    tensors (allocated if None); with accumulate=True the new gradients are
+    added to their contents.  Returns (dsrcs, dw)."""
+    srcs, T, D = _sources(srcs, "srcs")
+    N = len(srcs)
+    _check(dout, "dout", torch.bfloat16, (T, D))
+    _check(w, "w", torch.float32, (D,))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    dev = srcs[0].device
+    if dsrcs is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the gradient tensors to add to")
+        dsrcs = [torch.empty((T, D), dtype=torch.bfloat16, device=dev) for _ in range(N)]
+    dsrcs = list(dsrcs)
+    if len(dsrcs) != N:
+        raise ValueError("dsrcs must hold one tensor per source")
+    for i, t in enumerate(dsrcs):
+        _check(t, f"dsrcs[{i}]", torch.bfloat16, (T, D))
+    if dw is None:
+        dw = torch.empty((D,), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    _check(dw, "dw", torch.float32, (D,))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), w.data_ptr(), rstd.data_ptr(),
+                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), 1 if accumulate else 0,
+                                         dw.data_ptr(), workspace.data_ptr(), ws_bytes, _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_bwd_sources", code)
+    return dsrcs, dw
+
+
+__all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D",
            "DW_PARTIALS", "LIB_PATH"]

@@ -258,20 +258,30 @@ __device__ __forceinline__ void stage_w(const float* __restrict__ w, int32_t D, 
   }
 }
 
-// This thread's slice of token t's N source rows.  Row (i, t) starts at
-// src + (i*T + t)*D; its descriptor is built in scalar registers.  With
-// valid == false the descriptors have size 0: every lane reads zeros and no
-// memory is touched, but the instructions are still issued.  Keeping the
-// number of loads independent of the path lets the compiler's wait counts
-// stay exact (only the oldest outstanding loads are waited for).
-template <int N, int VPT>
-__device__ __forceinline__ void load_rows(uint4 (&x)[N][VPT], const uint16_t* __restrict__ src, int64_t T,
-                                          int64_t t, int32_t D, const Slice<VPT>& sl, bool valid = true) {
+// Per-source row bases: row (i, t) of a [T][D] bf16 tensor starts at p[i] + t*D.
+// Stacked [N][T][D] sources use p[i] = src + i*T*D; separately allocated
+// sources pass their own bases.  Passed by value (kernel arguments).
+struct SrcRows {
+  const uint16_t* p[ATTNRES_MAX_SOURCES];
+};
+struct DstRows {
+  uint16_t* p[ATTNRES_MAX_SOURCES];
+};
+
+// This thread's slice of token t's N source rows; each row's descriptor is
+// built in scalar registers.  With valid == false the descriptors have size 0:
+// every lane reads zeros and no memory is touched, but the instructions are
+// still issued.  Keeping the number of loads independent of the path lets the
+// compiler's wait counts stay exact (only the oldest outstanding loads are
+// waited for).
+template <int N, int VPT, typename Rows>
+__device__ __forceinline__ void load_rows(uint4 (&x)[N][VPT], const Rows& rows, int64_t t, int32_t D,
+                                          const Slice<VPT>& sl, bool valid = true) {
   const int64_t tt = valid ? t : 0;
   const uint32_t bytes = valid ? (uint32_t)D * 2u : 0u;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((int64_t)i * T + tt) * D, bytes);
+    const __amdgpu_buffer_rsrc_t r = rsrc(rows.p[i] + tt * D, bytes);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) x[i][k] = bload<kAuxStreamLoad>(r, sl.off[k]);
   }
@@ -304,16 +314,12 @@ __device__ __forceinline__ float lane_value(float v, int i) {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-// Largest workgroup of a kernel variant: a prefetching two-vector variant keeps
-// two row groups per thread, so it is limited to 512 threads (two waves per
-// SIMD, up to 256 VGPRs each); the others take up to 1024 threads.
-template <int VPT, bool PIPE>
-constexpr int max_threads() {
-  return (PIPE && VPT == 2) ? 512 : 1024;
-}
+// Launch bound MAXT: a prefetching two-vector variant keeps two row groups per
+// thread (and the accumulate variant a row group plus the old gradients), so
+// it is built for at most 512 threads (two waves per SIMD, up to 256 VGPRs
+// each); the others for up to 1024 threads.
 
 struct FwdCtx {
-  const uint16_t* src;
   int64_t T;
   int32_t D;
   float eps;
@@ -411,17 +417,13 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // other, and a set is refilled with the token two steps ahead as soon as its
 // token is done -- so up to two tokens' loads overlap one token's arithmetic.
 // Dynamic LDS holds w.
-template <int N, int VPT, bool PIPE>
-__global__ void __launch_bounds__((max_threads<VPT, PIPE>())) fwd_kernel(const uint16_t* __restrict__ src,
-                                                                         const float* __restrict__ w, float eps,
-                                                                         int64_t T, int32_t D,
-                                                                         uint16_t* __restrict__ out,
-                                                                         float* __restrict__ rstd_out,
-                                                                         float* __restrict__ alpha_out) {
+template <int N, int VPT, bool PIPE, int MAXT>
+__global__ void __launch_bounds__(MAXT) fwd_kernel(SrcRows src, const float* __restrict__ w, float eps, int64_t T,
+                                                   int32_t D, uint16_t* __restrict__ out,
+                                                   float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
   FwdCtx c;
-  c.src = src;
   c.T = T;
   c.D = D;
   c.eps = eps;
@@ -443,20 +445,20 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) fwd_kernel(const u
   if (PIPE) {
     uint4 xa[N][VPT], xb[N][VPT];
     int64_t t = blockIdx.x;
-    load_rows<N, VPT>(xa, src, T, t, D, sl);  // host guarantees gridDim.x <= T
+    load_rows<N, VPT>(xa, src, t, D, sl);  // host guarantees gridDim.x <= T
     sched_fence();
-    load_rows<N, VPT>(xb, src, T, t + G, D, sl, t + G < T);
+    load_rows<N, VPT>(xb, src, t + G, D, sl, t + G < T);
     sched_fence();
     while (true) {
       fwd_token<N, VPT>(xa, t, buf, c, sl);
       sched_fence();
-      load_rows<N, VPT>(xa, src, T, t + 2 * G, D, sl, t + 2 * G < T);
+      load_rows<N, VPT>(xa, src, t + 2 * G, D, sl, t + 2 * G < T);
       sched_fence();
       t += G;
       if (t >= T) break;
       fwd_token<N, VPT>(xb, t, buf, c, sl);
       sched_fence();
-      load_rows<N, VPT>(xb, src, T, t + 2 * G, D, sl, t + 2 * G < T);
+      load_rows<N, VPT>(xb, src, t + 2 * G, D, sl, t + 2 * G < T);
       sched_fence();
       t += G;
       if (t >= T) break;
@@ -464,7 +466,7 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) fwd_kernel(const u
   } else {
     for (int64_t t = blockIdx.x; t < T; t += G) {
       uint4 x[N][VPT];
-      load_rows<N, VPT>(x, src, T, t, D, sl);
+      load_rows<N, VPT>(x, src, t, D, sl);
       fwd_token<N, VPT>(x, t, buf, c, sl);
     }
   }
@@ -484,14 +486,10 @@ __device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t T, int64_t P) 
 }
 
 struct BwdCtx {
-  const uint16_t* dout;
-  const uint16_t* src;
-  const float* rstd;
-  const float* alpha;
   int64_t T;
   int32_t D;
   float inv_d;
-  uint16_t* dsrc;
+  DstRows dsrc;
   const float4* wl;
   float4* dwl;
   float (*red)[kMaxWaves];
@@ -500,8 +498,11 @@ struct BwdCtx {
 
 // Backward of token t whose sources and dout are already in x and g:
 // g.x_i and w.x_i, workgroup reduction, softmax backward, dsources stores and
-// this chunk's running dw (LDS).  Issues no loads of the row group.
-template <int N, int VPT>
+// this chunk's running dw (LDS).  Issues no loads of the row group.  With ACC
+// the old gradients are loaded once the partial sums are formed (so they are
+// in flight during the reduction but not live during the first pass) and the
+// new gradient is added to them in fp32 before rounding.
+template <int N, int VPT, bool ACC>
 __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], float sa, float sr, int64_t t,
                                           int& buf, const BwdCtx& c, const Slice<VPT>& sl) {
   // partial g.x_i (first N) and w.x_i (last N)
@@ -520,6 +521,12 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
     }
+  }
+  uint4 old[ACC ? N : 1][VPT];
+  if constexpr (ACC) {
+    sched_fence();
+    load_rows<N, VPT>(old, c.dsrc, t, c.D, sl);
+    sched_fence();
   }
   block_sums<2 * N>(part, c.red + buf * 2 * N, c.lane, c.wave);
   buf ^= 1;
@@ -563,7 +570,13 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
         d[e] = fmaf(-c2[i], f[e], fmaf(c1[i], wr[e], al[i] * gf[e]));
         dwr[e] = fmaf(c1[i], f[e], dwr[e]);
       }
-      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc + ((int64_t)i * c.T + t) * c.D, (uint32_t)c.D * 2u);
+      if constexpr (ACC) {
+        float o[8];
+        unpack8(old[i][k], o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = o[e] + d[e];
+      }
+      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc.p[i] + t * c.D, (uint32_t)c.D * 2u);
       bstore<kAuxStreamStore>(rd, sl.off[k], pack8(d));
     }
     store8(c.dwl, sl.slot[k], dwr);
@@ -584,24 +597,18 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
 
 // With PIPE, register sets A and B alternate as in the forward kernel, each
 // refilled with the token two steps ahead (in workgroup order) once its token
-// is done.  Dynamic LDS holds w and the running dw of the current chunk, in
-// the thread's private slots.
-template <int N, int VPT, bool PIPE>
-__global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const uint16_t* __restrict__ dout,
-                                                                         const uint16_t* __restrict__ src,
-                                                                         const float* __restrict__ w,
-                                                                         const float* __restrict__ rstd,
-                                                                         const float* __restrict__ alpha, int64_t T,
-                                                                         int32_t D, int32_t P,
-                                                                         uint16_t* __restrict__ dsrc,
-                                                                         float* __restrict__ ws) {
+// is done.  With ACC (no prefetch) the old gradients are loaded with the row
+// group.  Dynamic LDS holds w and the running dw of the current chunk, in the
+// thread's private slots.
+template <int N, int VPT, bool PIPE, bool ACC, int MAXT>
+__global__ void __launch_bounds__(MAXT) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
+                                                   const float* __restrict__ w, const float* __restrict__ rstd,
+                                                   const float* __restrict__ alpha, int64_t T, int32_t D, int32_t P,
+                                                   DstRows dsrc, float* __restrict__ ws) {
+  static_assert(!(PIPE && ACC), "the accumulate variant does not prefetch");
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
   BwdCtx c;
-  c.dout = dout;
-  c.src = src;
-  c.rstd = rstd;
-  c.alpha = alpha;
   c.T = T;
   c.D = D;
   c.inv_d = 1.0f / (float)D;
@@ -612,7 +619,6 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const u
   const int tid = threadIdx.x;
   c.lane = tid & (kWave - 1);
   c.wave = tid / kWave;
-  const int64_t G = gridDim.x;
   const Slice<VPT> sl(tid, blockDim.x);
   stage_w<VPT>(w, D, dyn_lds, sl);
   const float zero8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -628,25 +634,25 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const u
     float saa, sra, sab, srb;
     int64_t t = t0;
     load_row<VPT>(ga, dout, t, D, sl);
-    load_rows<N, VPT>(xa, src, T, t, D, sl);
+    load_rows<N, VPT>(xa, src, t, D, sl);
     load_saved<N>(saa, sra, alpha, rstd, t, c.lane);
     sched_fence();
     load_row<VPT>(gb, dout, t + 1, D, sl, t + 1 < t1);
-    load_rows<N, VPT>(xb, src, T, t + 1, D, sl, t + 1 < t1);
+    load_rows<N, VPT>(xb, src, t + 1, D, sl, t + 1 < t1);
     load_saved<N>(sab, srb, alpha, rstd, t + 1, c.lane, t + 1 < t1);
     sched_fence();
     while (true) {
-      bwd_token<N, VPT>(xa, ga, saa, sra, t, buf, c, sl);
+      bwd_token<N, VPT, false>(xa, ga, saa, sra, t, buf, c, sl);
       sched_fence();
       load_row<VPT>(ga, dout, t + 2, D, sl, t + 2 < t1);
-      load_rows<N, VPT>(xa, src, T, t + 2, D, sl, t + 2 < t1);
+      load_rows<N, VPT>(xa, src, t + 2, D, sl, t + 2 < t1);
       load_saved<N>(saa, sra, alpha, rstd, t + 2, c.lane, t + 2 < t1);
       sched_fence();
       if (++t >= t1) break;
-      bwd_token<N, VPT>(xb, gb, sab, srb, t, buf, c, sl);
+      bwd_token<N, VPT, false>(xb, gb, sab, srb, t, buf, c, sl);
       sched_fence();
       load_row<VPT>(gb, dout, t + 2, D, sl, t + 2 < t1);
-      load_rows<N, VPT>(xb, src, T, t + 2, D, sl, t + 2 < t1);
+      load_rows<N, VPT>(xb, src, t + 2, D, sl, t + 2 < t1);
       load_saved<N>(sab, srb, alpha, rstd, t + 2, c.lane, t + 2 < t1);
       sched_fence();
       if (++t >= t1) break;
@@ -656,9 +662,9 @@ __global__ void __launch_bounds__((max_threads<VPT, PIPE>())) bwd_kernel(const u
       uint4 x[N][VPT], g[VPT];
       float sa, sr;
       load_row<VPT>(g, dout, t, D, sl);
-      load_rows<N, VPT>(x, src, T, t, D, sl);
+      load_rows<N, VPT>(x, src, t, D, sl);
       load_saved<N>(sa, sr, alpha, rstd, t, c.lane);
-      bwd_token<N, VPT>(x, g, sa, sr, t, buf, c, sl);
+      bwd_token<N, VPT, ACC>(x, g, sa, sr, t, buf, c, sl);
     }
   }
   publish_dw<VPT>(ws, ch, D, c.dwl, sl);
@@ -717,32 +723,25 @@ __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
 // Host side
 // ---------------------------------------------------------------------------
 struct LaunchShape {
-  int vpt;      // 16-byte vectors per thread per row
   bool pipe;    // prefetch the next token's rows into a second register set
   int threads;  // workgroup size
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
-#ifndef ATTNRES_SMALL_D_VPT
-#define ATTNRES_SMALL_D_VPT 2
-#endif
+constexpr int kVpt = 2;  // 16-byte vectors per thread per row
 
-// Depends only on D: the per-token reduction tree must not change with T.
-// D <= 8192: prefetching variant, ATTNRES_SMALL_D_VPT vectors per thread;
-// D <= 16384: two vectors per thread, no prefetch (registers).
+// Depends only on D: the per-token reduction tree (two vectors per thread,
+// blockDim = D/16 rounded up to whole waves) never changes with T or with the
+// variant, so every variant gives bitwise the same per-token results.
+// D <= 8192: the prefetching variants (<= 512 threads); D <= 16384: no
+// prefetch (up to 1024 threads).
 LaunchShape shape_for(int32_t D) {
   const int V = D / 8;
   LaunchShape s;
-  if (V <= 1024) {
-    s.vpt = ATTNRES_SMALL_D_VPT;
-    s.pipe = true;
-  } else {
-    s.vpt = 2;
-    s.pipe = false;
-  }
-  const int need = (V + s.vpt - 1) / s.vpt;
+  s.pipe = V <= 2 * 512;
+  const int need = (V + kVpt - 1) / kVpt;
   s.threads = ((need + kWave - 1) / kWave) * kWave;
-  s.lds = (size_t)s.vpt * (size_t)s.threads * 32;
+  s.lds = (size_t)kVpt * (size_t)s.threads * 32;
   return s;
 }
 
@@ -785,7 +784,7 @@ hipError_t resident_blocks(const void* fn, int threads, size_t lds, int64_t* out
 }
 
 struct FwdArgs {
-  const uint16_t* src;
+  SrcRows src;
   const float* w;
   float eps;
   int64_t T;
@@ -797,150 +796,227 @@ struct FwdArgs {
 
 struct BwdArgs {
   const uint16_t* dout;
-  const uint16_t* src;
+  SrcRows src;
   const float* w;
   const float* rstd;
   const float* alpha;
   int64_t T;
   int32_t D;
   int32_t P;
-  uint16_t* dsrc;
+  DstRows dsrc;
   float* ws;
 };
 
-template <int N, int VPT, bool kPipe>
+template <int N, bool PIPE, int MAXT>
 hipError_t launch_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, kPipe>);
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt, PIPE, MAXT>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);
   if (e != hipSuccess) return e;
   const int64_t grid = a.T < res ? a.T : res;
-  hipLaunchKernelGGL((fwd_kernel<N, VPT, kPipe>), dim3((unsigned)grid), dim3((unsigned)s.threads), s.lds, st,
+  hipLaunchKernelGGL((fwd_kernel<N, kVpt, PIPE, MAXT>), dim3((unsigned)grid), dim3((unsigned)s.threads), s.lds, st,
                      a.src, a.w, a.eps, a.T, a.D, a.out, a.rstd, a.alpha);
   return hipGetLastError();
 }
 
-template <int N, int VPT, bool kPipe>
+template <int N, bool PIPE, bool ACC, int MAXT>
 hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, kPipe>);
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, kVpt, PIPE, ACC, MAXT>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   // one workgroup per dw chunk (P = min(T, ATTNRES_DW_PARTIALS))
-  hipLaunchKernelGGL((bwd_kernel<N, VPT, kPipe>), dim3((unsigned)a.P), dim3((unsigned)s.threads), 2 * s.lds, st,
-                     a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
+  hipLaunchKernelGGL((bwd_kernel<N, kVpt, PIPE, ACC, MAXT>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
+                     2 * s.lds, st, a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();
 }
 
-template <int VPT, bool PIPE>
-hipError_t dispatch_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  switch (N) {
-    case 1: return launch_fwd_n<1, VPT, PIPE>(s, st, a);
-    case 2: return launch_fwd_n<2, VPT, PIPE>(s, st, a);
-    case 3: return launch_fwd_n<3, VPT, PIPE>(s, st, a);
-    case 4: return launch_fwd_n<4, VPT, PIPE>(s, st, a);
-    case 5: return launch_fwd_n<5, VPT, PIPE>(s, st, a);
-    case 6: return launch_fwd_n<6, VPT, PIPE>(s, st, a);
-    case 7: return launch_fwd_n<7, VPT, PIPE>(s, st, a);
-    case 8: return launch_fwd_n<8, VPT, PIPE>(s, st, a);
-    case 9: return launch_fwd_n<9, VPT, PIPE>(s, st, a);
-    default: return hipErrorInvalidValue;
-  }
+template <int N>
+hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  return s.pipe ? launch_fwd_n<N, true, 512>(s, st, a) : launch_fwd_n<N, false, 1024>(s, st, a);
 }
 
-template <int VPT, bool PIPE>
-hipError_t dispatch_bwd(int32_t N, const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  switch (N) {
-    case 1: return launch_bwd_n<1, VPT, PIPE>(s, st, a);
-    case 2: return launch_bwd_n<2, VPT, PIPE>(s, st, a);
-    case 3: return launch_bwd_n<3, VPT, PIPE>(s, st, a);
-    case 4: return launch_bwd_n<4, VPT, PIPE>(s, st, a);
-    case 5: return launch_bwd_n<5, VPT, PIPE>(s, st, a);
-    case 6: return launch_bwd_n<6, VPT, PIPE>(s, st, a);
-    case 7: return launch_bwd_n<7, VPT, PIPE>(s, st, a);
-    case 8: return launch_bwd_n<8, VPT, PIPE>(s, st, a);
-    case 9: return launch_bwd_n<9, VPT, PIPE>(s, st, a);
-    default: return hipErrorInvalidValue;
-  }
+template <int N>
+hipError_t run_bwd_n(const LaunchShape& s, bool acc, hipStream_t st, const BwdArgs& a) {
+  if (acc) return s.pipe ? launch_bwd_n<N, false, true, 512>(s, st, a) : launch_bwd_n<N, false, true, 1024>(s, st, a);
+  return s.pipe ? launch_bwd_n<N, true, false, 512>(s, st, a) : launch_bwd_n<N, false, false, 1024>(s, st, a);
 }
 
 hipError_t run_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  if (!s.pipe) return dispatch_fwd<2, false>(N, s, st, a);
-  return s.vpt == 2 ? dispatch_fwd<ATTNRES_SMALL_D_VPT, true>(N, s, st, a) : dispatch_fwd<1, true>(N, s, st, a);
+  switch (N) {
+    case 1: return run_fwd_n<1>(s, st, a);
+    case 2: return run_fwd_n<2>(s, st, a);
+    case 3: return run_fwd_n<3>(s, st, a);
+    case 4: return run_fwd_n<4>(s, st, a);
+    case 5: return run_fwd_n<5>(s, st, a);
+    case 6: return run_fwd_n<6>(s, st, a);
+    case 7: return run_fwd_n<7>(s, st, a);
+    case 8: return run_fwd_n<8>(s, st, a);
+    case 9: return run_fwd_n<9>(s, st, a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t run_bwd(int32_t N, const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  if (!s.pipe) return dispatch_bwd<2, false>(N, s, st, a);
-  return s.vpt == 2 ? dispatch_bwd<ATTNRES_SMALL_D_VPT, true>(N, s, st, a) : dispatch_bwd<1, true>(N, s, st, a);
+hipError_t run_bwd(int32_t N, const LaunchShape& s, bool acc, hipStream_t st, const BwdArgs& a) {
+  switch (N) {
+    case 1: return run_bwd_n<1>(s, acc, st, a);
+    case 2: return run_bwd_n<2>(s, acc, st, a);
+    case 3: return run_bwd_n<3>(s, acc, st, a);
+    case 4: return run_bwd_n<4>(s, acc, st, a);
+    case 5: return run_bwd_n<5>(s, acc, st, a);
+    case 6: return run_bwd_n<6>(s, acc, st, a);
+    case 7: return run_bwd_n<7>(s, acc, st, a);
+    case 8: return run_bwd_n<8>(s, acc, st, a);
+    case 9: return run_bwd_n<9>(s, acc, st, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side validation and launch, shared by the stacked and per-source calls
+// ---------------------------------------------------------------------------
+attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                        uint16_t* out, float* rstd, float* alpha, void* stream) {
+  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
+  Range ins[ATTNRES_MAX_SOURCES + 1];
+  SrcRows rows{};
+  for (int i = 0; i < N; ++i) {
+    if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    rows.p[i] = srcs[i];
+    ins[i] = range_of(srcs[i], nTD * 2);
+  }
+  ins[N] = range_of(w, (size_t)D * 4);
+  if (out == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b <= N; ++b)
+      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  const LaunchShape s = shape_for(D);
+  const FwdArgs args{rows, w, eps, T, D, out, rstd, alpha};
+  const hipError_t e = run_fwd(N, s, reinterpret_cast<hipStream_t>(stream), args);
+  return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
+attnres_status fwd_common_checks(const float* w, float eps, int32_t N, int64_t T, int32_t D) {
+  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (w == nullptr || !aligned(w, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return ATTNRES_OK;
+}
+
+attnres_status bwd_zero_dw(float* dw, int32_t D, void* stream) {
+  const int n4 = D / 4;
+  hipLaunchKernelGGL(zero_kernel, dim3((n4 + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<float4*>(dw), n4);
+  return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
+attnres_status bwd_common_checks(const float* w, int32_t N, int64_t T, int32_t D, float* dw) {
+  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (w == nullptr || dw == nullptr || !aligned(w, 16) || !aligned(dw, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (overlap(range_of(dw, (size_t)D * 4), range_of(w, (size_t)D * 4))) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return ATTNRES_OK;
+}
+
+attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, const float* w, const float* rstd,
+                        const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* const* dsrcs, bool acc,
+                        float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dout == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(dout, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
+  Range ins[ATTNRES_MAX_SOURCES + 4];
+  int nin = 0;
+  SrcRows rows{};
+  DstRows drows{};
+  for (int i = 0; i < N; ++i) {
+    if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    if (dsrcs[i] == nullptr || !aligned(dsrcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    rows.p[i] = srcs[i];
+    drows.p[i] = dsrcs[i];
+    ins[nin++] = range_of(srcs[i], nTD * 2);
+  }
+  ins[nin++] = range_of(dout, nTD * 2);
+  ins[nin++] = range_of(w, (size_t)D * 4);
+  ins[nin++] = range_of(rstd, nTN * 4);
+  ins[nin++] = range_of(alpha, nTN * 4);
+  const size_t need = ATTNRES_BWD_WORKSPACE_BYTES(D);
+  if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  Range outs[ATTNRES_MAX_SOURCES + 2];
+  int nout = 0;
+  for (int i = 0; i < N; ++i) outs[nout++] = range_of(dsrcs[i], nTD * 2);
+  outs[nout++] = range_of(dw, (size_t)D * 4);
+  outs[nout++] = range_of(workspace, need);
+  for (int a = 0; a < nout; ++a) {
+    for (int b = 0; b < nin; ++b)
+      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < nout; ++b)
+      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  const LaunchShape s = shape_for(D);
+  const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
+  float* ws = reinterpret_cast<float*>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const BwdArgs args{dout, rows, w, rstd, alpha, T, D, P, drows, ws};
+  hipError_t e = run_bwd(N, s, acc, st, args);
+  if (e != hipSuccess) return ATTNRES_ERR_HIP;
+  const int D4 = D / 4;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
+                     reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
+  return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
 }  // namespace
 
 extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32_t N, int64_t T,
                                       int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream) {
-  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (w == nullptr || !aligned(w, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
-  if (src == nullptr || out == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!aligned(src, 16) || !aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4))
-    return ATTNRES_ERR_INVALID_ARGUMENT;
-  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
-  const Range r_src = range_of(src, (size_t)N * nTD * 2), r_w = range_of(w, (size_t)D * 4);
-  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
-  for (int a = 0; a < 3; ++a) {
-    if (overlap(outs[a], r_src) || overlap(outs[a], r_w)) return ATTNRES_ERR_INVALID_ARGUMENT;
-    for (int b = a + 1; b < 3; ++b)
-      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
-  }
+  if (src == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const uint16_t* srcs[ATTNRES_MAX_SOURCES];
+  for (int i = 0; i < N; ++i) srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, stream);
+}
 
-  const LaunchShape s = shape_for(D);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const FwdArgs a{src, w, eps, T, D, out, rstd, alpha};
-  const hipError_t e = run_fwd(N, s, st, a);
-  return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
+                                              int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
+                                              void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, stream);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
                                       const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (w == nullptr || dw == nullptr || !aligned(w, 16) || !aligned(dw, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (overlap(range_of(dw, (size_t)D * 4), range_of(w, (size_t)D * 4))) return ATTNRES_ERR_INVALID_ARGUMENT;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (T == 0) {
-    const int n4 = D / 4;
-    hipLaunchKernelGGL(zero_kernel, dim3((n4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(dw), n4);
-    return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+  const attnres_status st = bwd_common_checks(w, N, T, D, dw);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return bwd_zero_dw(dw, D, stream);
+  if (src == nullptr || dsrc == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const uint16_t* srcs[ATTNRES_MAX_SOURCES];
+  uint16_t* dsrcs[ATTNRES_MAX_SOURCES];
+  for (int i = 0; i < N; ++i) {
+    srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
+    dsrcs[i] = dsrc + (size_t)i * (size_t)T * (size_t)D;
   }
-  if (dout == nullptr || src == nullptr || rstd == nullptr || alpha == nullptr || dsrc == nullptr)
-    return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!aligned(dout, 16) || !aligned(src, 16) || !aligned(dsrc, 16) || !aligned(rstd, 4) || !aligned(alpha, 4))
-    return ATTNRES_ERR_INVALID_ARGUMENT;
-  const size_t need = ATTNRES_BWD_WORKSPACE_BYTES(D);
-  if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return bwd_impl(dout, srcs, w, rstd, alpha, N, T, D, dsrcs, false, dw, workspace, workspace_bytes, stream);
+}
 
-  const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
-  const Range ins[5] = {range_of(dout, nTD * 2), range_of(src, (size_t)N * nTD * 2), range_of(w, (size_t)D * 4),
-                        range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
-  const Range outs[3] = {range_of(dsrc, (size_t)N * nTD * 2), range_of(dw, (size_t)D * 4),
-                         range_of(workspace, need)};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 5; ++b)
-      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
-    for (int b = a + 1; b < 3; ++b)
-      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
-  }
-
-  const LaunchShape s = shape_for(D);
-  const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
-  float* ws = reinterpret_cast<float*>(workspace);
-  const BwdArgs a{dout, src, w, rstd, alpha, T, D, P, dsrc, ws};
-  hipError_t e = run_bwd(N, s, st, a);
-  if (e != hipSuccess) return ATTNRES_ERR_HIP;
-  const int D4 = D / 4;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
-                     reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
-  return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, const float* w,
+                                              const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
+                                              uint16_t* const* dsrcs, int32_t accumulate, float* dw,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+  const attnres_status st = bwd_common_checks(w, N, T, D, dw);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return bwd_zero_dw(dw, D, stream);
+  if (srcs == nullptr || dsrcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return bwd_impl(dout, srcs, w, rstd, alpha, N, T, D, dsrcs, accumulate != 0, dw, workspace, workspace_bytes,
+                  stream);
 }

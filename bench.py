@@ -204,6 +204,47 @@ def sweep(ar, torch, dev, reps=20):
         print(json.dumps(line), flush=True)
         del src, dout, w, bufs, out, rstd, alpha, dsrc, dw, ws
         torch.cuda.empty_cache()
+    sweep_sources(ar, torch, dev, flush, reps)
+
+
+def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
+    """Per-source calls (separately allocated sources and gradients) at T=32768,
+    N=9: the forward, the overwriting backward and the accumulating backward
+    (which also reads the old gradients: +2ND bytes per token)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    srcs = [(torch.randn((T, D), device=dev, generator=g) * (1 + 12 * i) ** 0.5).to(torch.bfloat16) for i in range(N)]
+    dout = torch.randn((T, D), device=dev, generator=g).to(torch.bfloat16)
+    w = torch.randn(D, device=dev, generator=g) / D ** 0.5
+    dsrcs = [torch.zeros((T, D), dtype=torch.bfloat16, device=dev) for _ in range(N)]
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dw = torch.empty((D,), dtype=torch.float32, device=dev)
+    ws = torch.empty((ar.workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    fb, bb, fe, be = algo_bytes(T, N, D)
+    calls = {
+        "fwd_sources": (lambda: ar.attnres_fwd_sources(srcs, w, 1e-6, out=out, rstd=rstd, alpha=alpha), fb + fe),
+        "bwd_sources": (lambda: ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=dsrcs, dw=dw, workspace=ws),
+                        bb + be),
+        "bwd_sources_accumulate": (lambda: ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=dsrcs,
+                                                                  accumulate=True, dw=dw, workspace=ws),
+                                   bb + be + T * 2 * N * D),
+    }
+    for name, (fn, nbytes) in calls.items():
+        ms = []
+        for r in range(reps + 3):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ms.append(e0.elapsed_time(e1))
+        m = sorted(ms)[len(ms) // 2]
+        print(json.dumps({"sweep": True, "call": name, "N": N, "T": T, "D": D, "ms": m,
+                          "GBps": nbytes / m / 1e6, "frac_of_8TBps": nbytes / m / 1e6 / HBM_PEAK_GBPS}), flush=True)
 
 
 def main():

@@ -109,6 +109,38 @@ attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const floa
                            const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward with the N sources as separately allocated [T][D] bf16 tensors
+ * instead of one stacked [N][T][D] tensor -- the form a model holds them in:
+ * the embedding, each completed block sum and the current partial sum live
+ * in their own buffers (architecture figure of "Kimi K3 模型结构（10）"), and
+ * stacking them would cost a copy of N*T*D values per sub-layer.
+ *   srcs  host array of N device pointers; srcs[i] -> [T][D] bf16, 16-byte
+ *         aligned.  A pointer may appear more than once.  May be NULL when
+ *         T == 0.
+ * Everything else as attnres_fwd.  Results are bitwise identical to
+ * attnres_fwd on the same rows stacked.
+ */
+attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T,
+                                   int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
+ * Backward with per-source pointers, optionally accumulating the source
+ * gradients.  A completed block sum is a source of every later sub-layer's
+ * AttnRes, so its gradient is the sum of those operators' contributions:
+ *   dsrcs       host array of N device pointers to [T][D] bf16 gradients,
+ *               pairwise disjoint and disjoint from every input.
+ *   accumulate  0: dsrcs[i] = dx_i (bitwise identical to attnres_bwd);
+ *               else: dsrcs[i] = bf16( fp32(dsrcs[i]) + dx_i ), rounded to
+ *               nearest even, each element read and written once.
+ * dw is always overwritten with this call's sum over the T tokens.  Other
+ * arguments as attnres_bwd.  srcs and dsrcs may be NULL when T == 0.
+ */
+attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, const float* w,
+                                   const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
+                                   uint16_t* const* dsrcs, int32_t accumulate, float* dw, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

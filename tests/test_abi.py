@@ -34,7 +34,7 @@ def _define(name):
 def test_library_loads_and_exports_declared_symbols():
     lib = ar.library()
     names = _declared()
-    assert names == ["attnres_fwd", "attnres_bwd"]
+    assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -134,3 +134,49 @@ def test_binding_refuses_host_tensors():
     w = torch.zeros(8)
     with pytest.raises(ValueError):
         ar.attnres_fwd(src, w, 1e-6)
+
+
+def _arr(vals):
+    a = (ctypes.c_void_p * len(vals))()
+    for i, v in enumerate(vals):
+        a[i] = v
+    return a
+
+
+def _fwd_src(srcs, N=3, T=16, D_=D, eps=1e-6, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
+             alpha=(1 << 36) + (1 << 31)):
+    return ar.library().attnres_fwd_sources(srcs, w, eps, N, T, D_, out, rstd, alpha, None)
+
+
+def test_fwd_sources_rejects():
+    g = 1 << 30
+    good = [g, 3 * g, 5 * g]
+    assert _fwd_src(None) == INVALID
+    assert _fwd_src(_arr([g, 0, 5 * g])) == INVALID  # null entry
+    assert _fwd_src(_arr([g, 3 * g + 8, 5 * g])) == INVALID  # misaligned entry
+    assert _fwd_src(_arr(good), out=3 * g + 64) == INVALID  # out inside a source
+    assert _fwd_src(_arr(good), N=10) == INVALID
+    assert _fwd_src(None, T=0) == OK  # nothing to do
+    # the same source twice is a legal input (no output overlaps it)
+    assert _fwd_src(_arr([g, g, 5 * g]), w=0) == INVALID  # still rejected, but only for the null w
+
+
+def _bwd_src(srcs, dsrcs, acc=1, N=3, T=16, D_=D, ws_bytes=None):
+    g = 1 << 30
+    if ws_bytes is None:
+        ws_bytes = ar.workspace_bytes(D_)
+    return ar.library().attnres_bwd_sources(1 * g, srcs, 20 * g, 21 * g, 22 * g, N, T, D_, dsrcs, acc, 23 * g,
+                                            24 * g, ws_bytes, None)
+
+
+def test_bwd_sources_rejects():
+    g = 1 << 30
+    srcs = _arr([2 * g, 3 * g, 4 * g])
+    assert _bwd_src(srcs, None) == INVALID
+    assert _bwd_src(None, _arr([8 * g, 9 * g, 10 * g])) == INVALID
+    assert _bwd_src(srcs, _arr([8 * g, 8 * g, 10 * g])) == INVALID  # two gradients on one buffer
+    assert _bwd_src(srcs, _arr([8 * g, 9 * g, 3 * g])) == INVALID  # gradient over a source
+    assert _bwd_src(srcs, _arr([8 * g, 9 * g, g + 128])) == INVALID  # gradient over dout
+    assert _bwd_src(srcs, _arr([8 * g, 9 * g + 2, 10 * g])) == INVALID  # misaligned
+    assert _bwd_src(srcs, _arr([8 * g, 0, 10 * g])) == INVALID  # null entry
+    assert _bwd_src(srcs, _arr([8 * g, 9 * g, 10 * g]), ws_bytes=8) == WORKSPACE

@@ -1,0 +1,113 @@
+"""Per-source pointers and gradient accumulation (attnres_fwd_sources /
+attnres_bwd_sources): bitwise agreement with the stacked calls, and parity of
+the accumulated gradients with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import oracle
+import synth
+from parity import (DEV, TOL_DSRC_REL_L2, TOL_DW_REL_L2, bf16_dev_to_f64, rel_l2, run_gpu, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
+
+
+def _separate(src_stacked):
+    """Copy each source into its own allocation (different addresses and order)."""
+    return [src_stacked[i].clone() for i in range(src_stacked.shape[0])]
+
+
+@pytest.mark.parametrize("N,T,D", [(9, 700, 7168), (3, 130, 1000), (5, 40, 12288), (1, 17, 7168)],
+                         ids=lambda v: str(v))
+def test_sources_match_stacked_bitwise(N, T, D):
+    wl = synth.Workload(f"src_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    dout = to_dev_bf16(wl.dout())
+    out, rstd, alpha, dsrc, dw = run_gpu(src, w, wl.eps, dout)
+    srcs = _separate(src)
+    o2, r2, a2 = ar.attnres_fwd_sources(srcs, w, wl.eps)
+    d2, dw2 = ar.attnres_bwd_sources(dout, srcs, w, r2, a2)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(o2))
+    assert torch.equal(_bits(rstd), _bits(r2))
+    assert torch.equal(_bits(alpha), _bits(a2))
+    for i in range(N):
+        assert torch.equal(_bits(dsrc[i]), _bits(d2[i])), i
+    assert torch.equal(_bits(dw), _bits(dw2))
+
+
+def test_repeated_source_pointer():
+    """The same tensor may be passed as two sources (reads only)."""
+    wl = synth.workload(1, T=64, N=3)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    srcs = [src[0], src[1], src[0]]
+    stacked = torch.stack(srcs).contiguous()
+    o1, r1, a1 = ar.attnres_fwd(stacked, w, wl.eps)
+    o2, r2, a2 = ar.attnres_fwd_sources(srcs, w, wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(a1), _bits(a2))
+
+
+@pytest.mark.parametrize("N,T,D", [(9, 512, 7168), (4, 300, 4104), (6, 33, 12288), (1, 20, 7168)],
+                         ids=lambda v: str(v))
+def test_accumulate_against_oracle(N, T, D):
+    wl = synth.Workload(f"acc_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src_h, dout_h, w_h = wl.sources(), wl.dout(), wl.w()
+    # prior gradients of the sources: seeded bf16 values of the size of a step's gradient
+    prior = synth.Workload(f"prior_N{N}_T{T}_D{D}", T=T, N=N, D=D, seed=7, kind="tiny",
+                           tiny_scales=tuple([0.1] * 9)).sources()
+    src = [to_dev_bf16(src_h[i]) for i in range(N)]
+    dsrcs = [to_dev_bf16(prior[i]) for i in range(N)]
+    w = torch.from_numpy(w_h).to(DEV)
+    dout = to_dev_bf16(dout_h)
+    out, rstd, alpha = ar.attnres_fwd_sources(src, w, wl.eps)
+    dsrcs, dw = ar.attnres_bwd_sources(dout, src, w, rstd, alpha, dsrcs=dsrcs, accumulate=True)
+    torch.cuda.synchronize()
+    o_dsrc, o_dw = oracle.bwd(src_h, w_h, wl.eps, dout_h)
+    expect = oracle.bf16_to_f64(prior) + o_dsrc
+    got = np.stack([bf16_dev_to_f64(d) for d in dsrcs])
+    e_acc = rel_l2(got, expect)
+    e_inc = rel_l2(got - oracle.bf16_to_f64(prior), o_dsrc)
+    e_dw = rel_l2(dw.cpu().double().numpy(), o_dw)
+    print(f"[parity] accumulate N={N} T={T} D={D}: result rel_l2={e_acc:.3e} increment rel_l2={e_inc:.3e} "
+          f"dw rel_l2={e_dw:.3e}", flush=True)
+    assert e_acc <= TOL_DSRC_REL_L2
+    assert e_inc <= TOL_DSRC_REL_L2
+    assert e_dw <= TOL_DW_REL_L2
+
+
+def test_accumulate_twice_equals_sum_of_two_calls():
+    """Two accumulating calls with the same inputs add the same increment twice."""
+    wl = synth.workload(1, T=256)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    dout = to_dev_bf16(wl.dout())
+    srcs = _separate(src)
+    out, rstd, alpha = ar.attnres_fwd_sources(srcs, w, wl.eps)
+    plain, _ = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha)
+    zero = [torch.zeros_like(s) for s in srcs]
+    acc, _ = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=zero, accumulate=True)
+    torch.cuda.synchronize()
+    # 0 + dx rounds exactly like dx
+    for a, p in zip(acc, plain):
+        assert torch.equal(_bits(a), _bits(p))
+    acc2, _ = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=acc, accumulate=True)
+    torch.cuda.synchronize()
+    for a, p in zip(acc2, plain):
+        assert torch.allclose(a.float(), 2 * p.float(), rtol=8e-3, atol=1e-6)
