@@ -475,15 +475,13 @@ __global__ void __launch_bounds__(MAXT) fwd_kernel(SrcRows src, const float* __r
 // ---------------------------------------------------------------------------
 // Backward: dsources and dw partial rows
 // ---------------------------------------------------------------------------
-// The tokens are cut into P fixed chunks: with q = T / P and r = T % P, chunk
-// c = [begin(c), begin(c + 1)) with begin(c) = c*q + min(c, r) (the first r
-// chunks hold one extra token).  Workgroup c handles chunk c and sums its dw
-// contributions in token order into partial row ws[c][:]; dw therefore does
-// not depend on how many workgroups are resident at once.
-__device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t T, int64_t P) {
-  const int64_t q = T / P, r = T - (T / P) * P;
-  return c * q + (c < r ? c : r);
-}
+// The launch has exactly P = min(T, 256) workgroups.  Workgroup c handles the
+// tokens c, c + P, c + 2P, ... and sums their dw contributions in token order
+// into partial row ws[c][:]; the split depends only on T, so dw does not
+// depend on how many workgroups are resident at once.  Interleaving the tokens
+// keeps the workgroups on neighbouring rows of each source at any moment
+// (contiguous per-workgroup ranges measured 2-7% slower on MI355X: the HBM
+// accesses of 256 separate streams per source are less local).
 
 struct BwdCtx {
   int64_t T;
@@ -498,7 +496,7 @@ struct BwdCtx {
 
 // Backward of token t whose sources and dout are already in x and g:
 // g.x_i and w.x_i, workgroup reduction, softmax backward, dsources stores and
-// this chunk's running dw (LDS).  Issues no loads of the row group.  With ACC
+// this workgroup's running dw (LDS).  Issues no loads of the row group.  With ACC
 // the old gradients are loaded once the partial sums are formed (so they are
 // in flight during the reduction but not live during the first pass) and the
 // new gradient is added to them in fp32 before rounding.
@@ -583,7 +581,7 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
   }
 }
 
-// Publish this workgroup's dw partial row (its chunk's sum).
+// Publish this workgroup's dw partial row (the sum over its tokens).
 template <int VPT>
 __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, int32_t D, const float4* dwl,
                                            const Slice<VPT>& sl) {
@@ -596,10 +594,10 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
 }
 
 // With PIPE, register sets A and B alternate as in the forward kernel, each
-// refilled with the token two steps ahead (in workgroup order) once its token
-// is done.  With ACC (no prefetch) the old gradients are loaded with the row
-// group.  Dynamic LDS holds w and the running dw of the current chunk, in the
-// thread's private slots.
+// refilled with the workgroup's token two steps ahead once its token is done.
+// With ACC (no prefetch) the old gradients are loaded during the reduction.
+// Dynamic LDS holds w and the workgroup's running dw, in the thread's private
+// slots.
 template <int N, int VPT, bool PIPE, bool ACC, int MAXT>
 __global__ void __launch_bounds__(MAXT) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
                                                    const float* __restrict__ w, const float* __restrict__ rstd,
@@ -628,37 +626,38 @@ __global__ void __launch_bounds__(MAXT) bwd_kernel(const uint16_t* __restrict__ 
 
   int buf = 0;
   const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
-  const int64_t t0 = chunk_begin(ch, T, P), t1 = chunk_begin(ch + 1, T, P);
   if (PIPE) {
     uint4 xa[N][VPT], xb[N][VPT], ga[VPT], gb[VPT];
     float saa, sra, sab, srb;
-    int64_t t = t0;
+    int64_t t = ch;
     load_row<VPT>(ga, dout, t, D, sl);
     load_rows<N, VPT>(xa, src, t, D, sl);
     load_saved<N>(saa, sra, alpha, rstd, t, c.lane);
     sched_fence();
-    load_row<VPT>(gb, dout, t + 1, D, sl, t + 1 < t1);
-    load_rows<N, VPT>(xb, src, t + 1, D, sl, t + 1 < t1);
-    load_saved<N>(sab, srb, alpha, rstd, t + 1, c.lane, t + 1 < t1);
+    load_row<VPT>(gb, dout, t + P, D, sl, t + P < T);
+    load_rows<N, VPT>(xb, src, t + P, D, sl, t + P < T);
+    load_saved<N>(sab, srb, alpha, rstd, t + P, c.lane, t + P < T);
     sched_fence();
     while (true) {
       bwd_token<N, VPT, false>(xa, ga, saa, sra, t, buf, c, sl);
       sched_fence();
-      load_row<VPT>(ga, dout, t + 2, D, sl, t + 2 < t1);
-      load_rows<N, VPT>(xa, src, t + 2, D, sl, t + 2 < t1);
-      load_saved<N>(saa, sra, alpha, rstd, t + 2, c.lane, t + 2 < t1);
+      load_row<VPT>(ga, dout, t + 2 * P, D, sl, t + 2 * P < T);
+      load_rows<N, VPT>(xa, src, t + 2 * P, D, sl, t + 2 * P < T);
+      load_saved<N>(saa, sra, alpha, rstd, t + 2 * P, c.lane, t + 2 * P < T);
       sched_fence();
-      if (++t >= t1) break;
+      t += P;
+      if (t >= T) break;
       bwd_token<N, VPT, false>(xb, gb, sab, srb, t, buf, c, sl);
       sched_fence();
-      load_row<VPT>(gb, dout, t + 2, D, sl, t + 2 < t1);
-      load_rows<N, VPT>(xb, src, t + 2, D, sl, t + 2 < t1);
-      load_saved<N>(sab, srb, alpha, rstd, t + 2, c.lane, t + 2 < t1);
+      load_row<VPT>(gb, dout, t + 2 * P, D, sl, t + 2 * P < T);
+      load_rows<N, VPT>(xb, src, t + 2 * P, D, sl, t + 2 * P < T);
+      load_saved<N>(sab, srb, alpha, rstd, t + 2 * P, c.lane, t + 2 * P < T);
       sched_fence();
-      if (++t >= t1) break;
+      t += P;
+      if (t >= T) break;
     }
   } else {
-    for (int64_t t = t0; t < t1; ++t) {
+    for (int64_t t = ch; t < T; t += P) {
       uint4 x[N][VPT], g[VPT];
       float sa, sr;
       load_row<VPT>(g, dout, t, D, sl);
@@ -825,7 +824,7 @@ hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) 
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
-  // one workgroup per dw chunk (P = min(T, ATTNRES_DW_PARTIALS))
+  // one workgroup per dw partial row (P = min(T, ATTNRES_DW_PARTIALS))
   hipLaunchKernelGGL((bwd_kernel<N, kVpt, PIPE, ACC, MAXT>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
                      2 * s.lds, st, a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();

@@ -117,11 +117,12 @@ def full_compare(wl: synth.Workload):
 
 
 def sample_tokens(T: int, n_random: int = 40, seed: int = 1) -> np.ndarray:
-    """First and last tokens, dw-chunk boundaries, and seeded random tokens."""
+    """First and last tokens, the first and last backward workgroup's first
+    tokens, the start of the last (ragged) round of tokens, and seeded random
+    tokens."""
     P = min(T, ar.DW_PARTIALS)
-    edges = {0, 1, T - 2, T - 1}
-    for c in (1, P // 2, P - 1):
-        edges.add(c * T // P)
-        edges.add(max(0, c * T // P - 1))
+    edges = {0, 1, T - 2, T - 1, P - 1, P, 2 * P - 1}
+    last_round = (T // P) * P if T % P else T - P
+    edges.update({last_round, last_round - 1, last_round + 1})
     rnd = np.random.default_rng(seed).integers(0, T, size=n_random)
     return np.array(sorted({int(t) for t in edges if 0 <= t < T} | {int(t) for t in rnd}), dtype=np.int64)
