@@ -15,6 +15,9 @@ The C entry points, declared in ``include/attnres.h``:
     attnres_fwd_sources / attnres_bwd_sources: the same with the N sources
                 (and their gradients) as separate [T][D] tensors, and an
                 accumulate flag for the source gradients.
+    attnres_fwd_decode: the per-source forward for small batches (one
+                workgroup per token), rstd/alpha optional; bitwise the same
+                per-token results as the other forward calls.
 """
 from __future__ import annotations
 
@@ -59,6 +62,8 @@ def library() -> ctypes.CDLL:
         lib.attnres_fwd_sources.restype = ctypes.c_int
         lib.attnres_bwd_sources.argtypes = [vp, pp, vp, vp, vp, i32, i64, i32, pp, i32, vp, vp, sz, vp]
         lib.attnres_bwd_sources.restype = ctypes.c_int
+        lib.attnres_fwd_decode.argtypes = [pp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_decode.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -182,6 +187,33 @@ def attnres_fwd_sources(srcs, w: torch.Tensor, eps: float, out=None, rstd=None, 
     return out, rstd, alpha
 
 
+def attnres_fwd_decode(srcs, w: torch.Tensor, eps: float, out=None, save_state: bool = False, rstd=None, alpha=None,
+                       stream=None):
+    """Small-batch forward on N separate [T][D] bf16 sources.  Writes rstd and
+    alpha only with save_state=True (or when they are passed).  Returns
+    (out, rstd, alpha), the last two None when not saved."""
+    srcs, T, D = _sources(srcs, "srcs")
+    N = len(srcs)
+    _check(w, "w", torch.float32, (D,))
+    dev = srcs[0].device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    if save_state or rstd is not None or alpha is not None:
+        if rstd is None:
+            rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+        if alpha is None:
+            alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+        _check(rstd, "rstd", torch.float32, (T, N))
+        _check(alpha, "alpha", torch.float32, (T, N))
+    code = library().attnres_fwd_decode(_ptr_array(srcs), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+                                        None if rstd is None else rstd.data_ptr(),
+                                        None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_fwd_decode", code)
+    return out, rstd, alpha
+
+
 def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.Tensor, alpha: torch.Tensor,
                         dsrcs=None, accumulate: bool = False, dw=None, workspace=None, stream=None):
     """Backward on N separate sources.  dsrcs: N separate [T][D] bf16 gradient
@@ -208,6 +240,8 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     if workspace is None:
         workspace = torch.empty((workspace_bytes(D),), dtype=torch.uint8, device=dev)
     _check(dw, "dw", torch.float32, (D,))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), w.data_ptr(), rstd.data_ptr(),
                                          alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), 1 if accumulate else 0,
@@ -217,5 +251,5 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     return dsrcs, dw
 
 
-__all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D",
-           "DW_PARTIALS", "LIB_PATH"]
+__all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
+           "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

@@ -7,13 +7,14 @@
 // of "Kimi K3 on Fireworks: Fast RL at frontier scale" fuses normalisation and
 // weighted sum so that nothing per-source is materialised; here that means:
 //
-//   forward   one kernel, one HBM pass over the sources.  A workgroup owns one
-//             token at a time; each thread keeps a fixed D-slice of all N
-//             source rows in registers, forms its partial sum of squares and
-//             w.x, reduces them across the wave with DPP and across waves
-//             through a few LDS words, computes rstd/softmax redundantly in
-//             every thread, and writes the fp32-accumulated weighted sum from
-//             the same registers.
+//   forward   one kernel, one HBM pass over the sources, one workgroup per
+//             token; each thread keeps a fixed D-slice of all N source rows
+//             in registers, forms its partial sum of squares and w.x,
+//             reduces them across the wave with DPP and across waves through
+//             a few LDS words, computes rstd/softmax redundantly in every
+//             thread, and writes the fp32-accumulated weighted sum from the
+//             same registers.  The same kernel serves training batches and
+//             single decoding steps.
 //   backward  one kernel re-reads each source row once (plus dout), forms
 //             da_i = g.x_i and w.x_i with the same reduction tree, then writes
 //             dsources from the registers and accumulates this workgroup's
@@ -30,6 +31,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <mutex>
 
 #include "attnres.h"
 
@@ -314,13 +317,7 @@ __device__ __forceinline__ float lane_value(float v, int i) {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-// Launch bound MAXT: a prefetching two-vector variant keeps two row groups per
-// thread (and the accumulate variant a row group plus the old gradients), so
-// it is built for at most 512 threads (two waves per SIMD, up to 256 VGPRs
-// each); the others for up to 1024 threads.
-
 struct FwdCtx {
-  int64_t T;
   int32_t D;
   float eps;
   float inv_d;
@@ -399,7 +396,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
     }
     bstore<kAuxStreamStore>(ro, sl.off[k], pack8(acc));
   }
-  if (c.tid < N) {
+  if (c.rstd_out != nullptr && c.tid < N) {  // the decode call may skip the saved state
     float rv = r[0], av = a[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) {
@@ -411,20 +408,22 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
   }
 }
 
-// Persistent: workgroup b handles tokens b, b + G, b + 2G, ... (G = gridDim.x).
-// With PIPE, two register sets A and B alternate: while the workgroup works on
-// the token in one set, the loads of the next token are in flight in the
-// other, and a set is refilled with the token two steps ahead as soon as its
-// token is done -- so up to two tokens' loads overlap one token's arithmetic.
-// Dynamic LDS holds w.
-template <int N, int VPT, bool PIPE, int MAXT>
-__global__ void __launch_bounds__(MAXT) fwd_kernel(SrcRows src, const float* __restrict__ w, float eps, int64_t T,
+// One workgroup per token: workgroup b handles token t0 + b.  The hardware
+// dispatcher starts the next token as soon as a workgroup retires, two
+// workgroups share a CU (114 VGPRs: four waves per SIMD), and the tokens in
+// flight at any moment are neighbours, so the rows the chip reads are close
+// together in every source.  This beat a persistent kernel with a two-token
+// software pipeline per workgroup at every T on MI355X (T = 32768, N = 9:
+// 5.79 vs 5.39 TB/s; T = 1: 6.9 vs 7.8 us kernel time).  The w slice is
+// requested first and the row group right behind it, so both latencies
+// overlap; w then goes to the thread's LDS slots while the rows arrive.
+template <int N, int VPT>
+__global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const float* __restrict__ w, float eps, int64_t t0,
                                                    int32_t D, uint16_t* __restrict__ out,
                                                    float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
   FwdCtx c;
-  c.T = T;
   c.D = D;
   c.eps = eps;
   c.inv_d = 1.0f / (float)D;
@@ -437,39 +436,28 @@ __global__ void __launch_bounds__(MAXT) fwd_kernel(SrcRows src, const float* __r
   c.lane = c.tid & (kWave - 1);
   c.wave = c.tid / kWave;
   const Slice<VPT> sl(c.tid, blockDim.x);
-  stage_w<VPT>(w, D, dyn_lds, sl);
-  clear_red<2 * N>(red);
+  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
 
-  const int64_t G = gridDim.x;
-  int buf = 0;
-  if (PIPE) {
-    uint4 xa[N][VPT], xb[N][VPT];
-    int64_t t = blockIdx.x;
-    load_rows<N, VPT>(xa, src, t, D, sl);  // host guarantees gridDim.x <= T
-    sched_fence();
-    load_rows<N, VPT>(xb, src, t + G, D, sl, t + G < T);
-    sched_fence();
-    while (true) {
-      fwd_token<N, VPT>(xa, t, buf, c, sl);
-      sched_fence();
-      load_rows<N, VPT>(xa, src, t + 2 * G, D, sl, t + 2 * G < T);
-      sched_fence();
-      t += G;
-      if (t >= T) break;
-      fwd_token<N, VPT>(xb, t, buf, c, sl);
-      sched_fence();
-      load_rows<N, VPT>(xb, src, t + 2 * G, D, sl, t + 2 * G < T);
-      sched_fence();
-      t += G;
-      if (t >= T) break;
-    }
-  } else {
-    for (int64_t t = blockIdx.x; t < T; t += G) {
-      uint4 x[N][VPT];
-      load_rows<N, VPT>(x, src, t, D, sl);
-      fwd_token<N, VPT>(x, t, buf, c, sl);
-    }
+  uint4 wv[VPT][2];
+  const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    wv[k][0] = bload(rw, 2u * sl.off[k]);
+    wv[k][1] = bload(rw, 2u * sl.off[k] + 16u);
   }
+  sched_fence();
+  uint4 x[N][VPT];
+  load_rows<N, VPT>(x, src, t, D, sl);
+  sched_fence();
+  float4* wl = dyn_lds;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    wl[2 * sl.slot[k]] = __builtin_bit_cast(float4, wv[k][0]);
+    wl[2 * sl.slot[k] + 1] = __builtin_bit_cast(float4, wv[k][1]);
+  }
+  clear_red<2 * N>(red);
+  int buf = 0;
+  fwd_token<N, VPT>(x, t, buf, c, sl);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,7 +710,7 @@ __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
 // Host side
 // ---------------------------------------------------------------------------
 struct LaunchShape {
-  bool pipe;    // prefetch the next token's rows into a second register set
+  bool pipe;    // backward: prefetch the next token's rows into a second register set
   int threads;  // workgroup size
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
@@ -731,9 +719,9 @@ constexpr int kVpt = 2;  // 16-byte vectors per thread per row
 
 // Depends only on D: the per-token reduction tree (two vectors per thread,
 // blockDim = D/16 rounded up to whole waves) never changes with T or with the
-// variant, so every variant gives bitwise the same per-token results.
-// D <= 8192: the prefetching variants (<= 512 threads); D <= 16384: no
-// prefetch (up to 1024 threads).
+// call, so every forward call gives bitwise the same per-token results.
+// Backward: D <= 8192 uses the prefetching variant (<= 512 threads), larger D
+// (up to 1024 threads) the one without prefetch.
 LaunchShape shape_for(int32_t D) {
   const int V = D / 8;
   LaunchShape s;
@@ -768,17 +756,42 @@ bool sizes_ok(int32_t N, int64_t T, int32_t D) {
 
 // Resident workgroups of `fn` on the current device (occupancy x CUs).  The
 // grid only sets how many workgroups share the tokens; results never depend
-// on it.
+// on it.  The answer is cached per (device, kernel, shape): the two runtime
+// queries cost more host time than a small launch itself.
+struct OccupancyEntry {
+  const void* fn;
+  int dev, threads;
+  size_t lds;
+  int64_t blocks;
+};
+constexpr int kOccupancySlots = 256;
+std::mutex g_occupancy_mu;
+OccupancyEntry g_occupancy[kOccupancySlots];
+int g_occupancy_used = 0;
+
 hipError_t resident_blocks(const void* fn, int threads, size_t lds, int64_t* out) {
-  int dev = 0, cus = 0, per_cu = 0;
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(g_occupancy_mu);
+    for (int i = 0; i < g_occupancy_used; ++i) {
+      const OccupancyEntry& o = g_occupancy[i];
+      if (o.fn == fn && o.dev == dev && o.threads == threads && o.lds == lds) {
+        *out = o.blocks;
+        return hipSuccess;
+      }
+    }
+  }
+  int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   *out = (int64_t)per_cu * cus;
+  std::lock_guard<std::mutex> lock(g_occupancy_mu);
+  if (g_occupancy_used < kOccupancySlots) g_occupancy[g_occupancy_used++] = OccupancyEntry{fn, dev, threads, lds, *out};
   return hipSuccess;
 }
 
@@ -806,16 +819,23 @@ struct BwdArgs {
   float* ws;
 };
 
-template <int N, bool PIPE, int MAXT>
-hipError_t launch_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt, PIPE, MAXT>);
+// One workgroup per token.  The dispatch packet counts work-items in 32 bits,
+// so very large T (possible only for tiny D) is split over several launches.
+template <int N>
+hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt>);
   int64_t res = 0;
-  hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);
+  hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
-  const int64_t grid = a.T < res ? a.T : res;
-  hipLaunchKernelGGL((fwd_kernel<N, kVpt, PIPE, MAXT>), dim3((unsigned)grid), dim3((unsigned)s.threads), s.lds, st,
-                     a.src, a.w, a.eps, a.T, a.D, a.out, a.rstd, a.alpha);
-  return hipGetLastError();
+  const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)s.threads);
+  for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
+    const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
+    hipLaunchKernelGGL((fwd_kernel<N, kVpt>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src, a.w,
+                       a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int N, bool PIPE, bool ACC, int MAXT>
@@ -828,11 +848,6 @@ hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) 
   hipLaunchKernelGGL((bwd_kernel<N, kVpt, PIPE, ACC, MAXT>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
                      2 * s.lds, st, a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();
-}
-
-template <int N>
-hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  return s.pipe ? launch_fwd_n<N, true, 512>(s, st, a) : launch_fwd_n<N, false, 1024>(s, st, a);
 }
 
 template <int N>
@@ -875,7 +890,7 @@ hipError_t run_bwd(int32_t N, const LaunchShape& s, bool acc, hipStream_t st, co
 // Host-side validation and launch, shared by the stacked and per-source calls
 // ---------------------------------------------------------------------------
 attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T, int32_t D,
-                        uint16_t* out, float* rstd, float* alpha, void* stream) {
+                        uint16_t* out, float* rstd, float* alpha, bool decode, void* stream) {
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
   Range ins[ATTNRES_MAX_SOURCES + 1];
   SrcRows rows{};
@@ -885,9 +900,12 @@ attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, 
     ins[i] = range_of(srcs[i], nTD * 2);
   }
   ins[N] = range_of(w, (size_t)D * 4);
-  if (out == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  // rstd and alpha are written together or (decode call only) not at all
+  const bool save = rstd != nullptr || alpha != nullptr;
+  if (out == nullptr || (save && (rstd == nullptr || alpha == nullptr))) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!save && !decode) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, nTN * 4), range_of(alpha, nTN * 4)};
+  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, save ? nTN * 4 : 0), range_of(alpha, save ? nTN * 4 : 0)};
   for (int a = 0; a < 3; ++a) {
     for (int b = 0; b <= N; ++b)
       if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -979,7 +997,7 @@ extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float
   if (src == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   const uint16_t* srcs[ATTNRES_MAX_SOURCES];
   for (int i = 0; i < N; ++i) srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, stream);
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, stream);
 }
 
 extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
@@ -989,7 +1007,17 @@ extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const
   if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
   if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, stream);
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, stream);
+}
+
+extern "C" attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
+                                             int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
+                                             void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, true, stream);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,

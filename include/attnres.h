@@ -23,16 +23,19 @@
  * that no per-source intermediate reaches memory; these calls materialise
  * only out, rstd and alpha (forward) and dsources, dw (backward).
  *
- * Conventions for both calls
+ * Conventions for every call
  *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
  *   - Layouts are dense and row-major: sources/dsources [N][T][D]
  *     (source-major), out/dout [T][D], rstd/alpha [T][N] (token-major).
- *   - Every pointer is a device pointer owned by the caller.  The library
- *     allocates nothing, frees nothing, never synchronises and keeps no state
- *     between calls; it is reentrant.  All work is enqueued on `stream`
+ *   - Every pointer is a device pointer owned by the caller (the per-source
+ *     calls take a host array of device pointers).  The library allocates no
+ *     device memory, frees nothing and never synchronises; its only state is
+ *     a mutex-guarded host cache of kernel occupancy per device, so calls are
+ *     thread-safe and reentrant.  All work is enqueued on `stream`
  *     (a hipStream_t; NULL selects the null stream) and the call returns once
  *     the work is enqueued.
- *   - Outputs are overwritten, never accumulated.  Inputs are not modified.
+ *   - Outputs are overwritten, never accumulated (except by the
+ *     accumulating mode of attnres_bwd_sources).  Inputs are not modified.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error the call returns a non-zero status and enqueues nothing.
  *   - Results for one token depend only on that token's inputs (and w): they
@@ -123,6 +126,23 @@ attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const floa
  */
 attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T,
                                    int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
+ * Forward for decoding and rollout: the per-source forward with the saved
+ * state made optional, for callers that will not run a backward pass (the
+ * rollout side of the RL loop in the determinism section of "Kimi K3 on
+ * Fireworks: Fast RL at frontier scale").  It runs the same one-workgroup-
+ * per-token kernel as attnres_fwd, so every output is bitwise the one the
+ * training forward gives for that token in any batch: rollout and training
+ * see the same numbers.  A single token costs about 7 us of kernel time on
+ * MI355X (D = 7168, N = 9).
+ *   srcs, w, eps, N, T, D, out   as attnres_fwd_sources.
+ *   rstd, alpha   [T][N] fp32 saved state as attnres_fwd, or both NULL: then
+ *                 only out is written.  Exactly one of them NULL is
+ *                 ATTNRES_ERR_INVALID_ARGUMENT.
+ */
+attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T,
+                                  int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
  * Backward with per-source pointers, optionally accumulating the source

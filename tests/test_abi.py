@@ -34,7 +34,8 @@ def _define(name):
 def test_library_loads_and_exports_declared_symbols():
     lib = ar.library()
     names = _declared()
-    assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources"]
+    assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
+                     "attnres_bwd_sources"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -180,3 +181,31 @@ def test_bwd_sources_rejects():
     assert _bwd_src(srcs, _arr([8 * g, 9 * g + 2, 10 * g])) == INVALID  # misaligned
     assert _bwd_src(srcs, _arr([8 * g, 0, 10 * g])) == INVALID  # null entry
     assert _bwd_src(srcs, _arr([8 * g, 9 * g, 10 * g]), ws_bytes=8) == WORKSPACE
+
+
+def _dec(srcs, N=3, T=16, D_=D, eps=1e-6, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
+         alpha=(1 << 36) + (1 << 31)):
+    return ar.library().attnres_fwd_decode(srcs, w, eps, N, T, D_, out, rstd, alpha, None)
+
+
+def test_fwd_decode_rejects():
+    g = 1 << 30
+    good = _arr([g, 3 * g, 5 * g])
+    assert _dec(None) == INVALID
+    assert _dec(_arr([g, 0, 5 * g])) == INVALID  # null entry
+    assert _dec(good, rstd=None) == INVALID  # saved state is both or neither
+    assert _dec(good, alpha=None) == INVALID
+    assert _dec(good, out=None, rstd=None, alpha=None) == INVALID  # out is always needed
+    assert _dec(good, out=3 * g + 64) == INVALID  # out inside a source
+    assert _dec(good, rstd=(1 << 36) + 8, alpha=(1 << 36) + 8 + 4 * 48) == INVALID  # rstd over out
+    assert _dec(good, T=(1 << 31)) == INVALID  # one workgroup per token: T fits a 32-bit grid
+    assert _dec(good, N=10) == INVALID
+    assert _dec(good, D_=12) == INVALID
+    assert _dec(good, w=0) == INVALID
+    assert _dec(None, T=0) == OK  # nothing to do
+
+
+def test_only_the_decode_call_may_skip_the_saved_state():
+    g = 1 << 30
+    assert _fwd(rstd=0, alpha=0) == INVALID
+    assert _fwd_src(_arr([g, 3 * g, 5 * g]), rstd=None, alpha=None) == INVALID
