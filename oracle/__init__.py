@@ -14,7 +14,9 @@ stay in double.
 
 Every function here is pinned by ``tests/test_oracle.py`` against finite
 differences, an independent PyTorch fp64 autograd route, hand-derived closed
-forms (``tests/golden/``) and invariants of the formula.
+forms (``tests/golden/``) and invariants of the formula; the partial-sum
+update (``add_bf16``) against exact rational arithmetic and hand-worked
+rounding cases.
 """
 from __future__ import annotations
 
@@ -41,8 +43,29 @@ class Oracle:
             f = getattr(lib, name)
             f.argtypes = [i32, i64, i64, vp, vp, f64, vp, vp, vp]
             f.restype = None
+        lib.oracle_add_bf16.argtypes = [i64, vp, vp, vp]
+        lib.oracle_add_bf16.restype = None
         self.lib = lib
         self.path = lib_path
+
+    def add_bf16(self, p_bits: np.ndarray, y_bits: np.ndarray) -> np.ndarray:
+        """Partial-sum update: bf16(p + y), rounded once, ties to even (bit patterns in and out)."""
+        p_bits = np.ascontiguousarray(p_bits, dtype=np.uint16)
+        y_bits = np.ascontiguousarray(y_bits, dtype=np.uint16)
+        assert p_bits.shape == y_bits.shape
+        out = np.empty_like(p_bits)
+        self.lib.oracle_add_bf16(p_bits.size, _p(p_bits), _p(y_bits), _p(out))
+        return out
+
+    def fwd_update(self, src_bits: np.ndarray, p_bits: np.ndarray, y_bits: np.ndarray, w: np.ndarray, eps: float):
+        """Forward whose last source is the updated partial sum bf16(p + y).
+
+        src_bits: the other N-1 sources [N-1][T][D] (N-1 may be 0); p_bits,
+        y_bits: [T][D].  Returns (out, rstd, alpha, p_new bits)."""
+        p_new = self.add_bf16(p_bits, y_bits)
+        srcs = np.concatenate([np.asarray(src_bits, dtype=np.uint16).reshape(-1, *p_new.shape), p_new[None]], axis=0)
+        out, rstd, alpha = self.fwd(srcs, w, eps)
+        return out, rstd, alpha, p_new
 
     def fwd(self, src_bits: np.ndarray, w: np.ndarray, eps: float):
         """Forward on bf16 bit patterns src [N][T][D] (uint16) and fp32 w [D].
@@ -134,6 +157,14 @@ def fwd_f64(x, w, eps):
 
 def bwd_f64(x, w, eps, g):
     return default().bwd_f64(x, w, eps, g)
+
+
+def add_bf16(p_bits, y_bits):
+    return default().add_bf16(p_bits, y_bits)
+
+
+def fwd_update(src_bits, p_bits, y_bits, w, eps):
+    return default().fwd_update(src_bits, p_bits, y_bits, w, eps)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

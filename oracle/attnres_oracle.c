@@ -207,3 +207,38 @@ void oracle_bwd(int N, int64_t T, int64_t D, const uint16_t* src, const float* w
   free(part);
   free(wd);
 }
+
+/* ---- partial-sum update ------------------------------------------------- */
+/* The architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理" lists
+ * the current block's partial sum (the sum of the sub-layer outputs already
+ * computed in the block) as one of the depth sources.  Adding a sub-layer
+ * output y to a partial sum p held in bf16 stores the exact value p + y
+ * rounded once to the nearest bf16, ties to even.  When the block is complete
+ * the same sum is the block's entry among the completed-block sources. */
+
+/* Round a double to the nearest bf16 (8 significant bits, float's exponent
+ * range, subnormals included), ties to even; returns the bit pattern. */
+static uint16_t f64_to_bf16_rne(double v) {
+  if (v != v) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  const double m = frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1: leading bit has weight 2^(e-1) */
+  int keep = 8;                  /* significant bits of a normal bf16 */
+  if (e - 1 < -126) keep -= -126 - (e - 1); /* below the normal range: fixed quantum 2^-133 */
+  const double q = nearbyint(ldexp(m, keep)); /* default rounding mode: nearest, ties to even */
+  const double r = ldexp(q, e - keep);         /* a bf16 value, or 2^128 when it overflows */
+  const float f = (float)r;                    /* exact; 2^128 becomes inf */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+/* out[k] = bf16(p[k] + y[k]) for k < n; all bf16 bit patterns.  The sum of two
+ * doubles widened from bf16 is exact whenever it can matter: if the exponents
+ * differ by more than 44 bits the smaller value is below half a bf16 unit of
+ * the larger and the rounded result is the larger value either way. */
+void oracle_add_bf16(int64_t n, const uint16_t* p, const uint16_t* y, uint16_t* out) {
+  for (int64_t k = 0; k < n; ++k) out[k] = f64_to_bf16_rne(bf16_to_f64(p[k]) + bf16_to_f64(y[k]));
+}

@@ -16,6 +16,7 @@ source (on the CPU, in a temp dir) and asserts every mutant fails some pin.
 from __future__ import annotations
 
 import json
+from fractions import Fraction
 import math
 import os
 import subprocess
@@ -235,7 +236,82 @@ def pin_bf16_entry(orc):
     return fails
 
 
-PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry]
+ROUNDING_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "partial_sum_rounding.json")
+
+
+def _bf16_value(bits: int) -> Fraction:
+    """Exact value of a finite bf16 bit pattern (sign, 8-bit exponent, 7-bit fraction)."""
+    sign = -1 if bits & 0x8000 else 1
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0:
+        return sign * Fraction(f, 1 << 7) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(f, 1 << 7)) * (Fraction(2) ** (e - 127))
+
+
+def _round_to_bf16(v: Fraction, negative_zero: bool = False) -> int:
+    """Nearest bf16 to the exact rational v, ties to even, by exhaustive
+    comparison with the two neighbouring bf16 values (independent of the C
+    oracle's frexp/nearbyint route)."""
+    if v == 0:
+        return 0x8000 if negative_zero else 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a >= (2 - Fraction(1, 1 << 8)) * (Fraction(2) ** 127):
+        return sign | 0x7F80
+    lo, hi = 0, 0x7F7F  # positive finite patterns are ordered like their values
+    while lo < hi:  # largest pattern whose value is <= a
+        mid = (lo + hi + 1) // 2
+        if _bf16_value(mid) <= a:
+            lo = mid
+        else:
+            hi = mid - 1
+    below, above = lo, lo + 1
+    if _bf16_value(below) == a:
+        return sign | below
+    d_lo, d_hi = a - _bf16_value(below), _bf16_value(above) - a
+    if d_lo < d_hi or (d_lo == d_hi and below % 2 == 0):
+        return sign | below
+    return sign | above
+
+
+def pin_partial_sum_update(orc):
+    """bf16(p + y): hand-worked rounding cases, then exact rational arithmetic
+    on random pairs concentrated on near ties and close exponents."""
+    fails = []
+    cases = json.load(open(ROUNDING_GOLDEN))["cases"]
+    p = np.array([int(c["p"], 16) for c in cases], dtype=np.uint16)
+    y = np.array([int(c["y"], 16) for c in cases], dtype=np.uint16)
+    got = orc.add_bf16(p, y)
+    for c, g in zip(cases, got):
+        if int(g) != int(c["expect"], 16):
+            fails.append(f"rounding golden {c['name']}: got {int(g):04X} want {c['expect']}")
+    rng = np.random.default_rng(11)
+    n = 4000
+    # exponents within a few binades of each other (where ties happen), plus spread-out ones
+    e1 = rng.integers(100, 150, n)
+    e2 = np.where(rng.random(n) < 0.7, e1 - rng.integers(0, 10, n), rng.integers(1, 254, n))
+    pb = ((rng.integers(0, 2, n) << 15) | (e1 << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+    yb = ((rng.integers(0, 2, n) << 15) | (np.clip(e2, 1, 254) << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+    got = orc.add_bf16(pb, yb)
+    for a, b, g in zip(pb.tolist(), yb.tolist(), got.tolist()):
+        want = _round_to_bf16(_bf16_value(a) + _bf16_value(b), negative_zero=bool(a & b & 0x8000))
+        if g != want:
+            fails.append(f"rounding {a:04X}+{b:04X}: got {g:04X} want {want:04X}")
+            if len(fails) > 5:
+                break
+    # the fused forward's last source is the updated partial sum
+    src = rng.integers(0x3E00, 0x4100, (2, 3, 16)).astype(np.uint16)
+    pp = rng.integers(0x3E00, 0x4100, (3, 16)).astype(np.uint16)
+    yy = rng.integers(0x3C00, 0x3F00, (3, 16)).astype(np.uint16)
+    w = rng.standard_normal(16).astype(np.float32)
+    out, _, alpha, p_new = orc.fwd_update(src, pp, yy, w, 1e-6)
+    ref_out, _, ref_alpha = orc.fwd(np.concatenate([src, orc.add_bf16(pp, yy)[None]]), w, 1e-6)
+    if not (np.array_equal(out, ref_out) and np.array_equal(alpha, ref_alpha)):
+        fails.append("fwd_update does not use bf16(p + y) as the last source")
+    return fails
+
+
+PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -265,6 +341,10 @@ MUTANTS = {
     "dw_chunks_overwrite": ("dw[d] += part[c * D + d];", "dw[d] = part[c * D + d];"),
     "bf16_widen_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     "w_narrowed": ("wd[d] = (double)w[d];", "wd[d] = (double)(int)(w[d] * 64.0) / 64.0;"),
+    "update_truncates": ("nearbyint(ldexp(m, keep))", "floor(ldexp(m, keep))"),
+    "update_ties_away": ("nearbyint(ldexp(m, keep))", "round(ldexp(m, keep))"),
+    "update_nine_bits": ("int keep = 8;", "int keep = 9;"),
+    "update_drops_output": ("bf16_to_f64(p[k]) + bf16_to_f64(y[k])", "bf16_to_f64(p[k])"),
 }
 
 
