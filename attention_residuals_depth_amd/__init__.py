@@ -15,9 +15,12 @@ The C entry points, declared in ``include/attnres.h``:
     attnres_fwd_sources / attnres_bwd_sources: the same with the N sources
                 (and their gradients) as separate [T][D] tensors, and an
                 accumulate flag for the source gradients.
-    attnres_fwd_decode: the per-source forward for small batches (one
-                workgroup per token), rstd/alpha optional; bitwise the same
-                per-token results as the other forward calls.
+    attnres_fwd_decode: the per-source forward with rstd/alpha optional
+                (decoding / rollout); bitwise the same per-token results as
+                the other forward calls.
+    attnres_fwd_update: the forward whose last source is the current block's
+                partial sum after adding the previous sub-layer's output
+                (partial_out = bf16(partial + delta), in place by default).
 """
 from __future__ import annotations
 
@@ -64,6 +67,8 @@ def library() -> ctypes.CDLL:
         lib.attnres_bwd_sources.restype = ctypes.c_int
         lib.attnres_fwd_decode.argtypes = [pp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_decode.restype = ctypes.c_int
+        lib.attnres_fwd_update.argtypes = [pp, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp, vp]
+        lib.attnres_fwd_update.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -214,6 +219,49 @@ def attnres_fwd_decode(srcs, w: torch.Tensor, eps: float, out=None, save_state: 
     return out, rstd, alpha
 
 
+def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torch.Tensor, eps: float,
+                       partial_out=None, in_place: bool = True, out=None, save_state: bool = True, rstd=None,
+                       alpha=None, stream=None):
+    """Forward on the sources srcs (N-1 separate [T][D] bf16 tensors, possibly
+    empty) plus the updated partial sum bf16(partial + delta) as the last one.
+    The new partial sum goes to partial_out (default: partial itself when
+    in_place, else a new tensor).  Returns (out, rstd, alpha, partial_out);
+    rstd and alpha are None when save_state is False and none is passed."""
+    srcs = list(srcs)
+    if partial.dim() != 2:
+        raise ValueError("partial must be [T][D]")
+    T, D = partial.shape
+    N = len(srcs) + 1
+    if N > MAX_SOURCES:
+        raise ValueError(f"at most {MAX_SOURCES} sources")
+    for i, t in enumerate(srcs):
+        _check(t, f"srcs[{i}]", torch.bfloat16, (T, D))
+    _check(partial, "partial", torch.bfloat16, (T, D))
+    _check(delta, "delta", torch.bfloat16, (T, D))
+    _check(w, "w", torch.float32, (D,))
+    dev = partial.device
+    if partial_out is None:
+        partial_out = partial if in_place else torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _check(partial_out, "partial_out", torch.bfloat16, (T, D))
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    if save_state or rstd is not None or alpha is not None:
+        if rstd is None:
+            rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+        if alpha is None:
+            alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+        _check(rstd, "rstd", torch.float32, (T, N))
+        _check(alpha, "alpha", torch.float32, (T, N))
+    code = library().attnres_fwd_update(_ptr_array(srcs) if srcs else None, partial.data_ptr(), delta.data_ptr(),
+                                        w.data_ptr(), float(eps), N, T, D, partial_out.data_ptr(), out.data_ptr(),
+                                        None if rstd is None else rstd.data_ptr(),
+                                        None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
+    if code != 0:
+        raise AttnResError("attnres_fwd_update", code)
+    return out, rstd, alpha, partial_out
+
+
 def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.Tensor, alpha: torch.Tensor,
                         dsrcs=None, accumulate: bool = False, dw=None, workspace=None, stream=None):
     """Backward on N separate sources.  dsrcs: N separate [T][D] bf16 gradient
@@ -252,4 +300,5 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
 
 
 __all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
+           "attnres_fwd_update",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

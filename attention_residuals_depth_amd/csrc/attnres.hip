@@ -417,9 +417,22 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // 5.79 vs 5.39 TB/s; T = 1: 6.9 vs 7.8 us kernel time).  The w slice is
 // requested first and the row group right behind it, so both latencies
 // overlap; w then goes to the thread's LDS slots while the rows arrive.
-template <int N, int VPT>
-__global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const float* __restrict__ w, float eps, int64_t t0,
-                                                   int32_t D, uint16_t* __restrict__ out,
+//
+// UPDATE: the last source is the current block's partial sum after adding
+// the previous sub-layer's output (architecture figure of "Kimi K3
+// 模型结构（10）"): src.p[N-1] holds the partial sum before the update and
+// `delta` the output to add.  Each thread adds its slice in fp32 and rounds
+// to bf16 once (for two bf16 operands the fp32 sum is exact whenever the
+// rounding can depend on it, so this is the correctly rounded sum), writes
+// the new partial sum to partial_out and uses it as the last source.  This
+// folds the separate elementwise update (read p and y, write p) into the
+// read the operator makes anyway: one row fewer read per token.  In place
+// (partial_out == src.p[N-1]) is fine: a thread rewrites only the slice it
+// has already read.
+template <int N, int VPT, bool UPDATE>
+__global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* __restrict__ delta,
+                                                   uint16_t* partial_out, const float* __restrict__ w, float eps,
+                                                   int64_t t0, int32_t D, uint16_t* __restrict__ out,
                                                    float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
@@ -447,8 +460,23 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const float* __r
   }
   sched_fence();
   uint4 x[N][VPT];
+  uint4 yv[UPDATE ? VPT : 1];
   load_rows<N, VPT>(x, src, t, D, sl);
+  if constexpr (UPDATE) load_row<VPT>(yv, delta, t, D, sl);
   sched_fence();
+  if constexpr (UPDATE) {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(partial_out + t * D, (uint32_t)D * 2u);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float a[8], b[8];
+      unpack8(x[N - 1][k], a);
+      unpack8(yv[k], b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += b[e];
+      x[N - 1][k] = pack8(a);
+      bstore<kAuxStreamStore>(rp, sl.off[k], x[N - 1][k]);
+    }
+  }
   float4* wl = dyn_lds;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
@@ -797,6 +825,8 @@ hipError_t resident_blocks(const void* fn, int threads, size_t lds, int64_t* out
 
 struct FwdArgs {
   SrcRows src;
+  const uint16_t* delta;  // update: output added to the partial sum (src.p[N-1])
+  uint16_t* partial_out;  // update: the new partial sum
   const float* w;
   float eps;
   int64_t T;
@@ -821,17 +851,17 @@ struct BwdArgs {
 
 // One workgroup per token.  The dispatch packet counts work-items in 32 bits,
 // so very large T (possible only for tiny D) is split over several launches.
-template <int N>
+template <int N, bool UPDATE>
 hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt>);
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt, UPDATE>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)s.threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_kernel<N, kVpt>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src, a.w,
-                       a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    hipLaunchKernelGGL((fwd_kernel<N, kVpt, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
+                       a.delta, a.partial_out, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -856,17 +886,17 @@ hipError_t run_bwd_n(const LaunchShape& s, bool acc, hipStream_t st, const BwdAr
   return s.pipe ? launch_bwd_n<N, true, false, 512>(s, st, a) : launch_bwd_n<N, false, false, 1024>(s, st, a);
 }
 
-hipError_t run_fwd(int32_t N, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+hipError_t run_fwd(int32_t N, const LaunchShape& s, bool update, hipStream_t st, const FwdArgs& a) {
   switch (N) {
-    case 1: return run_fwd_n<1>(s, st, a);
-    case 2: return run_fwd_n<2>(s, st, a);
-    case 3: return run_fwd_n<3>(s, st, a);
-    case 4: return run_fwd_n<4>(s, st, a);
-    case 5: return run_fwd_n<5>(s, st, a);
-    case 6: return run_fwd_n<6>(s, st, a);
-    case 7: return run_fwd_n<7>(s, st, a);
-    case 8: return run_fwd_n<8>(s, st, a);
-    case 9: return run_fwd_n<9>(s, st, a);
+    case 1: return update ? run_fwd_n<1, true>(s, st, a) : run_fwd_n<1, false>(s, st, a);
+    case 2: return update ? run_fwd_n<2, true>(s, st, a) : run_fwd_n<2, false>(s, st, a);
+    case 3: return update ? run_fwd_n<3, true>(s, st, a) : run_fwd_n<3, false>(s, st, a);
+    case 4: return update ? run_fwd_n<4, true>(s, st, a) : run_fwd_n<4, false>(s, st, a);
+    case 5: return update ? run_fwd_n<5, true>(s, st, a) : run_fwd_n<5, false>(s, st, a);
+    case 6: return update ? run_fwd_n<6, true>(s, st, a) : run_fwd_n<6, false>(s, st, a);
+    case 7: return update ? run_fwd_n<7, true>(s, st, a) : run_fwd_n<7, false>(s, st, a);
+    case 8: return update ? run_fwd_n<8, true>(s, st, a) : run_fwd_n<8, false>(s, st, a);
+    case 9: return update ? run_fwd_n<9, true>(s, st, a) : run_fwd_n<9, false>(s, st, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -889,10 +919,16 @@ hipError_t run_bwd(int32_t N, const LaunchShape& s, bool acc, hipStream_t st, co
 // ---------------------------------------------------------------------------
 // Host-side validation and launch, shared by the stacked and per-source calls
 // ---------------------------------------------------------------------------
+// srcs: N source rows (with an update, srcs[N-1] is the partial sum before
+// it).  allow_no_state: rstd and alpha may both be NULL (decoding calls).
+// delta / partial_out: the update's addend and result, or both NULL.
 attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T, int32_t D,
-                        uint16_t* out, float* rstd, float* alpha, bool decode, void* stream) {
+                        uint16_t* out, float* rstd, float* alpha, bool allow_no_state, const uint16_t* delta,
+                        uint16_t* partial_out, void* stream) {
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
-  Range ins[ATTNRES_MAX_SOURCES + 1];
+  const bool update = delta != nullptr || partial_out != nullptr;
+  if (update && (delta == nullptr || partial_out == nullptr)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  Range ins[ATTNRES_MAX_SOURCES + 2];
   SrcRows rows{};
   for (int i = 0; i < N; ++i) {
     if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -900,21 +936,27 @@ attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, 
     ins[i] = range_of(srcs[i], nTD * 2);
   }
   ins[N] = range_of(w, (size_t)D * 4);
-  // rstd and alpha are written together or (decode call only) not at all
+  ins[N + 1] = range_of(delta, update ? nTD * 2 : 0);
+  if (!aligned(delta, 16) || !aligned(partial_out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  // rstd and alpha are written together or (decoding calls only) not at all
   const bool save = rstd != nullptr || alpha != nullptr;
   if (out == nullptr || (save && (rstd == nullptr || alpha == nullptr))) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!save && !decode) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!save && !allow_no_state) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  const Range outs[3] = {range_of(out, nTD * 2), range_of(rstd, save ? nTN * 4 : 0), range_of(alpha, save ? nTN * 4 : 0)};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b <= N; ++b)
-      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
-    for (int b = a + 1; b < 3; ++b)
+  const Range outs[4] = {range_of(out, nTD * 2), range_of(rstd, save ? nTN * 4 : 0),
+                         range_of(alpha, save ? nTN * 4 : 0), range_of(partial_out, update ? nTD * 2 : 0)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b <= N + 1; ++b) {
+      // the partial sum may be updated in place: exactly its own buffer
+      const bool in_place = a == 3 && b == N - 1 && partial_out == srcs[N - 1];
+      if (!in_place && overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    }
+    for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   const LaunchShape s = shape_for(D);
-  const FwdArgs args{rows, w, eps, T, D, out, rstd, alpha};
-  const hipError_t e = run_fwd(N, s, reinterpret_cast<hipStream_t>(stream), args);
+  const FwdArgs args{rows, delta, partial_out, w, eps, T, D, out, rstd, alpha};
+  const hipError_t e = run_fwd(N, s, update, reinterpret_cast<hipStream_t>(stream), args);
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
@@ -997,7 +1039,7 @@ extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float
   if (src == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   const uint16_t* srcs[ATTNRES_MAX_SOURCES];
   for (int i = 0; i < N; ++i) srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, stream);
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
 }
 
 extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
@@ -1007,7 +1049,7 @@ extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const
   if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
   if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, stream);
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
 }
 
 extern "C" attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
@@ -1017,7 +1059,22 @@ extern "C" attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const 
   if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
   if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, true, stream);
+  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, true, nullptr, nullptr, stream);
+}
+
+extern "C" attnres_status attnres_fwd_update(const uint16_t* const* srcs, const uint16_t* partial,
+                                             const uint16_t* delta, const float* w, float eps, int32_t N, int64_t T,
+                                             int32_t D, uint16_t* partial_out, uint16_t* out, float* rstd,
+                                             float* alpha, void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return ATTNRES_OK;
+  if ((N > 1 && srcs == nullptr) || partial == nullptr || delta == nullptr || partial_out == nullptr)
+    return ATTNRES_ERR_INVALID_ARGUMENT;
+  const uint16_t* all[ATTNRES_MAX_SOURCES];
+  for (int i = 0; i + 1 < N; ++i) all[i] = srcs[i];
+  all[N - 1] = partial;
+  return fwd_impl(all, w, eps, N, T, D, out, rstd, alpha, true, delta, partial_out, stream);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,

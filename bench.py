@@ -209,8 +209,10 @@ def sweep(ar, torch, dev, reps=20):
 
 def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
     """Per-source calls (separately allocated sources and gradients) at T=32768,
-    N=9: the forward, the overwriting backward and the accumulating backward
-    (which also reads the old gradients: +2ND bytes per token)."""
+    N=9: the forward, the overwriting backward, the accumulating backward (which
+    also reads the old gradients: +2ND bytes per token), and the forward fused
+    with the partial-sum update next to the unfused route (elementwise add, then
+    the forward), both counted at the fused call's algorithmic bytes."""
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     srcs = [(torch.randn((T, D), device=dev, generator=g) * (1 + 12 * i) ** 0.5).to(torch.bfloat16) for i in range(N)]
@@ -231,20 +233,68 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
                                                                   accumulate=True, dw=dw, workspace=ws),
                                    bb + be + T * 2 * N * D),
     }
+    # partial-sum update fused into the forward (last source = bf16(p + y)),
+    # against the unfused route: a separate elementwise add, then the forward
+    p = srcs[-1].clone()
+    y = (torch.randn((T, D), device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    upd_bytes = T * (2 * (N + 1) * D + 4 * D + 8 * N) + 4 * D
+
+    def unfused():
+        torch.add(p, y, out=p)
+        ar.attnres_fwd_sources(srcs[:-1] + [p], w, 1e-6, out=out, rstd=rstd, alpha=alpha)
+
+    calls["fwd_update_fused"] = (lambda: ar.attnres_fwd_update(srcs[:-1], p, y, w, 1e-6, out=out, rstd=rstd,
+                                                               alpha=alpha), upd_bytes)
+    calls["fwd_update_unfused"] = (unfused, upd_bytes)
     for name, (fn, nbytes) in calls.items():
-        ms = []
-        for r in range(reps + 3):
-            flush.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            if r >= 3:
-                ms.append(e0.elapsed_time(e1))
-        m = sorted(ms)[len(ms) // 2]
+        m = _median_ms(torch, flush, fn, reps)
         print(json.dumps({"sweep": True, "call": name, "N": N, "T": T, "D": D, "ms": m,
                           "GBps": nbytes / m / 1e6, "frac_of_8TBps": nbytes / m / 1e6 / HBM_PEAK_GBPS}), flush=True)
+    del srcs, dsrcs, dout, p, y
+    torch.cuda.empty_cache()
+    sweep_decode(ar, torch, dev, flush)
+
+
+def _median_ms(torch, flush, fn, reps):
+    """Median event time of fn over reps calls, caches flushed before each."""
+    ms = []
+    for r in range(reps + 3):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 3:
+            ms.append(e0.elapsed_time(e1))
+    return sorted(ms)[len(ms) // 2]
+
+
+def sweep_decode(ar, torch, dev, flush, N=9, D=7168):
+    """Decoding-size batches through attnres_fwd_decode (no saved state): one
+    flushed call (latency, inputs in HBM) and the mean of 200 back-to-back calls
+    (inputs cache-resident; at these sizes the host's call rate bounds it)."""
+    for T in (1, 8, 64, 256, 1024):
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        srcs = [(torch.randn((T, D), device=dev, generator=g) * (1 + 12 * i) ** 0.5).to(torch.bfloat16)
+                for i in range(N)]
+        w = torch.randn(D, device=dev, generator=g) / D ** 0.5
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        fn = lambda: ar.attnres_fwd_decode(srcs, w, 1e-6, out=out)
+        cold_us = _median_ms(torch, flush, fn, 20) * 1e3
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(200):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_us = e0.elapsed_time(e1) / 200 * 1e3
+        print(json.dumps({"sweep": True, "call": "fwd_decode", "N": N, "T": T, "D": D, "cold_us": cold_us,
+                          "back_to_back_us": warm_us}), flush=True)
 
 
 def main():

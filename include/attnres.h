@@ -145,6 +145,37 @@ attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, f
                                   int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
+ * Forward fused with the update of the current block's partial sum.  The
+ * depth sources of a sub-layer are the embedding, the completed block sums
+ * and the current block's partial sum -- the sum of the sub-layer outputs
+ * already computed in the block (architecture figure of "Kimi K3
+ * 模型结构（10）：RL 与服务中的状态管理").  After each sub-layer its output y is
+ * added to that partial sum; this call does the addition while reading the
+ * sources for the next sub-layer's operator, instead of in a separate pass:
+ *   partial_out = bf16(partial + delta)   exact sum, rounded once to nearest
+ *                                         even (also the completed block sum
+ *                                         when delta is the block's last
+ *                                         sub-layer output)
+ *   then the forward of attnres_fwd_sources on {srcs[0..N-2], partial_out}.
+ * Bytes per token drop from 2ND + 2D + 8N (+ 6D for a separate update pass)
+ * to 2(N+1)D + 4D + 8N.
+ *   srcs         host array of the N-1 other sources (device pointers, [T][D]
+ *                bf16); may be NULL when N == 1.
+ *   partial      [T][D] bf16 partial sum before the update.
+ *   delta        [T][D] bf16 sub-layer output to add.
+ *   partial_out  [T][D] bf16 updated partial sum; may be `partial` itself
+ *                (in-place update), otherwise it must not overlap any input.
+ *   out, rstd, alpha, w, eps, N (total sources, partial included), T, D
+ *                as attnres_fwd_decode (rstd and alpha both NULL when no
+ *                backward follows).
+ * The backward is attnres_bwd_sources with partial_out as the last source;
+ * the gradient of partial_out then flows unchanged to both partial and delta.
+ */
+attnres_status attnres_fwd_update(const uint16_t* const* srcs, const uint16_t* partial, const uint16_t* delta,
+                                  const float* w, float eps, int32_t N, int64_t T, int32_t D, uint16_t* partial_out,
+                                  uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
  * Backward with per-source pointers, optionally accumulating the source
  * gradients.  A completed block sum is a source of every later sub-layer's
  * AttnRes, so its gradient is the sum of those operators' contributions:

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_declared_symbols():
     lib = ar.library()
     names = _declared()
     assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
-                     "attnres_bwd_sources"]
+                     "attnres_fwd_update", "attnres_bwd_sources"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -209,3 +209,28 @@ def test_only_the_decode_call_may_skip_the_saved_state():
     g = 1 << 30
     assert _fwd(rstd=0, alpha=0) == INVALID
     assert _fwd_src(_arr([g, 3 * g, 5 * g]), rstd=None, alpha=None) == INVALID
+
+
+def _upd(srcs, partial, delta, partial_out, N=3, T=16, D_=D, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
+         alpha=(1 << 36) + (1 << 31)):
+    return ar.library().attnres_fwd_update(srcs, partial, delta, w, 1e-6, N, T, D_, partial_out, out, rstd, alpha,
+                                           None)
+
+
+def test_fwd_update_rejects():
+    g = 1 << 30
+    srcs = _arr([g, 3 * g])
+    p, y = 5 * g, 7 * g
+    assert _upd(srcs, 0, y, p) == INVALID  # partial missing
+    assert _upd(srcs, p, 0, p) == INVALID  # delta missing
+    assert _upd(srcs, p, y, 0) == INVALID  # partial_out missing
+    assert _upd(None, p, y, p) == INVALID  # N = 3 needs the two other sources
+    assert _upd(srcs, p, y, p + 64) == INVALID  # partial_out overlapping partial, not equal to it
+    assert _upd(srcs, p, y, y) == INVALID  # partial_out on delta
+    assert _upd(srcs, p, y, 3 * g) == INVALID  # partial_out on another source
+    assert _upd(_arr([g, p]), p, y, p) == INVALID  # in place while the partial sum is also another source
+    assert _upd(srcs, p, y, 9 * g, out=9 * g + 128) == INVALID  # out overlapping partial_out
+    assert _upd(srcs, p, y + 8, p) == INVALID  # misaligned delta
+    assert _upd(srcs, p, y, p, rstd=None) == INVALID  # saved state is both or neither
+    assert _upd(srcs, p, y, p, N=10) == INVALID
+    assert _upd(None, p, y, p, T=0) == OK  # nothing to do
