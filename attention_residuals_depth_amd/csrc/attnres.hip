@@ -609,13 +609,16 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
   }
 }
 
-// With PIPE, register sets A and B alternate as in the forward kernel, each
-// refilled with the workgroup's token two steps ahead once its token is done.
-// With ACC (no prefetch) the old gradients are loaded during the reduction.
-// Dynamic LDS holds w and the workgroup's running dw, in the thread's private
-// slots.
-template <int N, int VPT, bool PIPE, bool ACC, int MAXT>
-__global__ void __launch_bounds__(MAXT) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
+// With PIPE, two register sets A and B alternate: while the workgroup works
+// on the token in one set, the next token's loads are in flight in the other,
+// and a set is refilled with the workgroup's token two steps ahead as soon as
+// its token is done.  Loads past the last token use size-0 descriptors and
+// scheduling fences keep each prefetch where it is issued, so the in-order
+// wait counts only ever wait for the oldest row group.  With ACC (no
+// prefetch) the old gradients are loaded during the reduction.  Dynamic LDS
+// holds w and the workgroup's running dw, in the thread's private slots.
+template <int N, int VPT, bool PIPE, bool ACC>
+__global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
                                                    const float* __restrict__ w, const float* __restrict__ rstd,
                                                    const float* __restrict__ alpha, int64_t T, int32_t D, int32_t P,
                                                    DstRows dsrc, float* __restrict__ ws) {
@@ -739,25 +742,38 @@ __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
 // ---------------------------------------------------------------------------
 struct LaunchShape {
   bool pipe;    // backward: prefetch the next token's rows into a second register set
+  int vpt;      // 16-byte vectors per thread per row
   int threads;  // workgroup size
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
-constexpr int kVpt = 2;  // 16-byte vectors per thread per row
+constexpr int kFwdVpt = 2;  // forward: two vectors per thread (448 threads at D = 7168)
 
-// Depends only on D: the per-token reduction tree (two vectors per thread,
-// blockDim = D/16 rounded up to whole waves) never changes with T or with the
-// call, so every forward call gives bitwise the same per-token results.
-// Backward: D <= 8192 uses the prefetching variant (<= 512 threads), larger D
-// (up to 1024 threads) the one without prefetch.
-LaunchShape shape_for(int32_t D) {
+LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
   const int V = D / 8;
   LaunchShape s;
-  s.pipe = V <= 2 * 512;
-  const int need = (V + kVpt - 1) / kVpt;
+  s.pipe = pipe;
+  s.vpt = vpt;
+  const int need = (V + vpt - 1) / vpt;
   s.threads = ((need + kWave - 1) / kWave) * kWave;
-  s.lds = (size_t)kVpt * (size_t)s.threads * 32;
+  s.lds = (size_t)vpt * (size_t)s.threads * 32;
   return s;
+}
+
+// Both shapes depend only on D, so the per-token reduction trees never change
+// with T or with the call: every forward call gives bitwise the same
+// per-token results, and so does every backward call (with or without
+// accumulation, stacked or per source).
+// Forward: two vectors per thread, blockDim = D/16 rounded up to whole waves.
+LaunchShape fwd_shape(int32_t D) { return make_shape(D, kFwdVpt, false); }
+
+// Backward: D <= 8192 takes one vector per thread (896 threads, 14 waves at
+// D = 7168) with a two-token prefetch; measured 1-2% faster on MI355X than
+// two vectors per thread with 7 waves.  Larger D takes two vectors per thread
+// (up to 1024 threads) without prefetch.
+LaunchShape bwd_shape(int32_t D) {
+  const int V = D / 8;
+  return V <= 1024 ? make_shape(D, 1, true) : make_shape(D, 2, false);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -853,14 +869,14 @@ struct BwdArgs {
 // so very large T (possible only for tiny D) is split over several launches.
 template <int N, bool UPDATE>
 hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kVpt, UPDATE>);
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kFwdVpt, UPDATE>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)s.threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_kernel<N, kVpt, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
+    hipLaunchKernelGGL((fwd_kernel<N, kFwdVpt, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
                        a.delta, a.partial_out, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -868,22 +884,23 @@ hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
   return hipSuccess;
 }
 
-template <int N, bool PIPE, bool ACC, int MAXT>
+template <int N, int VPT, bool PIPE, bool ACC>
 hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, kVpt, PIPE, ACC, MAXT>);
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, PIPE, ACC>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   // one workgroup per dw partial row (P = min(T, ATTNRES_DW_PARTIALS))
-  hipLaunchKernelGGL((bwd_kernel<N, kVpt, PIPE, ACC, MAXT>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
+  hipLaunchKernelGGL((bwd_kernel<N, VPT, PIPE, ACC>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
                      2 * s.lds, st, a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();
 }
 
 template <int N>
 hipError_t run_bwd_n(const LaunchShape& s, bool acc, hipStream_t st, const BwdArgs& a) {
-  if (acc) return s.pipe ? launch_bwd_n<N, false, true, 512>(s, st, a) : launch_bwd_n<N, false, true, 1024>(s, st, a);
-  return s.pipe ? launch_bwd_n<N, true, false, 512>(s, st, a) : launch_bwd_n<N, false, false, 1024>(s, st, a);
+  // the accumulating variant keeps the old gradients instead of a second row group: no prefetch
+  if (s.vpt == 1) return acc ? launch_bwd_n<N, 1, false, true>(s, st, a) : launch_bwd_n<N, 1, true, false>(s, st, a);
+  return acc ? launch_bwd_n<N, 2, false, true>(s, st, a) : launch_bwd_n<N, 2, false, false>(s, st, a);
 }
 
 hipError_t run_fwd(int32_t N, const LaunchShape& s, bool update, hipStream_t st, const FwdArgs& a) {
@@ -954,7 +971,7 @@ attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, 
     for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
-  const LaunchShape s = shape_for(D);
+  const LaunchShape s = fwd_shape(D);
   const FwdArgs args{rows, delta, partial_out, w, eps, T, D, out, rstd, alpha};
   const hipError_t e = run_fwd(N, s, update, reinterpret_cast<hipStream_t>(stream), args);
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
@@ -1016,7 +1033,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, const
     for (int b = a + 1; b < nout; ++b)
       if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
-  const LaunchShape s = shape_for(D);
+  const LaunchShape s = bwd_shape(D);
   const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
   float* ws = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
