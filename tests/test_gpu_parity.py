@@ -17,7 +17,7 @@ import attention_residuals_depth_amd as ar
 import oracle
 import synth
 from parity import (DEV, bf16_dev_to_f64, check_tokens, full_compare, rel_l2, run_gpu, sample_tokens,
-                    to_dev_bf16, within_tolerance, TOL_DW_REL_L2)
+                    to_dev_bf16, within_tolerance, TOL_DW_REL_L2, TOL_RSTD_REL)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,11 @@ def test_workload_full(cfg):
 
 
 # (N, T, D): ragged rows (D/8 not a multiple of the workgroup), the smallest and
-# largest D, a single token, T not a multiple of the dw chunk count, and the
-# two-vectors-per-thread path (D > 8192).
+# largest D, a single token, T not a multiple of the number of backward
+# workgroups, the largest one-vector backward (D = 8192: 1024 threads) and the
+# two-vectors-per-thread backward (D > 8192).
 SHAPES = [(1, 5, 7168), (2, 1, 7168), (9, 3, 8), (9, 37, 64), (5, 130, 1000), (3, 130, 4104),
-          (4, 600, 7176), (9, 513, 7168), (7, 17, 8200), (9, 9, ar.MAX_D), (6, 70, 12288)]
+          (4, 600, 7176), (9, 513, 7168), (8, 40, 8192), (7, 17, 8200), (9, 9, ar.MAX_D), (6, 70, 12288)]
 
 
 @pytest.mark.parametrize("N,T,D", SHAPES, ids=lambda v: str(v))
@@ -151,3 +152,27 @@ def test_dw_over_token_slices_adds_up():
         dws.append(dw.cpu().double().numpy())
     _, _, _, _, dw_all = run_gpu(to_dev_bf16(src), w_d, wl.eps, to_dev_bf16(dout))
     assert rel_l2(dw_all.cpu().double().numpy(), dws[0] + dws[1]) <= 1e-5
+
+
+@pytest.mark.slow
+def test_forward_split_over_launches():
+    """T above what one dispatch can hold (2^32 - 1 work-items): D = 8 gives 64-thread
+    workgroups, so the forward is split into launches of 67,108,863 tokens.  N = 1:
+    out must equal the source bit for bit and alpha be exactly 1 everywhere; rstd is
+    checked against the oracle on tokens around the launch boundary."""
+    D, per_launch = 8, (2 ** 32 - 1) // 64
+    T = per_launch + 37
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    print(f"[parity] split launches T={T} D={D}: generating", flush=True)
+    src = (torch.randn((1, T, D), device=DEV, generator=g) * 3).to(torch.bfloat16)
+    w = torch.randn(D, device=DEV, generator=g)
+    out, rstd, alpha = ar.attnres_fwd(src, w, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), src[0].view(torch.int16))
+    assert bool((alpha == 1.0).all())
+    toks = torch.tensor([0, 1, per_launch - 2, per_launch - 1, per_launch, per_launch + 1, T - 1], device=DEV)
+    rows = src[:, toks].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    _, o_rstd, _ = oracle.fwd(rows, w.cpu().numpy(), 1e-6)
+    got = rstd[toks].cpu().double().numpy()
+    assert float(np.max(np.abs(got / o_rstd - 1))) <= TOL_RSTD_REL
