@@ -63,7 +63,8 @@ typedef enum {
 #define ATTNRES_MAX_SOURCES 9
 /* Largest hidden size the kernels accept (a row group lives on chip). */
 #define ATTNRES_MAX_D 16384
-/* Rows of per-workgroup dw partial sums in the backward workspace. */
+/* Rows of dw partial sums in the backward workspace: with P = min(T, 256)
+ * backward workgroups, row c holds the sum over tokens c, c+P, c+2P, ... */
 #define ATTNRES_DW_PARTIALS 256
 /* Bytes of device workspace attnres_bwd needs for hidden size D. */
 #define ATTNRES_BWD_WORKSPACE_BYTES(D) ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float))
@@ -74,7 +75,8 @@ typedef enum {
  *   w     [D]       fp32   pseudo-query of this sub-layer
  *   eps             fp32   finite, >= 0; added to the mean square inside the root
  *   N               1 .. ATTNRES_MAX_SOURCES
- *   T               >= 0 tokens (T == 0 enqueues nothing and returns OK)
+ *   T               >= 0 tokens, T*N*D <= 2^40 (T == 0 enqueues nothing and
+ *                   returns OK)
  *   D               8 .. ATTNRES_MAX_D, a multiple of 8
  *   out   [T][D]    bf16   sum_i alpha_i x_i, fp32-accumulated, rounded to nearest even
  *   rstd  [T][N]    fp32   saved for the backward pass

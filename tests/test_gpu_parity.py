@@ -3,8 +3,9 @@
 Small and medium workloads are compared element by element on every output.
 The full-size workloads (T = 32768 .. 262144, D = 7168, N up to 9) run on the
 GPU in the same launch configuration the benchmark uses; out, alpha, rstd and
-dsources are compared on sampled tokens (first/last, dw-chunk boundaries and
-seeded random tokens, each recomputed by the oracle), and dw -- a sum over all
+dsources are compared on sampled tokens (first/last, the first and last backward
+workgroup's first tokens, the start of the ragged last round of tokens and seeded
+random tokens, each recomputed by the oracle), and dw -- a sum over all
 tokens -- is compared against the oracle's dw over the whole batch.
 """
 from __future__ import annotations
