@@ -61,13 +61,13 @@ def library() -> ctypes.CDLL:
         lib.attnres_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, sz, vp]
         lib.attnres_bwd.restype = ctypes.c_int
         pp = ctypes.POINTER(ctypes.c_void_p)
-        lib.attnres_fwd_sources.argtypes = [pp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_sources.argtypes = [pp, i64, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_sources.restype = ctypes.c_int
-        lib.attnres_bwd_sources.argtypes = [vp, pp, vp, vp, vp, i32, i64, i32, pp, i32, vp, vp, sz, vp]
+        lib.attnres_bwd_sources.argtypes = [vp, pp, i64, vp, vp, vp, i32, i64, i32, pp, i64, i32, vp, vp, sz, vp]
         lib.attnres_bwd_sources.restype = ctypes.c_int
-        lib.attnres_fwd_decode.argtypes = [pp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_decode.argtypes = [pp, i64, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_decode.restype = ctypes.c_int
-        lib.attnres_fwd_update.argtypes = [pp, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp, vp]
+        lib.attnres_fwd_update.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp, vp]
         lib.attnres_fwd_update.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -158,21 +158,49 @@ def _ptr_array(tensors):
     return arr
 
 
+def _rows(t: torch.Tensor, name: str, T: int, D: int) -> int:
+    """Check a [T][D] bf16 row set whose rows may be spaced apart (a view of one
+    source in a token-interleaved [T][N][D] cache); returns its row pitch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if tuple(t.shape) != (T, D):
+        raise ValueError(f"{name} must have shape {(T, D)}, got {tuple(t.shape)}")
+    if T > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return D if T <= 1 else t.stride(0)
+
+
 def _sources(srcs, name):
+    """Validate N source row sets sharing one row pitch; returns (srcs, T, D, pitch)."""
     srcs = list(srcs)
     if not 1 <= len(srcs) <= MAX_SOURCES:
         raise ValueError(f"{name} must hold 1..{MAX_SOURCES} tensors")
     if srcs[0].dim() != 2:
         raise ValueError(f"{name}[i] must be [T][D]")
     T, D = srcs[0].shape
-    for i, t in enumerate(srcs):
-        _check(t, f"{name}[{i}]", torch.bfloat16, (T, D))
-    return srcs, T, D
+    return srcs, T, D, _common_pitch(srcs, name, T, D)
+
+
+def _common_pitch(tensors, name, T, D, pitch=None):
+    for i, t in enumerate(tensors):
+        p = _rows(t, f"{name}[{i}]", T, D)
+        if T > 1:
+            if pitch is None:
+                pitch = p
+            elif p != pitch:
+                raise ValueError(f"all of {name} must share one row pitch ({pitch} vs {p})")
+    return D if pitch is None else pitch
 
 
 def attnres_fwd_sources(srcs, w: torch.Tensor, eps: float, out=None, rstd=None, alpha=None, stream=None):
-    """Forward on N separate [T][D] bf16 sources (no stacking copy)."""
-    srcs, T, D = _sources(srcs, "srcs")
+    """Forward on N [T][D] bf16 sources (no stacking copy).  Each source may be
+    a separate tensor or a strided view (e.g. cache[:, i, :] of a [T][N][D]
+    cache); all must share one row pitch."""
+    srcs, T, D, pitch = _sources(srcs, "srcs")
     N = len(srcs)
     _check(w, "w", torch.float32, (D,))
     dev = srcs[0].device
@@ -185,7 +213,7 @@ def attnres_fwd_sources(srcs, w: torch.Tensor, eps: float, out=None, rstd=None, 
     _check(out, "out", torch.bfloat16, (T, D))
     _check(rstd, "rstd", torch.float32, (T, N))
     _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_sources(_ptr_array(srcs), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+    code = library().attnres_fwd_sources(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
                                          rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream))
     if code != 0:
         raise AttnResError("attnres_fwd_sources", code)
@@ -197,7 +225,7 @@ def attnres_fwd_decode(srcs, w: torch.Tensor, eps: float, out=None, save_state: 
     """Small-batch forward on N separate [T][D] bf16 sources.  Writes rstd and
     alpha only with save_state=True (or when they are passed).  Returns
     (out, rstd, alpha), the last two None when not saved."""
-    srcs, T, D = _sources(srcs, "srcs")
+    srcs, T, D, pitch = _sources(srcs, "srcs")
     N = len(srcs)
     _check(w, "w", torch.float32, (D,))
     dev = srcs[0].device
@@ -211,7 +239,7 @@ def attnres_fwd_decode(srcs, w: torch.Tensor, eps: float, out=None, save_state: 
             alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
         _check(rstd, "rstd", torch.float32, (T, N))
         _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_decode(_ptr_array(srcs), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+    code = library().attnres_fwd_decode(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
                                         None if rstd is None else rstd.data_ptr(),
                                         None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
     if code != 0:
@@ -234,15 +262,18 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
     N = len(srcs) + 1
     if N > MAX_SOURCES:
         raise ValueError(f"at most {MAX_SOURCES} sources")
-    for i, t in enumerate(srcs):
-        _check(t, f"srcs[{i}]", torch.bfloat16, (T, D))
-    _check(partial, "partial", torch.bfloat16, (T, D))
+    pitch = _common_pitch(srcs + [partial], "srcs+partial", T, D)
     _check(delta, "delta", torch.bfloat16, (T, D))
     _check(w, "w", torch.float32, (D,))
     dev = partial.device
     if partial_out is None:
-        partial_out = partial if in_place else torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    _check(partial_out, "partial_out", torch.bfloat16, (T, D))
+        if in_place:
+            partial_out = partial
+        elif pitch == D:
+            partial_out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        else:
+            raise ValueError("with strided sources pass partial_out (a row set of the same pitch)")
+    _common_pitch([partial_out], "partial_out", T, D, pitch)
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, (T, D))
@@ -253,7 +284,7 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
             alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
         _check(rstd, "rstd", torch.float32, (T, N))
         _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_update(_ptr_array(srcs) if srcs else None, partial.data_ptr(), delta.data_ptr(),
+    code = library().attnres_fwd_update(_ptr_array(srcs) if srcs else None, pitch, partial.data_ptr(), delta.data_ptr(),
                                         w.data_ptr(), float(eps), N, T, D, partial_out.data_ptr(), out.data_ptr(),
                                         None if rstd is None else rstd.data_ptr(),
                                         None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
@@ -266,8 +297,9 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
                         dsrcs=None, accumulate: bool = False, dw=None, workspace=None, stream=None):
     """Backward on N separate sources.  dsrcs: N separate [T][D] bf16 gradient
     tensors (allocated if None); with accumulate=True the new gradients are
-    added to their contents.  Returns (dsrcs, dw)."""
-    srcs, T, D = _sources(srcs, "srcs")
+    added to their contents.  Sources and gradients may be strided views (one
+    row pitch for the sources, one for the gradients).  Returns (dsrcs, dw)."""
+    srcs, T, D, pitch = _sources(srcs, "srcs")
     N = len(srcs)
     _check(dout, "dout", torch.bfloat16, (T, D))
     _check(w, "w", torch.float32, (D,))
@@ -281,8 +313,7 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     dsrcs = list(dsrcs)
     if len(dsrcs) != N:
         raise ValueError("dsrcs must hold one tensor per source")
-    for i, t in enumerate(dsrcs):
-        _check(t, f"dsrcs[{i}]", torch.bfloat16, (T, D))
+    dpitch = _common_pitch(dsrcs, "dsrcs", T, D)
     if dw is None:
         dw = torch.empty((D,), dtype=torch.float32, device=dev)
     if workspace is None:
@@ -291,8 +322,8 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), w.data_ptr(), rstd.data_ptr(),
-                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), 1 if accumulate else 0,
+    code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), pitch, w.data_ptr(), rstd.data_ptr(),
+                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), dpitch, 1 if accumulate else 0,
                                          dw.data_ptr(), workspace.data_ptr(), ws_bytes, _stream_handle(stream))
     if code != 0:
         raise AttnResError("attnres_bwd_sources", code)

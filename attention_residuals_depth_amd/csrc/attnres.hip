@@ -261,14 +261,18 @@ __device__ __forceinline__ void stage_w(const float* __restrict__ w, int32_t D, 
   }
 }
 
-// Per-source row bases: row (i, t) of a [T][D] bf16 tensor starts at p[i] + t*D.
-// Stacked [N][T][D] sources use p[i] = src + i*T*D; separately allocated
-// sources pass their own bases.  Passed by value (kernel arguments).
+// Per-source rows: row (i, t) starts at p[i] + t*pitch (elements, pitch >= D).
+// Stacked [N][T][D] sources use p[i] = src + i*T*D and pitch D; separately
+// allocated sources pass their own bases and pitch D; sources interleaved by
+// token ([T][N][D]) use p[i] = base + i*D and pitch N*D.  Passed by value
+// (kernel arguments).
 struct SrcRows {
   const uint16_t* p[ATTNRES_MAX_SOURCES];
+  int64_t pitch;
 };
 struct DstRows {
   uint16_t* p[ATTNRES_MAX_SOURCES];
+  int64_t pitch;
 };
 
 // This thread's slice of token t's N source rows; each row's descriptor is
@@ -284,7 +288,7 @@ __device__ __forceinline__ void load_rows(uint4 (&x)[N][VPT], const Rows& rows, 
   const uint32_t bytes = valid ? (uint32_t)D * 2u : 0u;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(rows.p[i] + tt * D, bytes);
+    const __amdgpu_buffer_rsrc_t r = rsrc(rows.p[i] + tt * rows.pitch, bytes);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) x[i][k] = bload<kAuxStreamLoad>(r, sl.off[k]);
   }
@@ -465,7 +469,7 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* 
   if constexpr (UPDATE) load_row<VPT>(yv, delta, t, D, sl);
   sched_fence();
   if constexpr (UPDATE) {
-    const __amdgpu_buffer_rsrc_t rp = rsrc(partial_out + t * D, (uint32_t)D * 2u);
+    const __amdgpu_buffer_rsrc_t rp = rsrc(partial_out + t * src.pitch, (uint32_t)D * 2u);  // the sources' layout
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float a[8], b[8];
@@ -590,7 +594,7 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[e] = o[e] + d[e];
       }
-      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc.p[i] + t * c.D, (uint32_t)c.D * 2u);
+      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc.p[i] + t * c.dsrc.pitch, (uint32_t)c.D * 2u);
       bstore<kAuxStreamStore>(rd, sl.off[k], pack8(d));
     }
     store8(c.dwl, sl.slot[k], dwr);
@@ -778,16 +782,41 @@ LaunchShape bwd_shape(int32_t D) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// The bytes a buffer argument covers: `rows` rows of `row_bytes` bytes, one
+// every `pitch` bytes, from `lo` (a dense buffer is one row).
 struct Range {
-  uintptr_t lo, hi;  // [lo, hi)
+  uintptr_t lo;
+  uint64_t rows, row_bytes, pitch;
 };
 
-Range range_of(const void* p, size_t bytes) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  return Range{a, a + bytes};
+Range range_of(const void* p, size_t bytes) { return Range{reinterpret_cast<uintptr_t>(p), 1, bytes, bytes}; }
+
+Range rows_of(const void* p, int64_t rows, int64_t row_bytes, int64_t pitch_bytes) {
+  return Range{reinterpret_cast<uintptr_t>(p), (uint64_t)rows, (uint64_t)row_bytes, (uint64_t)pitch_bytes};
 }
 
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+uintptr_t range_end(const Range& a) { return a.lo + (a.rows - 1) * a.pitch + a.row_bytes; }
+
+// Do two argument ranges share a byte?  Exact for dense buffers and for two
+// row sets with the same pitch (their rows are compared modulo the pitch, so
+// sources interleaved by token do not collide); conservative otherwise (any
+// overlap of the spans counts).
+bool overlap(const Range& a, const Range& b) {
+  if (a.rows == 0 || a.row_bytes == 0 || b.rows == 0 || b.row_bytes == 0) return false;
+  if (!(a.lo < range_end(b) && b.lo < range_end(a))) return false;
+  if (a.rows > 1 && b.rows > 1 && a.pitch == b.pitch && a.row_bytes <= a.pitch && b.row_bytes <= a.pitch) {
+    const uint64_t P = a.pitch;
+    const uint64_t d = b.lo >= a.lo ? (b.lo - a.lo) % P : (P - (a.lo - b.lo) % P) % P;
+    return d < a.row_bytes || d + b.row_bytes > P;  // b's row segment against a's, modulo the pitch
+  }
+  return true;
+}
+
+// A source pitch (elements between consecutive tokens' rows) must keep rows
+// 16-byte aligned, not shorten them, and keep every offset well inside int64.
+bool pitch_ok(int64_t pitch, int64_t T, int32_t D) {
+  return pitch >= D && pitch % 8 == 0 && (T == 0 || pitch <= (INT64_C(1) << 41) / T);
+}
 
 bool sizes_ok(int32_t N, int64_t T, int32_t D) {
   if (N < 1 || N > ATTNRES_MAX_SOURCES) return false;
@@ -939,18 +968,20 @@ hipError_t run_bwd(int32_t N, const LaunchShape& s, bool acc, hipStream_t st, co
 // srcs: N source rows (with an update, srcs[N-1] is the partial sum before
 // it).  allow_no_state: rstd and alpha may both be NULL (decoding calls).
 // delta / partial_out: the update's addend and result, or both NULL.
-attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T, int32_t D,
-                        uint16_t* out, float* rstd, float* alpha, bool allow_no_state, const uint16_t* delta,
-                        uint16_t* partial_out, void* stream) {
+attnres_status fwd_impl(const uint16_t* const* srcs, int64_t pitch, const float* w, float eps, int32_t N, int64_t T,
+                        int32_t D, uint16_t* out, float* rstd, float* alpha, bool allow_no_state,
+                        const uint16_t* delta, uint16_t* partial_out, void* stream) {
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
   const bool update = delta != nullptr || partial_out != nullptr;
   if (update && (delta == nullptr || partial_out == nullptr)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   Range ins[ATTNRES_MAX_SOURCES + 2];
   SrcRows rows{};
+  rows.pitch = pitch;
   for (int i = 0; i < N; ++i) {
     if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
     rows.p[i] = srcs[i];
-    ins[i] = range_of(srcs[i], nTD * 2);
+    ins[i] = rows_of(srcs[i], T, (int64_t)D * 2, pitch * 2);
   }
   ins[N] = range_of(w, (size_t)D * 4);
   ins[N + 1] = range_of(delta, update ? nTD * 2 : 0);
@@ -961,7 +992,8 @@ attnres_status fwd_impl(const uint16_t* const* srcs, const float* w, float eps, 
   if (!save && !allow_no_state) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(out, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
   const Range outs[4] = {range_of(out, nTD * 2), range_of(rstd, save ? nTN * 4 : 0),
-                         range_of(alpha, save ? nTN * 4 : 0), range_of(partial_out, update ? nTD * 2 : 0)};
+                         range_of(alpha, save ? nTN * 4 : 0),
+                         rows_of(partial_out, update ? T : 0, (int64_t)D * 2, pitch * 2)};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b <= N + 1; ++b) {
       // the partial sum may be updated in place: exactly its own buffer
@@ -998,22 +1030,26 @@ attnres_status bwd_common_checks(const float* w, int32_t N, int64_t T, int32_t D
   return ATTNRES_OK;
 }
 
-attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, const float* w, const float* rstd,
-                        const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* const* dsrcs, bool acc,
-                        float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch, const float* w,
+                        const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
+                        uint16_t* const* dsrcs, int64_t dsrc_pitch, bool acc, float* dw, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (dout == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(dout, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
   Range ins[ATTNRES_MAX_SOURCES + 4];
   int nin = 0;
+  if (!pitch_ok(src_pitch, T, D) || !pitch_ok(dsrc_pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   SrcRows rows{};
   DstRows drows{};
+  rows.pitch = src_pitch;
+  drows.pitch = dsrc_pitch;
   for (int i = 0; i < N; ++i) {
     if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
     if (dsrcs[i] == nullptr || !aligned(dsrcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
     rows.p[i] = srcs[i];
     drows.p[i] = dsrcs[i];
-    ins[nin++] = range_of(srcs[i], nTD * 2);
+    ins[nin++] = rows_of(srcs[i], T, (int64_t)D * 2, src_pitch * 2);
   }
   ins[nin++] = range_of(dout, nTD * 2);
   ins[nin++] = range_of(w, (size_t)D * 4);
@@ -1024,7 +1060,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, const
   if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   Range outs[ATTNRES_MAX_SOURCES + 2];
   int nout = 0;
-  for (int i = 0; i < N; ++i) outs[nout++] = range_of(dsrcs[i], nTD * 2);
+  for (int i = 0; i < N; ++i) outs[nout++] = rows_of(dsrcs[i], T, (int64_t)D * 2, dsrc_pitch * 2);
   outs[nout++] = range_of(dw, (size_t)D * 4);
   outs[nout++] = range_of(workspace, need);
   for (int a = 0; a < nout; ++a) {
@@ -1056,33 +1092,33 @@ extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float
   if (src == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   const uint16_t* srcs[ATTNRES_MAX_SOURCES];
   for (int i = 0; i < N; ++i) srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
+  return fwd_impl(srcs, D, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
 }
 
-extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
-                                              int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
-                                              void* stream) {
+extern "C" attnres_status attnres_fwd_sources(const uint16_t* const* srcs, int64_t src_pitch, const float* w,
+                                              float eps, int32_t N, int64_t T, int32_t D, uint16_t* out,
+                                              float* rstd, float* alpha, void* stream) {
   const attnres_status st = fwd_common_checks(w, eps, N, T, D);
   if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
   if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
+  return fwd_impl(srcs, src_pitch, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream);
 }
 
-extern "C" attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, float eps, int32_t N,
-                                             int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
-                                             void* stream) {
-  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
-  if (st != ATTNRES_OK) return st;
-  if (T == 0) return ATTNRES_OK;
-  if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return fwd_impl(srcs, w, eps, N, T, D, out, rstd, alpha, true, nullptr, nullptr, stream);
-}
-
-extern "C" attnres_status attnres_fwd_update(const uint16_t* const* srcs, const uint16_t* partial,
-                                             const uint16_t* delta, const float* w, float eps, int32_t N, int64_t T,
-                                             int32_t D, uint16_t* partial_out, uint16_t* out, float* rstd,
+extern "C" attnres_status attnres_fwd_decode(const uint16_t* const* srcs, int64_t src_pitch, const float* w,
+                                             float eps, int32_t N, int64_t T, int32_t D, uint16_t* out, float* rstd,
                                              float* alpha, void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return fwd_impl(srcs, src_pitch, w, eps, N, T, D, out, rstd, alpha, true, nullptr, nullptr, stream);
+}
+
+extern "C" attnres_status attnres_fwd_update(const uint16_t* const* srcs, int64_t src_pitch,
+                                             const uint16_t* partial, const uint16_t* delta, const float* w,
+                                             float eps, int32_t N, int64_t T, int32_t D, uint16_t* partial_out,
+                                             uint16_t* out, float* rstd, float* alpha, void* stream) {
   const attnres_status st = fwd_common_checks(w, eps, N, T, D);
   if (st != ATTNRES_OK) return st;
   if (T == 0) return ATTNRES_OK;
@@ -1091,7 +1127,7 @@ extern "C" attnres_status attnres_fwd_update(const uint16_t* const* srcs, const 
   const uint16_t* all[ATTNRES_MAX_SOURCES];
   for (int i = 0; i + 1 < N; ++i) all[i] = srcs[i];
   all[N - 1] = partial;
-  return fwd_impl(all, w, eps, N, T, D, out, rstd, alpha, true, delta, partial_out, stream);
+  return fwd_impl(all, src_pitch, w, eps, N, T, D, out, rstd, alpha, true, delta, partial_out, stream);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
@@ -1107,17 +1143,18 @@ extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src,
     srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
     dsrcs[i] = dsrc + (size_t)i * (size_t)T * (size_t)D;
   }
-  return bwd_impl(dout, srcs, w, rstd, alpha, N, T, D, dsrcs, false, dw, workspace, workspace_bytes, stream);
+  return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, dsrcs, D, false, dw, workspace, workspace_bytes, stream);
 }
 
-extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, const float* w,
-                                              const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
-                                              uint16_t* const* dsrcs, int32_t accumulate, float* dw,
-                                              void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch,
+                                              const float* w, const float* rstd, const float* alpha, int32_t N,
+                                              int64_t T, int32_t D, uint16_t* const* dsrcs, int64_t dsrc_pitch,
+                                              int32_t accumulate, float* dw, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
   const attnres_status st = bwd_common_checks(w, N, T, D, dw);
   if (st != ATTNRES_OK) return st;
   if (T == 0) return bwd_zero_dw(dw, D, stream);
   if (srcs == nullptr || dsrcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return bwd_impl(dout, srcs, w, rstd, alpha, N, T, D, dsrcs, accumulate != 0, dw, workspace, workspace_bytes,
-                  stream);
+  return bwd_impl(dout, srcs, src_pitch, w, rstd, alpha, N, T, D, dsrcs, dsrc_pitch, accumulate != 0, dw, workspace,
+                  workspace_bytes, stream);
 }

@@ -160,10 +160,33 @@ def alloc_buffers(ar, torch, N, T, D, dev):
     return out, rstd, alpha, dsrc, dw, ws
 
 
+def _fwd_bwd_ms(torch, flush, fwd, bwd, reps):
+    """Median event times of fwd and bwd, caches flushed before each."""
+    f_ms, b_ms = [], []
+    for r in range(reps + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.zero_()
+        e[0].record()
+        fwd()
+        e[1].record()
+        flush.zero_()
+        e[2].record()
+        bwd()
+        e[3].record()
+        torch.cuda.synchronize()
+        if r >= 3:
+            f_ms.append(e[0].elapsed_time(e[1]))
+            b_ms.append(e[2].elapsed_time(e[3]))
+    return sorted(f_ms)[len(f_ms) // 2], sorted(b_ms)[len(b_ms) // 2]
+
+
 def sweep(ar, torch, dev, reps=20):
     """Per-T (N=9) and per-N (T=32768) lines, fwd and bwd timed separately,
     caches flushed (a 512 MiB write) between reps; inputs are device-side
-    random bf16 of the workload's scales (values do not affect timing)."""
+    random bf16 of the workload's scales (values do not affect timing).  Each
+    line gives the stacked [N][T][D] calls and, as "interleaved", the same
+    sources side by side per token ([T][N][D] cache, gradients likewise)
+    through the per-source calls."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     D = 7168
     cases = [(9, T) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
@@ -177,32 +200,30 @@ def sweep(ar, torch, dev, reps=20):
         w = torch.randn(D, device=dev, generator=g) / D ** 0.5
         bufs = alloc_buffers(ar, torch, N, T, D, dev)
         out, rstd, alpha, dsrc, dw, ws = bufs
-        f_ms, b_ms = [], []
-        for r in range(reps + 3):
-            flush.zero_()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record()
-            ar.attnres_fwd(src, w, 1e-6, out=out, rstd=rstd, alpha=alpha)
-            e[1].record()
-            flush.zero_()
-            e2 = torch.cuda.Event(enable_timing=True)
-            e2.record()
-            ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws)
-            e[2].record()
-            torch.cuda.synchronize()
-            if r >= 3:
-                f_ms.append(e[0].elapsed_time(e[1]))
-                b_ms.append(e2.elapsed_time(e[2]))
-        f = sorted(f_ms)[len(f_ms) // 2]
-        b = sorted(b_ms)[len(b_ms) // 2]
+        f, b = _fwd_bwd_ms(torch, flush, lambda: ar.attnres_fwd(src, w, 1e-6, out=out, rstd=rstd, alpha=alpha),
+                           lambda: ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws), reps)
+        del dsrc
+        cache = src.permute(1, 0, 2).contiguous()  # [T][N][D]
+        del src
+        torch.cuda.empty_cache()
+        dcache = torch.empty_like(cache)
+        views = [cache[:, i] for i in range(N)]
+        dviews = [dcache[:, i] for i in range(N)]
+        fi, bi = _fwd_bwd_ms(torch, flush,
+                             lambda: ar.attnres_fwd_sources(views, w, 1e-6, out=out, rstd=rstd, alpha=alpha),
+                             lambda: ar.attnres_bwd_sources(dout, views, w, rstd, alpha, dsrcs=dviews, dw=dw,
+                                                            workspace=ws), reps)
         fb, bb, fe, be = algo_bytes(T, N, D)
         line = {"sweep": True, "N": N, "T": T, "D": D, "fwd_ms": f, "bwd_ms": b,
                 "fwd_GBps": (fb + fe) / f / 1e6, "bwd_GBps": (bb + be) / b / 1e6,
                 "fwdbwd_tokens_per_s": T / ((f + b) * 1e-3),
                 "fwdbwd_GBps": (fb + bb + fe + be) / (f + b) / 1e6,
-                "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (f + b) / 1e6 / HBM_PEAK_GBPS}
+                "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (f + b) / 1e6 / HBM_PEAK_GBPS,
+                "interleaved": {"fwd_ms": fi, "bwd_ms": bi, "fwd_GBps": (fb + fe) / fi / 1e6,
+                                "bwd_GBps": (bb + be) / bi / 1e6, "fwdbwd_tokens_per_s": T / ((fi + bi) * 1e-3),
+                                "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (fi + bi) / 1e6 / HBM_PEAK_GBPS}}
         print(json.dumps(line), flush=True)
-        del src, dout, w, bufs, out, rstd, alpha, dsrc, dw, ws
+        del cache, dcache, views, dviews, dout, w, bufs, out, rstd, alpha, dw, ws
         torch.cuda.empty_cache()
     sweep_sources(ar, torch, dev, flush, reps)
 
@@ -246,11 +267,21 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
     calls["fwd_update_fused"] = (lambda: ar.attnres_fwd_update(srcs[:-1], p, y, w, 1e-6, out=out, rstd=rstd,
                                                                alpha=alpha), upd_bytes)
     calls["fwd_update_unfused"] = (unfused, upd_bytes)
+    # the same sources side by side per token ([T][N][D] cache, row pitch N*D),
+    # gradients into a cache of the same layout
+    cache = torch.stack(srcs, dim=1)
+    views = [cache[:, i] for i in range(N)]
+    dcache = torch.empty_like(cache)
+    dviews = [dcache[:, i] for i in range(N)]
+    calls["fwd_interleaved"] = (lambda: ar.attnres_fwd_sources(views, w, 1e-6, out=out, rstd=rstd, alpha=alpha),
+                                fb + fe)
+    calls["bwd_interleaved"] = (lambda: ar.attnres_bwd_sources(dout, views, w, rstd, alpha, dsrcs=dviews, dw=dw,
+                                                               workspace=ws), bb + be)
     for name, (fn, nbytes) in calls.items():
         m = _median_ms(torch, flush, fn, reps)
         print(json.dumps({"sweep": True, "call": name, "N": N, "T": T, "D": D, "ms": m,
                           "GBps": nbytes / m / 1e6, "frac_of_8TBps": nbytes / m / 1e6 / HBM_PEAK_GBPS}), flush=True)
-    del srcs, dsrcs, dout, p, y
+    del srcs, dsrcs, dout, p, y, cache, views, dcache, dviews
     torch.cuda.empty_cache()
     sweep_decode(ar, torch, dev, flush)
 

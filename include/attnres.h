@@ -25,8 +25,10 @@
  *
  * Conventions for every call
  *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
- *   - Layouts are dense and row-major: sources/dsources [N][T][D]
- *     (source-major), out/dout [T][D], rstd/alpha [T][N] (token-major).
+ *   - Layouts are row-major: stacked sources/dsources [N][T][D]
+ *     (source-major), per-source rows with a pitch (see
+ *     attnres_fwd_sources), out/dout [T][D], rstd/alpha [T][N]
+ *     (token-major).
  *   - Every pointer is a device pointer owned by the caller (the per-source
  *     calls take a host array of device pointers).  The library allocates no
  *     device memory, frees nothing and never synchronises; its only state is
@@ -115,19 +117,24 @@ attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const floa
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Forward with the N sources as separately allocated [T][D] bf16 tensors
- * instead of one stacked [N][T][D] tensor -- the form a model holds them in:
- * the embedding, each completed block sum and the current partial sum live
- * in their own buffers (architecture figure of "Kimi K3 模型结构（10）"), and
- * stacking them would cost a copy of N*T*D values per sub-layer.
- *   srcs  host array of N device pointers; srcs[i] -> [T][D] bf16, 16-byte
- *         aligned.  A pointer may appear more than once.  May be NULL when
- *         T == 0.
+ * Forward with the N sources given as N row sets instead of one stacked
+ * [N][T][D] tensor -- the form a model holds them in: the embedding, each
+ * completed block sum and the current partial sum (architecture figure of
+ * "Kimi K3 模型结构（10）") live in their own buffers, or side by side in one
+ * depth-source cache, and stacking them would cost a copy of N*T*D values per
+ * sub-layer.
+ *   srcs       host array of N device pointers; row t of source i starts at
+ *              srcs[i] + t*src_pitch (bf16 elements), 16-byte aligned.  A
+ *              pointer may appear more than once.  May be NULL when T == 0.
+ *   src_pitch  elements between consecutive tokens' rows: D for separate
+ *              [T][D] buffers; N*D with srcs[i] = base + i*D for a cache
+ *              interleaved by token ([T][N][D]).  A multiple of 8, >= D.
  * Everything else as attnres_fwd.  Results are bitwise identical to
  * attnres_fwd on the same rows stacked.
  */
-attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T,
-                                   int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+attnres_status attnres_fwd_sources(const uint16_t* const* srcs, int64_t src_pitch, const float* w, float eps,
+                                   int32_t N, int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
+                                   void* stream);
 
 /*
  * Forward for decoding and rollout: the per-source forward with the saved
@@ -138,13 +145,14 @@ attnres_status attnres_fwd_sources(const uint16_t* const* srcs, const float* w, 
  * training forward gives for that token in any batch: rollout and training
  * see the same numbers.  A single token costs about 7 us of kernel time on
  * MI355X (D = 7168, N = 9).
- *   srcs, w, eps, N, T, D, out   as attnres_fwd_sources.
+ *   srcs, src_pitch, w, eps, N, T, D, out   as attnres_fwd_sources.
  *   rstd, alpha   [T][N] fp32 saved state as attnres_fwd, or both NULL: then
  *                 only out is written.  Exactly one of them NULL is
  *                 ATTNRES_ERR_INVALID_ARGUMENT.
  */
-attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, float eps, int32_t N, int64_t T,
-                                  int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+attnres_status attnres_fwd_decode(const uint16_t* const* srcs, int64_t src_pitch, const float* w, float eps,
+                                  int32_t N, int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha,
+                                  void* stream);
 
 /*
  * Forward fused with the update of the current block's partial sum.  The
@@ -161,38 +169,43 @@ attnres_status attnres_fwd_decode(const uint16_t* const* srcs, const float* w, f
  *   then the forward of attnres_fwd_sources on {srcs[0..N-2], partial_out}.
  * Bytes per token drop from 2ND + 2D + 8N (+ 6D for a separate update pass)
  * to 2(N+1)D + 4D + 8N.
- *   srcs         host array of the N-1 other sources (device pointers, [T][D]
- *                bf16); may be NULL when N == 1.
- *   partial      [T][D] bf16 partial sum before the update.
- *   delta        [T][D] bf16 sub-layer output to add.
- *   partial_out  [T][D] bf16 updated partial sum; may be `partial` itself
- *                (in-place update), otherwise it must not overlap any input.
+ *   srcs         host array of the N-1 other sources (device pointers); may
+ *                be NULL when N == 1.
+ *   src_pitch    as attnres_fwd_sources; it also applies to partial and
+ *                partial_out (the partial sum is one of the sources).
+ *   partial      partial sum before the update (rows of D bf16 values).
+ *   delta        [T][D] bf16 (dense) sub-layer output to add.
+ *   partial_out  updated partial sum; may be `partial` itself (in-place
+ *                update), otherwise it must not overlap any input.
  *   out, rstd, alpha, w, eps, N (total sources, partial included), T, D
  *                as attnres_fwd_decode (rstd and alpha both NULL when no
  *                backward follows).
  * The backward is attnres_bwd_sources with partial_out as the last source;
  * the gradient of partial_out then flows unchanged to both partial and delta.
  */
-attnres_status attnres_fwd_update(const uint16_t* const* srcs, const uint16_t* partial, const uint16_t* delta,
-                                  const float* w, float eps, int32_t N, int64_t T, int32_t D, uint16_t* partial_out,
-                                  uint16_t* out, float* rstd, float* alpha, void* stream);
+attnres_status attnres_fwd_update(const uint16_t* const* srcs, int64_t src_pitch, const uint16_t* partial,
+                                  const uint16_t* delta, const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                                  uint16_t* partial_out, uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
  * Backward with per-source pointers, optionally accumulating the source
  * gradients.  A completed block sum is a source of every later sub-layer's
  * AttnRes, so its gradient is the sum of those operators' contributions:
- *   dsrcs       host array of N device pointers to [T][D] bf16 gradients,
- *               pairwise disjoint and disjoint from every input.
+ *   srcs, src_pitch   as attnres_fwd_sources.
+ *   dsrcs       host array of N device pointers to the bf16 gradients, row
+ *               t of gradient i at dsrcs[i] + t*dsrc_pitch (the same
+ *               choices of layout as the sources), pairwise disjoint and
+ *               disjoint from every input.
  *   accumulate  0: dsrcs[i] = dx_i (bitwise identical to attnres_bwd);
  *               else: dsrcs[i] = bf16( fp32(dsrcs[i]) + dx_i ), rounded to
  *               nearest even, each element read and written once.
  * dw is always overwritten with this call's sum over the T tokens.  Other
  * arguments as attnres_bwd.  srcs and dsrcs may be NULL when T == 0.
  */
-attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, const float* w,
-                                   const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
-                                   uint16_t* const* dsrcs, int32_t accumulate, float* dw, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch,
+                                   const float* w, const float* rstd, const float* alpha, int32_t N, int64_t T,
+                                   int32_t D, uint16_t* const* dsrcs, int64_t dsrc_pitch, int32_t accumulate,
+                                   float* dw, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

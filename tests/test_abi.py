@@ -145,8 +145,9 @@ def _arr(vals):
 
 
 def _fwd_src(srcs, N=3, T=16, D_=D, eps=1e-6, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
-             alpha=(1 << 36) + (1 << 31)):
-    return ar.library().attnres_fwd_sources(srcs, w, eps, N, T, D_, out, rstd, alpha, None)
+             alpha=(1 << 36) + (1 << 31), pitch=None):
+    return ar.library().attnres_fwd_sources(srcs, D_ if pitch is None else pitch, w, eps, N, T, D_, out, rstd, alpha,
+                                            None)
 
 
 def test_fwd_sources_rejects():
@@ -162,12 +163,13 @@ def test_fwd_sources_rejects():
     assert _fwd_src(_arr([g, g, 5 * g]), w=0) == INVALID  # still rejected, but only for the null w
 
 
-def _bwd_src(srcs, dsrcs, acc=1, N=3, T=16, D_=D, ws_bytes=None):
+def _bwd_src(srcs, dsrcs, acc=1, N=3, T=16, D_=D, ws_bytes=None, pitch=None, dpitch=None):
     g = 1 << 30
     if ws_bytes is None:
         ws_bytes = ar.workspace_bytes(D_)
-    return ar.library().attnres_bwd_sources(1 * g, srcs, 20 * g, 21 * g, 22 * g, N, T, D_, dsrcs, acc, 23 * g,
-                                            24 * g, ws_bytes, None)
+    return ar.library().attnres_bwd_sources(1 * g, srcs, D_ if pitch is None else pitch, 20 * g, 21 * g, 22 * g, N,
+                                            T, D_, dsrcs, D_ if dpitch is None else dpitch, acc, 23 * g, 24 * g,
+                                            ws_bytes, None)
 
 
 def test_bwd_sources_rejects():
@@ -185,7 +187,7 @@ def test_bwd_sources_rejects():
 
 def _dec(srcs, N=3, T=16, D_=D, eps=1e-6, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
          alpha=(1 << 36) + (1 << 31)):
-    return ar.library().attnres_fwd_decode(srcs, w, eps, N, T, D_, out, rstd, alpha, None)
+    return ar.library().attnres_fwd_decode(srcs, D_, w, eps, N, T, D_, out, rstd, alpha, None)
 
 
 def test_fwd_decode_rejects():
@@ -213,7 +215,7 @@ def test_only_the_decode_call_may_skip_the_saved_state():
 
 def _upd(srcs, partial, delta, partial_out, N=3, T=16, D_=D, w=2 * A, out=1 << 36, rstd=(1 << 36) + (1 << 30),
          alpha=(1 << 36) + (1 << 31)):
-    return ar.library().attnres_fwd_update(srcs, partial, delta, w, 1e-6, N, T, D_, partial_out, out, rstd, alpha,
+    return ar.library().attnres_fwd_update(srcs, D_, partial, delta, w, 1e-6, N, T, D_, partial_out, out, rstd, alpha,
                                            None)
 
 
@@ -234,3 +236,28 @@ def test_fwd_update_rejects():
     assert _upd(srcs, p, y, p, rstd=None) == INVALID  # saved state is both or neither
     assert _upd(srcs, p, y, p, N=10) == INVALID
     assert _upd(None, p, y, p, T=0) == OK  # nothing to do
+
+
+def test_source_pitch_rejects():
+    g = 1 << 30
+    good = _arr([g, 3 * g, 5 * g])
+    assert _fwd_src(good, pitch=D - 8) == INVALID  # rows would overlap their successors
+    assert _fwd_src(good, pitch=D + 4) == INVALID  # rows would lose 16-byte alignment
+    assert _fwd_src(good, pitch=1 << 40) == INVALID  # offsets beyond the supported range
+    # out inside the span of an interleaved source: spans are compared when pitches differ
+    base = 7 * g
+    inter = _arr([base, base + 2 * D, base + 4 * D])
+    assert _fwd_src(inter, pitch=3 * D, out=base + 6 * D * 5) == INVALID
+
+
+def test_interleaved_gradients_must_not_collide():
+    g = 1 << 30
+    srcs = _arr([2 * g, 3 * g, 4 * g])
+    base = 8 * g
+    # three gradients interleaved by token share a pitch of 3*D elements (6*D bytes)
+    assert _bwd_src(srcs, _arr([base, base + D, base + 3 * D]), dpitch=3 * D) == INVALID  # 1st and 2nd overlap
+    assert _bwd_src(srcs, _arr([base, base + 2 * D, base + 2 * D + 2 * D * 3 * 5]), dpitch=3 * D) == INVALID
+    # gradients interleaved over a source cache that is interleaved the same way
+    cache = 12 * g
+    assert _bwd_src(_arr([cache, cache + 2 * D, cache + 4 * D]), _arr([cache + 2 * D, base, base + 2 * D]),
+                    pitch=3 * D, dpitch=3 * D) == INVALID  # a gradient on a source row set

@@ -111,3 +111,61 @@ def test_accumulate_twice_equals_sum_of_two_calls():
     torch.cuda.synchronize()
     for a, p in zip(acc2, plain):
         assert torch.allclose(a.float(), 2 * p.float(), rtol=8e-3, atol=1e-6)
+
+
+def _interleave(src_stacked, pad=0):
+    """A [T][N][D + pad] cache holding the sources side by side per token, and the
+    per-source views into it (row pitch N*(D + pad))."""
+    N, T, D = src_stacked.shape
+    cache = torch.zeros((T, N, D + pad), dtype=src_stacked.dtype, device=src_stacked.device)
+    cache[:, :, :D] = src_stacked.permute(1, 0, 2)
+    return cache, [cache[:, i, :D] for i in range(N)]
+
+
+@pytest.mark.parametrize("N,T,D,pad", [(9, 300, 7168, 0), (4, 65, 1000, 8), (3, 17, 12288, 0), (9, 1, 7168, 0)],
+                         ids=lambda v: str(v))
+def test_interleaved_sources_match_stacked_bitwise(N, T, D, pad):
+    """Sources kept side by side per token ([T][N][D] cache, pitch N*D) and
+    gradients written into a cache of the same layout give the stacked calls'
+    results bit for bit: forward, decoding forward, backward, accumulating
+    backward."""
+    wl = synth.Workload(f"inter_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    dout = to_dev_bf16(wl.dout())
+    out, rstd, alpha, dsrc, dw = run_gpu(src, w, wl.eps, dout)
+    cache, views = _interleave(src, pad)
+    o2, r2, a2 = ar.attnres_fwd_sources(views, w, wl.eps)
+    o3, _, _ = ar.attnres_fwd_decode(views, w, wl.eps)
+    dcache, dviews = _interleave(torch.zeros_like(src), pad)
+    _, dw2 = ar.attnres_bwd_sources(dout, views, w, r2, a2, dsrcs=dviews)
+    acc_cache, acc_views = _interleave(dsrc, pad)  # accumulate onto a copy of the gradients
+    ar.attnres_bwd_sources(dout, views, w, r2, a2, dsrcs=acc_views, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(o2)) and torch.equal(_bits(out), _bits(o3))
+    assert torch.equal(_bits(rstd), _bits(r2)) and torch.equal(_bits(alpha), _bits(a2))
+    assert torch.equal(_bits(dw), _bits(dw2))
+    for i in range(N):
+        assert torch.equal(_bits(dsrc[i]), _bits(dviews[i])), i
+        want = (dsrc[i].float() + dsrc[i].float()).to(torch.bfloat16)  # bf16(x + x) is exact doubling
+        assert torch.equal(_bits(want), _bits(acc_views[i])), i
+    if pad:
+        assert not bool(dcache[:, :, D:].any()) and not bool(cache[:, :, D:].any())  # padding untouched
+
+
+def test_interleaved_partial_sum_update_in_place():
+    """The partial sum as the last slot of an interleaved cache, updated in place."""
+    N, T, D = 6, 200, 7168
+    wl = synth.Workload(f"inter_upd_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    y = to_dev_bf16(synth.Workload("inter_upd_y", T=T, N=1, D=D, seed=5, kind="tiny",
+                                   tiny_scales=(0.5,)).sources()[0])
+    out1, r1, a1, p1 = ar.attnres_fwd_update([src[i] for i in range(N - 1)], src[N - 1].clone(), y, w, wl.eps)
+    cache, views = _interleave(src)
+    out2, r2, a2, p2 = ar.attnres_fwd_update(views[:-1], views[-1], y, w, wl.eps)
+    torch.cuda.synchronize()
+    assert p2.data_ptr() == views[-1].data_ptr()
+    assert torch.equal(_bits(p1), _bits(cache[:, N - 1]))
+    assert torch.equal(_bits(out1), _bits(out2))
+    assert torch.equal(_bits(r1), _bits(r2)) and torch.equal(_bits(a1), _bits(a2))
