@@ -249,15 +249,26 @@ __device__ __forceinline__ void store8(float4* p, int slot, const float (&f)[8])
   p[2 * slot + 1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-// w (fp32, D values) into the thread's LDS slots; zeros past the row end.
+// The thread's slice of w (fp32, 8 values per vector; zeros past the row
+// end), requested into registers so that the row loads can be issued right
+// behind it, then parked in the thread's LDS slots.
 template <int VPT>
-__device__ __forceinline__ void stage_w(const float* __restrict__ w, int32_t D, float4* wl, const Slice<VPT>& sl) {
+__device__ __forceinline__ void load_w(uint4 (&wv)[VPT][2], const float* __restrict__ w, int32_t D,
+                                       const Slice<VPT>& sl) {
   const __amdgpu_buffer_rsrc_t r = rsrc(w, (uint32_t)D * 4u);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const uint4 a = bload(r, 2u * sl.off[k]), b = bload(r, 2u * sl.off[k] + 16u);
-    wl[2 * sl.slot[k]] = __builtin_bit_cast(float4, a);
-    wl[2 * sl.slot[k] + 1] = __builtin_bit_cast(float4, b);
+    wv[k][0] = bload(r, 2u * sl.off[k]);
+    wv[k][1] = bload(r, 2u * sl.off[k] + 16u);
+  }
+}
+
+template <int VPT>
+__device__ __forceinline__ void store_w(const uint4 (&wv)[VPT][2], float4* wl, const Slice<VPT>& sl) {
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    wl[2 * sl.slot[k]] = __builtin_bit_cast(float4, wv[k][0]);
+    wl[2 * sl.slot[k] + 1] = __builtin_bit_cast(float4, wv[k][1]);
   }
 }
 
@@ -456,12 +467,7 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* 
   const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
 
   uint4 wv[VPT][2];
-  const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    wv[k][0] = bload(rw, 2u * sl.off[k]);
-    wv[k][1] = bload(rw, 2u * sl.off[k] + 16u);
-  }
+  load_w<VPT>(wv, w, D, sl);
   sched_fence();
   uint4 x[N][VPT];
   uint4 yv[UPDATE ? VPT : 1];
@@ -481,12 +487,7 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* 
       bstore<kAuxStreamStore>(rp, sl.off[k], x[N - 1][k]);
     }
   }
-  float4* wl = dyn_lds;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    wl[2 * sl.slot[k]] = __builtin_bit_cast(float4, wv[k][0]);
-    wl[2 * sl.slot[k] + 1] = __builtin_bit_cast(float4, wv[k][1]);
-  }
+  store_w<VPT>(wv, dyn_lds, sl);
   clear_red<2 * N>(red);
   int buf = 0;
   fwd_token<N, VPT>(x, t, buf, c, sl);
@@ -641,22 +642,30 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
   c.lane = tid & (kWave - 1);
   c.wave = tid / kWave;
   const Slice<VPT> sl(tid, blockDim.x);
-  stage_w<VPT>(w, D, dyn_lds, sl);
+  const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
+
+  // w first, then (with PIPE) the first token's rows right behind it, so the
+  // set-up below overlaps their latency
+  uint4 wv[VPT][2];
+  load_w<VPT>(wv, w, D, sl);
+  sched_fence();
+  uint4 xa[PIPE ? N : 1][VPT], xb[PIPE ? N : 1][VPT], ga[VPT], gb[VPT];
+  float saa = 0.f, sra = 0.f, sab = 0.f, srb = 0.f;
+  if constexpr (PIPE) {
+    load_row<VPT>(ga, dout, ch, D, sl);
+    load_rows<N, VPT>(xa, src, ch, D, sl);
+    load_saved<N>(saa, sra, alpha, rstd, ch, c.lane);
+    sched_fence();
+  }
+  store_w<VPT>(wv, dyn_lds, sl);
   const float zero8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < VPT; ++k) store8(c.dwl, sl.slot[k], zero8);
   clear_red<2 * N>(red);
 
   int buf = 0;
-  const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
-  if (PIPE) {
-    uint4 xa[N][VPT], xb[N][VPT], ga[VPT], gb[VPT];
-    float saa, sra, sab, srb;
+  if constexpr (PIPE) {
     int64_t t = ch;
-    load_row<VPT>(ga, dout, t, D, sl);
-    load_rows<N, VPT>(xa, src, t, D, sl);
-    load_saved<N>(saa, sra, alpha, rstd, t, c.lane);
-    sched_fence();
     load_row<VPT>(gb, dout, t + P, D, sl, t + P < T);
     load_rows<N, VPT>(xb, src, t + P, D, sl, t + P < T);
     load_saved<N>(sab, srb, alpha, rstd, t + P, c.lane, t + P < T);
