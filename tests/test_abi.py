@@ -9,6 +9,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import attention_residuals_depth_amd as ar
@@ -261,3 +262,88 @@ def test_interleaved_gradients_must_not_collide():
     cache = 12 * g
     assert _bwd_src(_arr([cache, cache + 2 * D, cache + 4 * D]), _arr([cache + 2 * D, base, base + 2 * D]),
                     pitch=3 * D, dpitch=3 * D) == INVALID  # a gradient on a source row set
+
+
+# ----------------------------------------------------------------------------
+# argument-overlap validation against a byte-exact model (CPU only)
+# ----------------------------------------------------------------------------
+# A call whose arguments pass validation goes on to launch, which on a machine
+# without a GPU fails with ATTNRES_ERR_HIP: that tells "accepted" (3) from
+# "rejected" (1) without running anything.  The addresses are fake, so these
+# tests must never run where a GPU is present.
+
+def _no_gpu():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("passes fake device pointers to calls that would launch: CPU-only")
+
+
+def _bytes(base, rows, row_bytes, pitch_bytes):
+    return [(base + r * pitch_bytes, base + r * pitch_bytes + row_bytes) for r in range(rows)]
+
+
+def _collide(a, b):
+    return any(x0 < y1 and y0 < x1 for x0, x1 in a for y0, y1 in b)
+
+
+def _span(a):
+    return (a[0][0], a[-1][1])
+
+
+def _layout(rng, n, T, Dv, arena):
+    """n row sets of T rows of Dv bf16: either interleaved side by side (pitch
+    n*Dv, phase offset chosen at random) or separate dense blocks at random
+    16-byte positions of a small arena."""
+    rb = 2 * Dv
+    if rng.random() < 0.5:
+        pitch = n * Dv
+        base = arena + 16 * int(rng.integers(0, 64))
+        slots = rng.permutation(n) if rng.random() < 0.7 else rng.integers(0, n, n)  # sometimes a shared slot
+        return [base + int(k) * rb for k in slots], pitch
+    pitch = int(rng.choice([Dv, 2 * Dv]))
+    return [arena + 16 * int(rng.integers(0, 64)) for _ in range(n)], pitch
+
+
+@pytest.mark.parametrize("seed", range(400))
+def test_bwd_sources_overlap_checks_match_a_byte_model(seed):
+    """Random small layouts of the sources, gradients and dout (interleaved or
+    separate, in overlapping arenas): any pair of arguments sharing a byte that
+    must not is rejected; any layout whose forbidden pairs have disjoint spans,
+    or share one pitch and are byte-disjoint, is accepted."""
+    _no_gpu()
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 5))
+    Dv = int(rng.choice([8, 16]))
+    rb = Dv * 2
+    arena = 1 << 32
+    srcs, pitch = _layout(rng, N, T, Dv, arena)
+    dsrcs, dpitch = _layout(rng, N, T, Dv, arena + 16 * int(rng.integers(0, 64)))
+    dout = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.3 else (1 << 33)
+    wsb = ar.workspace_bytes(Dv)
+    dw = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.2 else (1 << 33) + (1 << 24)
+    ws = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.2 else (1 << 33) + (1 << 25)
+    w, rstd, alpha = (1 << 34), (1 << 35), (1 << 35) + (1 << 20)
+    ins = [_bytes(s, T, rb, 2 * pitch) for s in srcs] + [_bytes(dout, T, rb, rb), _bytes(w, 1, 4 * Dv, 4 * Dv)]
+    outs = [_bytes(d, T, rb, 2 * dpitch) for d in dsrcs] + [_bytes(dw, 1, 4 * Dv, 4 * Dv), _bytes(ws, 1, wsb, wsb)]
+    pitches_in = [2 * pitch] * N + [None, None]
+    pitches_out = [2 * dpitch] * N + [None, None]
+    pairs = [(o, i, po, pi) for o, po in zip(outs, pitches_out) for i, pi in zip(ins, pitches_in)]
+    pairs += [(outs[a], outs[b], pitches_out[a], pitches_out[b])
+              for a in range(len(outs)) for b in range(a + 1, len(outs))]
+    collide = any(_collide(a, b) for a, b, _, _ in pairs)
+
+    def clearly_ok(a, b, pa, pb):
+        (a0, a1), (b0, b1) = _span(a), _span(b)
+        if not (a0 < b1 and b0 < a1):
+            return True
+        return pa is not None and pa == pb and len(a) > 1 and len(b) > 1 and not _collide(a, b)
+
+    must_accept = all(clearly_ok(*p) for p in pairs)
+    code = ar.library().attnres_bwd_sources(dout, _arr(srcs), pitch, w, rstd, alpha, N, T, Dv, _arr(dsrcs), dpitch,
+                                            0, dw, ws, wsb, None)
+    assert code in (INVALID, 3)
+    if collide:
+        assert code == INVALID, "an overlapping layout was accepted"
+    elif must_accept:
+        assert code == 3, "a disjoint layout was rejected"
