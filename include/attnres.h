@@ -76,6 +76,8 @@ typedef enum {
  *   src   [N][T][D] bf16   depth sources, row (i, t) at src + (i*T + t)*D
  *   w     [D]       fp32   pseudo-query of this sub-layer
  *   eps             fp32   finite, >= 0; added to the mean square inside the root
+ *                          (with eps == 0 an all-zero source row has rstd = inf
+ *                          and makes that token's scores NaN, as the formula does)
  *   N               1 .. ATTNRES_MAX_SOURCES
  *   T               >= 0 tokens, T*N*D <= 2^40 (T == 0 enqueues nothing and
  *                   returns OK)
