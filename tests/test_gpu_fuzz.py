@@ -1,0 +1,124 @@
+"""Seeded random configurations through every call, against the fp64 oracle.
+
+Each case draws N, T, D, eps, the source scales, a layout (stacked, separate
+buffers, interleaved by token, padded rows) and a call mix (overwriting or
+accumulating backward, decoding forward, fused partial-sum update), runs it
+on the GPU and compares every output with the oracle at the operator's
+tolerances.  The cases are fixed by their seeds, so a failure names a
+reproducible configuration."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import oracle
+import synth
+from parity import (DEV, TOL_ALPHA_ABS, TOL_DSRC_REL_L2, TOL_DW_REL_L2, TOL_OUT_REL_L2, TOL_RSTD_REL,
+                    bf16_dev_to_f64, rel_l2, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _place(src: torch.Tensor, layout: str, rng):
+    """Views of the N sources [T][D] in the given layout (the data is the same)."""
+    N, T, D = src.shape
+    if layout == "separate":
+        return [src[i].clone() for i in range(N)]
+    if layout == "interleaved":
+        cache = src.permute(1, 0, 2).contiguous()
+        return [cache[:, i] for i in range(N)]
+    pad = 8 * int(rng.integers(1, 20))  # padded rows: pitch D + pad
+    buf = torch.zeros((N, T, D + pad), dtype=src.dtype, device=src.device)
+    buf[:, :, :D] = src
+    return [buf[i, :, :D] for i in range(N)]
+
+
+def _zeros_like_layout(views):
+    out = []
+    for v in views:
+        if v.is_contiguous():
+            out.append(torch.zeros_like(v))
+        else:
+            T, D = v.shape
+            base = torch.zeros((T, v.stride(0)), dtype=v.dtype, device=v.device)
+            out.append(base[:, :D])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configuration(seed):
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.integers(1, 10))
+    T = int(rng.integers(1, 200))
+    D = 8 * int(rng.choice([1, 2, 7, 64, 125, 513, 896, 1024, 1025, 1536, 2048]))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3]))
+    kind = "tiny" if N <= 3 and rng.random() < 0.5 else "depth"
+    scales = tuple(float(x) for x in np.exp(rng.uniform(-3, 3, 3)))
+    w_std = float(rng.choice([0.0, 0.5])) or None  # None: 1/sqrt(D); 0.5: the peaked workload's
+    wl = synth.Workload(f"fuzz{seed}", T=T, N=N, D=D, eps=eps, seed=seed, kind=kind, w_std=w_std, tiny_scales=scales)
+    layout = str(rng.choice(["stacked", "separate", "interleaved", "padded"]))
+    mode = str(rng.choice(["plain", "accumulate", "decode", "update"]))
+    src_h, w_h, dout_h = wl.sources(), wl.w(), wl.dout()
+    print(f"[fuzz] seed={seed} N={N} T={T} D={D} eps={eps} kind={kind} layout={layout} mode={mode}", flush=True)
+    src = to_dev_bf16(src_h)
+    w = torch.from_numpy(w_h).to(DEV)
+    dout = to_dev_bf16(dout_h)
+
+    if mode == "update":
+        y_h = synth.Workload(f"fuzzy{seed}", T=T, N=1, D=D, seed=seed + 77, kind="tiny",
+                             tiny_scales=(0.3,)).sources()[0]
+        views = _place(src, "separate" if layout == "stacked" else layout, rng)
+        out, rstd, alpha, p_new = ar.attnres_fwd_update(views[:-1], views[-1], to_dev_bf16(y_h), w, eps)
+        torch.cuda.synchronize()
+        o_out, o_rstd, o_alpha, o_p = oracle.fwd_update(src_h[:-1], src_h[-1], y_h, w_h, eps)
+        got_p = p_new.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got_p, o_p)
+    elif layout == "stacked" and mode != "decode":
+        out, rstd, alpha = ar.attnres_fwd(src, w, eps)
+        o_out, o_rstd, o_alpha = oracle.fwd(src_h, w_h, eps)
+    else:
+        views = _place(src, "separate" if layout == "stacked" else layout, rng)
+        if mode == "decode":
+            out, rstd, alpha = ar.attnres_fwd_decode(views, w, eps, save_state=True)
+        else:
+            out, rstd, alpha = ar.attnres_fwd_sources(views, w, eps)
+        o_out, o_rstd, o_alpha = oracle.fwd(src_h, w_h, eps)
+    torch.cuda.synchronize()
+    assert rel_l2(bf16_dev_to_f64(out), o_out) <= TOL_OUT_REL_L2
+    assert float(np.max(np.abs(alpha.cpu().double().numpy() - o_alpha))) <= TOL_ALPHA_ABS
+    assert float(np.max(np.abs(rstd.cpu().double().numpy() / o_rstd - 1))) <= TOL_RSTD_REL
+
+    if mode in ("plain", "accumulate"):
+        o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
+        if layout == "stacked":
+            dsrc, dw = ar.attnres_bwd(dout, src, w, rstd, alpha)
+            got = bf16_dev_to_f64(dsrc)
+            expect = o_dsrc
+        else:
+            views = _place(src, layout, rng)
+            grads = _zeros_like_layout(views)
+            prior_h = None
+            if mode == "accumulate":
+                prior_h = synth.Workload(f"fuzzp{seed}", T=T, N=N, D=D, seed=seed + 99, kind="tiny",
+                                         tiny_scales=tuple([0.05] * 9)).sources()
+                for i in range(N):
+                    grads[i].copy_(to_dev_bf16(prior_h[i]))
+            grads, dw = ar.attnres_bwd_sources(dout, views, w, rstd, alpha, dsrcs=grads,
+                                               accumulate=(mode == "accumulate"))
+            got = np.stack([bf16_dev_to_f64(g) for g in grads])
+            expect = o_dsrc if prior_h is None else oracle.bf16_to_f64(prior_h) + o_dsrc
+        torch.cuda.synchronize()
+        assert rel_l2(got, expect) <= TOL_DSRC_REL_L2
+        if np.linalg.norm(o_dw) > 0:
+            assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
+        else:
+            assert float(np.max(np.abs(dw.cpu().double().numpy()))) <= 1e-6
