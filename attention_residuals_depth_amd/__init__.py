@@ -158,15 +158,15 @@ def _ptr_array(tensors):
     return arr
 
 
-def _rows(t: torch.Tensor, name: str, T: int, D: int) -> int:
-    """Check a [T][D] bf16 row set whose rows may be spaced apart (a view of one
+def _rows(t: torch.Tensor, name: str, T: int, D: int, dtype=torch.bfloat16) -> int:
+    """Check a [T][D] row set whose rows may be spaced apart (a view of one
     source in a token-interleaved [T][N][D] cache); returns its row pitch."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != (T, D):
         raise ValueError(f"{name} must have shape {(T, D)}, got {tuple(t.shape)}")
     if T > 1 and t.stride(1) != 1:
@@ -185,9 +185,9 @@ def _sources(srcs, name):
     return srcs, T, D, _common_pitch(srcs, name, T, D)
 
 
-def _common_pitch(tensors, name, T, D, pitch=None):
+def _common_pitch(tensors, name, T, D, pitch=None, dtype=torch.bfloat16):
     for i, t in enumerate(tensors):
-        p = _rows(t, f"{name}[{i}]", T, D)
+        p = _rows(t, f"{name}[{i}]", T, D, dtype)
         if T > 1:
             if pitch is None:
                 pitch = p
@@ -293,12 +293,17 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
     return out, rstd, alpha, partial_out
 
 
+GRAD_ACCUMULATE = 1  # grad_mode bits of attnres_bwd_sources
+GRAD_F32 = 2
+
+
 def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.Tensor, alpha: torch.Tensor,
-                        dsrcs=None, accumulate: bool = False, dw=None, workspace=None, stream=None):
-    """Backward on N separate sources.  dsrcs: N separate [T][D] bf16 gradient
-    tensors (allocated if None); with accumulate=True the new gradients are
-    added to their contents.  Sources and gradients may be strided views (one
-    row pitch for the sources, one for the gradients).  Returns (dsrcs, dw)."""
+                        dsrcs=None, accumulate: bool = False, grad_dtype=None, dw=None, workspace=None, stream=None):
+    """Backward on N separate sources.  dsrcs: N [T][D] gradient tensors, all
+    bf16 or all fp32 (allocated if None, as grad_dtype, default bf16); with
+    accumulate=True the new gradients are added to their contents (in fp32,
+    then rounded once for bf16).  Sources and gradients may be strided views
+    (one row pitch for the sources, one for the gradients).  Returns (dsrcs, dw)."""
     srcs, T, D, pitch = _sources(srcs, "srcs")
     N = len(srcs)
     _check(dout, "dout", torch.bfloat16, (T, D))
@@ -309,11 +314,16 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     if dsrcs is None:
         if accumulate:
             raise ValueError("accumulate=True needs the gradient tensors to add to")
-        dsrcs = [torch.empty((T, D), dtype=torch.bfloat16, device=dev) for _ in range(N)]
+        gdt = torch.bfloat16 if grad_dtype is None else grad_dtype
+        dsrcs = [torch.empty((T, D), dtype=gdt, device=dev) for _ in range(N)]
     dsrcs = list(dsrcs)
     if len(dsrcs) != N:
         raise ValueError("dsrcs must hold one tensor per source")
-    dpitch = _common_pitch(dsrcs, "dsrcs", T, D)
+    gdt = dsrcs[0].dtype if isinstance(dsrcs[0], torch.Tensor) else torch.bfloat16
+    if gdt not in (torch.bfloat16, torch.float32) or (grad_dtype is not None and grad_dtype != gdt):
+        raise TypeError(f"gradients must all be torch.bfloat16 or all torch.float32 (got {gdt})")
+    dpitch = _common_pitch(dsrcs, "dsrcs", T, D, dtype=gdt)
+    mode = (GRAD_ACCUMULATE if accumulate else 0) | (GRAD_F32 if gdt == torch.float32 else 0)
     if dw is None:
         dw = torch.empty((D,), dtype=torch.float32, device=dev)
     if workspace is None:
@@ -323,7 +333,7 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), pitch, w.data_ptr(), rstd.data_ptr(),
-                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), dpitch, 1 if accumulate else 0,
+                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), dpitch, mode,
                                          dw.data_ptr(), workspace.data_ptr(), ws_bytes, _stream_handle(stream))
     if code != 0:
         raise AttnResError("attnres_bwd_sources", code)
@@ -331,5 +341,5 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
 
 
 __all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
-           "attnres_fwd_update",
+           "attnres_fwd_update", "GRAD_ACCUMULATE", "GRAD_F32",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

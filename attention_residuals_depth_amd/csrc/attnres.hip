@@ -149,6 +149,14 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// This lane's index in its wave, recomputed (two VALU ops) instead of kept live.
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// This wave's index in the workgroup, in a scalar register.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave); }
+
 // Workgroup-wide sums of K (<= 64) per-thread values, returned wave-uniform.
 // Each wave reduces its values, lane 63 stores them in red[k][wave], one
 // barrier, then lane k adds the kMaxWaves slots of red[k] in slot order (slots
@@ -158,8 +166,9 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 // wave can only overwrite a buffer after passing the next token's barrier,
 // which every wave reaches only after it finished reading that buffer.
 template <int K>
-__device__ __forceinline__ void block_sums(float (&v)[K], float (*red)[kMaxWaves], int lane, int wave) {
+__device__ __forceinline__ void block_sums(float (&v)[K], float (*red)[kMaxWaves]) {
   static_assert(K <= kWave, "one lane per value");
+  const int lane = lane_id(), wave = wave_id();
 #pragma unroll
   for (int k = 0; k < K; ++k) v[k] = wave_sum_lane63(v[k]);
   if (lane == kWave - 1) {
@@ -281,10 +290,45 @@ struct SrcRows {
   const uint16_t* p[ATTNRES_MAX_SOURCES];
   int64_t pitch;
 };
+// Source gradients: bf16 or fp32 rows (the backward's MODE says which), row
+// (i, t) at p[i] + t*pitch elements of that type.
 struct DstRows {
-  uint16_t* p[ATTNRES_MAX_SOURCES];
+  void* p[ATTNRES_MAX_SOURCES];
   int64_t pitch;
 };
+
+// Backward gradient modes: bit 0 accumulate into the existing gradients,
+// bit 1 fp32 gradients (else bf16).  Same values as ATTNRES_GRAD_* in the
+// header.
+constexpr int kGradAccumulate = 1;
+constexpr int kGradF32 = 2;
+
+template <bool F32>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t grad_row(const DstRows& d, int i, int64_t t, int32_t D) {
+  if constexpr (F32)
+    return rsrc(static_cast<float*>(d.p[i]) + t * d.pitch, (uint32_t)D * 4u);
+  else
+    return rsrc(static_cast<uint16_t*>(d.p[i]) + t * d.pitch, (uint32_t)D * 2u);
+}
+
+// Old gradients of sources [I0, I1) for vector k: bf16 rows give one 16-byte
+// vector per slice vector, fp32 rows two.
+template <bool F32, int I0, int I1, int VPT, int OW>
+__device__ __forceinline__ void load_grads(uint4 (&o)[I1 - I0][OW], const DstRows& d, int64_t t, int32_t D,
+                                           const Slice<VPT>& sl, int k) {
+#pragma unroll
+  for (int i = I0; i < I1; ++i) {
+    const __amdgpu_buffer_rsrc_t r = grad_row<F32>(d, i, t, D);
+    if constexpr (F32) {
+      // a lane's 32 bytes are split over two instructions with a 32-byte lane
+      // stride: default policy, so the second half finds the line in L2
+      o[i - I0][0] = bload(r, 2u * sl.off[k]);
+      o[i - I0][1] = bload(r, 2u * sl.off[k] + 16u);
+    } else {
+      o[i - I0][0] = bload<kAuxStreamLoad>(r, sl.off[k]);
+    }
+  }
+}
 
 // This thread's slice of token t's N source rows; each row's descriptor is
 // built in scalar registers.  With valid == false the descriptors have size 0:
@@ -318,7 +362,8 @@ __device__ __forceinline__ void load_row(uint4 (&g)[VPT], const uint16_t* __rest
 // read zeros).  Loaded with the row group, so they complete in the same order.
 template <int N>
 __device__ __forceinline__ void load_saved(float& a, float& r, const float* __restrict__ alpha,
-                                           const float* __restrict__ rstd, int64_t t, int lane, bool valid = true) {
+                                           const float* __restrict__ rstd, int64_t t, bool valid = true) {
+  const int lane = lane_id();
   const int64_t tt = valid ? t : 0;
   const uint32_t bytes = valid ? (uint32_t)N * 4u : 0u;
   a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(alpha + tt * N, bytes), lane * 4, 0, 0));
@@ -341,7 +386,7 @@ struct FwdCtx {
   float* alpha_out;
   const float4* wl;
   float (*red)[kMaxWaves];  // red[buf * 2N + k][wave]
-  int tid, lane, wave;
+  int tid;
 };
 
 // Forward of token t whose row group is already in x: partial sums, workgroup
@@ -366,7 +411,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
       for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
     }
   }
-  block_sums<2 * N>(part, c.red + buf * 2 * N, c.lane, c.wave);
+  block_sums<2 * N>(part, c.red + buf * 2 * N);
   buf ^= 1;
 #pragma unroll
   for (int i = 0; i < N; ++i)
@@ -461,8 +506,6 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* 
   c.wl = dyn_lds;
   c.red = &red[0][0];
   c.tid = threadIdx.x;
-  c.lane = c.tid & (kWave - 1);
-  c.wave = c.tid / kWave;
   const Slice<VPT> sl(c.tid, blockDim.x);
   const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
 
@@ -512,18 +555,27 @@ struct BwdCtx {
   const float4* wl;
   float4* dwl;
   float (*red)[kMaxWaves];
-  int lane, wave;
 };
 
 // Backward of token t whose sources and dout are already in x and g:
 // g.x_i and w.x_i, workgroup reduction, softmax backward, dsources stores and
-// this workgroup's running dw (LDS).  Issues no loads of the row group.  With ACC
-// the old gradients are loaded once the partial sums are formed (so they are
-// in flight during the reduction but not live during the first pass) and the
-// new gradient is added to them in fp32 before rounding.
-template <int N, int VPT, bool ACC>
+// this workgroup's running dw (LDS).  Issues no loads of the row group.
+// MODE (kGradAccumulate | kGradF32): with accumulation the old gradients are
+// loaded once the partial sums are formed (in flight during the reduction but
+// not live during the first pass) and the new gradient is added to them in
+// fp32 before the single rounding (bf16) or store (fp32).  Old fp32
+// gradients take twice the registers: the first half of the sources is
+// loaded then, the rest when the stores reach it.
+template <int N, int VPT, int MODE>
 __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], float sa, float sr, int64_t t,
                                           int& buf, const BwdCtx& c, const Slice<VPT>& sl) {
+  constexpr bool ACC = (MODE & kGradAccumulate) != 0;
+  constexpr bool F32 = (MODE & kGradF32) != 0;
+  constexpr int OW = F32 ? 2 : 1;            // 16-byte vectors of old gradient per slice vector
+  constexpr int H = F32 ? (N + 1) / 2 : N;   // sources whose old gradients are loaded early
+  constexpr int KP = F32 ? 1 : VPT;          // slice vectors loaded early
+  constexpr int R = N - H;                   // sources loaded when the stores reach them (fp32)
+
   // partial g.x_i (first N) and w.x_i (last N)
   float part[2 * N];
 #pragma unroll
@@ -541,13 +593,14 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
       for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
     }
   }
-  uint4 old[ACC ? N : 1][VPT];
+  uint4 old[ACC ? KP : 1][ACC ? H : 1][OW];
   if constexpr (ACC) {
     sched_fence();
-    load_rows<N, VPT>(old, c.dsrc, t, c.D, sl);
+#pragma unroll
+    for (int k = 0; k < KP; ++k) load_grads<F32, 0, H>(old[k], c.dsrc, t, c.D, sl, k);
     sched_fence();
   }
-  block_sums<2 * N>(part, c.red + buf * 2 * N, c.lane, c.wave);
+  block_sums<2 * N>(part, c.red + buf * 2 * N);
   buf ^= 1;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
@@ -580,8 +633,23 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
     unpack8(g[k], gf);
     load8(c.wl, sl.slot[k], wr);
     load8(c.dwl, sl.slot[k], dwr);
+    if constexpr (ACC && F32) {
+      if (k > 0) {  // later vectors of an fp32 accumulation: their first half now
+        sched_fence();
+        load_grads<true, 0, H>(old[0], c.dsrc, t, c.D, sl, k);
+        sched_fence();
+      }
+    }
+    uint4 rest[(ACC && F32 && R > 0) ? R : 1][OW];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
+      if constexpr (ACC && F32 && R > 0) {
+        if (i == H) {
+          sched_fence();
+          load_grads<true, H, N>(rest, c.dsrc, t, c.D, sl, k);
+          sched_fence();
+        }
+      }
       float f[8], d[8];
       unpack8(x[i][k], f);
 #pragma unroll
@@ -591,12 +659,34 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
       }
       if constexpr (ACC) {
         float o[8];
-        unpack8(old[i][k], o);
+        if constexpr (F32) {
+          const uint4& a = i < H ? old[0][i < H ? i : 0][0] : rest[i < H ? 0 : i - H][0];
+          const uint4& b = i < H ? old[0][i < H ? i : 0][1] : rest[i < H ? 0 : i - H][1];
+          o[0] = __builtin_bit_cast(float, a.x); o[1] = __builtin_bit_cast(float, a.y);
+          o[2] = __builtin_bit_cast(float, a.z); o[3] = __builtin_bit_cast(float, a.w);
+          o[4] = __builtin_bit_cast(float, b.x); o[5] = __builtin_bit_cast(float, b.y);
+          o[6] = __builtin_bit_cast(float, b.z); o[7] = __builtin_bit_cast(float, b.w);
+        } else {
+          unpack8(old[k][i][0], o);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[e] = o[e] + d[e];
       }
-      const __amdgpu_buffer_rsrc_t rd = rsrc(c.dsrc.p[i] + t * c.dsrc.pitch, (uint32_t)c.D * 2u);
-      bstore<kAuxStreamStore>(rd, sl.off[k], pack8(d));
+      const __amdgpu_buffer_rsrc_t rd = grad_row<F32>(c.dsrc, i, t, c.D);
+      if constexpr (F32) {
+        // two 16-byte halves per lane, 32 bytes apart between lanes: default
+        // policy, so L2 merges the halves into whole lines before they go out
+        bstore(rd, 2u * sl.off[k], make_uint4(__builtin_bit_cast(uint32_t, d[0]),
+                                                               __builtin_bit_cast(uint32_t, d[1]),
+                                                               __builtin_bit_cast(uint32_t, d[2]),
+                                                               __builtin_bit_cast(uint32_t, d[3])));
+        bstore(rd, 2u * sl.off[k] + 16u, make_uint4(__builtin_bit_cast(uint32_t, d[4]),
+                                                                     __builtin_bit_cast(uint32_t, d[5]),
+                                                                     __builtin_bit_cast(uint32_t, d[6]),
+                                                                     __builtin_bit_cast(uint32_t, d[7])));
+      } else {
+        bstore<kAuxStreamStore>(rd, sl.off[k], pack8(d));
+      }
     }
     store8(c.dwl, sl.slot[k], dwr);
   }
@@ -622,12 +712,12 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
 // wait counts only ever wait for the oldest row group.  With ACC (no
 // prefetch) the old gradients are loaded during the reduction.  Dynamic LDS
 // holds w and the workgroup's running dw, in the thread's private slots.
-template <int N, int VPT, bool PIPE, bool ACC>
+template <int N, int VPT, bool PIPE, int MODE>
 __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
                                                    const float* __restrict__ w, const float* __restrict__ rstd,
                                                    const float* __restrict__ alpha, int64_t T, int32_t D, int32_t P,
                                                    DstRows dsrc, float* __restrict__ ws) {
-  static_assert(!(PIPE && ACC), "the accumulate variant does not prefetch");
+  static_assert(!(PIPE && (MODE & kGradAccumulate)), "the accumulating variants do not prefetch");
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
   BwdCtx c;
@@ -639,8 +729,6 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
   c.dwl = dyn_lds + 2 * VPT * (int)blockDim.x;
   c.red = &red[0][0];
   const int tid = threadIdx.x;
-  c.lane = tid & (kWave - 1);
-  c.wave = tid / kWave;
   const Slice<VPT> sl(tid, blockDim.x);
   const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
 
@@ -654,7 +742,7 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
   if constexpr (PIPE) {
     load_row<VPT>(ga, dout, ch, D, sl);
     load_rows<N, VPT>(xa, src, ch, D, sl);
-    load_saved<N>(saa, sra, alpha, rstd, ch, c.lane);
+    load_saved<N>(saa, sra, alpha, rstd, ch);
     sched_fence();
   }
   store_w<VPT>(wv, dyn_lds, sl);
@@ -668,22 +756,22 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
     int64_t t = ch;
     load_row<VPT>(gb, dout, t + P, D, sl, t + P < T);
     load_rows<N, VPT>(xb, src, t + P, D, sl, t + P < T);
-    load_saved<N>(sab, srb, alpha, rstd, t + P, c.lane, t + P < T);
+    load_saved<N>(sab, srb, alpha, rstd, t + P, t + P < T);
     sched_fence();
     while (true) {
-      bwd_token<N, VPT, false>(xa, ga, saa, sra, t, buf, c, sl);
+      bwd_token<N, VPT, MODE>(xa, ga, saa, sra, t, buf, c, sl);
       sched_fence();
       load_row<VPT>(ga, dout, t + 2 * P, D, sl, t + 2 * P < T);
       load_rows<N, VPT>(xa, src, t + 2 * P, D, sl, t + 2 * P < T);
-      load_saved<N>(saa, sra, alpha, rstd, t + 2 * P, c.lane, t + 2 * P < T);
+      load_saved<N>(saa, sra, alpha, rstd, t + 2 * P, t + 2 * P < T);
       sched_fence();
       t += P;
       if (t >= T) break;
-      bwd_token<N, VPT, false>(xb, gb, sab, srb, t, buf, c, sl);
+      bwd_token<N, VPT, MODE>(xb, gb, sab, srb, t, buf, c, sl);
       sched_fence();
       load_row<VPT>(gb, dout, t + 2 * P, D, sl, t + 2 * P < T);
       load_rows<N, VPT>(xb, src, t + 2 * P, D, sl, t + 2 * P < T);
-      load_saved<N>(sab, srb, alpha, rstd, t + 2 * P, c.lane, t + 2 * P < T);
+      load_saved<N>(sab, srb, alpha, rstd, t + 2 * P, t + 2 * P < T);
       sched_fence();
       t += P;
       if (t >= T) break;
@@ -694,8 +782,8 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
       float sa, sr;
       load_row<VPT>(g, dout, t, D, sl);
       load_rows<N, VPT>(x, src, t, D, sl);
-      load_saved<N>(sa, sr, alpha, rstd, t, c.lane);
-      bwd_token<N, VPT, ACC>(x, g, sa, sr, t, buf, c, sl);
+      load_saved<N>(sa, sr, alpha, rstd, t);
+      bwd_token<N, VPT, MODE>(x, g, sa, sr, t, buf, c, sl);
     }
   }
   publish_dw<VPT>(ws, ch, D, c.dwl, sl);
@@ -922,23 +1010,35 @@ hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
   return hipSuccess;
 }
 
-template <int N, int VPT, bool PIPE, bool ACC>
+template <int N, int VPT, bool PIPE, int MODE>
 hipError_t launch_bwd_n(const LaunchShape& s, hipStream_t st, const BwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, PIPE, ACC>);
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<N, VPT, PIPE, MODE>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, 2 * s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   // one workgroup per dw partial row (P = min(T, ATTNRES_DW_PARTIALS))
-  hipLaunchKernelGGL((bwd_kernel<N, VPT, PIPE, ACC>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
+  hipLaunchKernelGGL((bwd_kernel<N, VPT, PIPE, MODE>), dim3((unsigned)a.P), dim3((unsigned)s.threads),
                      2 * s.lds, st, a.dout, a.src, a.w, a.rstd, a.alpha, a.T, a.D, a.P, a.dsrc, a.ws);
   return hipGetLastError();
 }
 
+template <int N, int VPT>
+hipError_t run_bwd_vpt(const LaunchShape& s, int mode, hipStream_t st, const BwdArgs& a) {
+  // with one vector per thread the overwriting modes prefetch the next token;
+  // the accumulating ones keep the old gradients instead of a second row group
+  constexpr bool P = VPT == 1;
+  switch (mode) {
+    case 0: return launch_bwd_n<N, VPT, P, 0>(s, st, a);
+    case kGradAccumulate: return launch_bwd_n<N, VPT, false, kGradAccumulate>(s, st, a);
+    case kGradF32: return launch_bwd_n<N, VPT, P, kGradF32>(s, st, a);
+    case kGradF32 | kGradAccumulate: return launch_bwd_n<N, VPT, false, kGradF32 | kGradAccumulate>(s, st, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int N>
-hipError_t run_bwd_n(const LaunchShape& s, bool acc, hipStream_t st, const BwdArgs& a) {
-  // the accumulating variant keeps the old gradients instead of a second row group: no prefetch
-  if (s.vpt == 1) return acc ? launch_bwd_n<N, 1, false, true>(s, st, a) : launch_bwd_n<N, 1, true, false>(s, st, a);
-  return acc ? launch_bwd_n<N, 2, false, true>(s, st, a) : launch_bwd_n<N, 2, false, false>(s, st, a);
+hipError_t run_bwd_n(const LaunchShape& s, int mode, hipStream_t st, const BwdArgs& a) {
+  return s.vpt == 1 ? run_bwd_vpt<N, 1>(s, mode, st, a) : run_bwd_vpt<N, 2>(s, mode, st, a);
 }
 
 hipError_t run_fwd(int32_t N, const LaunchShape& s, bool update, hipStream_t st, const FwdArgs& a) {
@@ -956,17 +1056,17 @@ hipError_t run_fwd(int32_t N, const LaunchShape& s, bool update, hipStream_t st,
   }
 }
 
-hipError_t run_bwd(int32_t N, const LaunchShape& s, bool acc, hipStream_t st, const BwdArgs& a) {
+hipError_t run_bwd(int32_t N, const LaunchShape& s, int mode, hipStream_t st, const BwdArgs& a) {
   switch (N) {
-    case 1: return run_bwd_n<1>(s, acc, st, a);
-    case 2: return run_bwd_n<2>(s, acc, st, a);
-    case 3: return run_bwd_n<3>(s, acc, st, a);
-    case 4: return run_bwd_n<4>(s, acc, st, a);
-    case 5: return run_bwd_n<5>(s, acc, st, a);
-    case 6: return run_bwd_n<6>(s, acc, st, a);
-    case 7: return run_bwd_n<7>(s, acc, st, a);
-    case 8: return run_bwd_n<8>(s, acc, st, a);
-    case 9: return run_bwd_n<9>(s, acc, st, a);
+    case 1: return run_bwd_n<1>(s, mode, st, a);
+    case 2: return run_bwd_n<2>(s, mode, st, a);
+    case 3: return run_bwd_n<3>(s, mode, st, a);
+    case 4: return run_bwd_n<4>(s, mode, st, a);
+    case 5: return run_bwd_n<5>(s, mode, st, a);
+    case 6: return run_bwd_n<6>(s, mode, st, a);
+    case 7: return run_bwd_n<7>(s, mode, st, a);
+    case 8: return run_bwd_n<8>(s, mode, st, a);
+    case 9: return run_bwd_n<9>(s, mode, st, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1041,8 +1141,9 @@ attnres_status bwd_common_checks(const float* w, int32_t N, int64_t T, int32_t D
 
 attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch, const float* w,
                         const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
-                        uint16_t* const* dsrcs, int64_t dsrc_pitch, bool acc, float* dw, void* workspace,
+                        void* const* dsrcs, int64_t dsrc_pitch, int mode, float* dw, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  const int64_t gsize = (mode & kGradF32) ? 4 : 2;  // bytes per gradient element
   if (dout == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(dout, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
@@ -1069,7 +1170,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
   if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   Range outs[ATTNRES_MAX_SOURCES + 2];
   int nout = 0;
-  for (int i = 0; i < N; ++i) outs[nout++] = rows_of(dsrcs[i], T, (int64_t)D * 2, dsrc_pitch * 2);
+  for (int i = 0; i < N; ++i) outs[nout++] = rows_of(dsrcs[i], T, (int64_t)D * gsize, dsrc_pitch * gsize);
   outs[nout++] = range_of(dw, (size_t)D * 4);
   outs[nout++] = range_of(workspace, need);
   for (int a = 0; a < nout; ++a) {
@@ -1083,7 +1184,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
   float* ws = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const BwdArgs args{dout, rows, w, rstd, alpha, T, D, P, drows, ws};
-  hipError_t e = run_bwd(N, s, acc, st, args);
+  hipError_t e = run_bwd(N, s, mode, st, args);
   if (e != hipSuccess) return ATTNRES_ERR_HIP;
   const int D4 = D / 4;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
@@ -1152,18 +1253,20 @@ extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src,
     srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
     dsrcs[i] = dsrc + (size_t)i * (size_t)T * (size_t)D;
   }
-  return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, dsrcs, D, false, dw, workspace, workspace_bytes, stream);
+  return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, reinterpret_cast<void* const*>(dsrcs), D, 0, dw, workspace,
+                  workspace_bytes, stream);
 }
 
 extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch,
                                               const float* w, const float* rstd, const float* alpha, int32_t N,
-                                              int64_t T, int32_t D, uint16_t* const* dsrcs, int64_t dsrc_pitch,
-                                              int32_t accumulate, float* dw, void* workspace,
+                                              int64_t T, int32_t D, void* const* dsrcs, int64_t dsrc_pitch,
+                                              int32_t grad_mode, float* dw, void* workspace,
                                               size_t workspace_bytes, void* stream) {
   const attnres_status st = bwd_common_checks(w, N, T, D, dw);
   if (st != ATTNRES_OK) return st;
+  if (grad_mode < 0 || grad_mode > (kGradAccumulate | kGradF32)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (T == 0) return bwd_zero_dw(dw, D, stream);
   if (srcs == nullptr || dsrcs == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  return bwd_impl(dout, srcs, src_pitch, w, rstd, alpha, N, T, D, dsrcs, dsrc_pitch, accumulate != 0, dw, workspace,
+  return bwd_impl(dout, srcs, src_pitch, w, rstd, alpha, N, T, D, dsrcs, dsrc_pitch, grad_mode, dw, workspace,
                   workspace_bytes, stream);
 }

@@ -254,6 +254,13 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
                                                                   accumulate=True, dw=dw, workspace=ws),
                                    bb + be + T * 2 * N * D),
     }
+    # fp32 gradients: written (2ND more bytes than bf16) and accumulated (4ND more read)
+    g32 = [torch.zeros((T, D), dtype=torch.float32, device=dev) for _ in range(N)]
+    calls["bwd_sources_f32"] = (lambda: ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=g32, dw=dw,
+                                                               workspace=ws), bb + be + T * 2 * N * D)
+    calls["bwd_sources_f32_accumulate"] = (lambda: ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=g32,
+                                                                          accumulate=True, dw=dw, workspace=ws),
+                                           bb + be + T * 6 * N * D)
     # partial-sum update fused into the forward (last source = bf16(p + y)),
     # against the unfused route: a separate elementwise add, then the forward
     p = srcs[-1].clone()
@@ -281,7 +288,7 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
         m = _median_ms(torch, flush, fn, reps)
         print(json.dumps({"sweep": True, "call": name, "N": N, "T": T, "D": D, "ms": m,
                           "GBps": nbytes / m / 1e6, "frac_of_8TBps": nbytes / m / 1e6 / HBM_PEAK_GBPS}), flush=True)
-    del srcs, dsrcs, dout, p, y, cache, views, dcache, dviews
+    del srcs, dsrcs, dout, p, y, cache, views, dcache, dviews, g32
     torch.cuda.empty_cache()
     sweep_decode(ar, torch, dev, flush)
 

@@ -68,6 +68,10 @@ typedef enum {
 /* Rows of dw partial sums in the backward workspace: with P = min(T, 256)
  * backward workgroups, row c holds the sum over tokens c, c+P, c+2P, ... */
 #define ATTNRES_DW_PARTIALS 256
+/* grad_mode flags of attnres_bwd_sources. */
+#define ATTNRES_GRAD_BF16 0
+#define ATTNRES_GRAD_ACCUMULATE 1
+#define ATTNRES_GRAD_F32 2
 /* Bytes of device workspace attnres_bwd needs for hidden size D. */
 #define ATTNRES_BWD_WORKSPACE_BYTES(D) ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float))
 
@@ -190,24 +194,32 @@ attnres_status attnres_fwd_update(const uint16_t* const* srcs, int64_t src_pitch
                                   uint16_t* partial_out, uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
- * Backward with per-source pointers, optionally accumulating the source
- * gradients.  A completed block sum is a source of every later sub-layer's
- * AttnRes, so its gradient is the sum of those operators' contributions:
+ * Backward with per-source row sets, writing or accumulating the source
+ * gradients in bf16 or fp32.  A completed block sum is a source of every
+ * later sub-layer's operator, so its gradient is the sum of those operators'
+ * contributions:
  *   srcs, src_pitch   as attnres_fwd_sources.
- *   dsrcs       host array of N device pointers to the bf16 gradients, row
- *               t of gradient i at dsrcs[i] + t*dsrc_pitch (the same
- *               choices of layout as the sources), pairwise disjoint and
- *               disjoint from every input.
- *   accumulate  0: dsrcs[i] = dx_i (bitwise identical to attnres_bwd);
- *               else: dsrcs[i] = bf16( fp32(dsrcs[i]) + dx_i ), rounded to
- *               nearest even, each element read and written once.
+ *   dsrcs       host array of N device pointers to the gradients, row t of
+ *               gradient i at dsrcs[i] + t*dsrc_pitch elements (bf16 or
+ *               fp32 as grad_mode says; the same choices of layout as the
+ *               sources), pairwise disjoint and disjoint from every input.
+ *   grad_mode   ATTNRES_GRAD_BF16 (0): dsrcs[i] = bf16(dx_i), bitwise what
+ *                 attnres_bwd writes;
+ *               ATTNRES_GRAD_ACCUMULATE (1): dsrcs[i] = bf16(dsrcs[i] + dx_i),
+ *                 the sum formed in fp32 and rounded once to nearest even;
+ *               ATTNRES_GRAD_F32 (2): dsrcs[i] = dx_i in fp32 (no rounding
+ *                 to bf16);
+ *               ATTNRES_GRAD_F32 | ATTNRES_GRAD_ACCUMULATE (3): fp32
+ *                 gradients, dsrcs[i] += dx_i in fp32.
+ *               Each gradient element is read (when accumulating) and
+ *               written once.  Other values: ATTNRES_ERR_INVALID_ARGUMENT.
  * dw is always overwritten with this call's sum over the T tokens.  Other
  * arguments as attnres_bwd.  srcs and dsrcs may be NULL when T == 0.
  */
 attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch,
                                    const float* w, const float* rstd, const float* alpha, int32_t N, int64_t T,
-                                   int32_t D, uint16_t* const* dsrcs, int64_t dsrc_pitch, int32_t accumulate,
-                                   float* dw, void* workspace, size_t workspace_bytes, void* stream);
+                                   int32_t D, void* const* dsrcs, int64_t dsrc_pitch, int32_t grad_mode, float* dw,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

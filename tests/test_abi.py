@@ -347,3 +347,17 @@ def test_bwd_sources_overlap_checks_match_a_byte_model(seed):
         assert code == INVALID, "an overlapping layout was accepted"
     elif must_accept:
         assert code == 3, "a disjoint layout was rejected"
+
+
+def test_bwd_sources_rejects_unknown_grad_modes():
+    g = 1 << 30
+    srcs, dsrcs = _arr([2 * g, 3 * g, 4 * g]), _arr([8 * g, 9 * g, 10 * g])
+    assert _bwd_src(srcs, dsrcs, acc=4) == INVALID
+    assert _bwd_src(srcs, dsrcs, acc=-1) == INVALID
+    assert _bwd_src(srcs, dsrcs, acc=7, T=0) == INVALID  # checked before the empty-batch shortcut
+
+
+def test_grad_mode_constants_match_binding():
+    assert _define("ATTNRES_GRAD_BF16") == 0
+    assert _define("ATTNRES_GRAD_ACCUMULATE") == ar.GRAD_ACCUMULATE
+    assert _define("ATTNRES_GRAD_F32") == ar.GRAD_F32

@@ -169,3 +169,58 @@ def test_interleaved_partial_sum_update_in_place():
     assert torch.equal(_bits(p1), _bits(cache[:, N - 1]))
     assert torch.equal(_bits(out1), _bits(out2))
     assert torch.equal(_bits(r1), _bits(r2)) and torch.equal(_bits(a1), _bits(a2))
+
+
+@pytest.mark.parametrize("N,T,D", [(9, 300, 7168), (4, 65, 1000), (3, 33, 12288), (1, 9, 7168)],
+                         ids=lambda v: str(v))
+def test_fp32_gradients(N, T, D):
+    """fp32 gradients: written (no bf16 rounding: the oracle's dx to fp32
+    precision, and bitwise the bf16 mode's values before rounding) and
+    accumulated in fp32 onto seeded prior gradients."""
+    wl = synth.Workload(f"f32_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src_h, w_h, dout_h = wl.sources(), wl.w(), wl.dout()
+    srcs = [to_dev_bf16(src_h[i]) for i in range(N)]
+    w = torch.from_numpy(w_h).to(DEV)
+    dout = to_dev_bf16(dout_h)
+    out, rstd, alpha = ar.attnres_fwd_sources(srcs, w, wl.eps)
+    g32, dw32 = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, grad_dtype=torch.float32)
+    g16, dw16 = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha)
+    prior = [torch.randn((T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(i)) * 0.1
+             for i in range(N)]
+    acc = [p.clone() for p in prior]
+    acc, _ = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=acc, accumulate=True)
+    torch.cuda.synchronize()
+    o_dsrc, o_dw = oracle.bwd(src_h, w_h, wl.eps, dout_h)
+    got = np.stack([g.double().cpu().numpy() for g in g32])
+    e32 = rel_l2(got, o_dsrc)
+    e_acc = rel_l2(np.stack([a.double().cpu().numpy() for a in acc]),
+                   np.stack([p.double().cpu().numpy() for p in prior]) + o_dsrc)
+    print(f"[parity] fp32 gradients N={N} T={T} D={D}: written rel_l2={e32:.3e} accumulated rel_l2={e_acc:.3e}",
+          flush=True)
+    assert e32 <= 1e-5
+    assert e_acc <= 1e-5
+    for i in range(N):
+        assert torch.equal(_bits(g32[i].to(torch.bfloat16)), _bits(g16[i])), i
+    assert torch.equal(_bits(dw32), _bits(dw16))
+    # fp32 accumulation adds exactly the fp32 increment (one fp32 rounding per element)
+    for i in range(N):
+        assert torch.equal(_bits(acc[i]), _bits(prior[i] + g32[i])), i
+
+
+def test_fp32_gradients_interleaved():
+    """fp32 gradients in a [T][N][D] fp32 cache (pitch N*D) equal dense ones."""
+    N, T, D = 6, 128, 7168
+    wl = synth.Workload(f"f32_inter_N{N}", T=T, N=N, D=D)
+    src = to_dev_bf16(wl.sources())
+    w = torch.from_numpy(wl.w()).to(DEV)
+    dout = to_dev_bf16(wl.dout())
+    srcs = [src[i] for i in range(N)]
+    _, rstd, alpha = ar.attnres_fwd_sources(srcs, w, wl.eps)
+    dense, _ = ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, grad_dtype=torch.float32)
+    cache = torch.zeros((T, N, D), dtype=torch.float32, device=DEV)
+    views = [cache[:, i] for i in range(N)]
+    ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=views)
+    ar.attnres_bwd_sources(dout, srcs, w, rstd, alpha, dsrcs=views, accumulate=True)
+    torch.cuda.synchronize()
+    for i in range(N):
+        assert torch.equal(_bits(views[i]), _bits(dense[i] + dense[i])), i
