@@ -203,6 +203,16 @@ __device__ __forceinline__ void clear_red(float (*red)[K][kMaxWaves]) {
   __syncthreads();
 }
 
+// For a single token: zero only the slots of absent waves in buffer 0.  No
+// barrier: no wave writes those slots, and the barrier inside block_sums
+// orders these stores before the slots are read.
+template <int K>
+__device__ __forceinline__ void clear_absent(float (*red)[K][kMaxWaves]) {
+  const int present = (int)blockDim.x / kWave;
+  const int absent = kMaxWaves - present;
+  for (int j = threadIdx.x; j < K * absent; j += blockDim.x) red[0][j / absent][present + j % absent] = 0.f;
+}
+
 // Hide a register's contents from the optimiser so values derived from it
 // (unpacked floats) are recomputed after a barrier instead of being kept live
 // across it: holding 8 unpacked floats per packed vector would double the
@@ -531,7 +541,7 @@ __global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* 
     }
   }
   store_w<VPT>(wv, dyn_lds, sl);
-  clear_red<2 * N>(red);
+  clear_absent<2 * N>(red);
   int buf = 0;
   fwd_token<N, VPT>(x, t, buf, c, sl);
 }
