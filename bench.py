@@ -342,6 +342,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="only the decoding-size forward calls (T = 1..1024), for latency profiles")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the operator is token-local and this build has no "
@@ -355,6 +357,9 @@ def main():
 
     dev = torch.device("cuda:0")
     ar.library()
+    if args.decode:
+        sweep_decode(ar, torch, dev, torch.empty(512 << 20, dtype=torch.uint8, device=dev))
+        return
     wl = synth.workload(1)  # T=4096, N=9, D=7168
     T, N, D = wl.T, wl.N, wl.D
     src, w, dout = make_inputs(wl, torch, dev)
