@@ -37,7 +37,9 @@
  *     (a hipStream_t; NULL selects the null stream) and the call returns once
  *     the work is enqueued.
  *   - Outputs are overwritten, never accumulated (except by the
- *     accumulating mode of attnres_bwd_sources).  Inputs are not modified.
+ *     accumulating modes of attnres_bwd_sources).  Inputs are not modified
+ *     (except the partial sum that attnres_fwd_update updates when
+ *     partial_out is the partial sum itself).
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error the call returns a non-zero status and enqueues nothing.
  *   - Results for one token depend only on that token's inputs (and w): they
