@@ -169,7 +169,7 @@ def _rows(t: torch.Tensor, name: str, T: int, D: int, dtype=torch.bfloat16) -> i
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != (T, D):
         raise ValueError(f"{name} must have shape {(T, D)}, got {tuple(t.shape)}")
-    if T > 1 and t.stride(1) != 1:
+    if T > 0 and D > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} rows must be contiguous")
     return D if T <= 1 else t.stride(0)
 
