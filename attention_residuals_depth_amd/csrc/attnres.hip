@@ -16,10 +16,11 @@
 //             same registers.  The same kernel serves training batches and
 //             single decoding steps.
 //   backward  one kernel re-reads each source row once (plus dout), forms
-//             da_i = g.x_i and w.x_i with the same reduction tree, then writes
-//             dsources from the registers and accumulates this workgroup's
-//             dw partial row; a second small kernel sums the fixed number of
-//             partial rows in index order (deterministic, no atomics).
+//             da_i = g.x_i and w.x_i with the same kind of fixed reduction
+//             tree, then writes (or accumulates into) dsources from the
+//             registers and accumulates this workgroup's dw partial row; a
+//             second small kernel sums the fixed number of partial rows in
+//             index order (deterministic, no atomics).
 //
 // Determinism and batch invariance (the determinism section of the Fireworks
 // report fixes reduction orders so results do not depend on the batch): the

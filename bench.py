@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -49,7 +50,14 @@ def algo_bytes(T: int, N: int, D: int):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are dropped, so
+    recorded counter traffic stays valid across comment edits and goes stale
+    (reported as null) on any change to the code."""
+    text = open(KERNEL_SRC, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()[:16]
 
 
 def load_traffic(T: int, N: int, D: int):
