@@ -720,8 +720,8 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
 // and a set is refilled with the workgroup's token two steps ahead as soon as
 // its token is done.  Loads past the last token use size-0 descriptors and
 // scheduling fences keep each prefetch where it is issued, so the in-order
-// wait counts only ever wait for the oldest row group.  With ACC (no
-// prefetch) the old gradients are loaded during the reduction.  Dynamic LDS
+// wait counts only ever wait for the oldest row group.  When accumulating
+// (no prefetch) the old gradients are loaded during the reduction.  Dynamic LDS
 // holds w and the workgroup's running dw, in the thread's private slots.
 template <int N, int VPT, bool PIPE, int MODE>
 __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
@@ -936,8 +936,10 @@ bool sizes_ok(int32_t N, int64_t T, int32_t D) {
 }
 
 // Resident workgroups of `fn` on the current device (occupancy x CUs).  The
-// grid only sets how many workgroups share the tokens; results never depend
-// on it.  The answer is cached per (device, kernel, shape): the two runtime
+// launches call it to validate their shape before enqueueing (a kernel that
+// cannot be resident at that block size and LDS is refused with an error
+// instead of failing at dispatch); grids are set by T and P, never by this
+// count.  The answer is cached per (device, kernel, shape): the two runtime
 // queries cost more host time than a small launch itself.
 struct OccupancyEntry {
   const void* fn;
