@@ -621,7 +621,7 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
   }
 
   // softmax backward: s = sum_j alpha_j da_j; dz_i = alpha_i (da_i - s)
-  float al[N], c1[N], c2[N];
+  float al[N], c1[N], kx[N];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -633,8 +633,12 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
     const float rs = lane_value(sr, i);
     const float dz = al[i] * (part[i] - s);
     const float z = rs * part[N + i];
-    c1[i] = uniform(dz * rs);                   // coefficient of w_d in dx and of x_id in dw
-    c2[i] = uniform(c1[i] * z * rs * c.inv_d);  // coefficient of x_id in dx
+    // dx_id = alpha_i g_d + c1 (w_d - kx x_id): c1 = dz rstd, kx = z rstd / D.
+    // The bracket is formed first, so no intermediate carries rstd^2 (with
+    // eps = 0 and a row of rms ~1e-15, dz rstd^2 alone would overflow fp32
+    // while dx itself is representable).
+    c1[i] = uniform(dz * rs);           // coefficient of the bracket in dx and of x_id in dw
+    kx[i] = uniform(z * rs * c.inv_d);  // coefficient of x_id inside the bracket
     al[i] = uniform(al[i]);
   }
 
@@ -665,7 +669,7 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
       unpack8(x[i][k], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        d[e] = fmaf(-c2[i], f[e], fmaf(c1[i], wr[e], al[i] * gf[e]));
+        d[e] = fmaf(c1[i], fmaf(-kx[i], f[e], wr[e]), al[i] * gf[e]);
         dwr[e] = fmaf(c1[i], f[e], dwr[e]);
       }
       if constexpr (ACC) {

@@ -1,0 +1,108 @@
+"""Degenerate inputs against the fp64 oracle.
+
+- All-zero source rows with eps > 0: the row's rstd is 1/sqrt(eps) and its
+  score 0, everything stays finite (including a token whose sources are all
+  zero: uniform weights, out = 0, dsources = dout / N).
+- An all-zero source row with eps = 0: the formula gives rstd = inf and a NaN
+  score, so that token's weights, output and source gradients are NaN -- on
+  the GPU exactly where the oracle has them, and no other token is touched
+  (dw, a sum over all tokens, is NaN on both sides).
+- Sources scaled by 2^+-50 (exact in bf16): mean squares of 1e-30 .. 1e30 stay
+  inside the fp32 range the kernels accumulate in, so the results match the
+  oracle at the usual tolerances, also with eps = 0."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import oracle
+import synth
+from parity import (DEV, TOL_ALPHA_ABS, TOL_DSRC_REL_L2, TOL_OUT_REL_L2, TOL_RSTD_REL, bf16_dev_to_f64,
+                    check_tokens, rel_l2, run_gpu, to_dev_bf16, within_tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _run(src_h, w_h, eps, dout_h):
+    out, rstd, alpha, dsrc, dw = run_gpu(to_dev_bf16(src_h), torch.from_numpy(w_h).to(DEV), eps, to_dev_bf16(dout_h))
+    gpu = dict(out=bf16_dev_to_f64(out), rstd=rstd.cpu().double().numpy(), alpha=alpha.cpu().double().numpy(),
+               dsrc=bf16_dev_to_f64(dsrc), dw=dw.cpu().double().numpy())
+    o_out, o_rstd, o_alpha = oracle.fwd(src_h, w_h, eps)
+    o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
+    ref = dict(out=o_out, rstd=o_rstd, alpha=o_alpha, dsrc=o_dsrc, dw=o_dw)
+    return gpu, ref
+
+
+def _scale_bf16(bits: np.ndarray, log2: int) -> np.ndarray:
+    """bf16 bit patterns times 2^log2 (exact: only the exponent moves)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2)
+    out = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((out.astype(np.uint32) << 16).view(np.float32), f)
+    return out
+
+
+@pytest.mark.parametrize("N,T,D", [(4, 70, 1000), (9, 33, 7168)], ids=lambda v: str(v))
+def test_zero_rows_with_eps(N, T, D):
+    wl = synth.Workload(f"zero_rows_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+    src = wl.sources().copy()
+    src[0, 0] = 0
+    src[N - 1, T // 2] = 0
+    src[:, T - 1] = 0  # every source of the last token
+    gpu, ref = _run(src, wl.w(), 1e-6, wl.dout())
+    errs = {}
+    e = check_tokens(errs, wl.name, gpu, ref)
+    print(f"[parity] {wl.name}: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert within_tolerance(e), e
+    assert np.all(np.isfinite(gpu["out"])) and np.all(np.isfinite(gpu["dsrc"]))
+    assert np.allclose(gpu["rstd"][T - 1], 1e3, rtol=1e-6)
+    assert np.all(gpu["alpha"][T - 1] == np.float32(1.0 / N))
+    assert np.all(gpu["out"][T - 1] == 0.0)
+
+
+def test_zero_row_without_eps_is_nan_in_its_token_only():
+    N, T, D, bad = 5, 40, 1000, 17
+    wl = synth.Workload("zero_row_eps0", T=T, N=N, D=D)
+    src = wl.sources().copy()
+    src[2, bad] = 0
+    gpu, ref = _run(src, wl.w(), 0.0, wl.dout())
+    assert np.isinf(ref["rstd"][bad, 2]) and gpu["rstd"][bad, 2] == np.inf
+    for name in ("alpha", "out"):
+        assert np.array_equal(np.isnan(gpu[name]), np.isnan(ref[name])), name
+        assert np.all(np.isnan(gpu[name][bad]))
+    assert np.array_equal(np.isnan(gpu["dsrc"]), np.isnan(ref["dsrc"]))
+    assert np.all(np.isnan(gpu["dsrc"][:, bad]))
+    assert np.all(np.isnan(gpu["dw"])) and np.all(np.isnan(ref["dw"]))
+    keep = np.arange(T) != bad
+    assert rel_l2(gpu["out"][keep], ref["out"][keep]) <= TOL_OUT_REL_L2
+    assert float(np.max(np.abs(gpu["alpha"][keep] - ref["alpha"][keep]))) <= TOL_ALPHA_ABS
+    assert float(np.max(np.abs(gpu["rstd"][keep] / ref["rstd"][keep] - 1))) <= TOL_RSTD_REL
+    assert rel_l2(gpu["dsrc"][:, keep], ref["dsrc"][:, keep]) <= TOL_DSRC_REL_L2
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+def test_magnitudes_across_the_fp32_range(eps):
+    """Sources scaled by 2^-50, 1 and 2^+50 in one call (mean squares from
+    ~1e-30 to ~1e31): with eps = 0 the weights equal those of the unscaled
+    sources (scale invariance of the normalised score)."""
+    N, T, D = 6, 50, 7168
+    wl = synth.Workload("magnitudes", T=T, N=N, D=D)
+    base = wl.sources()
+    shifts = [-50, 0, 50, -50, 50, 0]
+    src = np.stack([_scale_bf16(base[i], s) for i, s in enumerate(shifts)])
+    gpu, ref = _run(src, wl.w(), eps, wl.dout())
+    errs = {}
+    e = check_tokens(errs, "magnitudes", gpu, ref)
+    print(f"[parity] magnitudes eps={eps}: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert within_tolerance(e), e
+    if eps == 0.0:
+        _, _, alpha_unscaled = oracle.fwd(base, wl.w(), 0.0)
+        assert float(np.max(np.abs(gpu["alpha"] - alpha_unscaled))) <= TOL_ALPHA_ABS
