@@ -24,6 +24,7 @@ The C entry points, declared in ``include/attnres.h``:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -78,9 +79,28 @@ def workspace_bytes(D: int) -> int:
     return DW_PARTIALS * D * 4
 
 
-def _stream_handle(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream_handle(stream, dev: torch.device) -> int:
+    """The stream to enqueue on: the given one, else the current stream of the
+    tensors' device.  The library launches on the current device, so the call
+    sites run with `dev` current (see _device)."""
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if s.device != dev:
+        raise ValueError(f"stream is on {s.device}, the tensors on {dev}")
     return s.cuda_stream
+
+
+def _device(dev: torch.device):
+    """Make `dev` the current device for the duration of a library call (a
+    no-op when it already is)."""
+    if dev.index is None or torch.cuda.current_device() == dev.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
+def _same_device(dev: torch.device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} like the sources")
 
 
 def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple):
@@ -113,8 +133,10 @@ def attnres_fwd(src: torch.Tensor, w: torch.Tensor, eps: float, out=None, rstd=N
     _check(out, "out", torch.bfloat16, (T, D))
     _check(rstd, "rstd", torch.float32, (T, N))
     _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd(src.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
-                                 rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream))
+    _same_device(dev, w=w, out=out, rstd=rstd, alpha=alpha)
+    with _device(dev):
+        code = library().attnres_fwd(src.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+                                     rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd", code)
     return out, rstd, alpha
@@ -143,9 +165,11 @@ def attnres_bwd(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: to
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    code = library().attnres_bwd(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(), alpha.data_ptr(),
-                                 N, T, D, dsrc.data_ptr(), dw.data_ptr(), workspace.data_ptr(), ws_bytes,
-                                 _stream_handle(stream))
+    _same_device(dev, dout=dout, w=w, rstd=rstd, alpha=alpha, dsrc=dsrc, dw=dw, workspace=workspace)
+    with _device(dev):
+        code = library().attnres_bwd(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(),
+                                     alpha.data_ptr(), N, T, D, dsrc.data_ptr(), dw.data_ptr(), workspace.data_ptr(),
+                                     ws_bytes, _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_bwd", code)
     return dsrc, dw
@@ -213,8 +237,11 @@ def attnres_fwd_sources(srcs, w: torch.Tensor, eps: float, out=None, rstd=None, 
     _check(out, "out", torch.bfloat16, (T, D))
     _check(rstd, "rstd", torch.float32, (T, N))
     _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_sources(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
-                                         rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream))
+    _same_device(dev, w=w, out=out, rstd=rstd, alpha=alpha, **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_fwd_sources(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D,
+                                             out.data_ptr(), rstd.data_ptr(), alpha.data_ptr(),
+                                             _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd_sources", code)
     return out, rstd, alpha
@@ -239,9 +266,11 @@ def attnres_fwd_decode(srcs, w: torch.Tensor, eps: float, out=None, save_state: 
             alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
         _check(rstd, "rstd", torch.float32, (T, N))
         _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_decode(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
-                                        None if rstd is None else rstd.data_ptr(),
-                                        None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
+    _same_device(dev, w=w, out=out, rstd=rstd, alpha=alpha, **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_fwd_decode(_ptr_array(srcs), pitch, w.data_ptr(), float(eps), N, T, D,
+                                            out.data_ptr(), None if rstd is None else rstd.data_ptr(),
+                                            None if alpha is None else alpha.data_ptr(), _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd_decode", code)
     return out, rstd, alpha
@@ -284,10 +313,14 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
             alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
         _check(rstd, "rstd", torch.float32, (T, N))
         _check(alpha, "alpha", torch.float32, (T, N))
-    code = library().attnres_fwd_update(_ptr_array(srcs) if srcs else None, pitch, partial.data_ptr(), delta.data_ptr(),
-                                        w.data_ptr(), float(eps), N, T, D, partial_out.data_ptr(), out.data_ptr(),
-                                        None if rstd is None else rstd.data_ptr(),
-                                        None if alpha is None else alpha.data_ptr(), _stream_handle(stream))
+    _same_device(dev, delta=delta, w=w, partial_out=partial_out, out=out, rstd=rstd, alpha=alpha,
+                 **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_fwd_update(_ptr_array(srcs) if srcs else None, pitch, partial.data_ptr(),
+                                            delta.data_ptr(), w.data_ptr(), float(eps), N, T, D,
+                                            partial_out.data_ptr(), out.data_ptr(),
+                                            None if rstd is None else rstd.data_ptr(),
+                                            None if alpha is None else alpha.data_ptr(), _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd_update", code)
     return out, rstd, alpha, partial_out
@@ -332,9 +365,13 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), pitch, w.data_ptr(), rstd.data_ptr(),
-                                         alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), dpitch, mode,
-                                         dw.data_ptr(), workspace.data_ptr(), ws_bytes, _stream_handle(stream))
+    _same_device(dev, dout=dout, w=w, rstd=rstd, alpha=alpha, dw=dw, workspace=workspace,
+                 **{f"srcs[{i}]": t for i, t in enumerate(srcs)}, **{f"dsrcs[{i}]": t for i, t in enumerate(dsrcs)})
+    with _device(dev):
+        code = library().attnres_bwd_sources(dout.data_ptr(), _ptr_array(srcs), pitch, w.data_ptr(),
+                                             rstd.data_ptr(), alpha.data_ptr(), N, T, D, _ptr_array(dsrcs), dpitch,
+                                             mode, dw.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                             _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_bwd_sources", code)
     return dsrcs, dw

@@ -138,6 +138,19 @@ def test_binding_refuses_host_tensors():
         ar.attnres_fwd(src, w, 1e-6)
 
 
+def test_binding_requires_one_device():
+    """Every tensor of a call must sit on the sources' device (checked on the
+    host, so testable without a GPU: meta/host tensors stand in)."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    ar._same_device(dev, w=None)  # absent optional tensors are skipped
+    with pytest.raises(ValueError, match="w is on cpu"):
+        ar._same_device(dev, w=torch.zeros(8))
+    with pytest.raises(ValueError, match=r"srcs\[1\]"):
+        ar._same_device(torch.device("cpu"), **{"srcs[0]": torch.zeros(1), "srcs[1]": torch.zeros(1, device="meta")})
+
+
 def _arr(vals):
     a = (ctypes.c_void_p * len(vals))()
     for i, v in enumerate(vals):
