@@ -154,8 +154,8 @@ attnres_status attnres_fwd_sources(const uint16_t* const* srcs, int64_t src_pitc
  * Fireworks: Fast RL at frontier scale").  It runs the same one-workgroup-
  * per-token kernel as attnres_fwd, so every output is bitwise the one the
  * training forward gives for that token in any batch: rollout and training
- * see the same numbers.  A single token costs about 7 us of kernel time on
- * MI355X (D = 7168, N = 9).
+ * see the same numbers.  A single token costs 5-7 us of kernel time on
+ * MI355X (D = 7168, N = 9; sources in cache or in HBM).
  *   srcs, src_pitch, w, eps, N, T, D, out   as attnres_fwd_sources.
  *   rstd, alpha   [T][N] fp32 saved state as attnres_fwd, or both NULL: then
  *                 only out is written.  Exactly one of them NULL is
