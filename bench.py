@@ -356,7 +356,7 @@ def main():
                     help="only the decoding-size forward calls (T = 1..1024), for latency profiles")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the operator is token-local and this build has no "
+        print("bench.py runs on exactly one GPU: the operator is token-local and the library has no "
               "multi-GPU path (--gpus must be 1)", file=sys.stderr, flush=True)
         sys.exit(2)
 
