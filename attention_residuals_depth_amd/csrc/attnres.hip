@@ -580,20 +580,42 @@ struct BwdCtx {
 // g.x_i and w.x_i, workgroup reduction, softmax backward, dsources stores and
 // this workgroup's running dw (LDS).  Issues no loads of the row group.
 // MODE (kGradAccumulate | kGradF32): with accumulation the old gradients are
-// loaded once the partial sums are formed (in flight during the reduction but
-// not live during the first pass) and the new gradient is added to them in
-// fp32 before the single rounding (bf16) or store (fp32).  Old fp32
-// gradients take twice the registers: the first half of the sources is
-// loaded then, the rest when the stores reach it.
+// requested once the partial sums are formed (in flight during the reduction
+// but not live during the first pass; below, how many and when) and the new
+// gradient is added to them in fp32 before the single rounding (bf16) or
+// store (fp32).
 template <int N, int VPT, int MODE>
 __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], float sa, float sr, int64_t t,
                                           int& buf, const BwdCtx& c, const Slice<VPT>& sl) {
   constexpr bool ACC = (MODE & kGradAccumulate) != 0;
   constexpr bool F32 = (MODE & kGradF32) != 0;
-  constexpr int OW = F32 ? 2 : 1;            // 16-byte vectors of old gradient per slice vector
-  constexpr int H = F32 ? (N + 1) / 2 : N;   // sources whose old gradients are loaded early
-  constexpr int KP = F32 ? 1 : VPT;          // slice vectors loaded early
-  constexpr int R = N - H;                   // sources loaded when the stores reach them (fp32)
+  constexpr int OW = F32 ? 2 : 1;  // 16-byte vectors of old gradient per slice vector
+  // Accumulation with one vector per thread: the old gradients of the first H
+  // sources are requested before the reduction (all of them for bf16, half
+  // for fp32, whose old rows take twice the registers) and the other R when
+  // the stores reach source H.
+  constexpr int H = F32 ? (N + 1) / 2 : N;
+  constexpr int R = N - H;
+  // Accumulation with two vectors per thread (D > 8192): two vectors of old
+  // gradients next to two of sources exceed the 128 VGPRs of a 1024-thread
+  // workgroup, so the old gradients roll through a window of W items instead:
+  // W are requested before the reduction, and each one the stores consume is
+  // replaced by the request for the item W later (item j = k*N + i: slice
+  // vector k of source i).  Measured on MI355X at D = 12288 / 16384: bf16
+  // 3.55 -> 5.15 TB/s, fp32 4.5 -> 4.6 TB/s; with one vector per thread the
+  // loads above (all early for bf16, half early for fp32) stay faster.
+  constexpr bool ROLL = ACC && VPT > 1;
+  constexpr int W = F32 ? 3 : 4;
+  // request the old gradient of item j into dst
+  auto load_item = [&](uint4 (&dst)[OW], int j) {
+    const __amdgpu_buffer_rsrc_t r = grad_row<F32>(c.dsrc, j % N, t, c.D);
+    if constexpr (F32) {
+      dst[0] = bload(r, 2u * sl.off[j / N]);
+      dst[OW - 1] = bload(r, 2u * sl.off[j / N] + 16u);
+    } else {
+      dst[0] = bload<kAuxStreamLoad>(r, sl.off[j / N]);
+    }
+  };
 
   // partial g.x_i (first N) and w.x_i (last N)
   float part[2 * N];
@@ -612,11 +634,17 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
       for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
     }
   }
-  uint4 old[ACC ? KP : 1][ACC ? H : 1][OW];
+  static_assert(ROLL || !ACC || VPT == 1, "two vectors per thread accumulate through the window");
+  uint4 old[(ACC && !ROLL) ? H : 1][OW];
+  uint4 win[ROLL ? W : 1][OW];
   if constexpr (ACC) {
     sched_fence();
+    if constexpr (ROLL) {
 #pragma unroll
-    for (int k = 0; k < KP; ++k) load_grads<F32, 0, H>(old[k], c.dsrc, t, c.D, sl, k);
+      for (int j = 0; j < W && j < VPT * N; ++j) load_item(win[j], j);
+    } else {
+      load_grads<F32, 0, H>(old, c.dsrc, t, c.D, sl, 0);
+    }
     sched_fence();
   }
   block_sums<2 * N>(part, c.red + buf * 2 * N);
@@ -656,17 +684,10 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
     unpack8(g[k], gf);
     load8(c.wl, sl.slot[k], wr);
     load8(c.dwl, sl.slot[k], dwr);
-    if constexpr (ACC && F32) {
-      if (k > 0) {  // later vectors of an fp32 accumulation: their first half now
-        sched_fence();
-        load_grads<true, 0, H>(old[0], c.dsrc, t, c.D, sl, k);
-        sched_fence();
-      }
-    }
-    uint4 rest[(ACC && F32 && R > 0) ? R : 1][OW];
+    uint4 rest[(ACC && F32 && R > 0 && !ROLL) ? R : 1][OW];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if constexpr (ACC && F32 && R > 0) {
+      if constexpr (ACC && F32 && R > 0 && !ROLL) {
         if (i == H) {
           sched_fence();
           load_grads<true, H, N>(rest, c.dsrc, t, c.D, sl, k);
@@ -682,15 +703,34 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
       }
       if constexpr (ACC) {
         float o[8];
-        if constexpr (F32) {
-          const uint4& a = i < H ? old[0][i < H ? i : 0][0] : rest[i < H ? 0 : i - H][0];
-          const uint4& b = i < H ? old[0][i < H ? i : 0][1] : rest[i < H ? 0 : i - H][1];
+        if constexpr (ROLL) {
+          const int j = k * N + i;
+          if constexpr (F32) {
+            const uint4& a = win[j % W][0];
+            const uint4& b = win[j % W][OW - 1];
+            o[0] = __builtin_bit_cast(float, a.x); o[1] = __builtin_bit_cast(float, a.y);
+            o[2] = __builtin_bit_cast(float, a.z); o[3] = __builtin_bit_cast(float, a.w);
+            o[4] = __builtin_bit_cast(float, b.x); o[5] = __builtin_bit_cast(float, b.y);
+            o[6] = __builtin_bit_cast(float, b.z); o[7] = __builtin_bit_cast(float, b.w);
+          } else {
+            unpack8(win[j % W][0], o);
+          }
+          if (j + W < VPT * N) {
+            // fenced, or the scheduler hoists every later request to the top
+            // and the window is gone
+            sched_fence();
+            load_item(win[j % W], j + W);
+            sched_fence();
+          }
+        } else if constexpr (F32) {
+          const uint4& a = i < H ? old[i < H ? i : 0][0] : rest[i < H ? 0 : i - H][0];
+          const uint4& b = i < H ? old[i < H ? i : 0][1] : rest[i < H ? 0 : i - H][1];
           o[0] = __builtin_bit_cast(float, a.x); o[1] = __builtin_bit_cast(float, a.y);
           o[2] = __builtin_bit_cast(float, a.z); o[3] = __builtin_bit_cast(float, a.w);
           o[4] = __builtin_bit_cast(float, b.x); o[5] = __builtin_bit_cast(float, b.y);
           o[6] = __builtin_bit_cast(float, b.z); o[7] = __builtin_bit_cast(float, b.w);
         } else {
-          unpack8(old[k][i][0], o);
+          unpack8(old[i][0], o);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[e] = o[e] + d[e];

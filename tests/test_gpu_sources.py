@@ -64,7 +64,10 @@ def test_repeated_source_pointer():
     assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(a1), _bits(a2))
 
 
-@pytest.mark.parametrize("N,T,D", [(9, 512, 7168), (4, 300, 4104), (6, 33, 12288), (1, 20, 7168)],
+# D > 8192 (two vectors per thread) accumulates through a window of old-gradient
+# registers: (2, 45, 8200) has no more items than the window, (9, 70, 16384) has 18
+@pytest.mark.parametrize("N,T,D", [(9, 512, 7168), (4, 300, 4104), (6, 33, 12288), (1, 20, 7168), (9, 70, 16384),
+                                   (2, 45, 8200)],
                          ids=lambda v: str(v))
 def test_accumulate_against_oracle(N, T, D):
     wl = synth.Workload(f"acc_N{N}_T{T}_D{D}", T=T, N=N, D=D)
@@ -78,7 +81,12 @@ def test_accumulate_against_oracle(N, T, D):
     dout = to_dev_bf16(dout_h)
     out, rstd, alpha = ar.attnres_fwd_sources(src, w, wl.eps)
     dsrcs, dw = ar.attnres_bwd_sources(dout, src, w, rstd, alpha, dsrcs=dsrcs, accumulate=True)
+    g32, _ = ar.attnres_bwd_sources(dout, src, w, rstd, alpha, grad_dtype=torch.float32)
     torch.cuda.synchronize()
+    # bitwise: the accumulated bf16 gradient is the fp32 sum of the prior and
+    # the fp32 increment, rounded once to nearest even
+    for i in range(N):
+        assert torch.equal(_bits(dsrcs[i]), _bits((to_dev_bf16(prior[i]).float() + g32[i]).to(torch.bfloat16))), i
     o_dsrc, o_dw = oracle.bwd(src_h, w_h, wl.eps, dout_h)
     expect = oracle.bf16_to_f64(prior) + o_dsrc
     got = np.stack([bf16_dev_to_f64(d) for d in dsrcs])
@@ -171,7 +179,8 @@ def test_interleaved_partial_sum_update_in_place():
     assert torch.equal(_bits(r1), _bits(r2)) and torch.equal(_bits(a1), _bits(a2))
 
 
-@pytest.mark.parametrize("N,T,D", [(9, 300, 7168), (4, 65, 1000), (3, 33, 12288), (1, 9, 7168)],
+@pytest.mark.parametrize("N,T,D", [(9, 300, 7168), (4, 65, 1000), (3, 33, 12288), (1, 9, 7168), (9, 40, 16384),
+                                   (2, 21, 8200)],
                          ids=lambda v: str(v))
 def test_fp32_gradients(N, T, D):
     """fp32 gradients: written (no bf16 rounding: the oracle's dx to fp32
