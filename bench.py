@@ -193,7 +193,8 @@ def sweep(ar, torch, dev, reps=20):
     random bf16 of the workload's scales (values do not affect timing).  Each
     line gives the stacked [N][T][D] calls and, as "interleaved", the same
     sources side by side per token ([T][N][D] cache, gradients likewise)
-    through the per-source calls."""
+    through the per-source calls, and the peak allocated memory of the
+    stacked case (sources, dout, w, outputs, saved state, dw, workspace)."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     D = 7168
     cases = [(9, T) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
@@ -205,10 +206,15 @@ def sweep(ar, torch, dev, reps=20):
         src = (torch.randn((N, T, D), device=dev, generator=g) * scale).to(torch.bfloat16)
         dout = torch.randn((T, D), device=dev, generator=g).to(torch.bfloat16)
         w = torch.randn(D, device=dev, generator=g) / D ** 0.5
+        # peak allocated memory of the operator's own tensors (inputs, outputs,
+        # workspace): from here on only they and the flush buffer are allocated
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
         bufs = alloc_buffers(ar, torch, N, T, D, dev)
         out, rstd, alpha, dsrc, dw, ws = bufs
         f, b = _fwd_bwd_ms(torch, flush, lambda: ar.attnres_fwd(src, w, 1e-6, out=out, rstd=rstd, alpha=alpha),
                            lambda: ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws), reps)
+        peak_gib = (torch.cuda.max_memory_allocated() - flush.numel()) / 2**30
         del dsrc
         cache = src.permute(1, 0, 2).contiguous()  # [T][N][D]
         del src
@@ -226,6 +232,7 @@ def sweep(ar, torch, dev, reps=20):
                 "fwdbwd_tokens_per_s": T / ((f + b) * 1e-3),
                 "fwdbwd_GBps": (fb + bb + fe + be) / (f + b) / 1e6,
                 "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (f + b) / 1e6 / HBM_PEAK_GBPS,
+                "peak_alloc_GiB": peak_gib,
                 "interleaved": {"fwd_ms": fi, "bwd_ms": bi, "fwd_GBps": (fb + fe) / fi / 1e6,
                                 "bwd_GBps": (bb + be) / bi / 1e6, "fwdbwd_tokens_per_s": T / ((fi + bi) * 1e-3),
                                 "fwdbwd_frac_of_8TBps": (fb + bb + fe + be) / (fi + bi) / 1e6 / HBM_PEAK_GBPS}}
