@@ -13,11 +13,13 @@ storage, fp32 arithmetic).  Prints one JSON line (rank 0, N = 1 GPU):
 
 Flags: --gpus (1 only), --steps, --warmup, --sweep (extra per-T / per-N lines
 with fwd and bwd timed separately and caches flushed between reps),
---no-cpu-baseline.
+--no-cpu-baseline, --default-events (time with default HIP events instead of
+timing-only ones), --decode (only the decoding-size calls, for profiles).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import re
@@ -134,27 +136,88 @@ def copy_probe(torch, dev, nbytes=2 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def timed_steps(ar, torch, src, w, dout, eps, bufs, K):
-    """K steps (fwd then bwd) on the current stream.  One event sits between
-    every two calls (2K + 1 in all): the event after a step's backward is the
-    start of the next forward, so the split into fwd and bwd costs no extra
-    marker per step (each event record is a few microseconds of stream time)."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's libamdhip64, which
+    the library resolves to as well), opened by path so that no second copy
+    is loaded."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if os.path.basename(path).startswith("libamdhip64.so"):
+            return ctypes.CDLL(path)
+    raise RuntimeError("the HIP runtime is not loaded in this process")
+
+
+class TimingEvents:
+    """HIP events recorded on a given stream and used only for timestamps.
+    Created with hipEventDisableSystemFence: recording one then performs no
+    system-scope fence, i.e. no L2 writeback and invalidation between the
+    calls being timed (HIP documents the flag for timing-only events); the
+    elapsed times are read after a full device synchronisation.  Falls back
+    to default events if the runtime refuses the flag (`kind` says which)."""
+
+    def __init__(self, n: int, fenceless: bool = True):
+        self.hip = _hip_runtime()
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.kind = "hipEventDisableSystemFence" if fenceless else "default"
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE if fenceless else 0)
+            if rc != 0 and fenceless and not self.ev:
+                fenceless, self.kind = False, "default (hipEventDisableSystemFence refused)"
+                rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def record(self, i: int, stream: int):
+        rc = self.hip.hipEventRecord(self.ev[i], ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, i: int, j: int) -> float:
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def timed_steps(ar, torch, src, w, dout, eps, bufs, K, fenceless=True):
+    """K steps (fwd then bwd) on the current stream.  One timing event sits
+    between every two calls (2K + 1 in all): the event after a step's backward
+    is the start of the next forward, so the split into fwd and bwd costs no
+    extra marker per step."""
     out, rstd, alpha, dsrc, dw, ws = bufs
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = TimingEvents(2 * K + 1, fenceless)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record()
+    ev.record(0, stream)
     for k in range(K):
         ar.attnres_fwd(src, w, eps, out=out, rstd=rstd, alpha=alpha)
-        ev[2 * k + 1].record()
+        ev.record(2 * k + 1, stream)
         ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws)
-        ev[2 * k + 2].record()
+        ev.record(2 * k + 2, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = ev[0].elapsed_time(ev[2 * K])
-    fwd_ms = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(K)) / K
-    bwd_ms = sum(ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(K)) / K
-    return total_ms, wall, fwd_ms, bwd_ms
+    total_ms = ev.ms(0, 2 * K)
+    fwd_ms = sum(ev.ms(2 * k, 2 * k + 1) for k in range(K)) / K
+    bwd_ms = sum(ev.ms(2 * k + 1, 2 * k + 2) for k in range(K)) / K
+    kind = ev.kind
+    ev.close()
+    return total_ms, wall, fwd_ms, bwd_ms, kind
 
 
 def alloc_buffers(ar, torch, N, T, D, dev):
@@ -359,6 +422,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--default-events", action="store_true",
+                    help="time with default HIP events (a system-scope fence at every marker) instead of "
+                         "timing-only events, for comparison")
     ap.add_argument("--decode", action="store_true",
                     help="only the decoding-size forward calls (T = 1..1024), for latency profiles")
     args = ap.parse_args()
@@ -384,8 +450,10 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     bufs = alloc_buffers(ar, torch, N, T, D, dev)
 
-    timed_steps(ar, torch, src, w, dout, wl.eps, bufs, max(args.warmup, 1))
-    total_ms, wall, fwd_ms, bwd_ms = timed_steps(ar, torch, src, w, dout, wl.eps, bufs, args.steps)
+    fenceless = not args.default_events
+    timed_steps(ar, torch, src, w, dout, wl.eps, bufs, max(args.warmup, 1), fenceless)
+    total_ms, wall, fwd_ms, bwd_ms, ev_kind = timed_steps(ar, torch, src, w, dout, wl.eps, bufs, args.steps,
+                                                          fenceless)
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
 
     ms_step = total_ms / args.steps
@@ -417,6 +485,7 @@ def main():
         "bwd_ms": bwd_ms,
         "fwd_GBps": fwd_gbps,
         "wall_s_timed": wall,
+        "timing_events": ev_kind,
         "peak_alloc_GiB": peak_gib,
         "copy_probe_GBps": copy_gbps,
         "roofline": {
