@@ -233,20 +233,22 @@ def alloc_buffers(ar, torch, N, T, D, dev):
 def _fwd_bwd_ms(torch, flush, fwd, bwd, reps):
     """Median event times of fwd and bwd, caches flushed before each."""
     f_ms, b_ms = [], []
+    stream = torch.cuda.current_stream().cuda_stream
+    e = TimingEvents(4)
     for r in range(reps + 3):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         flush.zero_()
-        e[0].record()
+        e.record(0, stream)
         fwd()
-        e[1].record()
+        e.record(1, stream)
         flush.zero_()
-        e[2].record()
+        e.record(2, stream)
         bwd()
-        e[3].record()
+        e.record(3, stream)
         torch.cuda.synchronize()
         if r >= 3:
-            f_ms.append(e[0].elapsed_time(e[1]))
-            b_ms.append(e[2].elapsed_time(e[3]))
+            f_ms.append(e.ms(0, 1))
+            b_ms.append(e.ms(2, 3))
+    e.close()
     return sorted(f_ms)[len(f_ms) // 2], sorted(b_ms)[len(b_ms) // 2]
 
 
@@ -373,15 +375,17 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
 def _median_ms(torch, flush, fn, reps):
     """Median event time of fn over reps calls, caches flushed before each."""
     ms = []
+    stream = torch.cuda.current_stream().cuda_stream
+    e = TimingEvents(2)
     for r in range(reps + 3):
         flush.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e.record(0, stream)
         fn()
-        e1.record()
+        e.record(1, stream)
         torch.cuda.synchronize()
         if r >= 3:
-            ms.append(e0.elapsed_time(e1))
+            ms.append(e.ms(0, 1))
+    e.close()
     return sorted(ms)[len(ms) // 2]
 
 
@@ -401,13 +405,15 @@ def sweep_decode(ar, torch, dev, flush, N=9, D=7168):
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e = TimingEvents(2)
+        stream = torch.cuda.current_stream().cuda_stream
+        e.record(0, stream)
         for _ in range(200):
             fn()
-        e1.record()
+        e.record(1, stream)
         torch.cuda.synchronize()
-        warm_us = e0.elapsed_time(e1) / 200 * 1e3
+        warm_us = e.ms(0, 1) / 200 * 1e3
+        e.close()
         print(json.dumps({"sweep": True, "call": "fwd_decode", "N": N, "T": T, "D": D, "cold_us": cold_us,
                           "back_to_back_us": warm_us}), flush=True)
 
