@@ -13,7 +13,8 @@ import attention_residuals_depth_amd as ar
 import oracle
 import synth
 
-# Tolerances.  out, alpha, dsources and dw are fixed by the benchmark spec;
+# Tolerances.  out, alpha, dsources and dw: the operator's acceptance bounds
+# (relative L2 5e-3 forward and 1e-2 gradients, 1e-5 absolute on alpha);
 # rstd's is derived: an fp32 sum of D <= 16384 exact bf16 squares carries a
 # relative error below ~(log2 D + 8) * 2^-24 ~ 1.3e-6, and the square root and
 # reciprocal add < 1 ulp each, so 1e-5 relative leaves a wide margin.
