@@ -489,7 +489,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 
 // One workgroup per token: workgroup b handles token t0 + b.  The hardware
 // dispatcher starts the next token as soon as a workgroup retires, two
-// workgroups share a CU (114 VGPRs: four waves per SIMD), and the tokens in
+// workgroups share a CU (113-114 VGPRs: four waves per SIMD), and the tokens in
 // flight at any moment are neighbours, so the rows the chip reads are close
 // together in every source.  This beat a persistent kernel with a two-token
 // software pipeline per workgroup at every T on MI355X (T = 32768, N = 9:
