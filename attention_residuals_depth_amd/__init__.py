@@ -203,6 +203,8 @@ def _sources(srcs, name):
     srcs = list(srcs)
     if not 1 <= len(srcs) <= MAX_SOURCES:
         raise ValueError(f"{name} must hold 1..{MAX_SOURCES} tensors")
+    if not all(isinstance(t, torch.Tensor) for t in srcs):
+        raise TypeError(f"{name} must hold torch.Tensor objects")
     if srcs[0].dim() != 2:
         raise ValueError(f"{name}[i] must be [T][D]")
     T, D = srcs[0].shape
