@@ -10,6 +10,8 @@ storage, fp32 arithmetic).  Prints one JSON line (rank 0, N = 1 GPU):
   roofline      the dominant call (attnres_bwd) against the 8 TB/s HBM peak,
                 timed with HIP events on the stream the kernels run on
   cpu_baseline  the fp64 oracle on the host cores, same workload
+  parity        the timed run's outputs against that oracle run (errors and
+                whether they are within the parity bars)
 
 Flags: --gpus (1 only), --steps, --warmup, --sweep (extra per-T / per-N lines
 with fwd and bwd timed separately and caches flushed between reps),
@@ -107,15 +109,42 @@ def cpu_baseline(wl, min_seconds: float = 10.0):
     passes = 0
     t0 = time.perf_counter()
     while True:
-        oracle.fwd(src, w, wl.eps)
-        oracle.bwd(src, w, wl.eps, dout)
+        out, rstd, alpha = oracle.fwd(src, w, wl.eps)
+        dsrc, dw = oracle.bwd(src, w, wl.eps, dout)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= 1000:
             break
-    return {"value": passes * wl.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} passes of fwd+bwd over all {wl.T} tokens (N={wl.N}, D={wl.D}) in fp64, "
-                      f"{dt:.1f} s"}
+    rec = {"value": passes * wl.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{passes} passes of fwd+bwd over all {wl.T} tokens (N={wl.N}, D={wl.D}) in fp64, "
+                     f"{dt:.1f} s"}
+    return rec, {"out": out, "rstd": rstd, "alpha": alpha, "dsrc": dsrc, "dw": dw}
+
+
+# Parity bars: relative L2 for out (5e-3), dsources and dw (1e-2), absolute for
+# alpha (1e-5); rstd relative 1e-5 (an fp32 sum of D exact bf16 squares is
+# good to ~1e-6 relative).
+PARITY_BARS = {"out_rel_l2": 5e-3, "alpha_max_abs": 1e-5, "rstd_max_rel": 1e-5, "dsrc_rel_l2": 1e-2,
+               "dw_rel_l2": 1e-2}
+
+
+def parity_report(torch, ref, out, rstd, alpha, dsrc, dw):
+    """Errors of the timed run's last outputs (every timed step computes the
+    same batch) against the fp64 oracle's outputs for the same inputs."""
+    import numpy as np
+
+    def rel(a, b):
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    e = {
+        "out_rel_l2": rel(out.float().cpu().numpy().astype(np.float64), ref["out"]),
+        "alpha_max_abs": float(np.abs(alpha.cpu().numpy().astype(np.float64) - ref["alpha"]).max()),
+        "rstd_max_rel": float((np.abs(rstd.cpu().numpy().astype(np.float64) - ref["rstd"]) / ref["rstd"]).max()),
+        "dsrc_rel_l2": rel(dsrc.float().cpu().numpy().astype(np.float64), ref["dsrc"]),
+        "dw_rel_l2": rel(dw.cpu().numpy().astype(np.float64), ref["dw"]),
+    }
+    e["within_bars"] = all(e[k] <= v for k, v in PARITY_BARS.items())
+    return e
 
 
 def copy_probe(torch, dev, nbytes=2 << 30, reps=10):
@@ -505,7 +534,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"], ref = cpu_baseline(wl)
+        out, rstd, alpha, dsrc, dw, _ = bufs
+        result["parity"] = parity_report(torch, ref, out, rstd, alpha, dsrc, dw)
+        del ref
     print(json.dumps(result), flush=True)
     if args.sweep:
         del src, dout, bufs

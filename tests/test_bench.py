@@ -85,7 +85,28 @@ def test_more_than_one_gpu_is_refused():
 
 def test_cpu_baseline_record():
     wl = synth.Workload("bench_tiny", T=8, N=3, D=64)
-    rec = bench.cpu_baseline(wl, min_seconds=0.05)
+    rec, ref = bench.cpu_baseline(wl, min_seconds=0.05)
+    assert set(ref) == {"out", "rstd", "alpha", "dsrc", "dw"} and ref["dsrc"].shape == (3, 8, 64)
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert "fp64" in rec["sample"] and "8 tokens" in rec["sample"]
+
+
+def test_parity_report_against_the_oracle_outputs():
+    """The bench's parity record: the oracle's own values rounded to the device
+    dtypes give rounding-level errors within the bars; a planted 5% error in dw
+    is reported as such and fails them."""
+    import numpy as np
+    import torch
+
+    wl = synth.Workload("bench_tiny", T=8, N=3, D=64)
+    _, ref = bench.cpu_baseline(wl, min_seconds=0.0)
+    as_dev = dict(out=torch.from_numpy(ref["out"]).to(torch.bfloat16), rstd=torch.from_numpy(ref["rstd"]).float(),
+                  alpha=torch.from_numpy(ref["alpha"]).float(), dsrc=torch.from_numpy(ref["dsrc"]).to(torch.bfloat16),
+                  dw=torch.from_numpy(ref["dw"]).float())
+    e = bench.parity_report(torch, ref, **as_dev)
+    assert e["within_bars"] and e["out_rel_l2"] < 4e-3 and e["dw_rel_l2"] < 1e-6
+    bad = dict(as_dev, dw=as_dev["dw"] * 1.05)
+    e = bench.parity_report(torch, ref, **bad)
+    assert not e["within_bars"] and abs(e["dw_rel_l2"] - 0.05) < 1e-4
+    assert np.isfinite(e["alpha_max_abs"])
