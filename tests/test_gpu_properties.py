@@ -134,6 +134,47 @@ def test_stream_argument_is_honoured():
         assert torch.equal(_bits(x), _bits(y))
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two host threads, each with its own stream and workload, call fwd + bwd
+    three times at once (the library is stateless apart from its
+    mutex-guarded occupancy cache, and its kernels do not wait on each
+    other): every result equals the same workload run alone, bit for bit."""
+    import threading
+
+    cases = [synth.Workload("conc_a", T=700, N=9, D=7168, seed=31), synth.Workload("conc_b", T=333, N=5, D=4096, seed=32)]
+    inputs = [_inputs(wl) for wl in cases]
+    refs = [run_gpu(src, w, wl.eps, dout) for wl, (src, w, dout) in zip(cases, inputs)]
+    torch.cuda.synchronize()
+    results = [[None] * 3 for _ in cases]
+    errors = []
+
+    def worker(j):
+        try:
+            wl, (src, w, dout) = cases[j], inputs[j]
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for k in range(3):
+                    out, rstd, alpha = ar.attnres_fwd(src, w, wl.eps)
+                    dsrc, dw = ar.attnres_bwd(dout, src, w, rstd, alpha)
+                    results[j][k] = (out, rstd, alpha, dsrc, dw)
+            s.synchronize()
+        except Exception as e:  # surfaced in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for j, ref in enumerate(refs):
+        for k in range(3):
+            for name, x, y in zip(("out", "rstd", "alpha", "dsrc", "dw"), ref, results[j][k]):
+                assert torch.equal(_bits(x), _bits(y)), (cases[j].name, k, name)
+
+
 def test_graph_capture_replays_match_eager():
     """fwd, bwd and the decoding forward captured in one HIP graph (the library
     enqueues no memsets and allocates nothing): every replay, with new input
