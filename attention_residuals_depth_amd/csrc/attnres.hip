@@ -791,7 +791,8 @@ __device__ __forceinline__ void publish_dw(float* __restrict__ ws, int64_t ch, i
 // scheduling fences keep each prefetch where it is issued, so the in-order
 // wait counts only ever wait for the oldest row group.  When accumulating
 // (no prefetch) the old gradients are loaded during the reduction.  Dynamic LDS
-// holds w and the workgroup's running dw, in the thread's private slots.
+// holds w and the workgroup's running dw, in the thread's private slots, and
+// for written fp32 gradients a 2 KiB output stage per wave.
 template <int N, int VPT, bool PIPE, int MODE>
 __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ dout, SrcRows src,
                                                    const float* __restrict__ w, const float* __restrict__ rstd,
