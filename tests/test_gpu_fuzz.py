@@ -2,7 +2,8 @@
 
 Each case draws N, T, D, eps, the source scales, a layout (stacked, separate
 buffers, interleaved by token, padded rows) and a call mix (overwriting or
-accumulating backward, decoding forward, fused partial-sum update), runs it
+accumulating backward with bf16 or fp32 gradients, decoding forward, fused
+partial-sum update), runs it
 on the GPU and compares every output with the oracle at the operator's
 tolerances.  The cases are fixed by their seeds, so a failure names a
 reproducible configuration."""
@@ -42,19 +43,22 @@ def _place(src: torch.Tensor, layout: str, rng):
     return [buf[i, :, :D] for i in range(N)]
 
 
-def _zeros_like_layout(views):
+def _zeros_like_layout(views, dtype=None):
+    """Zero gradients in the layout of the source views (same row pitch), in
+    the sources' dtype or the given one."""
     out = []
     for v in views:
+        dt = v.dtype if dtype is None else dtype
         if v.is_contiguous():
-            out.append(torch.zeros_like(v))
+            out.append(torch.zeros(v.shape, dtype=dt, device=v.device))
         else:
             T, D = v.shape
-            base = torch.zeros((T, v.stride(0)), dtype=v.dtype, device=v.device)
+            base = torch.zeros((T, v.stride(0)), dtype=dt, device=v.device)
             out.append(base[:, :D])
     return out
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_configuration(seed):
     rng = np.random.default_rng(1000 + seed)
     N = int(rng.integers(1, 10))
@@ -66,7 +70,7 @@ def test_random_configuration(seed):
     w_std = float(rng.choice([0.0, 0.5])) or None  # None: 1/sqrt(D); 0.5: the peaked workload's
     wl = synth.Workload(f"fuzz{seed}", T=T, N=N, D=D, eps=eps, seed=seed, kind=kind, w_std=w_std, tiny_scales=scales)
     layout = str(rng.choice(["stacked", "separate", "interleaved", "padded"]))
-    mode = str(rng.choice(["plain", "accumulate", "decode", "update"]))
+    mode = str(rng.choice(["plain", "accumulate", "decode", "update", "f32", "f32acc"]))
     src_h, w_h, dout_h = wl.sources(), wl.w(), wl.dout()
     print(f"[fuzz] seed={seed} N={N} T={T} D={D} eps={eps} kind={kind} layout={layout} mode={mode}", flush=True)
     src = to_dev_bf16(src_h)
@@ -97,6 +101,24 @@ def test_random_configuration(seed):
     assert float(np.max(np.abs(alpha.cpu().double().numpy() - o_alpha))) <= TOL_ALPHA_ABS
     assert float(np.max(np.abs(rstd.cpu().double().numpy() / o_rstd - 1))) <= TOL_RSTD_REL
 
+    if mode in ("f32", "f32acc"):
+        # fp32 source gradients, written or accumulated onto seeded fp32 priors
+        o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
+        views = _place(src, "separate" if layout == "stacked" else layout, rng)
+        grads = _zeros_like_layout(views, torch.float32)
+        prior = None
+        if mode == "f32acc":
+            gen = torch.Generator(device=DEV).manual_seed(seed + 55)
+            prior = [torch.randn((T, D), device=DEV, generator=gen) * 0.1 for _ in range(N)]
+            for i in range(N):
+                grads[i].copy_(prior[i])
+        grads, dw = ar.attnres_bwd_sources(dout, views, w, rstd, alpha, dsrcs=grads, accumulate=(mode == "f32acc"))
+        torch.cuda.synchronize()
+        got = np.stack([g.double().cpu().numpy() for g in grads])
+        expect = o_dsrc if prior is None else np.stack([p.double().cpu().numpy() for p in prior]) + o_dsrc
+        assert rel_l2(got, expect) <= 1e-5  # fp32 gradients: no bf16 rounding
+        if np.linalg.norm(o_dw) > 0:
+            assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
     if mode in ("plain", "accumulate"):
         o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
         if layout == "stacked":
