@@ -379,6 +379,34 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     return dsrcs, dw
 
 
-__all__ = ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
+class _AttnResFunction(torch.autograd.Function):
+    """Autograd node of one operator call on N separate sources: the forward
+    runs attnres_fwd_sources and saves rstd and alpha, the backward runs
+    attnres_bwd_sources and returns the gradient of w (fp32) and of every
+    source (bf16; autograd adds it to whatever the source's other uses give)."""
+
+    @staticmethod
+    def forward(ctx, w, eps, *srcs):
+        out, rstd, alpha = attnres_fwd_sources(list(srcs), w, eps)
+        ctx.save_for_backward(w, rstd, alpha, *srcs)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        w, rstd, alpha, *srcs = ctx.saved_tensors
+        dout = dout.to(torch.bfloat16).contiguous()  # the backward takes dout in bf16
+        dsrcs, dw = attnres_bwd_sources(dout, srcs, w, rstd, alpha)
+        return (dw, None, *dsrcs)
+
+
+def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
+    """Differentiable call for training code: out [T][D] bf16 from the N
+    sources (bf16 [T][D] tensors or views with one common row pitch, e.g.
+    slices of a [T][N][D] cache) and w [D] fp32.  Gradients flow to every
+    source and to w through the library's backward."""
+    return _AttnResFunction.apply(w, float(eps), *_sources(srcs, "srcs")[0])
+
+
+__all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "GRAD_ACCUMULATE", "GRAD_F32",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]
