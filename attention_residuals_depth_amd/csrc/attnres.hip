@@ -489,13 +489,18 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 
 // One workgroup per token: workgroup b handles token t0 + b.  The hardware
 // dispatcher starts the next token as soon as a workgroup retires, two
-// workgroups share a CU (113-114 VGPRs: four waves per SIMD), and the tokens in
-// flight at any moment are neighbours, so the rows the chip reads are close
-// together in every source.  This beat a persistent kernel with a two-token
-// software pipeline per workgroup at every T on MI355X (T = 32768, N = 9:
-// 5.79 vs 5.39 TB/s; T = 1: 6.9 vs 7.8 us kernel time).  The w slice is
-// requested first and the row group right behind it, so both latencies
-// overlap; w then goes to the thread's LDS slots while the rows arrive.
+// workgroups share a CU, and the tokens in flight at any moment are
+// neighbours, so the rows the chip reads are close together in every source.
+// This beat a persistent kernel with a two-token software pipeline per
+// workgroup at every T on MI355X (T = 32768, N = 9: 5.79 vs 5.39 TB/s; T = 1:
+// 6.9 vs 7.8 us kernel time).  The w slice is requested first and the row
+// group right behind it, so both latencies overlap; w then goes to the
+// thread's LDS slots while the rows arrive.
+// VPT = 4 (D <= 8192: 224 threads, 192 VGPRs at D = 7168, N = 9, two waves
+// per SIMD) or 2 (larger D: up to 1024 threads, 113-114 VGPRs).  At D = 7168
+// four vectors per thread measured 3-5% faster than two at T = 2K-8K, the same
+// at T >= 16K, and 0.4 us slower for one token (fewer waves share its work);
+// one vector per thread (896 threads) was 12-20% slower.
 //
 // UPDATE: the last source is the current block's partial sum after adding
 // the previous sub-layer's output (architecture figure of "Kimi K3
@@ -509,7 +514,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // (partial_out == src.p[N-1]) is fine: a thread rewrites only the slice it
 // has already read.
 template <int N, int VPT, bool UPDATE>
-__global__ void __launch_bounds__(1024) fwd_kernel(SrcRows src, const uint16_t* __restrict__ delta,
+__global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src, const uint16_t* __restrict__ delta,
                                                    uint16_t* partial_out, const float* __restrict__ w, float eps,
                                                    int64_t t0, int32_t D, uint16_t* __restrict__ out,
                                                    float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
@@ -930,7 +935,9 @@ struct LaunchShape {
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
-constexpr int kFwdVpt = 2;  // forward: two vectors per thread (448 threads at D = 7168)
+// forward: four vectors per thread up to D = 8192 (224 threads at D = 7168),
+// two above (at most 1024 threads)
+constexpr int kFwdVptMaxV4 = 1024;  // largest D/8 taking four vectors per thread
 
 LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
   const int V = D / 8;
@@ -947,8 +954,9 @@ LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
 // with T or with the call: every forward call gives bitwise the same
 // per-token results, and so does every backward call (with or without
 // accumulation, stacked or per source).
-// Forward: two vectors per thread, blockDim = D/16 rounded up to whole waves.
-LaunchShape fwd_shape(int32_t D) { return make_shape(D, kFwdVpt, false); }
+// Forward: four vectors per thread for D <= 8192, else two; blockDim = D/(8*VPT)
+// rounded up to whole waves.
+LaunchShape fwd_shape(int32_t D) { return make_shape(D, D / 8 <= kFwdVptMaxV4 ? 4 : 2, false); }
 
 // Backward: D <= 8192 takes one vector per thread (896 threads, 14 waves at
 // D = 7168) with a two-token prefetch; measured 1-2% faster on MI355X than
@@ -1077,21 +1085,26 @@ struct BwdArgs {
 
 // One workgroup per token.  The dispatch packet counts work-items in 32 bits,
 // so very large T (possible only for tiny D) is split over several launches.
-template <int N, bool UPDATE>
-hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, kFwdVpt, UPDATE>);
+template <int N, int VPT, bool UPDATE>
+hipError_t run_fwd_vpt(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, UPDATE>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)s.threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_kernel<N, kFwdVpt, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
+    hipLaunchKernelGGL((fwd_kernel<N, VPT, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
                        a.delta, a.partial_out, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int N, bool UPDATE>
+hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  return s.vpt == 4 ? run_fwd_vpt<N, 4, UPDATE>(s, st, a) : run_fwd_vpt<N, 2, UPDATE>(s, st, a);
 }
 
 template <int N, int VPT, bool PIPE, int MODE>
