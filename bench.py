@@ -294,6 +294,8 @@ def sweep(ar, torch, dev, reps=20):
     cases = [(9, T) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
     cases += [(N, 32768) for N in range(2, 9)]
     for N, T in cases:
+        torch.cuda.synchronize()
+        held = torch.cuda.memory_allocated()  # the flush buffer and whatever the caller still holds
         g = torch.Generator(device=dev)
         g.manual_seed(0)
         scale = torch.sqrt(1 + 12 * torch.arange(N, device=dev, dtype=torch.float32)).view(N, 1, 1)
@@ -301,14 +303,14 @@ def sweep(ar, torch, dev, reps=20):
         dout = torch.randn((T, D), device=dev, generator=g).to(torch.bfloat16)
         w = torch.randn(D, device=dev, generator=g) / D ** 0.5
         # peak allocated memory of the operator's own tensors (inputs, outputs,
-        # workspace): from here on only they and the flush buffer are allocated
+        # workspace): from here on only they are allocated beyond `held`
         torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats()
         bufs = alloc_buffers(ar, torch, N, T, D, dev)
         out, rstd, alpha, dsrc, dw, ws = bufs
         f, b = _fwd_bwd_ms(torch, flush, lambda: ar.attnres_fwd(src, w, 1e-6, out=out, rstd=rstd, alpha=alpha),
                            lambda: ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws), reps)
-        peak_gib = (torch.cuda.max_memory_allocated() - flush.numel()) / 2**30
+        peak_gib = (torch.cuda.max_memory_allocated() - held) / 2**30
         del dsrc
         cache = src.permute(1, 0, 2).contiguous()  # [T][N][D]
         del src
