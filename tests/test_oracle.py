@@ -345,6 +345,17 @@ MUTANTS = {
     "update_ties_away": ("nearbyint(ldexp(m, keep))", "round(ldexp(m, keep))"),
     "update_nine_bits": ("int keep = 8;", "int keep = 9;"),
     "update_drops_output": ("bf16_to_f64(p[k]) + bf16_to_f64(y[k])", "bf16_to_f64(p[k])"),
+    "softmax_den_skips_first": ("for (int i = 0; i < N; ++i) den += exp(z[i] - m);",
+                                "for (int i = 1; i < N; ++i) den += exp(z[i] - m);"),
+    "weighted_sum_skips_first": ("for (int i = 0; i < N; ++i) acc += alpha[i] * x[i][d];",
+                                 "for (int i = 1; i < N; ++i) acc += alpha[i] * x[i][d];"),
+    "softmax_bwd_unweighted_mean": ("for (int i = 0; i < N; ++i) s += alpha[i] * da[i];",
+                                    "for (int i = 0; i < N; ++i) s += da[i] / N;"),
+    "mean_abs_not_square": ("for (int64_t d = 0; d < D; ++d) ss += x[i][d] * x[i][d];",
+                            "for (int64_t d = 0; d < D; ++d) ss += fabs(x[i][d]);"),
+    "dw_drops_last_chunk": ("for (int64_t c = 0; c < nchunk; ++c)\n    for (int64_t d = 0; d < D; ++d) dw[d] += part",
+                            "for (int64_t c = 0; c + 1 < nchunk; ++c)\n    for (int64_t d = 0; d < D; ++d) dw[d] += part"),
+    "dout_of_token_zero": ("g[d] = bf16_to_f64(dout[t * D + d]);", "g[d] = bf16_to_f64(dout[d]);"),
 }
 
 
