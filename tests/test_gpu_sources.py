@@ -233,3 +233,47 @@ def test_fp32_gradients_interleaved():
     torch.cuda.synchronize()
     for i in range(N):
         assert torch.equal(_bits(views[i]), _bits(dense[i] + dense[i])), i
+
+
+@pytest.mark.slow
+def test_interleaved_cache_at_full_size():
+    """A [T][N][D] depth-source cache at T = 131072, N = 9, D = 7168 (16.9 GB;
+    row addresses reach past 2^32 bytes through the per-token pitch), with the
+    gradients written into a [T][N][D] gradient cache: sampled tokens of out,
+    alpha, rstd and the gradients against the oracle, and dw over all tokens."""
+    from parity import check_tokens, sample_tokens, within_tolerance
+
+    wl = synth.workload(2, N=9, T=131072)
+    T, N, D = wl.T, wl.N, wl.D
+    print(f"[parity] interleaved full size T={T} N={N} D={D}: generating", flush=True)
+    src = wl.sources()
+    dout = wl.dout()
+    w = wl.w()
+    cache = torch.empty((T, N, D), dtype=torch.bfloat16, device=DEV)
+    for i in range(N):
+        cache[:, i].copy_(to_dev_bf16(src[i]))
+    gcache = torch.empty((T, N, D), dtype=torch.bfloat16, device=DEV)
+    w_d = torch.from_numpy(w).to(DEV)
+    dout_d = to_dev_bf16(dout)
+    views = [cache[:, i] for i in range(N)]
+    print("[parity] interleaved full size: running fwd+bwd", flush=True)
+    out, rstd, alpha = ar.attnres_fwd_sources(views, w_d, wl.eps)
+    _, dw = ar.attnres_bwd_sources(dout_d, views, w_d, rstd, alpha, dsrcs=[gcache[:, i] for i in range(N)])
+    torch.cuda.synchronize()
+
+    toks = sample_tokens(T)
+    s_src = np.ascontiguousarray(src[:, toks])
+    o_out, o_rstd, o_alpha = oracle.fwd(s_src, w, wl.eps)
+    o_dsrc, _ = oracle.bwd(s_src, w, wl.eps, np.ascontiguousarray(dout[toks]))
+    tk = torch.from_numpy(toks).to(DEV)
+    gpu = dict(out=bf16_dev_to_f64(out[tk]), rstd=rstd[tk].cpu().double().numpy(),
+               alpha=alpha[tk].cpu().double().numpy(), dsrc=bf16_dev_to_f64(gcache[tk].transpose(0, 1)))
+    ref = dict(out=o_out, rstd=o_rstd, alpha=o_alpha, dsrc=o_dsrc)
+    e = check_tokens({}, wl.name, gpu, ref)
+    print("[parity] interleaved full size: oracle dw over all tokens", flush=True)
+    _, o_dw = oracle.bwd(src, w, wl.eps, dout, want_dsrc=False)
+    e["dw_rel_l2"] = rel_l2(dw.cpu().double().numpy(), o_dw)
+    print("[parity] interleaved full size: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert within_tolerance(e), e
+    del cache, gcache, out, dout_d
+    torch.cuda.empty_cache()
