@@ -240,7 +240,8 @@ def test_interleaved_cache_at_full_size():
     """A [T][N][D] depth-source cache at T = 131072, N = 9, D = 7168 (16.9 GB;
     row addresses reach past 2^32 bytes through the per-token pitch), with the
     gradients written into a [T][N][D] gradient cache: sampled tokens of out,
-    alpha, rstd and the gradients against the oracle, and dw over all tokens."""
+    alpha, rstd and the gradients against the oracle, and dw over all tokens;
+    then fp32 gradients into a [T][N][D] fp32 cache, written and accumulated."""
     from parity import check_tokens, sample_tokens, within_tolerance
 
     wl = synth.workload(2, N=9, T=131072)
@@ -275,5 +276,19 @@ def test_interleaved_cache_at_full_size():
     e["dw_rel_l2"] = rel_l2(dw.cpu().double().numpy(), o_dw)
     print("[parity] interleaved full size: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
     assert within_tolerance(e), e
-    del cache, gcache, out, dout_d
+    del gcache, out
+    torch.cuda.empty_cache()
+
+    # fp32 gradients in a [T][N][D] fp32 cache (33.8 GB): written, then accumulated onto themselves
+    g32 = torch.empty((T, N, D), dtype=torch.float32, device=DEV)
+    g32_views = [g32[:, i] for i in range(N)]
+    for acc in (False, True):
+        ar.attnres_bwd_sources(dout_d, views, w_d, rstd, alpha, dsrcs=g32_views, accumulate=acc)
+        torch.cuda.synchronize()
+        got = g32[tk].transpose(0, 1).double().cpu().numpy()
+        err = rel_l2(got, (2.0 if acc else 1.0) * o_dsrc)
+        print(f"[parity] interleaved full size, fp32 gradients {'accumulated' if acc else 'written'}: "
+              f"rel-L2 {err:.3e}", flush=True)
+        assert err <= 1e-5, err
+    del cache, g32, dout_d
     torch.cuda.empty_cache()
