@@ -285,7 +285,13 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
     empty) plus the updated partial sum bf16(partial + delta) as the last one.
     The new partial sum goes to partial_out (default: partial itself when
     in_place, else a new tensor).  Returns (out, rstd, alpha, partial_out);
-    rstd and alpha are None when save_state is False and none is passed."""
+    rstd and alpha are None when save_state is False and none is passed.
+
+    The library writes partial_out behind autograd's back, so the call bumps
+    its version counter: an autograd node that saved that tensor (or a view of
+    it) then refuses to run its backward instead of reading the updated
+    values.  A partial_out that requires grad is refused outright (an
+    in-place write into a leaf or a graph tensor)."""
     srcs = list(srcs)
     if partial.dim() != 2:
         raise ValueError("partial must be [T][D]")
@@ -305,6 +311,8 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
         else:
             raise ValueError("with strided sources pass partial_out (a row set of the same pitch)")
     _common_pitch([partial_out], "partial_out", T, D, pitch)
+    if partial_out.requires_grad:
+        raise RuntimeError("partial_out requires grad: the library cannot write it in place under autograd")
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, (T, D))
@@ -325,6 +333,7 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
                                             None if alpha is None else alpha.data_ptr(), _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd_update", code)
+    torch.autograd.graph.increment_version(partial_out)
     return out, rstd, alpha, partial_out
 
 

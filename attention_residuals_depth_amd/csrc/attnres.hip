@@ -229,6 +229,15 @@ __device__ __forceinline__ void opaque(uint4& q) {
 // in-order wait counts would make a token wait for loads issued after it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Order this wave's LDS accesses across its lanes: everything before the
+// call (release) happens before everything after it (acquire) for every lane
+// of the wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Move a wave-uniform value into a scalar register (frees a VGPR per value).
 __device__ __forceinline__ float uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
@@ -245,17 +254,30 @@ __device__ __forceinline__ float uniform(float v) {
 // backward pass live in LDS slots private to the thread (slot j + k*blockDim.x
 // holds 8 floats), so they need no barrier and leave the register file to the
 // row group.
+// When the row's D/8 vectors do not fill VPT * blockDim.x slots, whole waves
+// can own no vector k at all (D = 7168 with 256 threads x 4 vectors: waves 2
+// and 3 have no fourth vector); bit k of `live` (wave-uniform, in a scalar
+// register) says whether any lane of this wave owns a vector k inside the
+// row, so the arithmetic on a dead vector is skipped with a scalar branch.
+// Its loads are still issued (size-checked to zeros), which keeps the number
+// of outstanding loads, and so the compiler's wait counts, the same in every
+// wave.
 template <int VPT>
 struct Slice {
   uint32_t off[VPT];  // byte offset in a bf16 row
   int slot[VPT];      // private LDS slot (8 floats)
-  __device__ __forceinline__ Slice(int tid, int nthreads) {
+  uint32_t live;      // bit k: this wave owns some vector k inside the row
+  __device__ __forceinline__ Slice(int tid, int nthreads, int32_t D) {
+    const int first = __builtin_amdgcn_readfirstlane(tid) & ~(kWave - 1);  // this wave's first thread
+    live = 0;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       slot[k] = tid + k * nthreads;
       off[k] = (uint32_t)slot[k] * 16u;
+      if (first + k * nthreads < D / 8) live |= 1u << k;
     }
   }
+  __device__ __forceinline__ bool has(int k) const { return k == 0 || ((live >> k) & 1u) != 0; }
 };
 
 __device__ __forceinline__ void load8(const float4* p, int slot, float (&f)[8]) {
@@ -411,6 +433,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
   for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
+    if (!sl.has(k)) continue;  // wave-uniform: no lane of this wave owns a vector k
     float wr[8];
     load8(c.wl, sl.slot[k], wr);
 #pragma unroll
@@ -459,6 +482,7 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
   const __amdgpu_buffer_rsrc_t ro = rsrc(c.out + t * c.D, (uint32_t)c.D * 2u);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
+    if (!sl.has(k)) continue;  // a dead vector's store would be dropped anyway
     float acc[8];
     {
       float f[8];
@@ -496,8 +520,10 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // 6.9 vs 7.8 us kernel time).  The w slice is requested first and the row
 // group right behind it, so both latencies overlap; w then goes to the
 // thread's LDS slots while the rows arrive.
-// VPT = 4 (D <= 8192: 224 threads, 192 VGPRs at D = 7168, N = 9, two waves
-// per SIMD) or 2 (larger D: up to 1024 threads, 113-114 VGPRs).  At D = 7168
+// VPT = 4 (D <= 8192: 256 threads at D = 7168 -- 224 are needed for its 896
+// vectors, rounded up to four waves, of which waves 2 and 3 own only three
+// vectors and skip the fourth; 192 VGPRs at N = 9, two waves per SIMD) or 2
+// (larger D: up to 1024 threads, 113-114 VGPRs).  At D = 7168
 // four vectors per thread measured 3-5% faster than two at T = 2K-8K, the same
 // at T >= 16K, and 0.4 us slower for one token (fewer waves share its work);
 // one vector per thread (896 threads) was 12-20% slower.
@@ -530,7 +556,7 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
   c.wl = dyn_lds;
   c.red = &red[0][0];
   c.tid = threadIdx.x;
-  const Slice<VPT> sl(c.tid, blockDim.x);
+  const Slice<VPT> sl(c.tid, blockDim.x, D);
   const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
 
   uint4 wv[VPT][2];
@@ -545,6 +571,7 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
     const __amdgpu_buffer_rsrc_t rp = rsrc(partial_out + t * src.pitch, (uint32_t)D * 2u);  // the sources' layout
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
+      if (!sl.has(k)) continue;
       float a[8], b[8];
       unpack8(x[N - 1][k], a);
       unpack8(yv[k], b);
@@ -750,11 +777,16 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
         // MI355X than two half-vector stores merged in L2 (bitwise the same
         // values).  The accumulating variant keeps the plain stores: its
         // registers are full and the stage cost it 1-2%.
+        // The exchange is between lanes of one wave, so a wave barrier (with
+        // wavefront-scope fences) orders the stage's writes before the reads
+        // of other lanes' data, and the reads before the next source's writes.
         const int lane = lane_id();
         float4* st = c.stage + wave_id() * (2 * kWave);
         st[2 * lane] = make_float4(d[0], d[1], d[2], d[3]);
         st[2 * lane + 1] = make_float4(d[4], d[5], d[6], d[7]);
+        wave_sync();
         const float4 lo = st[lane], hi = st[kWave + lane];
+        wave_sync();
         const uint32_t wbase = 2u * sl.off[k] - 32u * (uint32_t)lane;  // the wave's first vector, fp32 bytes
         bstore<kAuxStreamStore>(rd, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
         bstore<kAuxStreamStore>(rd, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
@@ -816,7 +848,7 @@ __global__ void __launch_bounds__(1024) bwd_kernel(const uint16_t* __restrict__ 
   c.stage = dyn_lds + 4 * VPT * (int)blockDim.x;  // after w and dw (used only by the written fp32 gradients)
   c.red = &red[0][0];
   const int tid = threadIdx.x;
-  const Slice<VPT> sl(tid, blockDim.x);
+  const Slice<VPT> sl(tid, blockDim.x, D);
   const int64_t ch = blockIdx.x;  // host launches exactly P <= T workgroups
 
   // w first, then (with PIPE) the first token's rows right behind it, so the
@@ -935,8 +967,9 @@ struct LaunchShape {
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
-// forward: four vectors per thread up to D = 8192 (224 threads at D = 7168),
-// two above (at most 1024 threads)
+// forward: four vectors per thread up to D = 8192 (256 threads at D = 7168:
+// ceil(896 / 4) = 224 rounded up to whole waves), two above (at most 1024
+// threads)
 constexpr int kFwdVptMaxV4 = 1024;  // largest D/8 taking four vectors per thread
 
 LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
@@ -1370,3 +1403,4 @@ extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16
   return bwd_impl(dout, srcs, src_pitch, w, rstd, alpha, N, T, D, dsrcs, dsrc_pitch, grad_mode, dw, workspace,
                   workspace_bytes, stream);
 }
+

@@ -3,20 +3,30 @@
 
 One step = attnres_fwd + attnres_bwd (every kernel of the operator) over one
 batch of synthetic depth sources that are resident in HBM before timing
-starts.  Default workload: T = 4096 tokens, N = 9 sources, D = 7168 (bf16
-storage, fp32 arithmetic).  Prints one JSON line (rank 0, N = 1 GPU):
+starts.  Default workload: T = 131072 local tokens, N = 9 sources, D = 7168,
+w ~ N(0, 0.5) (peaked softmax) -- the 128K-token point where the pages quote
+peak memory -- in bf16 storage with fp32 arithmetic.  Prints one JSON line
+(N = 1 GPU):
 
   value         tokens/s over the K timed steps (whole job, one GPU)
+  flushed       per-call medians with a 512 MiB cache flush before every call
+  ceilings_GBps bandwidth the memory system gives to plain read / write /
+                copy streams and to the operator's access patterns without
+                arithmetic (libattnres_probes), measured on the same device
   roofline      the dominant call (attnres_bwd) against the 8 TB/s HBM peak,
                 timed with HIP events on the stream the kernels run on
-  cpu_baseline  the fp64 oracle on the host cores, same workload
-  parity        the timed run's outputs against that oracle run (errors and
-                whether they are within the parity bars)
+  cpu_baseline  the fp64 oracle on the host cores: fwd and bwd timed
+                separately over the whole workload, and over a fixed token
+                sample of every workload
+  parity        the timed run's outputs against that oracle pass: out, alpha
+                and rstd on every token, dsources on sampled tokens, dw over
+                the whole batch
 
-Flags: --gpus (1 only), --steps, --warmup, --sweep (extra per-T / per-N lines
-with fwd and bwd timed separately and caches flushed between reps),
---no-cpu-baseline, --default-events (time with default HIP events instead of
-timing-only ones), --decode (only the decoding-size calls, for profiles).
+Flags: --gpus (1 only), --steps, --warmup, --workload (0..4, default 3),
+--sweep (extra per-T / per-N lines with fwd and bwd timed separately and
+caches flushed between reps), --no-cpu-baseline, --no-probes,
+--default-events (time with default HIP events instead of timing-only ones),
+--decode (only the decoding-size calls, for profiles).
 """
 from __future__ import annotations
 
@@ -34,9 +44,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PAGES_PEAK_GIB_128K = 35.03  # pages' fused figure at 128K local tokens (B300; context)
 METRIC = "AttnRes fwd+bwd tokens/s and achieved HBM GB/s (% of peak), D=7168 N=9"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_T4096_N9_D7168.json")
+DEFAULT_WORKLOAD = 3
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "attention_residuals_depth_amd", "csrc", "attnres.hip")
+PROBE_LIB = os.path.join(ROOT, "attention_residuals_depth_amd", "libattnres_probes.so")
 
 
 def algo_bytes(T: int, N: int, D: int):
@@ -64,13 +77,17 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(text.encode("utf-8")).hexdigest()[:16]
 
 
+def traffic_file(T: int, N: int, D: int) -> str:
+    return os.path.join(PROFILES, f"traffic_bwd_T{T}_N{N}_D{D}.json")
+
+
 def load_traffic(T: int, N: int, D: int):
     """HBM bytes per attnres_bwd call from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, calibrated against a copy of known size), used
-    only while the kernel source and the workload are the ones the counters
+    for this workload (FETCH_SIZE and WRITE_SIZE, calibrated against a copy of
+    known size), used only while the kernel source is the one the counters
     were taken on; otherwise None."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(T, N, D)))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
@@ -80,89 +97,160 @@ def load_traffic(T: int, N: int, D: int):
     return rec
 
 
-def make_inputs(wl, torch, dev):
+def log(msg: str):
+    """Progress on stderr (the JSON line is the only stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_inputs(wl, torch, dev, chunk: int = 8192):
+    """The workload's sources, dout and w, generated on the host chunk by chunk
+    (counter-based, so any token range is reproducible on its own) and copied
+    into device tensors; the host arrays are kept for the oracle pass."""
     import numpy as np
 
+    src_h = np.empty((wl.N, wl.T, wl.D), dtype=np.uint16)
+    dout_h = np.empty((wl.T, wl.D), dtype=np.uint16)
     src = torch.empty((wl.N, wl.T, wl.D), dtype=torch.bfloat16, device=dev)
-    src.view(torch.int16).copy_(torch.from_numpy(wl.sources().view(np.int16)))
     dout = torch.empty((wl.T, wl.D), dtype=torch.bfloat16, device=dev)
-    dout.view(torch.int16).copy_(torch.from_numpy(wl.dout().view(np.int16)))
-    w = torch.from_numpy(wl.w()).to(dev)
-    return src, w, dout
+    for t0 in range(0, wl.T, chunk):
+        t1 = min(wl.T, t0 + chunk)
+        wl.sources(t0, t1, out=src_h[:, t0:t1])  # row block i is contiguous in each source
+        wl.dout(t0, t1, out=dout_h[t0:t1])
+        src[:, t0:t1].view(torch.int16).copy_(torch.from_numpy(src_h[:, t0:t1].view(np.int16)))
+        dout[t0:t1].view(torch.int16).copy_(torch.from_numpy(dout_h[t0:t1].view(np.int16)))
+        if (t0 // chunk) % 4 == 3 or t1 == wl.T:
+            log(f"inputs: tokens 0..{t1} of {wl.T} generated")
+    w_h = wl.w()
+    return src, torch.from_numpy(w_h).to(dev), dout, (src_h, w_h, dout_h)
 
 
-def cpu_baseline(wl, min_seconds: float = 10.0):
-    """The oracle, as it stands, on the host cores: fwd + bwd over the whole
-    workload (all T tokens), repeated until at least `min_seconds` of CPU work
-    have been timed (monotonic clock); tokens/s over all passes."""
-    import ctypes
+def sample_tokens(T: int, n_random: int = 48, seed: int = 1):
+    """First and last tokens, the first and last backward workgroup's first
+    tokens, the start of the last (ragged) round of tokens, seeded random ones."""
+    import numpy as np
 
-    import oracle
+    P = min(T, 256)
+    edges = {0, 1, T - 2, T - 1, P - 1, P, 2 * P - 1}
+    last_round = (T // P) * P if T % P else T - P
+    edges.update({last_round, last_round - 1, last_round + 1})
+    rnd = np.random.default_rng(seed).integers(0, T, size=n_random)
+    return np.array(sorted({int(t) for t in edges if 0 <= t < T} | {int(t) for t in rnd}), dtype=np.int64)
 
-    src = wl.sources()
-    w = wl.w()
-    dout = wl.dout()
+
+def omp_threads() -> int:
     try:
-        cores = int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+        return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
     except OSError:
-        cores = os.cpu_count()
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        out, rstd, alpha = oracle.fwd(src, w, wl.eps)
-        dsrc, dw = oracle.bwd(src, w, wl.eps, dout)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= 1000:
-            break
-    rec = {"value": passes * wl.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-           "sample": f"{passes} passes of fwd+bwd over all {wl.T} tokens (N={wl.N}, D={wl.D}) in fp64, "
-                     f"{dt:.1f} s"}
-    return rec, {"out": out, "rstd": rstd, "alpha": alpha, "dsrc": dsrc, "dw": dw}
+        return os.cpu_count() or 1
 
 
 # Parity bars: relative L2 for out (5e-3), dsources and dw (1e-2), absolute for
 # alpha (1e-5); rstd relative 1e-5 (an fp32 sum of D exact bf16 squares is
 # good to ~1e-6 relative).
-PARITY_BARS = {"out_rel_l2": 5e-3, "alpha_max_abs": 1e-5, "rstd_max_rel": 1e-5, "dsrc_rel_l2": 1e-2,
-               "dw_rel_l2": 1e-2}
+PARITY_BARS = {"out_rel_l2": 5e-3, "out_token_rel_l2": 5e-3, "alpha_max_abs": 1e-5, "rstd_max_rel": 1e-5,
+               "dsrc_rel_l2": 1e-2, "dw_rel_l2": 1e-2}
 
 
-def parity_report(torch, ref, out, rstd, alpha, dsrc, dw):
-    """Errors of the timed run's last outputs (every timed step computes the
-    same batch) against the fp64 oracle's outputs for the same inputs."""
+class _Errors:
+    """Error metrics accumulated over token chunks (torch CPU ops, float64)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.v = {"out_err": 0.0, "out_ref": 0.0, "out_token_rel_l2": 0.0, "alpha_max_abs": 0.0, "rstd_max_rel": 0.0}
+
+    def fwd_chunk(self, out_gpu_bits, rstd_gpu, alpha_gpu, o_out, o_rstd, o_alpha):
+        import numpy as np
+
+        torch = self.torch
+        go = torch.from_numpy(np.ascontiguousarray(out_gpu_bits).view(np.int16)).view(torch.bfloat16).double()
+        ro = torch.from_numpy(o_out)
+        d2 = (go - ro).square_()
+        self.v["out_err"] += float(d2.sum())
+        self.v["out_ref"] += float(ro.square().sum())
+        den = ro.square().sum(1).sqrt_()
+        tok = d2.sum(1).sqrt_() / torch.where(den > 0, den, torch.ones_like(den))
+        self.v["out_token_rel_l2"] = max(self.v["out_token_rel_l2"], float(tok.max()))
+        self.v["alpha_max_abs"] = max(self.v["alpha_max_abs"], float(np.max(np.abs(alpha_gpu - o_alpha))))
+        self.v["rstd_max_rel"] = max(self.v["rstd_max_rel"], float(np.max(np.abs(rstd_gpu - o_rstd) / o_rstd)))
+
+
+def oracle_pass(wl, host, gpu, toks, torch, chunk: int = 4096):
+    """The oracle, as it stands, over the whole workload in token chunks: the
+    forward and the backward timed separately (monotonic clock around the
+    oracle calls only), and the timed run's outputs compared with it: out,
+    alpha, rstd on every token, dsources on the sampled tokens `toks`, dw
+    summed over all chunks in token order.  Returns (record, parity)."""
     import numpy as np
 
-    def rel(a, b):
-        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    import oracle
 
-    e = {
-        "out_rel_l2": rel(out.float().cpu().numpy().astype(np.float64), ref["out"]),
-        "alpha_max_abs": float(np.abs(alpha.cpu().numpy().astype(np.float64) - ref["alpha"]).max()),
-        "rstd_max_rel": float((np.abs(rstd.cpu().numpy().astype(np.float64) - ref["rstd"]) / ref["rstd"]).max()),
-        "dsrc_rel_l2": rel(dsrc.float().cpu().numpy().astype(np.float64), ref["dsrc"]),
-        "dw_rel_l2": rel(dw.cpu().numpy().astype(np.float64), ref["dw"]),
-    }
+    src_h, w_h, dout_h = host
+    T, N, D = wl.T, wl.N, wl.D
+    errs = _Errors(torch)
+    t_fwd = t_bwd = 0.0
+    o_dw = np.zeros(D)
+    dsrc_err = dsrc_ref = 0.0
+    pos = {int(t): j for j, t in enumerate(toks)}
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        xs = np.ascontiguousarray(src_h[:, t0:t1])
+        c = time.perf_counter()
+        o_out, o_rstd, o_alpha = oracle.fwd(xs, w_h, wl.eps)
+        t_fwd += time.perf_counter() - c
+        c = time.perf_counter()
+        o_dsrc, dw_c = oracle.bwd(xs, w_h, wl.eps, dout_h[t0:t1])
+        t_bwd += time.perf_counter() - c
+        o_dw += dw_c
+        errs.fwd_chunk(gpu["out_bits"][t0:t1], gpu["rstd"][t0:t1], gpu["alpha"][t0:t1], o_out, o_rstd, o_alpha)
+        for t in [t for t in pos if t0 <= t < t1]:
+            g = synth_bf16_to_f64(gpu["dsrc_bits"][:, pos[t]])
+            r = o_dsrc[:, t - t0]
+            dsrc_err += float(np.sum((g - r) ** 2))
+            dsrc_ref += float(np.sum(r ** 2))
+        del o_out, o_dsrc
+        if (t0 // chunk) % 8 == 7 or t1 == T:
+            log(f"oracle: tokens 0..{t1} of {T} (fwd {t_fwd:.1f} s, bwd {t_bwd:.1f} s)")
+    e = {"out_rel_l2": (errs.v["out_err"] / errs.v["out_ref"]) ** 0.5, "out_token_rel_l2": errs.v["out_token_rel_l2"],
+         "alpha_max_abs": errs.v["alpha_max_abs"], "rstd_max_rel": errs.v["rstd_max_rel"],
+         "dsrc_rel_l2": (dsrc_err / dsrc_ref) ** 0.5,
+         "dw_rel_l2": float(np.linalg.norm(gpu["dw"] - o_dw) / np.linalg.norm(o_dw))}
     e["within_bars"] = all(e[k] <= v for k, v in PARITY_BARS.items())
-    return e
+    e["compared"] = (f"out, alpha, rstd: all {T} tokens; dsources: {len(toks)} sampled tokens; "
+                     f"dw: sum over all {T} tokens")
+    cores = omp_threads()
+    rec = {"value": T / (t_fwd + t_bwd), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "fwd_tokens_per_s": T / t_fwd, "bwd_tokens_per_s": T / t_bwd,
+           "sample": f"the whole workload ({T} tokens, N={N}, D={D}) in chunks of {chunk}, fp64, "
+                     f"fwd {t_fwd:.1f} s + bwd {t_bwd:.1f} s on {cores} threads"}
+    return rec, e
 
 
-def copy_probe(torch, dev, nbytes=2 << 30, reps=10):
-    """Plain device-to-device copy of a known size: measured HBM copy rate."""
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a, b
-    torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+def synth_bf16_to_f64(bits):
+    import numpy as np
+
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def oracle_per_config(n_tokens: int = 2048):
+    """The oracle's fwd and bwd timed separately on the first min(T, n_tokens)
+    tokens of every workload (the N-sweep workload at N = 9)."""
+    import oracle
+    import synth
+
+    rows = []
+    for cfg in sorted(synth.WORKLOADS):
+        wl = synth.workload(cfg, N=9 if cfg == 2 else None)
+        S = min(wl.T, n_tokens)
+        src, dout, w = wl.sources(0, S), wl.dout(0, S), wl.w()
+        c = time.perf_counter()
+        oracle.fwd(src, w, wl.eps)
+        tf = time.perf_counter() - c
+        c = time.perf_counter()
+        oracle.bwd(src, w, wl.eps, dout)
+        tb = time.perf_counter() - c
+        rows.append({"workload": wl.name, "T": wl.T, "N": wl.N, "tokens_timed": S, "fwd_tokens_per_s": S / tf,
+                     "bwd_tokens_per_s": S / tb})
+    return rows
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
@@ -449,16 +537,94 @@ def sweep_decode(ar, torch, dev, flush, N=9, D=7168):
                           "back_to_back_us": warm_us}), flush=True)
 
 
+class Probes:
+    """ctypes view of libattnres_probes (bandwidth ceilings; not the operator)."""
+
+    def __init__(self):
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(PROBE_LIB)
+        vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        lib.attnres_probe_read.argtypes = [vp, sz, vp, vp]
+        lib.attnres_probe_write.argtypes = [vp, sz, vp]
+        lib.attnres_probe_copy.argtypes = [vp, vp, sz, vp]
+        lib.attnres_probe_fwd_pattern.argtypes = [pp, i32, i64, i32, vp, vp]
+        lib.attnres_probe_bwd_pattern.argtypes = [pp, vp, i32, i64, i32, pp, vp]
+        self.lib = lib
+
+    @staticmethod
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError(f"{name} returned {rc}")
+
+
+def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 << 30):
+    """Median GB/s of the probe kernels on this device: plain read, write and
+    copy streams of `nbytes` (one 4 KiB chunk per workgroup, nontemporal), and
+    the operator's forward and backward access patterns on the workload's own
+    buffers (same rows, same launch shapes, no arithmetic).  Overwrites out and
+    dsrc."""
+    pr = Probes()
+    stream = torch.cuda.current_stream().cuda_stream
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    N, T, D = src.shape
+    srcs = (ctypes.c_void_p * N)(*[src[i].data_ptr() for i in range(N)])
+    dsrcs = (ctypes.c_void_p * N)(*[dsrc[i].data_ptr() for i in range(N)])
+    calls = {
+        "read": (lambda: pr.check(pr.lib.attnres_probe_read(a.data_ptr(), nbytes, sink.data_ptr(), stream), "read"),
+                 nbytes),
+        "write": (lambda: pr.check(pr.lib.attnres_probe_write(b.data_ptr(), nbytes, stream), "write"), nbytes),
+        "copy": (lambda: pr.check(pr.lib.attnres_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, stream), "copy"),
+                 2 * nbytes),
+        "fwd_pattern": (lambda: pr.check(pr.lib.attnres_probe_fwd_pattern(srcs, N, T, D, out.data_ptr(), stream),
+                                         "fwd_pattern"), T * (2 * N * D + 2 * D)),
+        "bwd_pattern": (lambda: pr.check(pr.lib.attnres_probe_bwd_pattern(srcs, dout.data_ptr(), N, T, D, dsrcs,
+                                                                          stream), "bwd_pattern"),
+                        T * (4 * N * D + 2 * D)),
+    }
+    res = {}
+    ev = TimingEvents(2)
+    for name, (fn, moved) in calls.items():
+        if name.endswith("pattern") and D > 8192:
+            continue
+        ms = []
+        for r in range(reps + 2):
+            ev.record(0, stream)
+            fn()
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            if r >= 2:
+                ms.append(ev.ms(0, 1))
+        res[name] = moved / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
+    ev.close()
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def flushed_calls(torch, dev, fwd, bwd, reps: int = 10):
+    """Median event times of fwd and of bwd, each preceded by a 512 MiB write
+    that evicts the L2 and the 256 MB Infinity Cache."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    f, b = _fwd_bwd_ms(torch, flush, fwd, bwd, reps)
+    del flush
+    torch.cuda.empty_cache()
+    return f, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    # The first ~50 steps of a fresh process run ~3% slower than later ones on MI355X
-    # (measured: 5 warm-up steps give 0.330 ms per step, 100 give 0.318), so the
-    # default warm-up is 100 steps (~32 ms) and 200 steps are timed (~64 ms).
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[0, 1, 2, 3, 4],
+                    help="bench-line workload (default 3: T=131072, N=9, peaked softmax); 2 runs at N=9")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--default-events", action="store_true",
                     help="time with default HIP events (a system-scope fence at every marker) instead of "
                          "timing-only events, for comparison")
@@ -470,6 +636,7 @@ def main():
               "multi-GPU path (--gpus must be 1)", file=sys.stderr, flush=True)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import attention_residuals_depth_amd as ar
@@ -480,18 +647,37 @@ def main():
     if args.decode:
         sweep_decode(ar, torch, dev, torch.empty(512 << 20, dtype=torch.uint8, device=dev))
         return
-    wl = synth.workload(1)  # T=4096, N=9, D=7168
+    wl = synth.workload(args.workload, N=9 if args.workload == 2 else None)
     T, N, D = wl.T, wl.N, wl.D
-    src, w, dout = make_inputs(wl, torch, dev)
+    log(f"workload {wl.name}: T={T} N={N} D={D}")
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    src, w, dout, host = make_inputs(wl, torch, dev)
     bufs = alloc_buffers(ar, torch, N, T, D, dev)
+    out, rstd, alpha, dsrc, dw, ws = bufs
 
     fenceless = not args.default_events
+    log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
     timed_steps(ar, torch, src, w, dout, wl.eps, bufs, max(args.warmup, 1), fenceless)
     total_ms, wall, fwd_ms, bwd_ms, ev_kind = timed_steps(ar, torch, src, w, dout, wl.eps, bufs, args.steps,
                                                           fenceless)
-    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+    peak_gib = (torch.cuda.max_memory_allocated() - base) / 2**30
+    # the timed run's outputs (every step computes the same batch), kept for the parity check
+    toks = sample_tokens(T)
+    tk = torch.from_numpy(toks).to(dev)
+    gpu = {"out_bits": out.view(torch.int16).cpu().numpy().view(np.uint16),
+           "rstd": rstd.cpu().double().numpy(), "alpha": alpha.cpu().double().numpy(),
+           "dsrc_bits": dsrc[:, tk].contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
+           "dw": dw.cpu().double().numpy()}
+
+    log("flushed per-call timing")
+    f_fl, b_fl = flushed_calls(torch, dev, lambda: ar.attnres_fwd(src, w, wl.eps, out=out, rstd=rstd, alpha=alpha),
+                               lambda: ar.attnres_bwd(dout, src, w, rstd, alpha, dsrc=dsrc, dw=dw, workspace=ws))
+    ceil = None
+    if not args.no_probes:
+        log("bandwidth ceilings (probe kernels)")
+        ceil = ceilings(torch, dev, src, dout, out, dsrc)
 
     ms_step = total_ms / args.steps
     fb, bb, fe, be = algo_bytes(T, N, D)
@@ -499,7 +685,6 @@ def main():
     bwd_gbps = (bb + be) / (bwd_ms * 1e-3) / 1e9
     fwd_gbps = (fb + fe) / (fwd_ms * 1e-3) / 1e9
     traffic = load_traffic(T, N, D)
-    copy_gbps = copy_probe(torch, dev)
 
     result = {
         "metric": METRIC,
@@ -514,17 +699,24 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "accumulate": "f32",
-        "data": "synthetic (seeded; sources N(0,1)*sqrt(1+12i), w N(0,1/sqrt(D)), dout N(0,1))",
-        "config": {"workload": wl.name, "T": T, "N": N, "D": D, "eps": wl.eps, "parallelism": "single GPU"},
+        "data": ("synthetic (seeded counter-based generator; sources N(0,1)*sqrt(1+12i), "
+                 f"w N(0,{wl.w_std if wl.w_std is not None else '1/sqrt(D)'}), dout N(0,1))"),
+        "config": {"workload": wl.name, "T": T, "N": N, "D": D, "eps": wl.eps, "layout": "stacked [N][T][D]",
+                   "parallelism": "single GPU"},
         "achieved_GBps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "fwd_GBps": fwd_gbps,
+        "bwd_GBps": bwd_gbps,
+        "flushed": {"fwd_ms": f_fl, "bwd_ms": b_fl, "fwd_GBps": (fb + fe) / f_fl / 1e6,
+                    "bwd_GBps": (bb + be) / b_fl / 1e6, "fwdbwd_GBps": (fb + bb + fe + be) / (f_fl + b_fl) / 1e6,
+                    "fwdbwd_tokens_per_s": T / ((f_fl + b_fl) * 1e-3), "reps": "median of 10"},
         "wall_s_timed": wall,
         "timing_events": ev_kind,
         "peak_alloc_GiB": peak_gib,
-        "copy_probe_GBps": copy_gbps,
+        "pages_peak_alloc_GiB_at_128K": PAGES_PEAK_GIB_128K,
+        "ceilings_GBps": ceil,
         "roofline": {
             "kernel": "attnres_bwd (bwd_kernel + dw_reduce_kernel, one call)",
             "bound": "hbm",
@@ -536,13 +728,14 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], ref = cpu_baseline(wl)
-        out, rstd, alpha, dsrc, dw, _ = bufs
-        result["parity"] = parity_report(torch, ref, out, rstd, alpha, dsrc, dw)
-        del ref
+        log("oracle pass on the host (fwd and bwd timed separately)")
+        rec, parity = oracle_pass(wl, host, gpu, toks, torch)
+        rec["per_workload_sample"] = oracle_per_config()
+        result["cpu_baseline"] = rec
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
     if args.sweep:
-        del src, dout, bufs
+        del src, dout, bufs, out, rstd, alpha, dsrc, dw, ws, host, gpu
         torch.cuda.empty_cache()
         sweep(ar, torch, dev)
 

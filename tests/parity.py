@@ -72,19 +72,190 @@ def token_rows(wl: synth.Workload, tokens: np.ndarray):
     return src, g
 
 
-def check_tokens(errs: dict, name: str, gpu: dict, ref: dict):
-    """Record the error metrics of one comparison into errs[name]."""
+def check_tokens(errs: dict, name: str, gpu: dict, ref: dict, inputs=None):
+    """Record the error metrics of one comparison into errs[name].  With
+    inputs = (x_bits [N][n][D], g_bits [n][D], w) of the compared tokens, every
+    element of out and dsrc is also checked against its arithmetic error bound
+    and every token against the relative L2 bars."""
     e = {
         "out_rel_l2": rel_l2(gpu["out"], ref["out"]),
         "alpha_max_abs": float(np.abs(gpu["alpha"] - ref["alpha"]).max()),
         "rstd_max_rel": float((np.abs(gpu["rstd"] - ref["rstd"]) / np.abs(ref["rstd"])).max()),
+        "out_token_rel_l2": per_token_rel_l2(gpu["out"], ref["out"], 0),
     }
     if "dsrc" in ref:
         e["dsrc_rel_l2"] = rel_l2(gpu["dsrc"], ref["dsrc"])
+        e["dsrc_token_rel_l2"] = per_token_rel_l2(gpu["dsrc"], ref["dsrc"], 1)
     if "dw" in ref:
         e["dw_rel_l2"] = rel_l2(gpu["dw"], ref["dw"])
+    if inputs is not None:
+        x_bits, g_bits, w = inputs
+        e.update(elementwise_ratios(x_bits, g_bits, w, gpu, ref, device=DEV))
     errs[name] = e
     return e
+
+
+# ----------------------------------------------------------------------------
+# Element-by-element bounds
+# ----------------------------------------------------------------------------
+# The whole-tensor relative L2 above would let a few wrong elements through (one
+# wrong 16-byte vector in a 4096-token batch moves out's rel-L2 by ~5%).  So
+# every compared element of out and dsources must also lie within an error
+# bound derived from the arithmetic the kernels perform:
+#
+#   out'_d  = bf16( fl( sum_i a'_i x_id ) ), a' the GPU's saved alpha (the very
+#             values its weighted sum used):
+#             |out' - out| <= ulp/2 + sum_i |a'_i - a_i||x_id| + G_N sum_i a'_i |x_id|
+#   dx'_id  = bf16( fma(c1', fma(-k', x_id, w_d), a'_i g_d) ) with c1 = dz r,
+#             k = z r / D formed in fp32 from the dots g.x_i and w.x_i (fp32 tree
+#             sums: error <= G_D * sum_d |terms|), the saved r' and a'; the
+#             first-order propagation of those errors gives the bound below,
+#             doubled to cover second-order terms.
+#
+# G_n = n u / (1 - n u) with u = 2^-24; G_D uses 64 for the depth of the fp32
+# summation trees of a D-long dot (at most ~40 roundings along any path for
+# D <= 16384).  ulp is the bf16 spacing at max(|ref|, |gpu|).
+U32 = 2.0 ** -24
+GAMMA_DOT = 64 * U32
+
+
+def _t(a, device="cpu") -> torch.Tensor:
+    """float64 tensor on `device` from a numpy array, a float tensor, or bf16 bits
+    (uint16 numpy arrays are bf16 bit patterns, widened exactly)."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=torch.float64)
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16).double()
+    return torch.from_numpy(a).to(device=device, dtype=torch.float64)
+
+
+def bf16_ulp(a: torch.Tensor) -> torch.Tensor:
+    """Spacing of bf16 numbers (8 significant bits) at |a|, normal range."""
+    _, e = torch.frexp(a.abs().clamp_min(2.0 ** -126))  # |a| = m 2^e, 0.5 <= m < 1
+    return torch.ldexp(torch.ones_like(a), (e - 8).to(a.dtype))
+
+
+def out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
+    """Per-element bound on |out_gpu - out_ref|.  x [N][n][D] (values of the
+    bf16 sources), alpha [n][N], out [n][D]; float64 tensors."""
+    N = x.shape[0]
+    ax = x.abs()
+    da = (a_gpu - a_ref).abs().T[:, :, None]  # [N][n][1]
+    gN = N * U32 / (1 - N * U32)
+    b = (da * ax).sum(0) + gN * (a_gpu.abs().T[:, :, None] * ax).sum(0)
+    return 0.5 * bf16_ulp(torch.maximum(out_ref.abs(), out_gpu.abs())) + b
+
+
+def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu) -> torch.Tensor:
+    """Per-element bound on |dsrc_gpu - dsrc_ref| for the overwriting backward.
+    x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors."""
+    N, n, D = x.shape
+    u = U32
+    r = r_ref.T[:, :, None]                   # [N][n][1]
+    dr = (r_gpu - r_ref).abs().T[:, :, None]
+    a = a_ref.T[:, :, None]
+    dal = (a_gpu - a_ref).abs().T[:, :, None]
+    gx = x * g[None]
+    da = gx.sum(2, keepdim=True)              # g . x_i
+    e_da = GAMMA_DOT * gx.abs_().sum(2, keepdim=True)
+    del gx
+    wxt = x * w[None, None, :]
+    wx = wxt.sum(2, keepdim=True)             # w . x_i
+    e_wx = GAMMA_DOT * wxt.abs_().sum(2, keepdim=True)
+    del wxt
+    s = (a * da).sum(0, keepdim=True)
+    e_s = (dal * da.abs() + a * e_da + N * u * a * da.abs()).sum(0, keepdim=True)
+    dz = a * (da - s)
+    e_dz = dal * (da - s).abs() + a * (e_da + e_s) + 2 * u * dz.abs()
+    c1 = dz * r
+    e_c1 = e_dz * r + dz.abs() * dr + u * c1.abs()
+    z = r * wx
+    e_z = dr * wx.abs() + r * e_wx + u * z.abs()
+    k = z * r / D
+    e_k = (e_z * r + z.abs() * dr) / D + 2 * u * k.abs()
+    # per element: 2 (|da| |g| + u |a g| + e_c1 |inner| + |c1| (e_k |x| + u |inner|) + u (|a g| + |c1 inner|))
+    inner = (w[None, None, :] - k * x).abs_()
+    b = inner * (e_c1 + 2 * u * c1.abs())
+    b += x.abs() * (c1.abs() * e_k)
+    b += g.abs()[None] * (dal + 2 * u * a.abs())
+    b *= 2.0
+    b += 0.5 * bf16_ulp(torch.maximum(dsrc_ref.abs(), dsrc_gpu.abs()))
+    return b
+
+
+class Accum:
+    """Error metrics of a comparison built up over token chunks: relative L2 of
+    out and dsrc over everything compared, the largest per-token relative L2,
+    the largest alpha and rstd errors, and the largest ratio of an element's
+    error to its bound (out_bound / dsrc_bound).  `device` is where the
+    comparison arithmetic runs (expected values always come from the oracle
+    on the host)."""
+
+    def __init__(self, device="cpu"):
+        self.dev = device
+        self.sq = {}
+        self.mx = {}
+
+    def _add(self, k, v):
+        self.sq[k] = self.sq.get(k, 0.0) + float(v)
+
+    def _max(self, k, v):
+        self.mx[k] = max(self.mx.get(k, 0.0), float(v))
+
+    def update(self, x, g, w, gpu: dict, ref: dict):
+        """x [N][n][D] and g [n][D]: the chunk's inputs (bf16 bits or tensors);
+        w [D]; gpu / ref: dicts of out [n][D], rstd and alpha [n][N] and
+        optionally dsrc [N][n][D] (tensors or arrays)."""
+        d = self.dev
+        go, ro = _t(gpu["out"], d), _t(ref["out"], d)
+        ga, ra = _t(gpu["alpha"], d), _t(ref["alpha"], d)
+        gr, rr = _t(gpu["rstd"], d), _t(ref["rstd"], d)
+        xx = _t(x, d)
+        self._max("alpha_max_abs", (ga - ra).abs().max())
+        self._max("rstd_max_rel", ((gr - rr).abs() / rr.abs()).max())
+        self._add("out_err", (go - ro).square().sum())
+        self._add("out_ref", ro.square().sum())
+        tok_num = (go - ro).square().sum(1).sqrt()
+        tok_den = ro.square().sum(1).sqrt()
+        self._max("out_token_rel_l2", (tok_num / torch.where(tok_den > 0, tok_den, torch.ones_like(tok_den))).max())
+        self._max("out_elem_ratio", ((go - ro).abs() / out_bound(xx, ga, ra, ro, go)).max())
+        del go, ro
+        if "dsrc" in ref:
+            gd, rd = _t(gpu["dsrc"], d), _t(ref["dsrc"], d)
+            self._add("dsrc_err", (gd - rd).square().sum())
+            self._add("dsrc_ref", rd.square().sum())
+            tok_num = (gd - rd).square().sum((0, 2)).sqrt()
+            tok_den = rd.square().sum((0, 2)).sqrt()
+            self._max("dsrc_token_rel_l2",
+                      (tok_num / torch.where(tok_den > 0, tok_den, torch.ones_like(tok_den))).max())
+            bd = dsrc_bound(xx, _t(g, d), _t(w, d), rr, gr, ra, ga, rd, gd)
+            self._max("dsrc_elem_ratio", ((gd - rd).abs() / bd).max())
+
+    def result(self) -> dict:
+        e = dict(self.mx)
+        e["out_rel_l2"] = (self.sq["out_err"] / max(self.sq["out_ref"], 1e-300)) ** 0.5
+        if "dsrc_err" in self.sq:
+            e["dsrc_rel_l2"] = (self.sq["dsrc_err"] / max(self.sq["dsrc_ref"], 1e-300)) ** 0.5
+        return e
+
+
+def elementwise_ratios(x_bits, g_bits, w, gpu: dict, ref: dict, device="cpu") -> dict:
+    """Largest |gpu - ref| / bound over every element of out (and dsrc when
+    present) of the given tokens."""
+    acc = Accum(device)
+    acc.update(x_bits, g_bits, w, gpu, ref)
+    e = acc.result()
+    return {k: e[k] for k in ("out_elem_ratio", "dsrc_elem_ratio") if k in e}
+
+
+def per_token_rel_l2(a, b, token_axis: int) -> float:
+    """Largest relative L2 error of any single token's values."""
+    a, b = _t(a), _t(b)
+    dims = tuple(i for i in range(a.dim()) if i != token_axis)
+    num = (a - b).square_().sum(dims).sqrt_()
+    den = b.square().sum(dims).sqrt_()
+    return float((num / torch.where(den > 0, den, torch.ones_like(den))).max())
 
 
 def within_tolerance(e: dict) -> bool:
@@ -93,6 +264,14 @@ def within_tolerance(e: dict) -> bool:
         ok = ok and e["dsrc_rel_l2"] <= TOL_DSRC_REL_L2
     if "dw_rel_l2" in e:
         ok = ok and e["dw_rel_l2"] <= TOL_DW_REL_L2
+    # element-by-element and per-token checks, where they were computed
+    for k in ("out_elem_ratio", "dsrc_elem_ratio"):
+        if k in e:
+            ok = ok and e[k] <= 1.0
+    if "out_token_rel_l2" in e:
+        ok = ok and e["out_token_rel_l2"] <= TOL_OUT_REL_L2
+    if "dsrc_token_rel_l2" in e:
+        ok = ok and e["dsrc_token_rel_l2"] <= TOL_DSRC_REL_L2
     return ok
 
 
@@ -114,7 +293,7 @@ def full_compare(wl: synth.Workload):
     gpu = dict(out=bf16_dev_to_f64(out), rstd=rstd.cpu().double().numpy(), alpha=alpha.cpu().double().numpy(),
                dsrc=bf16_dev_to_f64(dsrc), dw=dw.cpu().double().numpy())
     ref = dict(out=o_out, rstd=o_rstd, alpha=o_alpha, dsrc=o_dsrc, dw=o_dw)
-    return gpu, ref
+    return gpu, ref, (src, dout, w)
 
 
 def sample_tokens(T: int, n_random: int = 40, seed: int = 1) -> np.ndarray:

@@ -374,3 +374,31 @@ def test_grad_mode_constants_match_binding():
     assert _define("ATTNRES_GRAD_BF16") == 0
     assert _define("ATTNRES_GRAD_ACCUMULATE") == ar.GRAD_ACCUMULATE
     assert _define("ATTNRES_GRAD_F32") == ar.GRAD_F32
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "attnres_probes.h")
+PROBE_LIB = os.path.join(ROOT, "attention_residuals_depth_amd", "libattnres_probes.so")
+
+
+def test_probe_library_exports_declared_symbols_and_refuses_bad_arguments():
+    names = re.findall(r"^int\s+(attnres_probe_\w+)\s*\(", open(PROBE_HEADER).read(), re.M)
+    assert names == ["attnres_probe_read", "attnres_probe_write", "attnres_probe_copy", "attnres_probe_fwd_pattern",
+                     "attnres_probe_bwd_pattern"]
+    lib = ctypes.CDLL(PROBE_LIB)
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    lib.attnres_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.attnres_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.attnres_probe_fwd_pattern.argtypes = [vp, i32, i64, i32, vp, vp]
+    # invalid arguments are refused on the host (status 1), nothing is enqueued
+    assert lib.attnres_probe_read(None, 4096, A, None) == 1
+    assert lib.attnres_probe_read(A + 8, 4096, A, None) == 1      # misaligned
+    assert lib.attnres_probe_read(A, 4100, A, None) == 1          # not a multiple of 16
+    assert lib.attnres_probe_copy(A, A + 4096, 8192, None) == 1   # overlapping
+    ptrs = (ctypes.c_void_p * 9)(*([A] * 9))
+    assert lib.attnres_probe_fwd_pattern(ptrs, 10, 16, D, A, None) == 1   # N > 9
+    assert lib.attnres_probe_fwd_pattern(ptrs, 9, 16, 8200, A, None) == 1  # D > 8192
+    assert lib.attnres_probe_read(A, 0, A, None) == 0              # empty: nothing to do
+

@@ -1,7 +1,7 @@
 """Host-side logic of bench.py (CPU): the algorithmic byte counts behind every
 reported GB/s and roofline fraction, the guard that keeps stale counter
-traffic out of the JSON line, the single-GPU refusal and the CPU-baseline
-record."""
+traffic out of the JSON line, the single-GPU refusal, the oracle pass behind
+the CPU-baseline and parity records, and the token sample."""
 from __future__ import annotations
 
 import json
@@ -27,16 +27,19 @@ def test_algorithmic_bytes_per_token():
 
 
 def test_algorithmic_bytes_of_the_default_workload():
-    wl = synth.workload(1)
+    wl = synth.workload(bench.DEFAULT_WORKLOAD)
     fwd, bwd, fe, be = bench.algo_bytes(wl.T, wl.N, wl.D)
-    assert (wl.T, wl.N, wl.D) == (4096, 9, 7168)
+    assert (wl.T, wl.N, wl.D) == (131072, 9, 7168) and wl.w_std == 0.5
     # one attnres_bwd call: per-token bytes, w, 256 dw partial rows written and read, dw
-    assert bwd + be == 1_130_717_184
-    assert fwd + fe == 587_526_144
-    # the committed counter record refers to the same byte count
-    rec = json.load(open(bench.TRAFFIC_FILE))
-    assert rec["algorithmic_bytes_per_call"] == bwd + be
-    assert rec["fwd_kernel"]["algorithmic_bytes"] == fwd + fe
+    assert bwd + be == 131072 * 272_456 + 4 * 7168 + 8 * 256 * 7168 + 4 * 7168 == 35_726_090_240
+    assert fwd + fe == 131072 * 143_432 + 4 * 7168 == 18_799_947_776
+    # a committed counter record, if present, refers to the same byte count
+    f = bench.traffic_file(wl.T, wl.N, wl.D)
+    assert os.path.basename(f) == "traffic_bwd_T131072_N9_D7168.json"
+    if os.path.exists(f):
+        rec = json.load(open(f))
+        assert rec["algorithmic_bytes_per_call"] == bwd + be
+        assert rec["fwd_kernel"]["algorithmic_bytes"] == fwd + fe
 
 
 def test_partial_rows_follow_min_T_256():
@@ -62,13 +65,13 @@ def test_stale_traffic_is_not_reported(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("__global__ void k() {}\n")
     monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     rec = {"kernel_source_sha256_16": bench.kernel_source_hash(), "T": 4096, "N": 9, "D": 7168,
            "bytes_per_call": 123}
-    f = tmp_path / "traffic.json"
+    f = tmp_path / "traffic_bwd_T4096_N9_D7168.json"
     f.write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.load_traffic(4096, 9, 7168)["bytes_per_call"] == 123
-    assert bench.load_traffic(4096, 9, 1024) is None  # another workload
+    assert bench.load_traffic(4096, 9, 1024) is None  # another workload: no record
     src.write_text("__global__ void k() { return; }\n")  # the kernel changed since the counters
     assert bench.load_traffic(4096, 9, 7168) is None
     f.write_text("not json")
@@ -83,30 +86,48 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_cpu_baseline_record():
-    wl = synth.Workload("bench_tiny", T=8, N=3, D=64)
-    rec, ref = bench.cpu_baseline(wl, min_seconds=0.05)
-    assert set(ref) == {"out", "rstd", "alpha", "dsrc", "dw"} and ref["dsrc"].shape == (3, 8, 64)
-    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
-    assert rec["value"] > 0 and rec["cores"] >= 1
-    assert "fp64" in rec["sample"] and "8 tokens" in rec["sample"]
-
-
-def test_parity_report_against_the_oracle_outputs():
-    """The bench's parity record: the oracle's own values rounded to the device
-    dtypes give rounding-level errors within the bars; a planted 5% error in dw
-    is reported as such and fails them."""
+def _rounded_outputs(wl, toks):
+    """The oracle's own outputs rounded to the device dtypes: what an exact
+    implementation would store."""
     import numpy as np
     import torch
 
-    wl = synth.Workload("bench_tiny", T=8, N=3, D=64)
-    _, ref = bench.cpu_baseline(wl, min_seconds=0.0)
-    as_dev = dict(out=torch.from_numpy(ref["out"]).to(torch.bfloat16), rstd=torch.from_numpy(ref["rstd"]).float(),
-                  alpha=torch.from_numpy(ref["alpha"]).float(), dsrc=torch.from_numpy(ref["dsrc"]).to(torch.bfloat16),
-                  dw=torch.from_numpy(ref["dw"]).float())
-    e = bench.parity_report(torch, ref, **as_dev)
-    assert e["within_bars"] and e["out_rel_l2"] < 4e-3 and e["dw_rel_l2"] < 1e-6
-    bad = dict(as_dev, dw=as_dev["dw"] * 1.05)
-    e = bench.parity_report(torch, ref, **bad)
+    import oracle
+
+    src, dout, w = wl.sources(), wl.dout(), wl.w()
+    o_out, o_rstd, o_alpha = oracle.fwd(src, w, wl.eps)
+    o_dsrc, o_dw = oracle.bwd(src, w, wl.eps, dout)
+    bits = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    gpu = {"out_bits": bits(o_out), "rstd": o_rstd.astype(np.float32).astype(np.float64),
+           "alpha": o_alpha.astype(np.float32).astype(np.float64),
+           "dsrc_bits": bits(np.ascontiguousarray(o_dsrc[:, toks])), "dw": o_dw.astype(np.float32).astype(np.float64)}
+    return (src, w, dout), gpu
+
+
+def test_oracle_pass_record_and_parity():
+    """The CPU-baseline record (fwd and bwd timed separately) and the parity
+    record: the oracle's values rounded to the device dtypes are within the
+    bars; a planted 5% error in dw, or one wrong token of out, is reported."""
+    import torch
+
+    wl = synth.Workload("bench_tiny", T=40, N=3, D=64)
+    toks = bench.sample_tokens(wl.T)
+    host, gpu = _rounded_outputs(wl, toks)
+    rec, e = bench.oracle_pass(wl, host, gpu, toks, torch, chunk=16)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["cores"] >= 1
+    assert rec["value"] > 0 and rec["fwd_tokens_per_s"] > rec["value"] and rec["bwd_tokens_per_s"] > rec["value"]
+    assert "40 tokens" in rec["sample"] and "fp64" in rec["sample"]
+    assert e["within_bars"] and e["out_rel_l2"] < 4e-3 and e["dw_rel_l2"] < 1e-6, e
+    bad = dict(gpu, dw=gpu["dw"] * 1.05)
+    e = bench.oracle_pass(wl, host, bad, toks, torch, chunk=16)[1]
     assert not e["within_bars"] and abs(e["dw_rel_l2"] - 0.05) < 1e-4
-    assert np.isfinite(e["alpha_max_abs"])
+    bad_out = gpu["out_bits"].copy()
+    bad_out[17] = bad_out[3]  # one token's row replaced by another's
+    e = bench.oracle_pass(wl, host, dict(gpu, out_bits=bad_out), toks, torch, chunk=16)[1]
+    assert not e["within_bars"] and e["out_token_rel_l2"] > 0.1
+
+
+def test_sample_tokens_cover_edges():
+    toks = bench.sample_tokens(131072)
+    assert {0, 1, 255, 256, 511, 131070, 131071} <= set(toks.tolist())
+    assert len(toks) > 40 and toks.max() < 131072

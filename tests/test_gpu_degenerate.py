@@ -57,9 +57,10 @@ def test_zero_rows_with_eps(N, T, D):
     src[0, 0] = 0
     src[N - 1, T // 2] = 0
     src[:, T - 1] = 0  # every source of the last token
-    gpu, ref = _run(src, wl.w(), 1e-6, wl.dout())
+    dout = wl.dout()
+    gpu, ref = _run(src, wl.w(), 1e-6, dout)
     errs = {}
-    e = check_tokens(errs, wl.name, gpu, ref)
+    e = check_tokens(errs, wl.name, gpu, ref, (src, dout, wl.w()))
     print(f"[parity] {wl.name}: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
     assert within_tolerance(e), e
     assert np.all(np.isfinite(gpu["out"])) and np.all(np.isfinite(gpu["dsrc"]))
@@ -98,9 +99,10 @@ def test_magnitudes_across_the_fp32_range(eps):
     base = wl.sources()
     shifts = [-50, 0, 50, -50, 50, 0]
     src = np.stack([_scale_bf16(base[i], s) for i, s in enumerate(shifts)])
-    gpu, ref = _run(src, wl.w(), eps, wl.dout())
+    dout = wl.dout()
+    gpu, ref = _run(src, wl.w(), eps, dout)
     errs = {}
-    e = check_tokens(errs, "magnitudes", gpu, ref)
+    e = check_tokens(errs, "magnitudes", gpu, ref, (src, dout, wl.w()))
     print(f"[parity] magnitudes eps={eps}: " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
     assert within_tolerance(e), e
     if eps == 0.0:

@@ -270,7 +270,7 @@ def test_interleaved_cache_at_full_size():
     gpu = dict(out=bf16_dev_to_f64(out[tk]), rstd=rstd[tk].cpu().double().numpy(),
                alpha=alpha[tk].cpu().double().numpy(), dsrc=bf16_dev_to_f64(gcache[tk].transpose(0, 1)))
     ref = dict(out=o_out, rstd=o_rstd, alpha=o_alpha, dsrc=o_dsrc)
-    e = check_tokens({}, wl.name, gpu, ref)
+    e = check_tokens({}, wl.name, gpu, ref, (s_src, np.ascontiguousarray(dout[toks]), w))
     print("[parity] interleaved full size: oracle dw over all tokens", flush=True)
     _, o_dw = oracle.bwd(src, w, wl.eps, dout, want_dsrc=False)
     e["dw_rel_l2"] = rel_l2(dw.cpu().double().numpy(), o_dw)

@@ -102,3 +102,30 @@ def test_backward_through_the_updated_partial_sum():
     got = np.stack([bf16_dev_to_f64(d) for d in dsrcs])
     assert rel_l2(got, o_dsrc) <= 1e-2
     assert rel_l2(dw.cpu().double().numpy(), o_dw) <= 1e-2
+
+
+def test_in_place_update_invalidates_saved_partial_sum():
+    """An autograd node that saved the partial sum must refuse its backward once
+    attnres_fwd_update has rewritten that tensor in place (the binding bumps the
+    tensor's version counter); a partial sum that requires grad is refused."""
+    wl, src_h, p_h, y_h = _case(3, 64, 1024)
+    srcs = [to_dev_bf16(src_h[i]) for i in range(2)]
+    p = to_dev_bf16(p_h)
+    y = to_dev_bf16(y_h)
+    w = torch.from_numpy(wl.w()).to(DEV).requires_grad_(True)
+    out = ar.attnres(srcs + [p], w, wl.eps)  # saves p for its backward
+    v0 = p._version
+    ar.attnres_fwd_update(srcs, p, y, w.detach(), wl.eps)  # rewrites p in place
+    assert p._version > v0
+    with pytest.raises(RuntimeError, match="modified by an inplace operation"):
+        out.float().sum().backward()
+    leaf = to_dev_bf16(p_h).requires_grad_(True)
+    with pytest.raises(RuntimeError, match="requires grad"):
+        ar.attnres_fwd_update(srcs, leaf, y, w.detach(), wl.eps)
+    # not in place: the saved tensor is untouched and the backward runs
+    p2 = to_dev_bf16(p_h)
+    out2 = ar.attnres(srcs + [p2], w, wl.eps)
+    ar.attnres_fwd_update(srcs, p2, y, w.detach(), wl.eps, in_place=False)
+    out2.float().sum().backward()
+    torch.cuda.synchronize()
+    assert w.grad is not None and bool(torch.isfinite(w.grad).all())
