@@ -21,6 +21,9 @@ The C entry points, declared in ``include/attnres.h``:
     attnres_fwd_update: the forward whose last source is the current block's
                 partial sum after adding the previous sub-layer's output
                 (partial_out = bf16(partial + delta), in place by default).
+    attnres_bwd_noalloc: attnres_bwd without a workspace argument, for
+                callers that cannot allocate (its dw partial rows live in a
+                static device array of the library, D <= 8192).
 """
 from __future__ import annotations
 
@@ -70,6 +73,8 @@ def library() -> ctypes.CDLL:
         lib.attnres_fwd_decode.restype = ctypes.c_int
         lib.attnres_fwd_update.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp, vp]
         lib.attnres_fwd_update.restype = ctypes.c_int
+        lib.attnres_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp]
+        lib.attnres_bwd_noalloc.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -172,6 +177,36 @@ def attnres_bwd(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: to
                                      ws_bytes, _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_bwd", code)
+    return dsrc, dw
+
+
+NOALLOC_MAX_D = 8192
+
+
+def attnres_bwd_noalloc(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
+                        alpha: torch.Tensor, dsrc: torch.Tensor, dw: torch.Tensor, stream=None):
+    """Backward like attnres_bwd, for callers that cannot allocate: no workspace
+    (the library keeps the dw partial rows in a static device array, D <= 8192)
+    and the outputs must be passed in -- this wrapper allocates nothing either.
+    Calls that overlap in time on one device race on that array."""
+    if src.dim() != 3:
+        raise ValueError("src must be [N][T][D]")
+    N, T, D = src.shape
+    _check(src, "src", torch.bfloat16, (N, T, D))
+    _check(dout, "dout", torch.bfloat16, (T, D))
+    _check(w, "w", torch.float32, (D,))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    _check(dsrc, "dsrc", torch.bfloat16, (N, T, D))
+    _check(dw, "dw", torch.float32, (D,))
+    dev = src.device
+    _same_device(dev, dout=dout, w=w, rstd=rstd, alpha=alpha, dsrc=dsrc, dw=dw)
+    with _device(dev):
+        code = library().attnres_bwd_noalloc(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(),
+                                             alpha.data_ptr(), N, T, D, dsrc.data_ptr(), dw.data_ptr(),
+                                             _stream_handle(stream, dev))
+    if code != 0:
+        raise AttnResError("attnres_bwd_noalloc", code)
     return dsrc, dw
 
 
@@ -417,5 +452,5 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 
 
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
-           "attnres_fwd_update", "GRAD_ACCUMULATE", "GRAD_F32",
+           "attnres_fwd_update", "attnres_bwd_noalloc", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

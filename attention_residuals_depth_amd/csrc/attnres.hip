@@ -1327,6 +1327,39 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Entry point without allocation: dw partial rows in a static device array
+// ---------------------------------------------------------------------------
+// The backward's only scratch is its dw partial rows (ATTNRES_DW_PARTIALS rows
+// of D fp32).  attnres_bwd_noalloc keeps them in this file-scope array instead
+// of a caller workspace: 256 x 8192 x 4 B = 8 MiB per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory, so the kernels receive the device address that hipGetSymbolAddress
+// returns for the current device (each device has its own copy at its own
+// address), looked up once per device and cached.
+static __device__ __align__(256) float scratch[ATTNRES_DW_PARTIALS * ATTNRES_NOALLOC_MAX_D];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr if the runtime refuses).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32_t N, int64_t T,
                                       int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream) {
   const attnres_status st = fwd_common_checks(w, eps, N, T, D);
@@ -1404,3 +1437,22 @@ extern "C" attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16
                   workspace_bytes, stream);
 }
 
+extern "C" attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16_t* src, const float* w,
+                                              const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
+                                              uint16_t* dsrc, float* dw, void* stream) {
+  const attnres_status st = bwd_common_checks(w, N, T, D, dw);
+  if (st != ATTNRES_OK) return st;
+  if (D > ATTNRES_NOALLOC_MAX_D) return ATTNRES_ERR_WORKSPACE;  // the static partial rows hold D <= 8192
+  if (T == 0) return bwd_zero_dw(dw, D, stream);
+  if (src == nullptr || dsrc == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  void* ws = scratch_address();
+  if (ws == nullptr) return ATTNRES_ERR_HIP;
+  const uint16_t* srcs[ATTNRES_MAX_SOURCES];
+  uint16_t* dsrcs[ATTNRES_MAX_SOURCES];
+  for (int i = 0; i < N; ++i) {
+    srcs[i] = src + (size_t)i * (size_t)T * (size_t)D;
+    dsrcs[i] = dsrc + (size_t)i * (size_t)T * (size_t)D;
+  }
+  return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, reinterpret_cast<void* const*>(dsrcs), D, 0, dw, ws,
+                  ATTNRES_BWD_WORKSPACE_BYTES(D), stream);
+}

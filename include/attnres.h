@@ -226,6 +226,29 @@ attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* 
                                    int32_t D, void* const* dsrcs, int64_t dsrc_pitch, int32_t grad_mode, float* dw,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as attnres_bwd --
+ * bitwise the same dsrc and dw, from the same kernels -- except that the dw
+ * partial rows live in a static device array of the library
+ * (ATTNRES_DW_PARTIALS x ATTNRES_NOALLOC_MAX_D fp32 = 8 MiB on every device the
+ * library runs on, held until the process ends).  The call allocates nothing
+ * (no hipMalloc, no library routine that allocates).
+ *   D > ATTNRES_NOALLOC_MAX_D   ATTNRES_ERR_WORKSPACE, nothing enqueued.
+ * The first call on a device looks up that device's address of the array
+ * (ATTNRES_ERR_HIP if the runtime refuses).  Every call on a device shares its
+ * array: calls that overlap in time on one device (concurrent streams, or
+ * host threads on different streams) race on it and may return wrong dw;
+ * serialise them, or use attnres_bwd with a workspace per stream.  Nothing in
+ * the array needs to start at zero: each call writes every partial row it
+ * reads.
+ */
+#define ATTNRES_NOALLOC_MAX_D 8192
+attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
+                                   const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def test_library_loads_and_exports_declared_symbols():
     lib = ar.library()
     names = _declared()
     assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
-                     "attnres_fwd_update", "attnres_bwd_sources"]
+                     "attnres_fwd_update", "attnres_bwd_sources", "attnres_bwd_noalloc"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -52,6 +52,7 @@ def test_library_is_built_for_gfx950():
 
 
 def test_header_constants_match_binding():
+    assert _define("ATTNRES_NOALLOC_MAX_D") == ar.NOALLOC_MAX_D == 8192
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
@@ -402,3 +403,21 @@ def test_probe_library_exports_declared_symbols_and_refuses_bad_arguments():
     assert lib.attnres_probe_fwd_pattern(ptrs, 9, 16, 8200, A, None) == 1  # D > 8192
     assert lib.attnres_probe_read(A, 0, A, None) == 0              # empty: nothing to do
 
+
+def test_noalloc_backward_refuses_on_the_host():
+    """attnres_bwd_noalloc: the static partial rows hold D <= 8192, a larger D is
+    ATTNRES_ERR_WORKSPACE; the shared argument checks of attnres_bwd apply
+    first.  Nothing reaches the GPU (every call has an invalid argument)."""
+    lib = ar.library()
+    g = 1 << 30
+
+    def call(N=9, T=16, D_=D, dw=12 * g, w=3 * g, src=2 * g):
+        return lib.attnres_bwd_noalloc(1 * g, src, w, 4 * g, 5 * g, N, T, D_, 8 * g, dw, None)
+
+    assert call(D_=8200) == WORKSPACE
+    assert call(D_=16384) == WORKSPACE
+    assert call(N=10) == INVALID
+    assert call(D_=7170) == INVALID
+    assert call(dw=0) == INVALID
+    assert call(w=12 * g) == INVALID  # dw overlaps w
+    assert call(T=-1) == INVALID

@@ -1,0 +1,78 @@
+"""attnres_bwd_noalloc (through the C ABI): the backward without a workspace
+argument gives bitwise the dsources and dw of attnres_bwd with a caller
+workspace -- on two calls in a row, the second with a smaller input, so the
+static partial rows carry the first call's contents into the second -- and
+allocates no device memory."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import synth
+from parity import DEV, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_noalloc_matches_the_workspace_call_on_two_calls():
+    lib = ar.library()
+    stream = torch.cuda.current_stream().cuda_stream
+    for N, T, D in [(9, 4096, 7168), (5, 300, 1024)]:  # second call smaller: fewer partial rows, shorter rows
+        print(f"[noalloc] N={N} T={T} D={D}", flush=True)
+        wl = synth.Workload(f"noalloc_N{N}_T{T}_D{D}", T=T, N=N, D=D)
+        src = to_dev_bf16(wl.sources())
+        dout = to_dev_bf16(wl.dout())
+        w = torch.from_numpy(wl.w()).to(DEV)
+        _, rstd, alpha = ar.attnres_fwd(src, w, wl.eps)
+        ref_dsrc, ref_dw = ar.attnres_bwd(dout, src, w, rstd, alpha)
+        dsrc = torch.full_like(ref_dsrc, float("nan"))
+        dw = torch.full_like(ref_dw, float("nan"))
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        rc = lib.attnres_bwd_noalloc(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(),
+                                     alpha.data_ptr(), N, T, D, dsrc.data_ptr(), dw.data_ptr(), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        assert rc == 0
+        assert torch.cuda.memory_allocated() == before
+        assert torch.equal(_bits(dsrc), _bits(ref_dsrc))
+        assert torch.equal(_bits(dw), _bits(ref_dw))
+    # the binding's wrapper: same call, outputs passed in
+    dsrc2, dw2 = ar.attnres_bwd_noalloc(dout, src, w, rstd, alpha, torch.empty_like(ref_dsrc),
+                                        torch.empty_like(ref_dw))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(dsrc2), _bits(ref_dsrc)) and torch.equal(_bits(dw2), _bits(ref_dw))
+
+
+def test_noalloc_refuses_large_D_and_zero_fills_dw_for_empty_batches():
+    lib = ar.library()
+    D = 8200
+    src = torch.zeros((2, 4, D), dtype=torch.bfloat16, device=DEV)
+    dout = torch.zeros((4, D), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros(D, device=DEV)
+    rstd = torch.ones((4, 2), device=DEV)
+    alpha = torch.full((4, 2), 0.5, device=DEV)
+    dsrc = torch.empty_like(src)
+    dw = torch.full((D,), 7.0, device=DEV)
+    rc = lib.attnres_bwd_noalloc(dout.data_ptr(), src.data_ptr(), w.data_ptr(), rstd.data_ptr(), alpha.data_ptr(),
+                                 2, 4, D, dsrc.data_ptr(), dw.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == 2  # ATTNRES_ERR_WORKSPACE: nothing enqueued
+    assert bool((dw == 7.0).all())
+    dw0 = torch.full((1024,), 7.0, device=DEV)
+    rc = lib.attnres_bwd_noalloc(None, None, w[:1024].data_ptr(), None, None, 3, 0, 1024, None, dw0.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == 0 and bool((dw0 == 0).all())
