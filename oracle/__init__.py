@@ -16,7 +16,10 @@ Every function here is pinned by ``tests/test_oracle.py`` against finite
 differences, an independent PyTorch fp64 autograd route, hand-derived closed
 forms (``tests/golden/``) and invariants of the formula; the partial-sum
 update (``add_bf16``) against exact rational arithmetic and hand-worked
-rounding cases.
+rounding cases; the block-batched scores (``block_scores``) against PyTorch's
+fp64 ``rms_norm`` and matmul and hand-derived constant-row cases, and the
+forward from given scores (``fwd_scored``) against the plain forward and the
+two-source sigmoid closed form.
 """
 from __future__ import annotations
 
@@ -45,6 +48,10 @@ class Oracle:
             f.restype = None
         lib.oracle_add_bf16.argtypes = [i64, vp, vp, vp]
         lib.oracle_add_bf16.restype = None
+        lib.oracle_block_scores.argtypes = [i32, i64, i64, i32, vp, vp, f64, vp, vp]
+        lib.oracle_block_scores.restype = None
+        lib.oracle_fwd_scored.argtypes = [i32, i64, i64, vp, vp, vp, vp, f64, vp, vp, vp]
+        lib.oracle_fwd_scored.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -93,6 +100,37 @@ class Oracle:
         dw = np.empty(D)
         self.lib.oracle_bwd(N, T, D, _p(src_bits), _p(w), float(eps), _p(dout_bits), _p(dsrc), _p(dw))
         return dsrc, dw
+
+    def block_scores(self, src_bits: np.ndarray, W: np.ndarray, eps: float):
+        """Block-batched scores: for the n sources src [n][T][D] (bf16 bits) shared
+        by the L sub-layers of a block and their pseudo-queries W [L][D] (fp32),
+        returns (rstd [T][n], z [L][T][n]) in float64."""
+        src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        n, T, D = _shape(src_bits)
+        L = W.shape[0]
+        assert W.shape == (L, D)
+        rstd = np.empty((T, n))
+        z = np.empty((L, T, n))
+        self.lib.oracle_block_scores(n, T, D, L, _p(src_bits), _p(W), float(eps), _p(rstd), _p(z))
+        return rstd, z
+
+    def fwd_scored(self, src_bits: np.ndarray, z_given: np.ndarray, r_given: np.ndarray, w: np.ndarray, eps: float):
+        """Forward of one sub-layer from given scores: src [N][T][D] bf16 bits (the
+        partial sum last), z_given and r_given [T][N-1] for the first N-1
+        sources, w [D] fp32 for the last.  Returns (out, rstd [T][N], alpha [T][N])."""
+        src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        N, T, D = _shape(src_bits)
+        z_given = np.ascontiguousarray(z_given, dtype=np.float64).reshape(T, N - 1)
+        r_given = np.ascontiguousarray(r_given, dtype=np.float64).reshape(T, N - 1)
+        assert w.shape == (D,)
+        out = np.empty((T, D))
+        rstd = np.empty((T, N))
+        alpha = np.empty((T, N))
+        self.lib.oracle_fwd_scored(N, T, D, _p(src_bits), _p(z_given), _p(r_given), _p(w), float(eps), _p(out),
+                                   _p(rstd), _p(alpha))
+        return out, rstd, alpha
 
     def fwd_f64(self, x: np.ndarray, w: np.ndarray, eps: float):
         """Forward on float64 sources x [N][T][D] and float64 w [D]."""
@@ -157,6 +195,14 @@ def fwd_f64(x, w, eps):
 
 def bwd_f64(x, w, eps, g):
     return default().bwd_f64(x, w, eps, g)
+
+
+def block_scores(src_bits, W, eps):
+    return default().block_scores(src_bits, W, eps)
+
+
+def fwd_scored(src_bits, z_given, r_given, w, eps):
+    return default().fwd_scored(src_bits, z_given, r_given, w, eps)
 
 
 def add_bf16(p_bits, y_bits):

@@ -208,6 +208,80 @@ void oracle_bwd(int N, int64_t T, int64_t D, const uint16_t* src, const float* w
   free(wd);
 }
 
+/* ---- block-batched scores ----------------------------------------------- */
+/* The architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理" groups
+ * every 12 layers into one AttnRes block and puts the same set of sources
+ * before every alpha of a block: the embedding and the completed block sums
+ * do not change while a block runs, only the current partial sum does, and
+ * each sub-layer has its own pseudo-query.  So for those n sources the RMS
+ * statistic is the same for all L sub-layers of the block, and the L scores of
+ * each source can be formed together:
+ *
+ *   rb_ti      = 1 / sqrt(mean_d x_tid^2 + eps)
+ *   zb_{l,t,i} = sum_d W_ld (rb_ti x_tid)
+ *
+ * src: bf16 bits [n][T][D]; W: fp32 [L][D] (row l = sub-layer l's
+ * pseudo-query); rstd: [T][n]; z: [L][T][n]. */
+void oracle_block_scores(int n, int64_t T, int64_t D, int L, const uint16_t* src, const float* W, double eps,
+                         double* rstd, double* z) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int i = 0; i < n; ++i) {
+      const uint16_t* row = src + ((int64_t)i * T + t) * D;
+      double sq = 0.0;
+      for (int64_t d = 0; d < D; ++d) sq += bf16_to_f64(row[d]) * bf16_to_f64(row[d]);
+      const double rb = 1.0 / sqrt(sq / (double)D + eps);
+      rstd[t * n + i] = rb;
+      for (int l = 0; l < L; ++l) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += (double)W[(int64_t)l * D + d] * (rb * bf16_to_f64(row[d]));
+        z[((int64_t)l * T + t) * n + i] = acc;
+      }
+    }
+  }
+}
+
+/* The forward of one sub-layer whose first N-1 sources were scored by
+ * oracle_block_scores: their rstd and this sub-layer's scores are given, and
+ * only the last source -- the current block's partial sum -- is normalised
+ * and scored here with the sub-layer's w; then the softmax over all N scores
+ * and the weighted sum of all N raw sources, as in the plain forward.
+ * src: bf16 bits [N][T][D] (all N sources, the partial sum last);
+ * zg, rg: [T][N-1] given scores and rstd; outputs as oracle_fwd. */
+void oracle_fwd_scored(int N, int64_t T, int64_t D, const uint16_t* src, const double* zg, const double* rg,
+                       const float* w, double eps, double* out, double* rstd, double* alpha) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    double zs[16], rs[16], as[16];
+    for (int i = 0; i + 1 < N; ++i) {
+      zs[i] = zg[t * (N - 1) + i];
+      rs[i] = rg[t * (N - 1) + i];
+    }
+    const uint16_t* last = src + ((int64_t)(N - 1) * T + t) * D;
+    double sq = 0.0;
+    for (int64_t d = 0; d < D; ++d) sq += bf16_to_f64(last[d]) * bf16_to_f64(last[d]);
+    rs[N - 1] = 1.0 / sqrt(sq / (double)D + eps);
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += (double)w[d] * (rs[N - 1] * bf16_to_f64(last[d]));
+    zs[N - 1] = acc;
+    double top = zs[0];
+    for (int i = 1; i < N; ++i)
+      if (zs[i] > top) top = zs[i];
+    double sum = 0.0;
+    for (int i = 0; i < N; ++i) sum += exp(zs[i] - top);
+    for (int i = 0; i < N; ++i) as[i] = exp(zs[i] - top) / sum;
+    for (int64_t d = 0; d < D; ++d) {
+      double o = 0.0;
+      for (int i = 0; i < N; ++i) o += as[i] * bf16_to_f64(src[((int64_t)i * T + t) * D + d]);
+      out[t * D + d] = o;
+    }
+    for (int i = 0; i < N; ++i) {
+      rstd[t * N + i] = rs[i];
+      alpha[t * N + i] = as[i];
+    }
+  }
+}
+
 /* ---- partial-sum update ------------------------------------------------- */
 /* The architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理" lists
  * the current block's partial sum (the sum of the sub-layer outputs already

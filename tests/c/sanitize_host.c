@@ -43,6 +43,10 @@ void oracle_fwd_f64(int N, int64_t T, int64_t D, const double* x, const double* 
 void oracle_bwd_f64(int N, int64_t T, int64_t D, const double* x, const double* w, double eps, const double* g,
                     double* dx, double* dw);
 void oracle_add_bf16(int64_t n, const uint16_t* p, const uint16_t* y, uint16_t* out);
+void oracle_block_scores(int n, int64_t T, int64_t D, int L, const uint16_t* src, const float* W, double eps,
+                         double* rstd, double* z);
+void oracle_fwd_scored(int N, int64_t T, int64_t D, const uint16_t* src, const double* zg, const double* rg,
+                       const float* w, double eps, double* out, double* rstd, double* alpha);
 
 static double bf(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
@@ -97,6 +101,25 @@ static void run_oracle(void) {
   oracle_bwd_f64(N, T, D, x, wd, 1e-6, g, dx2, dw2);
   EXPECT(memcmp(out, out2, sizeof(double) * T * D) == 0);
   EXPECT(memcmp(dx, dx2, sizeof(double) * N * T * D) == 0);
+
+  /* block-batched scores of the first N-1 sources for three pseudo-queries (w
+   * the last), then the forward from those scores equals the plain forward */
+  {
+    enum { L = 3 };
+    float* W = malloc(sizeof(float) * L * D);
+    for (int l = 0; l < L; ++l) synth_normal_f32(W + l * D, D, 0, 7 + l, 0, 0.3f);
+    memcpy(W + (L - 1) * D, w, sizeof(float) * D);
+    double* rb = malloc(sizeof(double) * T * (N - 1));
+    double* zb = malloc(sizeof(double) * L * T * (N - 1));
+    double* out3 = malloc(sizeof(double) * T * D);
+    double* rstd3 = malloc(sizeof(double) * T * N);
+    double* alpha3 = malloc(sizeof(double) * T * N);
+    oracle_block_scores(N - 1, T, D, L, src, W, 1e-6, rb, zb);
+    oracle_fwd_scored(N, T, D, src, zb + (size_t)(L - 1) * T * (N - 1), rb, w, 1e-6, out3, rstd3, alpha3);
+    for (size_t k = 0; k < (size_t)T * D; ++k) EXPECT(fabs(out3[k] - out[k]) <= 1e-12 * (1.0 + fabs(out[k])));
+    for (size_t k = 0; k < (size_t)T * N; ++k) EXPECT(fabs(alpha3[k] - alpha[k]) <= 1e-12);
+    free(W); free(rb); free(zb); free(out3); free(rstd3); free(alpha3);
+  }
 
   /* bf16 add over every exponent and sign of the first operand */
   enum { M = 1 << 16 };

@@ -311,7 +311,93 @@ def pin_partial_sum_update(orc):
     return fails
 
 
-PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update]
+GOLDEN_BLOCK = os.path.join(HERE, "golden", "block_scores.json")
+
+
+def _bits_of(values) -> np.ndarray:
+    """bf16 bit patterns of values that are exact in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    b = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), f), "not exact in bf16"
+    return b
+
+
+def _random_bits(r, shape, scales):
+    """Random bf16 bit patterns, source i scaled by scales[i] (rounded to bf16 by truncation of the draw)."""
+    x = (r.standard_normal(shape) * np.asarray(scales)[:, None, None]).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_block_scores(orc):
+    """Block-batched scores: hand-derived constant-row cases; PyTorch fp64
+    rms_norm + matmul (library route); the softmax of each sub-layer's scores
+    equals the plain forward's weights for that sub-layer's pseudo-query."""
+    fails = []
+    for c in json.load(open(GOLDEN_BLOCK))["block_scores"]:
+        x = _bits_of(c["x"])[:, None, :]  # [n][1][D]
+        W = np.array(c["W"], dtype=np.float32)
+        rstd, z = orc.block_scores(x, W, c["eps"])
+        want_r = np.array(_ev(c["expect"]["rstd"]))
+        want_z = np.array(_ev(c["expect"]["z"]))  # [L][n]
+        if not np.allclose(rstd[0], want_r, rtol=1e-12, atol=1e-12):
+            fails.append(f"block golden {c['name']} rstd: {rstd[0]} vs {want_r}")
+        if not np.allclose(z[:, 0, :], want_z, rtol=1e-12, atol=1e-12):
+            fails.append(f"block golden {c['name']} z: {z[:, 0, :]} vs {want_z}")
+    for seed, (n, T, D, L, eps) in enumerate([(1, 3, 16, 2, 1e-6), (3, 5, 32, 4, 0.1), (8, 7, 64, 24, 1e-6),
+                                             (2, 4, 8, 3, 0.0)]):
+        r = _rng(300 + seed)
+        bits = _random_bits(r, (n, T, D), 1.0 + np.arange(n))
+        W = (r.standard_normal((L, D)) / math.sqrt(D) * 2.0).astype(np.float32)
+        rstd, z = orc.block_scores(bits, W, eps)
+        xt = torch.from_numpy(oracle.bf16_to_f64(bits))
+        xn = torch.nn.functional.rms_norm(xt, (D,), eps=eps)                 # [n][T][D]
+        z_t = torch.matmul(xn, torch.from_numpy(W.astype(np.float64)).T)     # [n][T][L]
+        r_t = (xn * xt).sum(-1) / (xt * xt).sum(-1)                          # the factor rms_norm applied
+        e_z = _rel(z, z_t.permute(2, 1, 0).numpy())
+        e_r = _rel(rstd, r_t.T.numpy())
+        if not (e_z < 1e-12 and e_r < 1e-12):
+            fails.append(f"block torch route n={n} T={T} D={D} L={L}: z rel {e_z:.3e}, rstd rel {e_r:.3e}")
+        for l in range(L):
+            _, _, a_plain = orc.fwd(bits, W[l], eps)
+            zz = z[l] - z[l].max(axis=1, keepdims=True)
+            a_blk = np.exp(zz) / np.exp(zz).sum(axis=1, keepdims=True)
+            if not np.allclose(a_blk, a_plain, rtol=1e-12, atol=1e-14):
+                fails.append(f"block scores of sub-layer {l} do not give the plain forward's weights")
+                break
+    return fails
+
+
+def pin_fwd_scored(orc):
+    """Forward from given scores: the two-source closed form with a given score;
+    with the scores and rstd of the first N-1 sources from block_scores, every
+    output equals the plain forward on all N sources."""
+    fails = []
+    for c in json.load(open(GOLDEN_BLOCK))["fwd_scored"]:
+        x = _bits_of(c["x"])[:, None, :]
+        zg = np.array(_ev(c["z_given"]))[None, :]
+        rg = np.array(_ev(c["r_given"]))[None, :]
+        out, rstd, alpha = orc.fwd_scored(x, zg, rg, np.array(c["w"], dtype=np.float32), c["eps"])
+        for key, got in (("alpha", alpha[0]), ("out", out[0]), ("rstd", rstd[0])):
+            want = np.array(_ev(c["expect"][key]))
+            if not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+                fails.append(f"scored golden {c['name']} {key}: {got} vs {want}")
+    for seed, (N, T, D, eps) in enumerate([(2, 3, 16, 1e-6), (5, 6, 32, 0.05), (9, 9, 64, 1e-6), (9, 4, 8, 0.0)]):
+        r = _rng(400 + seed)
+        bits = _random_bits(r, (N, T, D), np.sqrt(1.0 + 12.0 * np.arange(N)))
+        W = (r.standard_normal((3, D)) * 0.5).astype(np.float32)
+        rb, zb = orc.block_scores(bits[:N - 1], W, eps)
+        for l in range(3):
+            got = orc.fwd_scored(bits, zb[l], rb, W[l], eps)
+            want = orc.fwd(bits, W[l], eps)
+            for name, a, b in zip(("out", "rstd", "alpha"), got, want):
+                e = _rel(a, b)
+                if not e < 1e-12:
+                    fails.append(f"scored vs plain N={N} T={T} D={D} l={l} {name}: rel {e:.3e}")
+    return fails
+
+
+PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update,
+        pin_block_scores, pin_fwd_scored]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -356,6 +442,23 @@ MUTANTS = {
     "dw_drops_last_chunk": ("for (int64_t c = 0; c < nchunk; ++c)\n    for (int64_t d = 0; d < D; ++d) dw[d] += part",
                             "for (int64_t c = 0; c + 1 < nchunk; ++c)\n    for (int64_t d = 0; d < D; ++d) dw[d] += part"),
     "dout_of_token_zero": ("g[d] = bf16_to_f64(dout[t * D + d]);", "g[d] = bf16_to_f64(dout[d]);"),
+    # block-batched scores and the forward from given scores
+    "block_sum_not_mean": ("const double rb = 1.0 / sqrt(sq / (double)D + eps);",
+                           "const double rb = 1.0 / sqrt(sq + eps);"),
+    "block_eps_outside_sqrt": ("const double rb = 1.0 / sqrt(sq / (double)D + eps);",
+                               "const double rb = 1.0 / sqrt(sq / (double)D) + eps;"),
+    "block_W_transposed": ("acc += (double)W[(int64_t)l * D + d] * (rb * bf16_to_f64(row[d]));",
+                           "acc += (double)W[d * L + l] * (rb * bf16_to_f64(row[d]));"),
+    "block_score_unnormalised": ("acc += (double)W[(int64_t)l * D + d] * (rb * bf16_to_f64(row[d]));",
+                                 "acc += (double)W[(int64_t)l * D + d] * bf16_to_f64(row[d]);"),
+    "block_z_token_major": ("z[((int64_t)l * T + t) * n + i] = acc;", "z[((int64_t)t * L + l) * n + i] = acc;"),
+    "scored_first_score_everywhere": ("zs[i] = zg[t * (N - 1) + i];", "zs[i] = zg[t * (N - 1)];"),
+    "scored_rstd_not_given": ("rs[i] = rg[t * (N - 1) + i];", "rs[i] = 1.0;"),
+    "scored_last_unnormalised": ("acc += (double)w[d] * (rs[N - 1] * bf16_to_f64(last[d]));",
+                                 "acc += (double)w[d] * bf16_to_f64(last[d]);"),
+    "scored_last_is_first_source": ("const uint16_t* last = src + ((int64_t)(N - 1) * T + t) * D;",
+                                    "const uint16_t* last = src + t * D;"),
+    "scored_sum_skips_last": ("for (int i = 0; i < N; ++i) o += as[i]", "for (int i = 0; i + 1 < N; ++i) o += as[i]"),
 }
 
 
