@@ -24,6 +24,10 @@ The C entry points, declared in ``include/attnres.h``:
     attnres_bwd_noalloc: attnres_bwd without a workspace argument, for
                 callers that cannot allocate (its dw partial rows live in a
                 static device array of the library, D <= 8192).
+    attnres_block_scores / attnres_fwd_scored: the rstd and the scores of
+                all L pseudo-queries of a block against the sources its
+                sub-layers share, in one MFMA pass; then each sub-layer's
+                forward from its slice of those scores.
 """
 from __future__ import annotations
 
@@ -75,6 +79,10 @@ def library() -> ctypes.CDLL:
         lib.attnres_fwd_update.restype = ctypes.c_int
         lib.attnres_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp]
         lib.attnres_bwd_noalloc.restype = ctypes.c_int
+        lib.attnres_block_scores.argtypes = [pp, i64, vp, i32, f32, i32, i64, i32, vp, vp, vp, sz, vp]
+        lib.attnres_block_scores.restype = ctypes.c_int
+        lib.attnres_fwd_scored.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_scored.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -372,6 +380,82 @@ def attnres_fwd_update(srcs, partial: torch.Tensor, delta: torch.Tensor, w: torc
     return out, rstd, alpha, partial_out
 
 
+MAX_QUERIES = 64
+
+
+def block_scores_workspace_bytes(L: int, D: int) -> int:
+    """Bytes of device workspace attnres_block_scores needs (ATTNRES_BLOCK_SCORES_WORKSPACE_BYTES)."""
+    return 3 * ((L + 15) // 16 * 16) * ((D + 31) // 32 * 32) * 2
+
+
+def attnres_block_scores(srcs, W: torch.Tensor, eps: float, rstd=None, z=None, workspace=None, stream=None):
+    """Block-batched scores of the n sources a block's sub-layers share (n
+    [T][D] bf16 tensors or views with one row pitch) against the block's L
+    pseudo-queries W [L][D] fp32: returns (rstd [T][n] fp32, z [L][T][n] fp32),
+    z[l] being sub-layer l's scores for attnres_fwd_scored."""
+    srcs, T, D, pitch = _sources(srcs, "srcs")
+    n = len(srcs)
+    if W.dim() != 2:
+        raise ValueError("W must be [L][D]")
+    L = W.shape[0]
+    _check(W, "W", torch.float32, (L, D))
+    dev = srcs[0].device
+    if rstd is None:
+        rstd = torch.empty((T, n), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((L, T, n), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((block_scores_workspace_bytes(L, D),), dtype=torch.uint8, device=dev)
+    _check(rstd, "rstd", torch.float32, (T, n))
+    _check(z, "z", torch.float32, (L, T, n))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    _same_device(dev, W=W, rstd=rstd, z=z, workspace=workspace, **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_block_scores(_ptr_array(srcs), pitch, W.data_ptr(), L, float(eps), n, T, D,
+                                              rstd.data_ptr(), z.data_ptr(), workspace.data_ptr(),
+                                              workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    if code != 0:
+        raise AttnResError("attnres_block_scores", code)
+    return rstd, z
+
+
+def attnres_fwd_scored(srcs, z_given: torch.Tensor, rstd_given: torch.Tensor, w: torch.Tensor, eps: float, out=None,
+                       rstd=None, alpha=None, stream=None):
+    """Forward of one sub-layer from block-batched scores: srcs are the N
+    sources, the block's shared ones first and the current partial sum last;
+    z_given ([T][N-1], e.g. z[l] of attnres_block_scores) and rstd_given
+    ([T][N-1]) are the shared sources' scores and rstd; w [D] scores the
+    partial sum.  Returns (out, rstd [T][N], alpha [T][N]) like
+    attnres_fwd_sources."""
+    srcs, T, D, pitch = _sources(srcs, "srcs")
+    N = len(srcs)
+    if N < 2:
+        raise ValueError("the scored forward needs the shared sources and the partial sum (N >= 2)")
+    _check(z_given, "z_given", torch.float32, (T, N - 1))
+    _check(rstd_given, "rstd_given", torch.float32, (T, N - 1))
+    _check(w, "w", torch.float32, (D,))
+    dev = srcs[0].device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if rstd is None:
+        rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    _same_device(dev, z_given=z_given, rstd_given=rstd_given, w=w, out=out, rstd=rstd, alpha=alpha,
+                 **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_fwd_scored(_ptr_array(srcs), pitch, z_given.data_ptr(), rstd_given.data_ptr(),
+                                            w.data_ptr(), float(eps), N, T, D, out.data_ptr(), rstd.data_ptr(),
+                                            alpha.data_ptr(), _stream_handle(stream, dev))
+    if code != 0:
+        raise AttnResError("attnres_fwd_scored", code)
+    return out, rstd, alpha
+
+
 GRAD_ACCUMULATE = 1  # grad_mode bits of attnres_bwd_sources
 GRAD_F32 = 2
 
@@ -452,5 +536,6 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 
 
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
-           "attnres_fwd_update", "attnres_bwd_noalloc", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
+           "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
+           "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

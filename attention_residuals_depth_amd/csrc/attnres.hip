@@ -424,28 +424,36 @@ struct FwdCtx {
 
 // Forward of token t whose row group is already in x: partial sums, workgroup
 // reduction, softmax, weighted sum, stores.  Issues no loads of its own.
-template <int N, int VPT>
+// SCORED: the first N-1 sources arrive with their rstd and this sub-layer's
+// score already formed (block-batched scores); lane i of (rgv, zgv) holds
+// source i's.  Only the last source -- the current block's partial sum -- is
+// reduced here.  Without SCORED every source is reduced (the code is the
+// plain forward's).
+template <int N, int VPT, bool SCORED = false>
 __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& buf, const FwdCtx& c,
-                                          const Slice<VPT>& sl) {
-  // partial sum of squares (first N) and w.x (last N)
-  float part[2 * N];
+                                          const Slice<VPT>& sl, float zgv = 0.f, float rgv = 0.f) {
+  constexpr int NR = SCORED ? 1 : N;  // sources reduced here: the last NR
+  constexpr int I0 = N - NR;
+  // partial sum of squares (first NR) and w.x (last NR)
+  float part[2 * NR];
 #pragma unroll
-  for (int i = 0; i < 2 * N; ++i) part[i] = 0.f;
+  for (int i = 0; i < 2 * NR; ++i) part[i] = 0.f;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if (!sl.has(k)) continue;  // wave-uniform: no lane of this wave owns a vector k
     float wr[8];
     load8(c.wl, sl.slot[k], wr);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int ii = 0; ii < NR; ++ii) {
+      const int i = I0 + ii;
       float f[8];
       unpack8(x[i][k], f);
-      part[i] = dot8_bf16(x[i][k], x[i][k], part[i]);
+      part[ii] = dot8_bf16(x[i][k], x[i][k], part[ii]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[N + i] = fmaf(wr[e], f[e], part[N + i]);
+      for (int e = 0; e < 8; ++e) part[NR + ii] = fmaf(wr[e], f[e], part[NR + ii]);
     }
   }
-  block_sums<2 * N>(part, c.red + buf * 2 * N);
+  block_sums<2 * NR>(part, c.red + buf * 2 * N);
   buf ^= 1;
 #pragma unroll
   for (int i = 0; i < N; ++i)
@@ -464,8 +472,13 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    r[i] = uniform(__builtin_amdgcn_rsqf(part[i] * c.inv_d + c.eps));
-    a[i] = r[i] * part[N + i];  // z_i
+    if (i < I0) {  // given (SCORED only)
+      r[i] = uniform(lane_value(rgv, i));
+      a[i] = uniform(lane_value(zgv, i));
+    } else {
+      r[i] = uniform(__builtin_amdgcn_rsqf(part[i - I0] * c.inv_d + c.eps));
+      a[i] = r[i] * part[NR + i - I0];  // z_i
+    }
     m = fmaxf(m, a[i]);
   }
   float den = 0.f;
@@ -539,11 +552,23 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // read the operator makes anyway: one row fewer read per token.  In place
 // (partial_out == src.p[N-1]) is fine: a thread rewrites only the slice it
 // has already read.
-template <int N, int VPT, bool UPDATE>
+//
+// SCORED: the first N-1 sources' rstd and scores come from the block-batched
+// scores (zg, rg: [T][N-1] fp32, lane i of each wave loads source i's with the
+// row group); only the last source is reduced here.
+constexpr int kFwdPlain = 0;
+constexpr int kFwdUpdate = 1;
+constexpr int kFwdScored = 2;
+
+template <int N, int VPT, int VARIANT>
 __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src, const uint16_t* __restrict__ delta,
-                                                   uint16_t* partial_out, const float* __restrict__ w, float eps,
-                                                   int64_t t0, int32_t D, uint16_t* __restrict__ out,
+                                                   uint16_t* partial_out, const float* __restrict__ zg,
+                                                   const float* __restrict__ rg, const float* __restrict__ w,
+                                                   float eps, int64_t t0, int32_t D, uint16_t* __restrict__ out,
                                                    float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
+  constexpr bool UPDATE = VARIANT == kFwdUpdate;
+  constexpr bool SCORED = VARIANT == kFwdScored;
+  static_assert(!SCORED || N >= 2, "the scored forward has given sources and the partial sum");
   __shared__ __attribute__((aligned(16))) float red[2][2 * N][kMaxWaves];
   extern __shared__ float4 dyn_lds[];
   FwdCtx c;
@@ -566,6 +591,13 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
   uint4 yv[UPDATE ? VPT : 1];
   load_rows<N, VPT>(x, src, t, D, sl);
   if constexpr (UPDATE) load_row<VPT>(yv, delta, t, D, sl);
+  float zgv = 0.f, rgv = 0.f;
+  if constexpr (SCORED) {  // lane i: source i's given score and rstd (lanes >= N-1 read zeros)
+    const int lane = lane_id();
+    constexpr uint32_t gb = (uint32_t)(N - 1) * 4u;
+    zgv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(zg + t * (N - 1), gb), lane * 4, 0, 0));
+    rgv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(rg + t * (N - 1), gb), lane * 4, 0, 0));
+  }
   sched_fence();
   if constexpr (UPDATE) {
     const __amdgpu_buffer_rsrc_t rp = rsrc(partial_out + t * src.pitch, (uint32_t)D * 2u);  // the sources' layout
@@ -584,7 +616,196 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
   store_w<VPT>(wv, dyn_lds, sl);
   clear_absent<2 * N>(red);
   int buf = 0;
-  fwd_token<N, VPT>(x, t, buf, c, sl);
+  fwd_token<N, VPT, SCORED>(x, t, buf, c, sl, zgv, rgv);
+}
+
+// ---------------------------------------------------------------------------
+// Block-batched scores (MFMA)
+// ---------------------------------------------------------------------------
+// Every 12 layers form one AttnRes block, and the embedding and the completed
+// block sums are the same sources before every alpha of the block, while each
+// sub-layer has its own pseudo-query (architecture figure of "Kimi K3
+// 模型结构（10）：RL 与服务中的状态管理").  For those n sources the RMS
+// statistic is shared by the block's L sub-layers, and the L scores of a row
+// are one row of a skinny product [T*n x D] . [D x L]: the only dense
+// contraction on this path, so it runs on the matrix cores.
+//
+// The pseudo-queries are fp32; each is split exactly into three bf16 parts
+// (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid: 8 + 8 + 8 significand
+// bits cover fp32's 24), so the bf16 MFMA forms every product w_d x_d exactly
+// and sums in fp32 -- the same precision as the forward's fp32 dots.  Each
+// run of 16 k-steps accumulates into a fresh fp32 accumulator that is then
+// added to an fp64 running sum, which keeps the rounding error of a score at
+// a few fp32 ulps (below).
+//
+// Layout: workgroup = 4 waves x 64 rows (tokens t of one source); wave rows
+// are four 16-row MFMA tiles; per k-step of 32 channels lane l holds 8
+// channels of row l % 16 (A) and of query column l % 16 (B), both at channel
+// 32 s + 8 (l / 16), and after the loop rows 4 (l / 16) + j, column l % 16
+// of the 16 x 16 result (v_mfma_f32_16x16x32_bf16; lane layout verified on
+// the device).  Wp: the parts [3][Lpad][Dpad] bf16, zero past L and D.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef ATTNRES_BS_TILES
+#define ATTNRES_BS_TILES 4
+#endif
+#ifndef ATTNRES_BS_PREFETCH
+#define ATTNRES_BS_PREFETCH 1
+#endif
+constexpr int kBsWaves = 4;
+constexpr int kBsTiles = ATTNRES_BS_TILES;        // 16-row tiles per wave
+constexpr int kBsWaveRows = kBsTiles * 16;        // 64
+constexpr int kBsRows = kBsWaves * kBsWaveRows;   // 256 tokens per workgroup
+constexpr int kBsChunk = 16;                      // k-steps per fresh accumulator
+
+__global__ void __launch_bounds__(256) split_queries_kernel(const float* __restrict__ W, int32_t L, int32_t D,
+                                                            int32_t Lpad, int32_t Dpad, uint16_t* __restrict__ Wp) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)Lpad * Dpad;
+  if (idx >= total) return;
+  const int l = (int)(idx / Dpad), d = (int)(idx % Dpad);
+  const float w = (l < L && d < D) ? W[(int64_t)l * D + d] : 0.f;
+  const __bf16 hi = (__bf16)w;  // round to nearest even
+  const float r1 = w - (float)hi;  // exact
+  const __bf16 mid = (__bf16)r1;
+  const __bf16 lo = (__bf16)(r1 - (float)mid);  // exact: at most 8 significant bits remain
+  Wp[idx] = __builtin_bit_cast(uint16_t, hi);
+  Wp[total + idx] = __builtin_bit_cast(uint16_t, mid);
+  Wp[2 * total + idx] = __builtin_bit_cast(uint16_t, lo);
+}
+
+// Loads of one k-step: this lane's 16 bytes of each of its four rows (A) and
+// of each query part of each column tile (B).
+template <int CT>
+__device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3], __amdgpu_buffer_rsrc_t ra,
+                                        __amdgpu_buffer_rsrc_t rb, const uint32_t (&roff)[kBsTiles], int s, int q,
+                                        int r, int32_t D, int32_t Lpad, int32_t Dpad) {
+  const int ch = 32 * s + 8 * q;  // this lane's first channel
+  const uint32_t kb = (uint32_t)ch * 2u;
+#pragma unroll
+  for (int m = 0; m < kBsTiles; ++m) a[m] = bload<kAuxStreamLoad>(ra, ch < D ? roff[m] + kb : 0xFFFFFFF0u);
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) b[c][p] = bload(rb, (uint32_t)(((p * Lpad + 16 * c + r) * Dpad) * 2) + kb);
+}
+
+// One k-step: squares of the rows (exact products, fp32 sums) and the three
+// query parts into the chunk accumulators.
+template <int CT>
+__device__ __forceinline__ void bs_step(const uint4 (&a)[kBsTiles], const uint4 (&b)[CT][3],
+                                        f32x4_t (&acc)[kBsTiles][CT], float (&ss)[kBsTiles]) {
+#pragma unroll
+  for (int m = 0; m < kBsTiles; ++m) {
+    ss[m] += dot8_bf16(a[m], a[m], 0.f);
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[m]);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int p = 2; p >= 0; --p)  // lo, mid, hi
+        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][p]), acc[m][c], 0, 0,
+                                                            0);
+  }
+}
+
+// Accuracy: the scores of a peaked softmax reach |z| ~ 150, where one ulp of
+// relative error in z moves a weight by ~4e-6.  So the chunk sums (16 k-steps
+// each, fp32 MFMA accumulation) are added into fp64 running sums, the rstd
+// comes from a double-precision reciprocal square root of the fp32 sum of
+// squares, and z = rstd * dot is formed in fp64 and rounded once.
+template <int CT>  // query column tiles: L <= 16 * CT
+__global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t T, int32_t D, float eps, int32_t n,
+                                                           const uint16_t* __restrict__ Wp, int32_t L, int32_t Lpad,
+                                                           int32_t Dpad, int64_t wg_per_source,
+                                                           float* __restrict__ rstd_out, float* __restrict__ z_out) {
+  const int wave = wave_id(), lane = lane_id();
+  const int r = lane & 15, q = lane >> 4;
+  const int i = (int)(blockIdx.x / wg_per_source);
+  const int64_t tw = (int64_t)(blockIdx.x % wg_per_source) * kBsRows + wave * kBsWaveRows;  // wave's first token
+  if (tw >= T) return;  // no barrier in this kernel
+  const int64_t rows = T - tw < kBsWaveRows ? T - tw : kBsWaveRows;
+  const int64_t pitch_b = src.pitch * 2;
+  // one descriptor over the wave's rows of source i: lanes of rows past T
+  // (offset >= the size) read zeros
+  const __amdgpu_buffer_rsrc_t ra = rsrc(src.p[i] + tw * src.pitch, (uint32_t)((rows - 1) * pitch_b + (int64_t)D * 2));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(Wp, (uint32_t)(3u * (uint32_t)Lpad * (uint32_t)Dpad * 2u));
+  uint32_t roff[kBsTiles];
+#pragma unroll
+  for (int m = 0; m < kBsTiles; ++m) roff[m] = (uint32_t)((16 * m + r) * pitch_b);
+  f32x4_t acc[kBsTiles][CT];
+  double run[kBsTiles][CT][4];
+  float ss_acc[kBsTiles];
+  double ss_run[kBsTiles];
+#pragma unroll
+  for (int m = 0; m < kBsTiles; ++m) {
+    ss_run[m] = 0.0;
+    ss_acc[m] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) run[m][c][j] = 0.0;
+    }
+  }
+  auto fold = [&]() {  // chunk sums into the fp64 running sums
+#pragma unroll
+    for (int m = 0; m < kBsTiles; ++m) {
+      ss_run[m] += (double)ss_acc[m];
+      ss_acc[m] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) run[m][c][j] += (double)acc[m][c][j];
+        acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  // two register sets alternate: the loads of step s + 1 are in flight while
+  // step s runs on the matrix cores
+  const int S = Dpad / 32;
+#if !ATTNRES_BS_PREFETCH
+  for (int s = 0; s < S; ++s) {
+    uint4 a[kBsTiles], b[CT][3];
+    bs_load<CT>(a, b, ra, rb, roff, s, q, r, D, Lpad, Dpad);
+    bs_step<CT>(a, b, acc, ss_acc);
+    if (s % kBsChunk == kBsChunk - 1 || s + 1 >= S) fold();
+  }
+#else
+  uint4 a0[kBsTiles], a1[kBsTiles], b0[CT][3], b1[CT][3];
+  bs_load<CT>(a0, b0, ra, rb, roff, 0, q, r, D, Lpad, Dpad);
+  for (int s = 0; s < S; s += 2) {
+    if (s + 1 < S) bs_load<CT>(a1, b1, ra, rb, roff, s + 1, q, r, D, Lpad, Dpad);
+    sched_fence();
+    bs_step<CT>(a0, b0, acc, ss_acc);  // s is even: a chunk never ends here except at the last step
+    if (s + 1 >= S) fold();
+    if (s + 1 >= S) break;
+    if (s + 2 < S) bs_load<CT>(a0, b0, ra, rb, roff, s + 2, q, r, D, Lpad, Dpad);
+    sched_fence();
+    bs_step<CT>(a1, b1, acc, ss_acc);
+    if ((s + 1) % kBsChunk == kBsChunk - 1 || s + 2 >= S) fold();
+  }
+#endif
+  const double inv_d = 1.0 / (double)D;
+#pragma unroll
+  for (int m = 0; m < kBsTiles; ++m) {
+    // row 16 m + r: its four k groups sit in lanes r, r + 16, r + 32, r + 48
+    double ss = ss_run[m];
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const double rs = __builtin_amdgcn_rsq(ss * inv_d + (double)eps);
+    if (q == 0 && 16 * m + r < rows) rstd_out[(tw + 16 * m + r) * n + i] = (float)rs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * m + 4 * q + j;          // this lane's result row
+      const double rr = __shfl(rs, row - 16 * m);  // that row's rstd (lane row - 16 m holds it)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int col = 16 * c + r;
+        if (col < L && row < rows) z_out[((int64_t)col * T + tw + row) * n + i] = (float)(rr * run[m][c][j]);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1094,6 +1315,8 @@ struct FwdArgs {
   SrcRows src;
   const uint16_t* delta;  // update: output added to the partial sum (src.p[N-1])
   uint16_t* partial_out;  // update: the new partial sum
+  const float* zg;        // scored: given scores of the first N-1 sources, [T][N-1]
+  const float* rg;        // scored: their rstd, [T][N-1]
   const float* w;
   float eps;
   int64_t T;
@@ -1118,26 +1341,36 @@ struct BwdArgs {
 
 // One workgroup per token.  The dispatch packet counts work-items in 32 bits,
 // so very large T (possible only for tiny D) is split over several launches.
-template <int N, int VPT, bool UPDATE>
+template <int N, int VPT, int VARIANT>
 hipError_t run_fwd_vpt(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, UPDATE>);
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<N, VPT, VARIANT>);
   int64_t res = 0;
   hipError_t e = resident_blocks(fn, s.threads, s.lds, &res);  // validates the launch shape
   if (e != hipSuccess) return e;
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)s.threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_kernel<N, VPT, UPDATE>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
-                       a.delta, a.partial_out, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    hipLaunchKernelGGL((fwd_kernel<N, VPT, VARIANT>), dim3((unsigned)n), dim3((unsigned)s.threads), s.lds, st, a.src,
+                       a.delta, a.partial_out, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-template <int N, bool UPDATE>
+template <int N, int VARIANT>
 hipError_t run_fwd_n(const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
-  return s.vpt == 4 ? run_fwd_vpt<N, 4, UPDATE>(s, st, a) : run_fwd_vpt<N, 2, UPDATE>(s, st, a);
+  return s.vpt == 4 ? run_fwd_vpt<N, 4, VARIANT>(s, st, a) : run_fwd_vpt<N, 2, VARIANT>(s, st, a);
+}
+
+template <int N>
+hipError_t run_fwd_variant(int variant, const LaunchShape& s, hipStream_t st, const FwdArgs& a) {
+  if (variant == kFwdUpdate) return run_fwd_n<N, kFwdUpdate>(s, st, a);
+  if constexpr (N >= 2) {
+    if (variant == kFwdScored) return run_fwd_n<N, kFwdScored>(s, st, a);
+  }
+  if (variant == kFwdPlain) return run_fwd_n<N, kFwdPlain>(s, st, a);
+  return hipErrorInvalidValue;
 }
 
 template <int N, int VPT, bool PIPE, int MODE>
@@ -1174,17 +1407,17 @@ hipError_t run_bwd_n(const LaunchShape& s, int mode, hipStream_t st, const BwdAr
   return s.vpt == 1 ? run_bwd_vpt<N, 1>(s, mode, st, a) : run_bwd_vpt<N, 2>(s, mode, st, a);
 }
 
-hipError_t run_fwd(int32_t N, const LaunchShape& s, bool update, hipStream_t st, const FwdArgs& a) {
+hipError_t run_fwd(int32_t N, const LaunchShape& s, int variant, hipStream_t st, const FwdArgs& a) {
   switch (N) {
-    case 1: return update ? run_fwd_n<1, true>(s, st, a) : run_fwd_n<1, false>(s, st, a);
-    case 2: return update ? run_fwd_n<2, true>(s, st, a) : run_fwd_n<2, false>(s, st, a);
-    case 3: return update ? run_fwd_n<3, true>(s, st, a) : run_fwd_n<3, false>(s, st, a);
-    case 4: return update ? run_fwd_n<4, true>(s, st, a) : run_fwd_n<4, false>(s, st, a);
-    case 5: return update ? run_fwd_n<5, true>(s, st, a) : run_fwd_n<5, false>(s, st, a);
-    case 6: return update ? run_fwd_n<6, true>(s, st, a) : run_fwd_n<6, false>(s, st, a);
-    case 7: return update ? run_fwd_n<7, true>(s, st, a) : run_fwd_n<7, false>(s, st, a);
-    case 8: return update ? run_fwd_n<8, true>(s, st, a) : run_fwd_n<8, false>(s, st, a);
-    case 9: return update ? run_fwd_n<9, true>(s, st, a) : run_fwd_n<9, false>(s, st, a);
+    case 1: return run_fwd_variant<1>(variant, s, st, a);
+    case 2: return run_fwd_variant<2>(variant, s, st, a);
+    case 3: return run_fwd_variant<3>(variant, s, st, a);
+    case 4: return run_fwd_variant<4>(variant, s, st, a);
+    case 5: return run_fwd_variant<5>(variant, s, st, a);
+    case 6: return run_fwd_variant<6>(variant, s, st, a);
+    case 7: return run_fwd_variant<7>(variant, s, st, a);
+    case 8: return run_fwd_variant<8>(variant, s, st, a);
+    case 9: return run_fwd_variant<9>(variant, s, st, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1210,14 +1443,20 @@ hipError_t run_bwd(int32_t N, const LaunchShape& s, int mode, hipStream_t st, co
 // srcs: N source rows (with an update, srcs[N-1] is the partial sum before
 // it).  allow_no_state: rstd and alpha may both be NULL (decoding calls).
 // delta / partial_out: the update's addend and result, or both NULL.
+// zg / rg: the scored forward's given scores and rstd of the first N-1
+// sources ([T][N-1] fp32), or both NULL.
 attnres_status fwd_impl(const uint16_t* const* srcs, int64_t pitch, const float* w, float eps, int32_t N, int64_t T,
                         int32_t D, uint16_t* out, float* rstd, float* alpha, bool allow_no_state,
-                        const uint16_t* delta, uint16_t* partial_out, void* stream) {
+                        const uint16_t* delta, uint16_t* partial_out, void* stream, const float* zg = nullptr,
+                        const float* rg = nullptr) {
   const size_t nTD = (size_t)T * (size_t)D, nTN = (size_t)T * (size_t)N;
   const bool update = delta != nullptr || partial_out != nullptr;
+  const bool scored = zg != nullptr || rg != nullptr;
   if (update && (delta == nullptr || partial_out == nullptr)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (scored && (zg == nullptr || rg == nullptr || update || N < 2)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(zg, 4) || !aligned(rg, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  Range ins[ATTNRES_MAX_SOURCES + 2];
+  Range ins[ATTNRES_MAX_SOURCES + 4];
   SrcRows rows{};
   rows.pitch = pitch;
   for (int i = 0; i < N; ++i) {
@@ -1227,6 +1466,9 @@ attnres_status fwd_impl(const uint16_t* const* srcs, int64_t pitch, const float*
   }
   ins[N] = range_of(w, (size_t)D * 4);
   ins[N + 1] = range_of(delta, update ? nTD * 2 : 0);
+  const size_t nTG = scored ? (size_t)T * (size_t)(N - 1) * 4 : 0;
+  ins[N + 2] = range_of(zg, nTG);
+  ins[N + 3] = range_of(rg, nTG);
   if (!aligned(delta, 16) || !aligned(partial_out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   // rstd and alpha are written together or (decoding calls only) not at all
   const bool save = rstd != nullptr || alpha != nullptr;
@@ -1237,7 +1479,7 @@ attnres_status fwd_impl(const uint16_t* const* srcs, int64_t pitch, const float*
                          range_of(alpha, save ? nTN * 4 : 0),
                          rows_of(partial_out, update ? T : 0, (int64_t)D * 2, pitch * 2)};
   for (int a = 0; a < 4; ++a) {
-    for (int b = 0; b <= N + 1; ++b) {
+    for (int b = 0; b <= N + 3; ++b) {
       // the partial sum may be updated in place: exactly its own buffer
       const bool in_place = a == 3 && b == N - 1 && partial_out == srcs[N - 1];
       if (!in_place && overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -1246,9 +1488,67 @@ attnres_status fwd_impl(const uint16_t* const* srcs, int64_t pitch, const float*
       if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   const LaunchShape s = fwd_shape(D);
-  const FwdArgs args{rows, delta, partial_out, w, eps, T, D, out, rstd, alpha};
-  const hipError_t e = run_fwd(N, s, update, reinterpret_cast<hipStream_t>(stream), args);
+  const FwdArgs args{rows, delta, partial_out, zg, rg, w, eps, T, D, out, rstd, alpha};
+  const int variant = update ? kFwdUpdate : scored ? kFwdScored : kFwdPlain;
+  const hipError_t e = run_fwd(N, s, variant, reinterpret_cast<hipStream_t>(stream), args);
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
+// Block-batched scores: validate, split the queries into the workspace, run
+// the MFMA kernel.
+attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, const float* W, int32_t L, float eps,
+                                 int32_t n, int64_t T, int32_t D, float* rstd, float* z, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(n, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (L < 1 || L > ATTNRES_MAX_QUERIES) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (W == nullptr || !aligned(W, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr || rstd == nullptr || z == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(rstd, 4) || !aligned(z, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  // the wave descriptors span 64 rows: keep them inside 32-bit byte offsets
+  if (pitch > (INT64_C(1) << 24)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const size_t need = ATTNRES_BLOCK_SCORES_WORKSPACE_BYTES(L, D);
+  if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const int64_t wg_per_source = (T + kBsRows - 1) / kBsRows;
+  if (wg_per_source * n > (int64_t)UINT32_MAX / 256) return ATTNRES_ERR_INVALID_ARGUMENT;
+  Range ins[ATTNRES_MAX_SOURCES + 1];
+  SrcRows rows{};
+  rows.pitch = pitch;
+  for (int i = 0; i < n; ++i) {
+    if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    rows.p[i] = srcs[i];
+    ins[i] = rows_of(srcs[i], T, (int64_t)D * 2, pitch * 2);
+  }
+  ins[n] = range_of(W, (size_t)L * (size_t)D * 4);
+  const Range outs[3] = {range_of(rstd, (size_t)T * (size_t)n * 4), range_of(z, (size_t)L * (size_t)T * (size_t)n * 4),
+                         range_of(workspace, need)};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b <= n; ++b)
+      if (overlap(outs[a], ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  const int32_t Lpad = (L + 15) / 16 * 16, Dpad = (D + 31) / 32 * 32;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint16_t* Wp = reinterpret_cast<uint16_t*>(workspace);
+  const int64_t total = (int64_t)Lpad * Dpad;
+  hipLaunchKernelGGL(split_queries_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, W, L, D, Lpad, Dpad,
+                     Wp);
+  if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+  const dim3 grid((unsigned)(wg_per_source * n)), block(kBsWaves * kWave);
+  if (Lpad <= 16)
+    hipLaunchKernelGGL(block_scores_kernel<1>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
+                       wg_per_source, rstd, z);
+  else if (Lpad <= 32)
+    hipLaunchKernelGGL(block_scores_kernel<2>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
+                       wg_per_source, rstd, z);
+  else
+    hipLaunchKernelGGL(block_scores_kernel<4>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
+                       wg_per_source, rstd, z);
+  return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
 attnres_status fwd_common_checks(const float* w, float eps, int32_t N, int64_t T, int32_t D) {
@@ -1404,6 +1704,24 @@ extern "C" attnres_status attnres_fwd_update(const uint16_t* const* srcs, int64_
   for (int i = 0; i + 1 < N; ++i) all[i] = srcs[i];
   all[N - 1] = partial;
   return fwd_impl(all, src_pitch, w, eps, N, T, D, out, rstd, alpha, true, delta, partial_out, stream);
+}
+
+extern "C" attnres_status attnres_block_scores(const uint16_t* const* srcs, int64_t src_pitch, const float* W,
+                                               int32_t L, float eps, int32_t n, int64_t T, int32_t D, float* rstd,
+                                               float* z, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_scores_impl(srcs, src_pitch, W, L, eps, n, T, D, rstd, z, workspace, workspace_bytes, stream);
+}
+
+extern "C" attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch, const float* z_given,
+                                             const float* rstd_given, const float* w, float eps, int32_t N, int64_t T,
+                                             int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (N < 2) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr || z_given == nullptr || rstd_given == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  return fwd_impl(srcs, src_pitch, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream, z_given,
+                  rstd_given);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,

@@ -22,11 +22,15 @@ peak memory -- in bf16 storage with fp32 arithmetic.  Prints one JSON line
                 and rstd on every token, dsources on sampled tokens, dw over
                 the whole batch
 
+  block_batched_scores  one block's 24 sub-layer forwards the plain way vs
+                one block-scores pass (MFMA) plus 24 forwards from its scores
+
 Flags: --gpus (1 only), --steps, --warmup, --workload (0..4, default 3),
 --sweep (extra per-T / per-N lines with fwd and bwd timed separately and
-caches flushed between reps), --no-cpu-baseline, --no-probes,
+caches flushed between reps), --no-cpu-baseline, --no-probes, --no-block,
 --default-events (time with default HIP events instead of timing-only ones),
---decode (only the decoding-size calls, for profiles).
+--decode / --block (only the decoding-size calls / only the block-batched
+measurement, for profiles).
 """
 from __future__ import annotations
 
@@ -605,6 +609,75 @@ def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 <<
     return res
 
 
+def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: int = 7168, reps: int = 5):
+    """One block's forwards two ways (the model's last block: n = 8 shared
+    sources -- embedding and 7 completed block sums -- plus the partial sum,
+    L = 24 sub-layers): L plain per-source forwards, against one block-scores
+    pass (MFMA) followed by L forwards from those scores.  Median of `reps`
+    whole-block timings, each preceded by a 512 MiB cache flush; per-call
+    times from the same runs.  Device-side random inputs of the workload's
+    scales (values do not change the timing)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    N = n + 1
+    srcs = [(torch.randn((T, D), device=dev, generator=g) * (1 + 12 * i) ** 0.5).to(torch.bfloat16) for i in range(N)]
+    W = torch.randn((L, D), device=dev, generator=g) / D ** 0.5
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    rb = torch.empty((T, n), dtype=torch.float32, device=dev)
+    zb = torch.empty((L, T, n), dtype=torch.float32, device=dev)
+    ws = torch.empty((ar.block_scores_workspace_bytes(L, D),), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = TimingEvents(L + 2)
+
+    def plain():
+        ev.record(0, stream)
+        for l in range(L):
+            ar.attnres_fwd_sources(srcs, W[l], 1e-6, out=out, rstd=rstd, alpha=alpha)
+            ev.record(l + 1, stream)
+
+    def batched():
+        ev.record(0, stream)
+        ar.attnres_block_scores(srcs[:n], W, 1e-6, rstd=rb, z=zb, workspace=ws)
+        ev.record(1, stream)
+        for l in range(L):
+            ar.attnres_fwd_scored(srcs, zb[l], rb, W[l], 1e-6, out=out, rstd=rstd, alpha=alpha)
+            ev.record(l + 2, stream)
+
+    res = {}
+    for name, fn, last in (("plain", plain, L), ("batched", batched, L + 1)):
+        tot, first = [], []
+        for r in range(reps + 2):
+            flush.zero_()
+            fn()
+            torch.cuda.synchronize()
+            if r >= 2:
+                tot.append(ev.ms(0, last))
+                first.append(ev.ms(0, 1))
+        res[name] = (sorted(tot)[len(tot) // 2], sorted(first)[len(first) // 2])
+    ev.close()
+    plain_ms, plain_first = res["plain"]
+    batched_ms, scores_ms = res["batched"]
+    scored_ms = (batched_ms - scores_ms) / L
+    scores_bytes = T * n * (2 * D + 4) + L * T * n * 4 + 4 * L * D  # sources read; rstd, z written; W read
+    fwd_bytes = T * (2 * N * D + 2 * D + 8 * N) + 4 * D
+    scored_bytes = fwd_bytes + T * (N - 1) * 8  # + the given scores and rstd
+    rec = {"T": T, "n_shared": n, "N": N, "L": L, "D": D,
+           "plain_block_ms": plain_ms, "batched_block_ms": batched_ms, "batched_vs_plain": plain_ms / batched_ms,
+           "plain_fwd_ms": plain_ms / L, "first_plain_fwd_ms": plain_first,
+           "block_scores_ms": scores_ms, "block_scores_GBps": scores_bytes / scores_ms / 1e6,
+           "block_scores_TFLOPs": 2.0 * T * n * D * L / scores_ms / 1e9,
+           "block_scores_mfma_TFLOPs": 2.0 * T * n * D * (16 * ((L + 15) // 16)) * 3 / scores_ms / 1e9,
+           "scored_fwd_ms": scored_ms, "scored_fwd_GBps": scored_bytes / scored_ms / 1e6,
+           "plain_fwd_GBps": fwd_bytes / (plain_ms / L) / 1e6,
+           "reps": f"median of {reps}, 512 MiB flush before each block"}
+    del srcs, W, out, rstd, alpha, rb, zb, ws, flush
+    torch.cuda.empty_cache()
+    return rec
+
+
 def flushed_calls(torch, dev, fwd, bwd, reps: int = 10):
     """Median event times of fwd and of bwd, each preceded by a 512 MiB write
     that evicts the L2 and the 256 MB Infinity Cache."""
@@ -630,6 +703,9 @@ def main():
                          "timing-only events, for comparison")
     ap.add_argument("--decode", action="store_true",
                     help="only the decoding-size forward calls (T = 1..1024), for latency profiles")
+    ap.add_argument("--block", action="store_true",
+                    help="only the block-batched scores measurement (one JSON line), for profiles")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-batched scores measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the operator is token-local and the library has no "
@@ -646,6 +722,9 @@ def main():
     ar.library()
     if args.decode:
         sweep_decode(ar, torch, dev, torch.empty(512 << 20, dtype=torch.uint8, device=dev))
+        return
+    if args.block:
+        print(json.dumps({"block_batched_scores": block_batched(ar, torch, dev)}), flush=True)
         return
     wl = synth.workload(args.workload, N=9 if args.workload == 2 else None)
     T, N, D = wl.T, wl.N, wl.D
@@ -678,6 +757,10 @@ def main():
     if not args.no_probes:
         log("bandwidth ceilings (probe kernels)")
         ceil = ceilings(torch, dev, src, dout, out, dsrc)
+    blk = None
+    if not args.no_block:
+        log("block-batched scores vs plain forwards (T=32768, 8 shared sources, 24 sub-layers)")
+        blk = block_batched(ar, torch, dev)
 
     ms_step = total_ms / args.steps
     fb, bb, fe, be = algo_bytes(T, N, D)
@@ -717,6 +800,7 @@ def main():
         "peak_alloc_GiB": peak_gib,
         "pages_peak_alloc_GiB_at_128K": PAGES_PEAK_GIB_128K,
         "ceilings_GBps": ceil,
+        "block_batched_scores": blk,
         "roofline": {
             "kernel": "attnres_bwd (bwd_kernel + dw_reduce_kernel, one call)",
             "bound": "hbm",

@@ -227,6 +227,56 @@ attnres_status attnres_bwd_sources(const uint16_t* dout, const uint16_t* const* 
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-batched scores.  Every 12 layers form one AttnRes block, and the same
+ * set of sources stands before every alpha of the block: the embedding and
+ * the completed block sums do not change while the block runs (only the
+ * current partial sum does), and each sub-layer has its own pseudo-query w_l
+ * (architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理").  For
+ * those n sources this call forms, in one pass over them, their rstd and the
+ * scores of all L pseudo-queries of the block:
+ *     rstd[t][i]  = 1 / sqrt(mean_d x[i][t][d]^2 + eps)
+ *     z[l][t][i]  = rstd[t][i] * sum_d W[l][d] x[i][t][d]
+ * Each sub-layer's forward then takes its slice z[l] through
+ * attnres_fwd_scored and reduces only the partial sum.  The product
+ * [T*n x D] . [D x L] runs on the matrix cores (bf16 MFMA on an exact
+ * three-part bf16 split of each fp32 pseudo-query, fp32 accumulation).
+ *   srcs, src_pitch  the n sources as in attnres_fwd_sources (src_pitch <=
+ *                    2^24 elements).
+ *   W      [L][D] fp32   the block's pseudo-queries, 16-byte aligned
+ *   L      1 .. ATTNRES_MAX_QUERIES
+ *   eps, T, D        as attnres_fwd; n = 1 .. ATTNRES_MAX_SOURCES
+ *   rstd   [T][n] fp32, z [L][T][n] fp32   outputs (4-byte aligned)
+ *   workspace        at least ATTNRES_BLOCK_SCORES_WORKSPACE_BYTES(L, D)
+ *                    bytes of device scratch, 16-byte aligned (the split
+ *                    queries); contents on entry ignored, on exit unspecified.
+ * Outputs and workspace must not overlap each other or any input.  T == 0:
+ * nothing is enqueued.  Results are within fp32 rounding of the forward's own
+ * rstd and scores (the summation order differs), not bitwise equal to them.
+ */
+#define ATTNRES_MAX_QUERIES 64
+#define ATTNRES_BLOCK_SCORES_WORKSPACE_BYTES(L, D) \
+  ((size_t)3 * (size_t)(((L) + 15) / 16 * 16) * (size_t)(((D) + 31) / 32 * 32) * 2)
+attnres_status attnres_block_scores(const uint16_t* const* srcs, int64_t src_pitch, const float* W, int32_t L,
+                                    float eps, int32_t n, int64_t T, int32_t D, float* rstd, float* z,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward of one sub-layer from block-batched scores: the first N-1 sources
+ * are the block's shared sources, whose rstd and this sub-layer's scores come
+ * from attnres_block_scores (rstd_given = its rstd, z_given = its z + l*T*(N-1)
+ * for sub-layer l, both [T][N-1] fp32, 4-byte aligned); the last source is the
+ * current block's partial sum, normalised and scored here with w.  Then the
+ * softmax over all N scores and the weighted sum of all N raw sources, as
+ * attnres_fwd_sources (same outputs; rstd[t][i] = rstd_given[t][i] for
+ * i < N-1).  N = 2 .. ATTNRES_MAX_SOURCES; other arguments as
+ * attnres_fwd_sources.  The backward is attnres_bwd_sources with these
+ * outputs.
+ */
+attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch, const float* z_given,
+                                  const float* rstd_given, const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                                  uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
  * Backward without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments, results and errors as attnres_bwd --

@@ -36,7 +36,8 @@ def test_library_loads_and_exports_declared_symbols():
     lib = ar.library()
     names = _declared()
     assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
-                     "attnres_fwd_update", "attnres_bwd_sources", "attnres_bwd_noalloc"]
+                     "attnres_fwd_update", "attnres_bwd_sources", "attnres_block_scores", "attnres_fwd_scored",
+                     "attnres_bwd_noalloc"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -49,6 +50,41 @@ def test_library_is_built_for_gfx950():
     # the offload bundle of a library built here names its target triple
     blob = open(ar.LIB_PATH, "rb").read()
     assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_block_scores_refuses_on_the_host():
+    """attnres_block_scores / attnres_fwd_scored: every call below has one bad
+    argument and returns its status before anything reaches the GPU."""
+    lib = ar.library()
+    g = 1 << 30
+    srcs = (ctypes.c_void_p * 9)(*[(i + 1) * g for i in range(9)])
+    ws = ar.block_scores_workspace_bytes(24, D)
+
+    def blk(n=8, T=16, D_=D, L=24, W=20 * g, eps=1e-6, rstd=21 * g, z=22 * g, w_=23 * g, wsb=None, pitch=None,
+            s=srcs):
+        return lib.attnres_block_scores(s, D_ if pitch is None else pitch, W, L, eps, n, T, D_, rstd, z, w_,
+                                        ws if wsb is None else wsb, None)
+
+    assert _define("ATTNRES_MAX_QUERIES") == ar.MAX_QUERIES == 64
+    assert blk(L=0) == INVALID and blk(L=65) == INVALID
+    assert blk(n=0) == INVALID and blk(n=10) == INVALID
+    assert blk(D_=7170) == INVALID and blk(eps=-1.0) == INVALID and blk(eps=float("nan")) == INVALID
+    assert blk(W=20 * g + 4) == INVALID                    # W not 16-byte aligned
+    assert blk(rstd=0) == INVALID and blk(z=21 * g + 2) == INVALID
+    assert blk(wsb=ws - 16) == WORKSPACE and blk(w_=0) == WORKSPACE
+    assert blk(z=1 * g) == INVALID                         # z overlaps source 0
+    assert blk(rstd=20 * g) == INVALID                     # rstd overlaps W
+    assert blk(pitch=D - 8) == INVALID and blk(pitch=(1 << 24) + 8) == INVALID
+    assert blk(T=0, s=None, rstd=0, z=0, w_=0) == OK       # empty: nothing to do
+
+    def scored(N=9, T=16, D_=D, zg=30 * g, rg=31 * g, w=32 * g, out=33 * g, rstd=34 * g, alpha=35 * g):
+        return lib.attnres_fwd_scored(srcs, D_, zg, rg, w, 1e-6, N, T, D_, out, rstd, alpha, None)
+
+    assert scored(N=1) == INVALID                          # no shared source
+    assert scored(zg=0) == INVALID and scored(rg=0) == INVALID
+    assert scored(zg=30 * g + 2) == INVALID                # misaligned
+    assert scored(out=30 * g) == INVALID                   # out overlaps the given scores
+    assert scored(rstd=31 * g) == INVALID                  # rstd overlaps the given rstd
 
 
 def test_header_constants_match_binding():
