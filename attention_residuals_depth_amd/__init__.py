@@ -87,9 +87,19 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def workspace_bytes(D: int) -> int:
-    """Bytes of device workspace attnres_bwd needs (ATTNRES_BWD_WORKSPACE_BYTES)."""
-    return DW_PARTIALS * D * 4
+SPLIT_MAX_D = 8192
+SPLIT_TOKENS = 4
+SPLIT_RING = 4096
+
+
+def workspace_bytes(T: int, N: int, D: int) -> int:
+    """Bytes of device workspace attnres_bwd / attnres_bwd_sources need
+    (ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)): the dw partial rows and, for
+    D <= 8192, the split backward's exchange ring and per-group partial rows."""
+    b = DW_PARTIALS * D * 4
+    if D <= SPLIT_MAX_D:
+        b += SPLIT_RING * ((D + 1023) // 1024) * 2 * N * 8 + ((T + SPLIT_TOKENS - 1) // SPLIT_TOKENS) * D * 4
+    return b
 
 
 def _stream_handle(stream, dev: torch.device) -> int:
@@ -172,7 +182,7 @@ def attnres_bwd(dout: torch.Tensor, src: torch.Tensor, w: torch.Tensor, rstd: to
     if dw is None:
         dw = torch.empty((D,), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty((workspace_bytes(D),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((workspace_bytes(T, N, D),), dtype=torch.uint8, device=dev)
     _check(dsrc, "dsrc", torch.bfloat16, (N, T, D))
     _check(dw, "dw", torch.float32, (D,))
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
@@ -490,7 +500,7 @@ def attnres_bwd_sources(dout: torch.Tensor, srcs, w: torch.Tensor, rstd: torch.T
     if dw is None:
         dw = torch.empty((D,), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty((workspace_bytes(D),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((workspace_bytes(T, N, D),), dtype=torch.uint8, device=dev)
     _check(dw, "dw", torch.float32, (D,))
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
@@ -538,4 +548,5 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
            "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
+           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

@@ -1173,6 +1173,359 @@ __global__ void __launch_bounds__(kReduceThreads) dw_reduce_kernel(const float4*
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward with tokens split over workgroups (D <= 8192)
+// ---------------------------------------------------------------------------
+// Each token's D channels are cut into K slices of 128 16-byte vectors, and a
+// workgroup takes one slice of ATTNRES_SPLIT_TOKENS consecutive tokens side
+// by side (4 x 128 threads, one vector per thread): workgroup b = span * K +
+// slice.  Measured on MI355X, the memory system moves the backward's 19 row
+// streams faster when each token is spread over K short-lived workgroups than
+// when one workgroup walks whole tokens (5.4-5.8 vs 5.1-5.4 TB/s over
+// 32K-256K tokens at N = 9, D = 7168), and 512-thread workgroups (two per CU
+// at this kernel's register use) beat 1024-thread ones, whose tails leave
+// the CU idle, and workgroups that walk two or four such spans in turn.
+//
+// The per-token sums g.x_i and w.x_i then span K workgroups.  Each member
+// publishes its slice's 2N partial sums as 64-bit {tag, value} words in a
+// ring indexed by token (tag = token + 1; the ring is zeroed by the host
+// before the launch), agent-scope relaxed atomics, and reads the other
+// members' words, spinning with a bound.  Members are consecutive workgroups,
+// dispatched together, and walk their rounds in step.  Should a word not
+// arrive within the bound (a member not resident, e.g. the device shared with
+// other work), the waiting workgroup recomputes that member's partial sums
+// from HBM with the same per-slice reduction tree, so the result does not
+// depend on which route was taken.  The totals are the K partials added in
+// member order: every token's reduction tree depends only on (N, D), as in
+// the other kernels.
+//
+// dw: the workgroup sums its tokens' contributions to its slice in side
+// order and writes one partial row slice; ceil(T / ATTNRES_SPLIT_TOKENS)
+// partial rows are then summed in a fixed two-level order (dw_fold_kernel,
+// dw_reduce_kernel).  No atomics touch dw.
+constexpr int kSpSliceVectors = 128;                        // vectors (threads) per slice
+constexpr int kSpSide = ATTNRES_SPLIT_TOKENS;               // tokens side by side
+constexpr int kSpThreads = kSpSliceVectors * kSpSide;       // 512
+constexpr int kSpRing = ATTNRES_SPLIT_RING;                 // exchange ring, tokens
+constexpr int kSpMaxSlices = ATTNRES_SPLIT_MAX_D / 8 / kSpSliceVectors;  // 8
+constexpr int kSpSpin = 4096;                               // polls before a word is recomputed
+static_assert(kSpRing % kSpSide == 0, "ring of whole spans");
+
+struct SplitArgs {
+  const uint16_t* dout;
+  SrcRows src;
+  const float* w;
+  const float* rstd;
+  const float* alpha;
+  int64_t T;
+  int32_t D;
+  int32_t K;  // slices per row
+  DstRows dsrc;
+  uint64_t* ring;   // [kSpRing][K][2N] words
+  float* partial;   // [ceil(T / ATTNRES_SPLIT_TOKENS)][D]
+  int64_t s0;       // first token span of this launch
+};
+
+// This thread's partial g.x_i and w.x_i over its vector of source i: v_dot2
+// on the bf16 pairs, fp32 FMAs for w (the plain backward's per-thread
+// arithmetic).  Used by both routes to a member's partial sums, so they agree
+// bit for bit.
+__device__ __forceinline__ void split_partial(float& gx, float& wx, const uint4& x, const uint4& g,
+                                              const float (&wr)[8]) {
+  float f[8];
+  unpack8(x, f);
+  gx = dot8_bf16(g, x, 0.f);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a = fmaf(wr[e], f[e], a);
+  wx = a;
+}
+
+template <int N>
+__device__ __forceinline__ void split_partials(float (&part)[2 * N], const uint4 (&x)[N], const uint4& g,
+                                               const float (&wr)[8]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) split_partial(part[i], part[N + i], x[i], g, wr);
+}
+
+// Wave sums of part[], complete in lane 63, into red[side][half][j].
+template <int N>
+__device__ __forceinline__ void split_wave_sums(float (&part)[2 * N], float (*red)[2][2 * N], int side, int half) {
+#pragma unroll
+  for (int j = 0; j < 2 * N; ++j) part[j] = wave_sum_lane63(part[j]);
+  if (lane_id() == kWave - 1) {
+#pragma unroll
+    for (int j = 0; j < 2 * N; ++j) red[side][half][j] = part[j];
+  }
+}
+
+template <int N, int MODE>
+__global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
+  constexpr bool ACC = (MODE & kGradAccumulate) != 0;
+  constexpr bool F32 = (MODE & kGradF32) != 0;
+  constexpr int OW = F32 ? 2 : 1;
+  constexpr int H = F32 ? (N + 1) / 2 : N;  // accumulating: old gradients of the first H sources early
+  __shared__ float red[kSpSide][2][2 * N];                                  // per-wave sums
+  __shared__ float words[kSpSide][kSpMaxSlices][2 * N];                     // the K members' partials
+  __shared__ float tot[kSpSide][2 * N];
+  __shared__ int redo[kSpSide][kSpMaxSlices];                               // members to recompute
+  __shared__ int any_redo;
+  __shared__ __attribute__((aligned(16))) float4 dws[kSpSide][kSpSliceVectors][2];
+
+  const int tid = threadIdx.x;
+  // a side is two whole waves: its index is wave-uniform, and saying so keeps
+  // every token address (and the buffer descriptors made from it) scalar
+  const int side = __builtin_amdgcn_readfirstlane(tid / kSpSliceVectors);
+  const int tl = tid % kSpSliceVectors;
+  const int half = __builtin_amdgcn_readfirstlane(tl / kWave);  // wave within the side
+  const int K = a.K;
+  const int64_t span = a.s0 + blockIdx.x / K;
+  const int k = (int)(blockIdx.x % K);
+  const int32_t D = a.D;
+  const int V = D / 8;
+  const int v = k * kSpSliceVectors + tl;
+  const uint32_t off = v < V ? (uint32_t)v * 16u : 0xFFFFFFF0u;  // past the row: zeros, stores dropped
+
+  // this thread's 8 elements of w (the slice is read by every side: L2 hits)
+  float wr[8];
+  {
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, (uint32_t)D * 4u);
+    const uint4 w0 = bload(rw, 2u * off), w1 = bload(rw, 2u * off + 16u);
+    wr[0] = __builtin_bit_cast(float, w0.x); wr[1] = __builtin_bit_cast(float, w0.y);
+    wr[2] = __builtin_bit_cast(float, w0.z); wr[3] = __builtin_bit_cast(float, w0.w);
+    wr[4] = __builtin_bit_cast(float, w1.x); wr[5] = __builtin_bit_cast(float, w1.y);
+    wr[6] = __builtin_bit_cast(float, w1.z); wr[7] = __builtin_bit_cast(float, w1.w);
+  }
+
+  const int64_t t = span * kSpSide + side;
+  const bool valid = t < a.T;  // uniform over the side's two waves
+  const int64_t tt = valid ? t : 0;
+  const uint32_t row_bytes = valid ? (uint32_t)D * 2u : 0u;
+
+  // this side's rows, dout, and the saved alpha / rstd (lane i: source i) of its token
+  uint4 g = bload<kAuxStreamLoad>(rsrc(a.dout + tt * D, row_bytes), off);
+  uint4 x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = bload<kAuxStreamLoad>(rsrc(a.src.p[i] + tt * a.src.pitch, row_bytes), off);
+  float sa, sr;
+  load_saved<N>(sa, sr, a.alpha, a.rstd, t, valid);
+  sched_fence();
+  if (tid < kSpSide * kSpMaxSlices) redo[tid / kSpMaxSlices][tid % kSpMaxSlices] = 0;
+  if (tid == 0) any_redo = 0;
+
+  // this member's partial sums of its slice
+  float part[2 * N];
+  split_partials<N>(part, x, g, wr);
+  split_wave_sums<N>(part, red, side, half);
+  __syncthreads();
+  uint64_t* ring = a.ring + (t % kSpRing) * (int64_t)K * (2 * N);
+  const uint32_t tag = (uint32_t)t + 1u;
+  if (valid && tl < 2 * N) {
+    const float p = red[side][0][tl] + red[side][1][tl];
+    const uint64_t word = ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, p);
+    __hip_atomic_store(ring + k * (2 * N) + tl, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the K members' words, member by member (this one's included)
+  if (valid) {
+    for (int q = tl; q < K * 2 * N; q += kSpSliceVectors) {
+      uint64_t word = 0;
+      bool got = false;
+      for (int n = 0; n < kSpSpin; ++n) {
+        word = __hip_atomic_load(ring + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(word >> 32) == tag) {
+          got = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      words[side][q / (2 * N)][q % (2 * N)] = __builtin_bit_cast(float, (uint32_t)word);
+      if (!got) {
+        redo[side][q / (2 * N)] = 1;
+        any_redo = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (any_redo) {
+    // recompute the missing members' partial sums from HBM, with the
+    // member's own per-thread arithmetic and wave tree: every side runs the
+    // loop (its barriers are workgroup-wide), only sides missing member m load
+    for (int m = 0; m < K; ++m) {
+      const bool mine = redo[side][m] != 0;
+      float pm[2 * N];
+      if (mine) {  // source by source: one row of member m in registers at a time
+        const int vm = m * kSpSliceVectors + tl;
+        const uint32_t om = vm < V ? (uint32_t)vm * 16u : 0xFFFFFFF0u;
+        const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, (uint32_t)D * 4u);
+        const uint4 wa = bload(rw, 2u * om), wb = bload(rw, 2u * om + 16u);
+        const float wm[8] = {__builtin_bit_cast(float, wa.x), __builtin_bit_cast(float, wa.y),
+                             __builtin_bit_cast(float, wa.z), __builtin_bit_cast(float, wa.w),
+                             __builtin_bit_cast(float, wb.x), __builtin_bit_cast(float, wb.y),
+                             __builtin_bit_cast(float, wb.z), __builtin_bit_cast(float, wb.w)};
+        const uint4 gm = bload(rsrc(a.dout + tt * D, row_bytes), om);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const uint4 xm = bload(rsrc(a.src.p[i] + tt * a.src.pitch, row_bytes), om);
+          split_partial(pm[i], pm[N + i], xm, gm, wm);
+        }
+        split_wave_sums<N>(pm, red, side, half);
+      }
+      __syncthreads();
+      if (mine && tl < 2 * N) words[side][m][tl] = red[side][0][tl] + red[side][1][tl];
+      __syncthreads();
+    }
+    // this route is rare: the side's own rows are loaded again instead of
+    // being held in registers across the recomputation
+    g = bload<kAuxStreamLoad>(rsrc(a.dout + tt * D, row_bytes), off);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = bload<kAuxStreamLoad>(rsrc(a.src.p[i] + tt * a.src.pitch, row_bytes), off);
+  }
+  // the token's totals: the K partials in member order
+  if (tl < 2 * N) {
+    float s = 0.f;
+    for (int m = 0; m < K; ++m) s += words[side][m][tl];
+    tot[side][tl] = valid ? s : 0.f;
+  }
+  __syncthreads();
+
+  // accumulating: old gradients of the first H sources (the rest after the
+  // first H are stored, in the registers those sources free)
+  uint4 old[ACC ? H : 1][OW];
+  if constexpr (ACC) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const __amdgpu_buffer_rsrc_t r = grad_row<F32>(a.dsrc, i, tt, valid ? D : 0);
+      if constexpr (F32) {
+        old[i][0] = bload(r, 2u * off);
+        old[i][OW - 1] = bload(r, 2u * off + 16u);
+      } else {
+        old[i][0] = bload<kAuxStreamLoad>(r, off);
+      }
+    }
+  }
+
+  // softmax backward (every lane evaluates the N-value formulas, as the other kernels)
+  // (the side's two waves hold the same token: these values are wave-uniform)
+  float al[N], c1[N], kx[N], da[N];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    al[i] = lane_value(sa, i);
+    da[i] = uniform(tot[side][i]);
+    s = fmaf(al[i], da[i], s);
+  }
+  const float inv_d = 1.0f / (float)D;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float rs = lane_value(sr, i);
+    const float dz = al[i] * (da[i] - s);
+    const float z = rs * uniform(tot[side][N + i]);
+    // dx_id = alpha_i g_d + c1 (w_d - kx x_id): the bracket is formed first, so
+    // no intermediate carries rstd^2 (see the plain backward)
+    c1[i] = uniform(dz * rs);           // coefficient of the bracket in dx and of x_id in dw
+    kx[i] = uniform(z * rs * inv_d);    // coefficient of x_id inside the bracket
+    al[i] = uniform(al[i]);
+  }
+
+  // dsources and this token's dw contribution (none from a token past T)
+  float gf[8], dwr[8];
+  unpack8(g, gf);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dwr[e] = 0.f;
+  uint4 rest[(ACC && H < N) ? N - H : 1][OW];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (ACC && H < N) {
+      if (i == H) {
+        sched_fence();
+#pragma unroll
+        for (int j = H; j < N; ++j) {
+          const __amdgpu_buffer_rsrc_t r = grad_row<F32>(a.dsrc, j, tt, valid ? D : 0);
+          rest[j - H][0] = bload(r, 2u * off);
+          rest[j - H][OW - 1] = bload(r, 2u * off + 16u);
+        }
+        sched_fence();
+      }
+    }
+    float f[8], d[8];
+    unpack8(x[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      d[e] = fmaf(c1[i], fmaf(-kx[i], f[e], wr[e]), al[i] * gf[e]);
+      dwr[e] = valid ? fmaf(c1[i], f[e], dwr[e]) : dwr[e];
+    }
+    if constexpr (ACC) {
+      float o[8];
+      if constexpr (F32) {
+        const uint4& p0 = i < H ? old[i < H ? i : 0][0] : rest[i < H ? 0 : i - H][0];
+        const uint4& p1 = i < H ? old[i < H ? i : 0][OW - 1] : rest[i < H ? 0 : i - H][OW - 1];
+        o[0] = __builtin_bit_cast(float, p0.x); o[1] = __builtin_bit_cast(float, p0.y);
+        o[2] = __builtin_bit_cast(float, p0.z); o[3] = __builtin_bit_cast(float, p0.w);
+        o[4] = __builtin_bit_cast(float, p1.x); o[5] = __builtin_bit_cast(float, p1.y);
+        o[6] = __builtin_bit_cast(float, p1.z); o[7] = __builtin_bit_cast(float, p1.w);
+      } else {
+        unpack8(old[i][0], o);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = o[e] + d[e];
+    }
+    if (valid) {
+      const __amdgpu_buffer_rsrc_t rd = grad_row<F32>(a.dsrc, i, t, D);
+      if constexpr (F32) {
+        bstore(rd, 2u * off, make_uint4(__builtin_bit_cast(uint32_t, d[0]), __builtin_bit_cast(uint32_t, d[1]),
+                                        __builtin_bit_cast(uint32_t, d[2]), __builtin_bit_cast(uint32_t, d[3])));
+        bstore(rd, 2u * off + 16u, make_uint4(__builtin_bit_cast(uint32_t, d[4]), __builtin_bit_cast(uint32_t, d[5]),
+                                              __builtin_bit_cast(uint32_t, d[6]), __builtin_bit_cast(uint32_t, d[7])));
+      } else {
+        bstore<kAuxStreamStore>(rd, off, pack8(d));
+      }
+    }
+  }
+  // dw: this slice's sum over the workgroup's tokens, in side order
+  dws[side][tl][0] = make_float4(dwr[0], dwr[1], dwr[2], dwr[3]);
+  dws[side][tl][1] = make_float4(dwr[4], dwr[5], dwr[6], dwr[7]);
+  __syncthreads();
+  if (side == 0) {
+    float4 s0 = dws[0][tl][0], s1 = dws[0][tl][1];
+#pragma unroll
+    for (int q = 1; q < kSpSide; ++q) {
+      const float4 u0 = dws[q][tl][0], u1 = dws[q][tl][1];
+      s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+      s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+    }
+    const __amdgpu_buffer_rsrc_t rp = rsrc(a.partial + span * D, (uint32_t)D * 4u);
+    bstore(rp, 2u * off, __builtin_bit_cast(uint4, s0));
+    bstore(rp, 2u * off + 16u, __builtin_bit_cast(uint4, s1));
+  }
+}
+
+// dw stage 2a: rows [b * R, (b + 1) * R) of the partial rows summed in row
+// order into fold row b; thread c owns float4 column c of its column block.
+constexpr int kFoldCols = 256;  // float4 columns per workgroup
+__global__ void __launch_bounds__(kFoldCols) dw_fold_kernel(const float4* __restrict__ partial, int64_t rows,
+                                                            int64_t rows_per_fold, int32_t D4,
+                                                            float4* __restrict__ fold) {
+  const int c = blockIdx.y * kFoldCols + threadIdx.x;
+  if (c >= D4) return;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_fold;
+  const int64_t r1 = r0 + rows_per_fold < rows ? r0 + rows_per_fold : rows;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {  // four loads in flight, added in row order
+    const float4 u0 = partial[r * D4 + c], u1 = partial[(r + 1) * D4 + c];
+    const float4 u2 = partial[(r + 2) * D4 + c], u3 = partial[(r + 3) * D4 + c];
+    s.x += u0.x; s.y += u0.y; s.z += u0.z; s.w += u0.w;
+    s.x += u1.x; s.y += u1.y; s.z += u1.z; s.w += u1.w;
+    s.x += u2.x; s.y += u2.y; s.z += u2.z; s.w += u2.w;
+    s.x += u3.x; s.y += u3.y; s.z += u3.z; s.w += u3.w;
+  }
+  for (; r < r1; ++r) {
+    const float4 u = partial[r * D4 + c];
+    s.x += u.x; s.y += u.y; s.z += u.z; s.w += u.w;
+  }
+  fold[(int64_t)blockIdx.x * D4 + c] = s;
+}
+
 __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1422,6 +1775,50 @@ hipError_t run_fwd(int32_t N, const LaunchShape& s, int variant, hipStream_t st,
   }
 }
 
+template <int N, int MODE>
+hipError_t launch_split_n(hipStream_t st, SplitArgs a, int64_t groups) {
+  const void* fn = reinterpret_cast<const void*>(&bwd_split_kernel<N, MODE>);
+  int64_t res = 0;
+  hipError_t e = resident_blocks(fn, kSpThreads, 0, &res);  // validates the launch shape
+  if (e != hipSuccess) return e;
+  // the dispatch packet counts work-items in 32 bits
+  const int64_t per_launch = (int64_t)(UINT32_MAX / kSpThreads) / a.K;
+  for (int64_t g0 = 0; g0 < groups; g0 += per_launch) {
+    const int64_t n = groups - g0 < per_launch ? groups - g0 : per_launch;
+    a.s0 = g0;
+    hipLaunchKernelGGL((bwd_split_kernel<N, MODE>), dim3((unsigned)(n * a.K)), dim3(kSpThreads), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int N>
+hipError_t run_split_n(int mode, hipStream_t st, const SplitArgs& a, int64_t groups) {
+  switch (mode) {
+    case 0: return launch_split_n<N, 0>(st, a, groups);
+    case kGradAccumulate: return launch_split_n<N, kGradAccumulate>(st, a, groups);
+    case kGradF32: return launch_split_n<N, kGradF32>(st, a, groups);
+    case kGradF32 | kGradAccumulate: return launch_split_n<N, kGradF32 | kGradAccumulate>(st, a, groups);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t run_split(int32_t N, int mode, hipStream_t st, const SplitArgs& a, int64_t groups) {
+  switch (N) {
+    case 1: return run_split_n<1>(mode, st, a, groups);
+    case 2: return run_split_n<2>(mode, st, a, groups);
+    case 3: return run_split_n<3>(mode, st, a, groups);
+    case 4: return run_split_n<4>(mode, st, a, groups);
+    case 5: return run_split_n<5>(mode, st, a, groups);
+    case 6: return run_split_n<6>(mode, st, a, groups);
+    case 7: return run_split_n<7>(mode, st, a, groups);
+    case 8: return run_split_n<8>(mode, st, a, groups);
+    case 9: return run_split_n<9>(mode, st, a, groups);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t run_bwd(int32_t N, const LaunchShape& s, int mode, hipStream_t st, const BwdArgs& a) {
   switch (N) {
     case 1: return run_bwd_n<1>(s, mode, st, a);
@@ -1572,10 +1969,14 @@ attnres_status bwd_common_checks(const float* w, int32_t N, int64_t T, int32_t D
   return ATTNRES_OK;
 }
 
+// split: the split-token backward (D <= ATTNRES_SPLIT_MAX_D) with the
+// workspace layout [fold rows][ring][partial rows]; otherwise the
+// one-token-per-workgroup backward with its ATTNRES_DW_PARTIALS rows.
 attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch, const float* w,
                         const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
                         void* const* dsrcs, int64_t dsrc_pitch, int mode, float* dw, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool split = true) {
+  split = split && D <= ATTNRES_SPLIT_MAX_D;
   const int64_t gsize = (mode & kGradF32) ? 4 : 2;  // bytes per gradient element
   if (dout == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(dout, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -1598,7 +1999,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
   ins[nin++] = range_of(w, (size_t)D * 4);
   ins[nin++] = range_of(rstd, nTN * 4);
   ins[nin++] = range_of(alpha, nTN * 4);
-  const size_t need = ATTNRES_BWD_WORKSPACE_BYTES(D);
+  const size_t need = split ? ATTNRES_BWD_WORKSPACE_BYTES(T, N, D) : (size_t)ATTNRES_DW_PARTIALS * (size_t)D * 4;
   if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   Range outs[ATTNRES_MAX_SOURCES + 2];
@@ -1612,14 +2013,36 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
     for (int b = a + 1; b < nout; ++b)
       if (overlap(outs[a], outs[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
-  const LaunchShape s = bwd_shape(D);
-  const int32_t P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
   float* ws = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const BwdArgs args{dout, rows, w, rstd, alpha, T, D, P, drows, ws};
-  hipError_t e = run_bwd(N, s, mode, st, args);
-  if (e != hipSuccess) return ATTNRES_ERR_HIP;
   const int D4 = D / 4;
+  int32_t P = 0;  // rows dw_reduce_kernel sums
+  if (split) {
+    const int K = (D / 8 + kSpSliceVectors - 1) / kSpSliceVectors;
+    const int64_t groups = (T + kSpSide - 1) / kSpSide;  // token spans
+    uint64_t* ring = reinterpret_cast<uint64_t*>(ws + (size_t)ATTNRES_DW_PARTIALS * D);
+    const size_t ring_words = (size_t)kSpRing * K * 2 * N;
+    float* partial = reinterpret_cast<float*>(ring + ring_words);
+    // tags are token + 1: a zeroed ring holds no valid word
+    const int ring4 = (int)(ring_words / 2);
+    hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
+                       ring4);
+    if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+    const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, 0};
+    if (run_split(N, mode, st, sa, groups) != hipSuccess) return ATTNRES_ERR_HIP;
+    // fold the partial rows into at most ATTNRES_DW_PARTIALS rows, in row order
+    const int64_t per_fold = (groups + ATTNRES_DW_PARTIALS - 1) / ATTNRES_DW_PARTIALS;
+    P = (int32_t)((groups + per_fold - 1) / per_fold);
+    hipLaunchKernelGGL(dw_fold_kernel, dim3((unsigned)P, (unsigned)((D4 + kFoldCols - 1) / kFoldCols)), dim3(kFoldCols),
+                       0, st, reinterpret_cast<const float4*>(partial), groups, per_fold, D4,
+                       reinterpret_cast<float4*>(ws));
+    if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+  } else {
+    const LaunchShape s = bwd_shape(D);
+    P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);
+    const BwdArgs args{dout, rows, w, rstd, alpha, T, D, P, drows, ws};
+    if (run_bwd(N, s, mode, st, args) != hipSuccess) return ATTNRES_ERR_HIP;
+  }
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
                      reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
   return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
@@ -1772,5 +2195,5 @@ extern "C" attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16
     dsrcs[i] = dsrc + (size_t)i * (size_t)T * (size_t)D;
   }
   return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, reinterpret_cast<void* const*>(dsrcs), D, 0, dw, ws,
-                  ATTNRES_BWD_WORKSPACE_BYTES(D), stream);
+                  (size_t)ATTNRES_DW_PARTIALS * (size_t)D * 4, stream, /*split=*/false);
 }

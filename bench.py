@@ -60,14 +60,28 @@ def algo_bytes(T: int, N: int, D: int):
     """Bytes the operator must move (single pass, nothing materialised beyond
     the outputs): fwd reads sources and writes out + rstd + alpha; bwd reads
     sources, dout, rstd, alpha and writes dsources.  Per-call extras: w read
-    (4D per call), the dw partial rows written and read back (2 * 4 * P * D)
-    and dw itself (4D)."""
+    (4D per call) and, for the backward, dw written (4D).  The backward's own
+    workspace traffic (dw partial rows written and read back) is not counted
+    here; workspace_traffic() gives it."""
     fwd = T * (2 * N * D + 2 * D + 8 * N)
     bwd = T * (4 * N * D + 2 * D + 8 * N)
-    P = min(T, 256)
     fwd_extra = 4 * D
-    bwd_extra = 4 * D + 8 * P * D + 4 * D
+    bwd_extra = 4 * D + 4 * D
     return fwd, bwd, fwd_extra, bwd_extra
+
+
+def workspace_traffic(T: int, N: int, D: int) -> int:
+    """HBM bytes of one attnres_bwd call's workspace: for D <= 8192 the
+    per-span dw partial rows (ceil(T/4) rows of D fp32) written and read back,
+    the folded rows (<= 256) written and read, and the exchange ring cleared;
+    otherwise the 256 partial rows written and read."""
+    if D <= 8192:
+        groups = (T + 3) // 4
+        per_fold = (groups + 255) // 256
+        folds = (groups + per_fold - 1) // per_fold
+        ring = 4096 * ((D + 1023) // 1024) * 2 * N * 8
+        return 8 * groups * D + 8 * folds * D + ring
+    return 8 * min(T, 256) * D
 
 
 def kernel_source_hash() -> str:
@@ -347,7 +361,7 @@ def alloc_buffers(ar, torch, N, T, D, dev):
     alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
     dsrc = torch.empty((N, T, D), dtype=torch.bfloat16, device=dev)
     dw = torch.empty((D,), dtype=torch.float32, device=dev)
-    ws = torch.empty((ar.workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((ar.workspace_bytes(T, N, D),), dtype=torch.uint8, device=dev)
     return out, rstd, alpha, dsrc, dw, ws
 
 
@@ -446,7 +460,7 @@ def sweep_sources(ar, torch, dev, flush, reps, N=9, T=32768, D=7168):
     rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
     alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
     dw = torch.empty((D,), dtype=torch.float32, device=dev)
-    ws = torch.empty((ar.workspace_bytes(D),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((ar.workspace_bytes(T, N, D),), dtype=torch.uint8, device=dev)
     fb, bb, fe, be = algo_bytes(T, N, D)
     calls = {
         "fwd_sources": (lambda: ar.attnres_fwd_sources(srcs, w, 1e-6, out=out, rstd=rstd, alpha=alpha), fb + fe),
@@ -801,8 +815,9 @@ def main():
         "pages_peak_alloc_GiB_at_128K": PAGES_PEAK_GIB_128K,
         "ceilings_GBps": ceil,
         "block_batched_scores": blk,
+        "bwd_workspace_bytes_moved": workspace_traffic(T, N, D),
         "roofline": {
-            "kernel": "attnres_bwd (bwd_kernel + dw_reduce_kernel, one call)",
+            "kernel": "attnres_bwd (one call: ring clear, bwd_split_kernel, dw_fold_kernel, dw_reduce_kernel)",
             "bound": "hbm",
             "achieved": bwd_gbps,
             "peak": HBM_PEAK_GBPS,

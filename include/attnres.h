@@ -74,8 +74,25 @@ typedef enum {
 #define ATTNRES_GRAD_BF16 0
 #define ATTNRES_GRAD_ACCUMULATE 1
 #define ATTNRES_GRAD_F32 2
-/* Bytes of device workspace attnres_bwd needs for hidden size D. */
-#define ATTNRES_BWD_WORKSPACE_BYTES(D) ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float))
+/* The backward for D <= ATTNRES_SPLIT_MAX_D spreads every token over
+ * ceil(D / 1024) workgroups, each taking one 1024-channel slice of
+ * ATTNRES_SPLIT_TOKENS consecutive tokens side by side; the per-token sums are exchanged
+ * through a ring of ATTNRES_SPLIT_RING tokens in the workspace, and every
+ * workgroup writes one dw partial row slice. */
+#define ATTNRES_SPLIT_MAX_D 8192
+#define ATTNRES_SPLIT_TOKENS 4
+#define ATTNRES_SPLIT_RING 4096
+/* Bytes of device workspace attnres_bwd / attnres_bwd_sources need for T
+ * tokens, N sources and hidden size D: ATTNRES_DW_PARTIALS fp32 rows of D,
+ * plus for D <= ATTNRES_SPLIT_MAX_D the exchange ring (8-byte words) and
+ * ceil(T / ATTNRES_SPLIT_TOKENS) fp32 partial rows of D (at T = 131072,
+ * N = 9, D = 7168: 7.3 + 4.1 + 939.5 MB). */
+#define ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)                                                                       \
+  ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float) +                                                   \
+   ((D) <= ATTNRES_SPLIT_MAX_D                                                                                   \
+        ? (size_t)ATTNRES_SPLIT_RING * (size_t)(((D) + 1023) / 1024) * 2 * (size_t)(N) * 8 +                      \
+              (size_t)(((T) + ATTNRES_SPLIT_TOKENS - 1) / ATTNRES_SPLIT_TOKENS) * (size_t)(D) * sizeof(float)    \
+        : 0))
 
 /*
  * Forward.
@@ -115,7 +132,7 @@ attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32
  *   dw    [D]       fp32   gradient of w summed over all T tokens (overwritten;
  *                          zero-filled when T == 0)
  *   workspace              device scratch of at least
- *                          ATTNRES_BWD_WORKSPACE_BYTES(D) bytes, 16-byte
+ *                          ATTNRES_BWD_WORKSPACE_BYTES(T, N, D) bytes, 16-byte
  *                          aligned; contents on entry are ignored and on exit
  *                          unspecified.  May be NULL when T == 0.
  * Alignment: dout, src, w, dsrc, dw, workspace 16-byte aligned; rstd, alpha
@@ -279,12 +296,15 @@ attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch
 /*
  * Backward without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
- * that forbid hipMalloc.  Same arguments, results and errors as attnres_bwd --
- * bitwise the same dsrc and dw, from the same kernels -- except that the dw
- * partial rows live in a static device array of the library
- * (ATTNRES_DW_PARTIALS x ATTNRES_NOALLOC_MAX_D fp32 = 8 MiB on every device the
- * library runs on, held until the process ends).  The call allocates nothing
- * (no hipMalloc, no library routine that allocates).
+ * that forbid hipMalloc.  Same arguments, contract and errors as attnres_bwd,
+ * except that the dw partial rows live in a static device array of the
+ * library (ATTNRES_DW_PARTIALS x ATTNRES_NOALLOC_MAX_D fp32 = 8 MiB on every
+ * device the library runs on, held until the process ends), so this call
+ * runs the one-token-per-workgroup backward, whose partial rows fit that
+ * array, also where attnres_bwd splits tokens over workgroups: its dsrc and
+ * dw equal attnres_bwd's to within fp32 rounding (another summation order),
+ * not bit for bit.  The call allocates nothing (no hipMalloc, no library
+ * routine that allocates).
  *   D > ATTNRES_NOALLOC_MAX_D   ATTNRES_ERR_WORKSPACE, nothing enqueued.
  * The first call on a device looks up that device's address of the array
  * (ATTNRES_ERR_HIP if the runtime refuses).  Every call on a device shares its

@@ -80,7 +80,7 @@ int main(void) {
   uint16_t *d_src, *d_dout, *d_out, *d_out2, *d_dsrc;
   float *d_w, *d_rstd, *d_alpha, *d_rstd2, *d_alpha2, *d_dw;
   void* d_ws;
-  const size_t ws_bytes = ATTNRES_BWD_WORKSPACE_BYTES(D);
+  const size_t ws_bytes = ATTNRES_BWD_WORKSPACE_BYTES(T, N, D);
   CHECK_HIP(hipMalloc((void**)&d_src, nsrc * 2));
   CHECK_HIP(hipMalloc((void**)&d_dsrc, nsrc * 2));
   CHECK_HIP(hipMalloc((void**)&d_dout, nTD * 2));

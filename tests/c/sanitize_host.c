@@ -158,7 +158,7 @@ static void run_abi(void) {
   float* dw = (float*)(A + ((uintptr_t)6 << 28));
   void* ws = (void*)(A + ((uintptr_t)7 << 28));
   const uint16_t* dout = (const uint16_t*)(A + ((uintptr_t)8 << 28));
-  const size_t wsb = ATTNRES_BWD_WORKSPACE_BYTES(D);
+  const size_t wsb = ATTNRES_BWD_WORKSPACE_BYTES(T, N, D);
 
   EXPECT(attnres_fwd(NULL, w, 1e-6f, N, T, D, out, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
   EXPECT(attnres_fwd(src, w, 1e-6f, 0, T, D, out, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);

@@ -92,7 +92,14 @@ def test_header_constants_match_binding():
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
-    assert ar.workspace_bytes(D) == ar.DW_PARTIALS * D * 4
+    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING"):
+        assert _define("ATTNRES_" + name) == getattr(ar, name)
+    # the backward's workspace: 256 partial rows, and for D <= 8192 the exchange
+    # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and
+    # ceil(T/4) partial rows
+    assert ar.workspace_bytes(131072, 9, D) == 256 * D * 4 + 4096 * 7 * 18 * 8 + 32768 * D * 4 == 950_992_896
+    assert ar.workspace_bytes(1, 1, 8) == 256 * 8 * 4 + 4096 * 1 * 2 * 8 + 8 * 4
+    assert ar.workspace_bytes(1000, 9, 12288) == 256 * 12288 * 4  # one-token-per-workgroup backward
 
 
 def _fwd(src=A, w=2 * A, eps=1e-6, N=9, T=16, D_=D, out=None, rstd=None, alpha=None):
@@ -111,7 +118,7 @@ def _bwd(dout=None, src=None, w=None, rstd=None, alpha=None, N=9, T=16, D_=D, ds
         if v is not None:
             vals[k] = v
     if ws_bytes is None:
-        ws_bytes = ar.workspace_bytes(D_)
+        ws_bytes = ar.workspace_bytes(T, max(N, 1), D_)
     return ar.library().attnres_bwd(vals["dout"], vals["src"], vals["w"], vals["rstd"], vals["alpha"], N, T, D_,
                                     vals["dsrc"], vals["dw"], vals["ws"], ws_bytes, None)
 
@@ -154,7 +161,7 @@ def test_bwd_rejects(kw):
 
 def test_bwd_workspace_errors():
     assert _bwd(ws=0) == WORKSPACE
-    assert _bwd(ws_bytes=ar.workspace_bytes(D) - 1) == WORKSPACE
+    assert _bwd(ws_bytes=ar.workspace_bytes(16, 9, D) - 1) == WORKSPACE
 
 
 def test_bwd_rejects_aliasing():
@@ -217,7 +224,7 @@ def test_fwd_sources_rejects():
 def _bwd_src(srcs, dsrcs, acc=1, N=3, T=16, D_=D, ws_bytes=None, pitch=None, dpitch=None):
     g = 1 << 30
     if ws_bytes is None:
-        ws_bytes = ar.workspace_bytes(D_)
+        ws_bytes = ar.workspace_bytes(T, max(N, 1), D_)
     return ar.library().attnres_bwd_sources(1 * g, srcs, D_ if pitch is None else pitch, 20 * g, 21 * g, 22 * g, N,
                                             T, D_, dsrcs, D_ if dpitch is None else dpitch, acc, 23 * g, 24 * g,
                                             ws_bytes, None)
@@ -370,7 +377,7 @@ def test_bwd_sources_overlap_checks_match_a_byte_model(seed):
     srcs, pitch = _layout(rng, N, T, Dv, arena)
     dsrcs, dpitch = _layout(rng, N, T, Dv, arena + 16 * int(rng.integers(0, 64)))
     dout = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.3 else (1 << 33)
-    wsb = ar.workspace_bytes(Dv)
+    wsb = ar.workspace_bytes(T, N, Dv)
     dw = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.2 else (1 << 33) + (1 << 24)
     ws = arena + 16 * int(rng.integers(0, 256)) if rng.random() < 0.2 else (1 << 33) + (1 << 25)
     w, rstd, alpha = (1 << 34), (1 << 35), (1 << 35) + (1 << 20)

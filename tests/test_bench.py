@@ -23,15 +23,15 @@ def test_algorithmic_bytes_per_token():
     assert fwd == 2 * N * D + 2 * D + 8 * N == 143_432
     assert bwd == 4 * N * D + 2 * D + 8 * N == 272_456
     assert fe == 4 * D  # w
-    assert be == 4 * D + 8 * 1 * D + 4 * D  # w, one dw partial row written and read, dw
+    assert be == 4 * D + 4 * D  # w read, dw written (the workspace's own traffic is reported apart)
 
 
 def test_algorithmic_bytes_of_the_default_workload():
     wl = synth.workload(bench.DEFAULT_WORKLOAD)
     fwd, bwd, fe, be = bench.algo_bytes(wl.T, wl.N, wl.D)
     assert (wl.T, wl.N, wl.D) == (131072, 9, 7168) and wl.w_std == 0.5
-    # one attnres_bwd call: per-token bytes, w, 256 dw partial rows written and read, dw
-    assert bwd + be == 131072 * 272_456 + 4 * 7168 + 8 * 256 * 7168 + 4 * 7168 == 35_726_090_240
+    # one attnres_bwd call: per-token bytes, w, dw
+    assert bwd + be == 131072 * 272_456 + 4 * 7168 + 4 * 7168 == 35_711_410_176
     assert fwd + fe == 131072 * 143_432 + 4 * 7168 == 18_799_947_776
     # a committed counter record, if present, refers to the same byte count
     f = bench.traffic_file(wl.T, wl.N, wl.D)
@@ -42,11 +42,17 @@ def test_algorithmic_bytes_of_the_default_workload():
         assert rec["fwd_kernel"]["algorithmic_bytes"] == fwd + fe
 
 
-def test_partial_rows_follow_min_T_256():
-    D = 64
-    for T, P in [(1, 1), (100, 100), (256, 256), (257, 256), (100000, 256)]:
-        _, _, _, be = bench.algo_bytes(T, 3, D)
-        assert be == 8 * D + 8 * P * D
+def test_workspace_traffic():
+    """The backward's workspace traffic, reported next to (not inside) the
+    algorithmic bytes: per-group partial rows and fold rows written and read,
+    the exchange ring cleared (D <= 8192); 256 partial rows otherwise."""
+    D = 7168
+    # T = 131072: 32768 spans of 4 tokens, folded 128 at a time into 256 rows
+    assert bench.workspace_traffic(131072, 9, D) == 8 * 32768 * D + 8 * 256 * D + 4096 * 7 * 18 * 8
+    # T = 100: 25 spans, one per fold row
+    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 8 * 25 * 64 + 4096 * 1 * 6 * 8
+    assert bench.workspace_traffic(5000, 9, 12288) == 8 * 256 * 12288
+    assert bench.workspace_traffic(100, 9, 12288) == 8 * 100 * 12288
 
 
 def test_kernel_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):

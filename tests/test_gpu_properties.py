@@ -189,7 +189,7 @@ def test_graph_capture_replays_match_eager():
     alpha = torch.empty_like(rstd)
     dsrc = torch.empty_like(src)
     dw = torch.empty((D,), dtype=torch.float32, device=DEV)
-    ws = torch.empty((ar.workspace_bytes(D),), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((ar.workspace_bytes(T, N, D),), dtype=torch.uint8, device=DEV)
 
     def step():
         ar.attnres_fwd(s_src, w, wl.eps, out=out, rstd=rstd, alpha=alpha)

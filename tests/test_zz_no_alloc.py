@@ -1,18 +1,26 @@
 """attnres_bwd_noalloc (through the C ABI): the backward without a workspace
-argument gives bitwise the dsources and dw of attnres_bwd with a caller
-workspace -- on two calls in a row, the second with a smaller input, so the
-static partial rows carry the first call's contents into the second -- and
-allocates no device memory."""
+argument against attnres_bwd with a caller workspace, on two calls in a row --
+the second with a smaller input, so the static partial rows carry the first
+call's contents into the second -- and against the fp64 oracle; it allocates
+no device memory.  The two calls run different kernels for D <= 8192 (the
+no-allocation call keeps the one-token-per-workgroup backward, whose 256
+partial rows fit its static array), so they agree to the parity bars, not bit
+for bit: dsources within relative L2 1e-2 and the element bound of
+tests/parity.py against the oracle, dw within relative L2 1e-2.
+"""
 from __future__ import annotations
 
 import ctypes
+
+import numpy as np
 
 import pytest
 import torch
 
 import attention_residuals_depth_amd as ar
+import oracle
 import synth
-from parity import DEV, to_dev_bf16
+from parity import DEV, TOL_DSRC_REL_L2, TOL_DW_REL_L2, Accum, rel_l2, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -48,13 +56,26 @@ def test_noalloc_matches_the_workspace_call_on_two_calls():
         torch.cuda.synchronize()
         assert rc == 0
         assert torch.cuda.memory_allocated() == before
-        assert torch.equal(_bits(dsrc), _bits(ref_dsrc))
-        assert torch.equal(_bits(dw), _bits(ref_dw))
-    # the binding's wrapper: same call, outputs passed in
+        g = lambda t: t.double().cpu().numpy()
+        e_ws = (rel_l2(g(dsrc), g(ref_dsrc)), rel_l2(g(dw), g(ref_dw)))
+        o_dsrc, o_dw = oracle.bwd(wl.sources(), wl.w(), wl.eps, wl.dout())
+        acc = Accum(DEV)
+        acc.update(wl.sources(), wl.dout(), wl.w(),
+                   dict(out=torch.zeros((T, D)), rstd=rstd, alpha=alpha, dsrc=dsrc),
+                   dict(out=np.zeros((T, D)), rstd=rstd.double().cpu().numpy(),
+                        alpha=alpha.double().cpu().numpy(), dsrc=o_dsrc))
+        e = acc.result()
+        print(f"[noalloc] vs attnres_bwd: dsrc {e_ws[0]:.3e}, dw {e_ws[1]:.3e}; vs oracle: dsrc "
+              f"{e['dsrc_rel_l2']:.3e} (element ratio {e['dsrc_elem_ratio']:.3f}), dw {rel_l2(g(dw), o_dw):.3e}",
+              flush=True)
+        assert e_ws[0] <= TOL_DSRC_REL_L2 and e_ws[1] <= TOL_DW_REL_L2
+        assert e["dsrc_rel_l2"] <= TOL_DSRC_REL_L2 and e["dsrc_elem_ratio"] <= 1.0
+        assert rel_l2(g(dw), o_dw) <= TOL_DW_REL_L2
+    # the binding's wrapper: same call, outputs passed in -- bitwise the direct call
     dsrc2, dw2 = ar.attnres_bwd_noalloc(dout, src, w, rstd, alpha, torch.empty_like(ref_dsrc),
                                         torch.empty_like(ref_dw))
     torch.cuda.synchronize()
-    assert torch.equal(_bits(dsrc2), _bits(ref_dsrc)) and torch.equal(_bits(dw2), _bits(ref_dw))
+    assert torch.equal(_bits(dsrc2), _bits(dsrc)) and torch.equal(_bits(dw2), _bits(dw))
 
 
 def test_noalloc_refuses_large_D_and_zero_fills_dw_for_empty_batches():
