@@ -83,6 +83,8 @@ def library() -> ctypes.CDLL:
         lib.attnres_block_scores.restype = ctypes.c_int
         lib.attnres_fwd_scored.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_scored.restype = ctypes.c_int
+        lib.attnres_set_split_spin.argtypes = [ctypes.c_uint32]
+        lib.attnres_set_split_spin.restype = ctypes.c_uint32
         _lib = lib
     return _lib
 
@@ -90,6 +92,15 @@ def library() -> ctypes.CDLL:
 SPLIT_MAX_D = 8192
 SPLIT_TOKENS = 4
 SPLIT_RING = 4096
+SPLIT_SPIN_DEFAULT = 4096
+
+
+def set_split_spin(polls: int) -> int:
+    """attnres_set_split_spin: the split backward's poll bound for later calls
+    (0 recomputes every member's partial sums); returns the previous bound."""
+    if not 0 <= polls < 2**32:
+        raise ValueError("polls must fit in 32 bits")
+    return int(library().attnres_set_split_spin(polls))
 
 
 def workspace_bytes(T: int, N: int, D: int) -> int:
@@ -548,5 +559,5 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
            "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
-           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING",
+           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_SPIN_DEFAULT", "set_split_spin",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

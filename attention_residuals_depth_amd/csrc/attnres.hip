@@ -33,6 +33,7 @@
 
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "attnres.h"
@@ -1208,8 +1209,11 @@ constexpr int kSpSide = ATTNRES_SPLIT_TOKENS;               // tokens side by si
 constexpr int kSpThreads = kSpSliceVectors * kSpSide;       // 512
 constexpr int kSpRing = ATTNRES_SPLIT_RING;                 // exchange ring, tokens
 constexpr int kSpMaxSlices = ATTNRES_SPLIT_MAX_D / 8 / kSpSliceVectors;  // 8
-constexpr int kSpSpin = 4096;                               // polls before a word is recomputed
+constexpr uint32_t kSpSpin = ATTNRES_SPLIT_SPIN_DEFAULT;    // polls before a word is recomputed
 static_assert(kSpRing % kSpSide == 0, "ring of whole spans");
+
+// The poll bound the next split-backward launches use (attnres_set_split_spin).
+std::atomic<uint32_t> g_split_spin{kSpSpin};
 
 struct SplitArgs {
   const uint16_t* dout;
@@ -1224,6 +1228,7 @@ struct SplitArgs {
   uint64_t* ring;   // [kSpRing][K][2N] words
   float* partial;   // [ceil(T / ATTNRES_SPLIT_TOKENS)][D]
   int64_t s0;       // first token span of this launch
+  uint32_t spin;    // polls before a member's word is recomputed
 };
 
 // This thread's partial g.x_i and w.x_i over its vector of source i: v_dot2
@@ -1330,7 +1335,7 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
     for (int q = tl; q < K * 2 * N; q += kSpSliceVectors) {
       uint64_t word = 0;
       bool got = false;
-      for (int n = 0; n < kSpSpin; ++n) {
+      for (uint32_t n = 0; n < a.spin; ++n) {
         word = __hip_atomic_load(ring + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((uint32_t)(word >> 32) == tag) {
           got = true;
@@ -2028,7 +2033,8 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
     hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
                        ring4);
     if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
-    const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, 0};
+    const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, 0,
+                       g_split_spin.load(std::memory_order_relaxed)};
     if (run_split(N, mode, st, sa, groups) != hipSuccess) return ATTNRES_ERR_HIP;
     // fold the partial rows into at most ATTNRES_DW_PARTIALS rows, in row order
     const int64_t per_fold = (groups + ATTNRES_DW_PARTIALS - 1) / ATTNRES_DW_PARTIALS;
@@ -2196,4 +2202,11 @@ extern "C" attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16
   }
   return bwd_impl(dout, srcs, D, w, rstd, alpha, N, T, D, reinterpret_cast<void* const*>(dsrcs), D, 0, dw, ws,
                   (size_t)ATTNRES_DW_PARTIALS * (size_t)D * 4, stream, /*split=*/false);
+}
+
+// ---------------------------------------------------------------------------
+// Poll bound of the split backward's exchange
+// ---------------------------------------------------------------------------
+extern "C" uint32_t attnres_set_split_spin(uint32_t polls) {
+  return g_split_spin.exchange(polls, std::memory_order_relaxed);
 }

@@ -82,6 +82,9 @@ typedef enum {
 #define ATTNRES_SPLIT_MAX_D 8192
 #define ATTNRES_SPLIT_TOKENS 4
 #define ATTNRES_SPLIT_RING 4096
+/* Polls of a member's ring word before the waiting workgroup recomputes that
+ * member's partial sums itself (attnres_set_split_spin). */
+#define ATTNRES_SPLIT_SPIN_DEFAULT 4096
 /* Bytes of device workspace attnres_bwd / attnres_bwd_sources need for T
  * tokens, N sources and hidden size D: ATTNRES_DW_PARTIALS fp32 rows of D,
  * plus for D <= ATTNRES_SPLIT_MAX_D the exchange ring (8-byte words) and
@@ -318,6 +321,22 @@ attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch
 attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,
                                    const float* alpha, int32_t N, int64_t T, int32_t D, uint16_t* dsrc, float* dw,
                                    void* stream);
+
+/*
+ * Poll bound of the split backward (D <= ATTNRES_SPLIT_MAX_D): a workgroup
+ * waiting for another slice's partial sums of a token reads that member's
+ * ring word at most `polls` times, then recomputes the member's partial sums
+ * from HBM itself, with the member's own arithmetic and reduction tree, so
+ * dsrc and dw do not depend on which route was taken.  The route is taken
+ * when the members of a token are not resident together (a device shared
+ * with other work); polls = 0 takes it for every word, which makes the
+ * backward slower (each slice workgroup then reads every slice of its
+ * tokens) but still correct -- the way to exercise that route.
+ * The bound applies to attnres_bwd / attnres_bwd_sources calls enqueued after
+ * this call, in every thread; it returns the previous bound (default
+ * ATTNRES_SPLIT_SPIN_DEFAULT).  It enqueues nothing and cannot fail.
+ */
+uint32_t attnres_set_split_spin(uint32_t polls);
 
 #ifdef __cplusplus
 }

@@ -144,5 +144,18 @@ int main(void) {
   printf("out rel_l2 %.3e  alpha max abs %.3e  rstd max rel %.3e  dsrc rel_l2 %.3e  dw rel_l2 %.3e  "
          "per-source == stacked: %s\n", e_out, e_alpha, e_rstd, e_dsrc, e_dw, same ? "yes" : "no");
   if (!(e_out <= 5e-3 && e_alpha <= 1e-5 && e_rstd <= 1e-5 && e_dsrc <= 1e-2 && e_dw <= 1e-2 && same)) ++fails;
+
+  /* the backward again with every exchanged word recomputed: bitwise the same */
+  const uint32_t prev = attnres_set_split_spin(0);
+  st = attnres_bwd(d_dout, d_src, d_w, d_rstd, d_alpha, N, T, (int32_t)D, d_dsrc, d_dw, d_ws, ws_bytes, NULL);
+  attnres_set_split_spin(prev);
+  if (st != ATTNRES_OK) { fprintf(stderr, "attnres_bwd (poll bound 0) returned %d\n", (int)st); return 1; }
+  uint16_t* dsrc0 = malloc(nsrc * 2);
+  float* dw0 = malloc(D * 4);
+  CHECK_HIP(hipMemcpy(dsrc0, d_dsrc, nsrc * 2, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(dw0, d_dw, D * 4, hipMemcpyDeviceToHost));
+  const int same0 = memcmp(dsrc, dsrc0, nsrc * 2) == 0 && memcmp(dw, dw0, D * 4) == 0;
+  printf("recomputed exchange == ring exchange: %s\n", same0 ? "yes" : "no");
+  if (prev != ATTNRES_SPLIT_SPIN_DEFAULT || !same0) ++fails;
   return fails == 0 ? 0 : 1;
 }

@@ -38,6 +38,9 @@ def test_library_loads_and_exports_declared_symbols():
     assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
                      "attnres_fwd_update", "attnres_bwd_sources", "attnres_block_scores", "attnres_fwd_scored",
                      "attnres_bwd_noalloc"]
+    others = re.findall(r"^uint32_t\s+(attnres_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert others == ["attnres_set_split_spin"]
+    names += others
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ar.LIB_PATH], capture_output=True, text=True, check=True).stdout
@@ -92,7 +95,7 @@ def test_header_constants_match_binding():
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
-    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING"):
+    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_SPIN_DEFAULT"):
         assert _define("ATTNRES_" + name) == getattr(ar, name)
     # the backward's workspace: 256 partial rows, and for D <= 8192 the exchange
     # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and
@@ -464,3 +467,12 @@ def test_noalloc_backward_refuses_on_the_host():
     assert call(dw=0) == INVALID
     assert call(w=12 * g) == INVALID  # dw overlaps w
     assert call(T=-1) == INVALID
+
+
+def test_split_spin_setter_returns_the_previous_bound():
+    """attnres_set_split_spin is host state only (no GPU): it swaps the bound."""
+    assert ar.set_split_spin(7) == ar.SPLIT_SPIN_DEFAULT
+    assert ar.set_split_spin(0) == 7
+    assert ar.set_split_spin(ar.SPLIT_SPIN_DEFAULT) == 0
+    with pytest.raises(ValueError):
+        ar.set_split_spin(-1)
