@@ -92,6 +92,7 @@ def library() -> ctypes.CDLL:
 SPLIT_MAX_D = 8192
 SPLIT_TOKENS = 4
 SPLIT_RING = 4096
+SPLIT_CHUNK_SPANS = 8192
 SPLIT_SPIN_DEFAULT = 4096
 
 
@@ -109,7 +110,8 @@ def workspace_bytes(T: int, N: int, D: int) -> int:
     D <= 8192, the split backward's exchange ring and per-group partial rows."""
     b = DW_PARTIALS * D * 4
     if D <= SPLIT_MAX_D:
-        b += SPLIT_RING * ((D + 1023) // 1024) * 2 * N * 8 + ((T + SPLIT_TOKENS - 1) // SPLIT_TOKENS) * D * 4
+        spans = min((T + SPLIT_TOKENS - 1) // SPLIT_TOKENS, SPLIT_CHUNK_SPANS)
+        b += SPLIT_RING * ((D + 1023) // 1024) * 2 * N * 8 + spans * D * 4
     return b
 
 
@@ -559,5 +561,5 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
            "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
-           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_SPIN_DEFAULT", "set_split_spin",
+           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT", "set_split_spin",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

@@ -1201,9 +1201,15 @@ __global__ void __launch_bounds__(kReduceThreads) dw_reduce_kernel(const float4*
 // the other kernels.
 //
 // dw: the workgroup sums its tokens' contributions to its slice in side
-// order and writes one partial row slice; ceil(T / ATTNRES_SPLIT_TOKENS)
-// partial rows are then summed in a fixed two-level order (dw_fold_kernel,
-// dw_reduce_kernel).  No atomics touch dw.
+// order and writes one partial row slice per span.  The spans run in chunks
+// of ATTNRES_SPLIT_CHUNK_SPANS (one launch each), and after each chunk
+// dw_fold_kernel adds the chunk's partial rows into at most 256 fold rows;
+// dw_reduce_kernel sums those in index order.  The order depends on T alone
+// and no atomics touch dw.  A chunk's partial rows (235 MB at D = 7168) stay
+// in the 256 MB Infinity Cache until the fold reads them: measured on MI355X
+// at N = 9, one launch over all spans was 3% slower at T = 128K-256K, when
+// the partial rows of the whole batch (0.9-1.9 GB) went to HBM and back, and
+// chunks of 12K or 16K spans lost the gain again.
 constexpr int kSpSliceVectors = 128;                        // vectors (threads) per slice
 constexpr int kSpSide = ATTNRES_SPLIT_TOKENS;               // tokens side by side
 constexpr int kSpThreads = kSpSliceVectors * kSpSide;       // 512
@@ -1211,6 +1217,7 @@ constexpr int kSpRing = ATTNRES_SPLIT_RING;                 // exchange ring, to
 constexpr int kSpMaxSlices = ATTNRES_SPLIT_MAX_D / 8 / kSpSliceVectors;  // 8
 constexpr uint32_t kSpSpin = ATTNRES_SPLIT_SPIN_DEFAULT;    // polls before a word is recomputed
 constexpr int kSpFirstPollSleep = 48;                       // s_sleep units (64 cycles) before the first poll
+constexpr int64_t kSpChunk = ATTNRES_SPLIT_CHUNK_SPANS;     // spans per launch and fold
 static_assert(kSpRing % kSpSide == 0, "ring of whole spans");
 
 // The poll bound the next split-backward launches use (attnres_set_split_spin).
@@ -1227,8 +1234,9 @@ struct SplitArgs {
   int32_t K;  // slices per row
   DstRows dsrc;
   uint64_t* ring;   // [kSpRing][K][2N] words
-  float* partial;   // [ceil(T / ATTNRES_SPLIT_TOKENS)][D]
+  float* partial;   // [ATTNRES_SPLIT_PARTIAL_ROWS(T)][D]: one row per span of the chunk
   int64_t s0;       // first token span of this launch
+  int64_t p0;       // the span whose dw partial row is partial[0] (first span of the chunk)
   uint32_t spin;    // polls before a member's word is recomputed
 };
 
@@ -1505,37 +1513,42 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
       s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
       s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
     }
-    const __amdgpu_buffer_rsrc_t rp = rsrc(a.partial + span * D, (uint32_t)D * 4u);
+    const __amdgpu_buffer_rsrc_t rp = rsrc(a.partial + (span - a.p0) * D, (uint32_t)D * 4u);
     bstore(rp, 2u * off, __builtin_bit_cast(uint4, s0));
     bstore(rp, 2u * off + 16u, __builtin_bit_cast(uint4, s1));
   }
 }
 
-// dw stage 2a: rows [b * R, (b + 1) * R) of the partial rows summed in row
-// order into fold row b; thread c owns float4 column c of its column block.
+// dw stage 2a: fold row b (of P = min(spans, ATTNRES_DW_PARTIALS)) sums the
+// partial rows of the spans s = b (mod P), in increasing s.  One launch
+// covers the spans [c0, c0 + n) of one chunk, whose partial rows sit at
+// partial[s - c0]; the first chunk writes the fold rows, later chunks add to
+// them, so the order over all spans is fixed by T alone.  At any moment the
+// workgroups read neighbouring rows; thread c owns float4 column c of its
+// column block.
 constexpr int kFoldCols = 256;  // float4 columns per workgroup
-__global__ void __launch_bounds__(kFoldCols) dw_fold_kernel(const float4* __restrict__ partial, int64_t rows,
-                                                            int64_t rows_per_fold, int32_t D4,
+__global__ void __launch_bounds__(kFoldCols) dw_fold_kernel(const float4* __restrict__ partial, int64_t c0, int64_t n,
+                                                            int32_t P, int32_t D4, int first,
                                                             float4* __restrict__ fold) {
   const int c = blockIdx.y * kFoldCols + threadIdx.x;
   if (c >= D4) return;
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_fold;
-  const int64_t r1 = r0 + rows_per_fold < rows ? r0 + rows_per_fold : rows;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  int64_t r = r0;
-  for (; r + 4 <= r1; r += 4) {  // four loads in flight, added in row order
-    const float4 u0 = partial[r * D4 + c], u1 = partial[(r + 1) * D4 + c];
-    const float4 u2 = partial[(r + 2) * D4 + c], u3 = partial[(r + 3) * D4 + c];
+  const int b = blockIdx.x;
+  float4 s = first ? make_float4(0.f, 0.f, 0.f, 0.f) : fold[(int64_t)b * D4 + c];
+  const int64_t end = c0 + n;
+  int64_t sp = c0 + ((b - c0 % P) % P + P) % P;  // the chunk's first span that is b (mod P)
+  for (; sp + 3 * (int64_t)P < end; sp += 4 * (int64_t)P) {  // four loads in flight, added in span order
+    const float4 u0 = partial[(sp - c0) * D4 + c], u1 = partial[(sp + P - c0) * D4 + c];
+    const float4 u2 = partial[(sp + 2 * P - c0) * D4 + c], u3 = partial[(sp + 3 * P - c0) * D4 + c];
     s.x += u0.x; s.y += u0.y; s.z += u0.z; s.w += u0.w;
     s.x += u1.x; s.y += u1.y; s.z += u1.z; s.w += u1.w;
     s.x += u2.x; s.y += u2.y; s.z += u2.z; s.w += u2.w;
     s.x += u3.x; s.y += u3.y; s.z += u3.z; s.w += u3.w;
   }
-  for (; r < r1; ++r) {
-    const float4 u = partial[r * D4 + c];
+  for (; sp < end; sp += P) {
+    const float4 u = partial[(sp - c0) * D4 + c];
     s.x += u.x; s.y += u.y; s.z += u.z; s.w += u.w;
   }
-  fold[(int64_t)blockIdx.x * D4 + c] = s;
+  fold[(int64_t)b * D4 + c] = s;
 }
 
 __global__ void zero_kernel(float4* __restrict__ p, int32_t n4) {
@@ -1795,9 +1808,10 @@ hipError_t launch_split_n(hipStream_t st, SplitArgs a, int64_t groups) {
   if (e != hipSuccess) return e;
   // the dispatch packet counts work-items in 32 bits
   const int64_t per_launch = (int64_t)(UINT32_MAX / kSpThreads) / a.K;
+  const int64_t first = a.s0;
   for (int64_t g0 = 0; g0 < groups; g0 += per_launch) {
     const int64_t n = groups - g0 < per_launch ? groups - g0 : per_launch;
-    a.s0 = g0;
+    a.s0 = first + g0;
     hipLaunchKernelGGL((bwd_split_kernel<N, MODE>), dim3((unsigned)(n * a.K)), dim3(kSpThreads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2040,16 +2054,18 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
     hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
                        ring4);
     if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
-    const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, 0,
-                       g_split_spin.load(std::memory_order_relaxed)};
-    if (run_split(N, mode, st, sa, groups) != hipSuccess) return ATTNRES_ERR_HIP;
-    // fold the partial rows into at most ATTNRES_DW_PARTIALS rows, in row order
-    const int64_t per_fold = (groups + ATTNRES_DW_PARTIALS - 1) / ATTNRES_DW_PARTIALS;
-    P = (int32_t)((groups + per_fold - 1) / per_fold);
-    hipLaunchKernelGGL(dw_fold_kernel, dim3((unsigned)P, (unsigned)((D4 + kFoldCols - 1) / kFoldCols)), dim3(kFoldCols),
-                       0, st, reinterpret_cast<const float4*>(partial), groups, per_fold, D4,
-                       reinterpret_cast<float4*>(ws));
-    if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+    // chunks of spans, each folded into the P rows dw_reduce_kernel sums
+    P = (int32_t)(groups < ATTNRES_DW_PARTIALS ? groups : ATTNRES_DW_PARTIALS);
+    const uint32_t spin = g_split_spin.load(std::memory_order_relaxed);
+    for (int64_t c0 = 0; c0 < groups; c0 += kSpChunk) {
+      const int64_t n = groups - c0 < kSpChunk ? groups - c0 : kSpChunk;
+      const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, c0, c0, spin};
+      if (run_split(N, mode, st, sa, n) != hipSuccess) return ATTNRES_ERR_HIP;
+      hipLaunchKernelGGL(dw_fold_kernel, dim3((unsigned)P, (unsigned)((D4 + kFoldCols - 1) / kFoldCols)),
+                         dim3(kFoldCols), 0, st, reinterpret_cast<const float4*>(partial), c0, n, P, D4,
+                         c0 == 0 ? 1 : 0, reinterpret_cast<float4*>(ws));
+      if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+    }
   } else {
     const LaunchShape s = bwd_shape(D);
     P = (int32_t)(T < ATTNRES_DW_PARTIALS ? T : ATTNRES_DW_PARTIALS);

@@ -71,16 +71,19 @@ def algo_bytes(T: int, N: int, D: int):
 
 
 def workspace_traffic(T: int, N: int, D: int) -> int:
-    """HBM bytes of one attnres_bwd call's workspace: for D <= 8192 the
-    per-span dw partial rows (ceil(T/4) rows of D fp32) written and read back,
-    the folded rows (<= 256) written and read, and the exchange ring cleared;
-    otherwise the 256 partial rows written and read."""
+    """Bytes one attnres_bwd call moves through its workspace (written plus
+    read; not HBM bytes: a chunk's partial rows mostly stay in the Infinity
+    Cache).  For D <= 8192: the per-span dw partial rows (ceil(T/4) rows of D
+    fp32) written and read back, the P = min(spans, 256) fold rows written by
+    every chunk's fold, re-read by every later one and read by the final sum,
+    and the exchange ring cleared; otherwise the 256 partial rows written and
+    read."""
     if D <= 8192:
         groups = (T + 3) // 4
-        per_fold = (groups + 255) // 256
-        folds = (groups + per_fold - 1) // per_fold
+        chunks = (groups + 8191) // 8192
+        P = min(groups, 256)
         ring = 4096 * ((D + 1023) // 1024) * 2 * N * 8
-        return 8 * groups * D + 8 * folds * D + ring
+        return 8 * groups * D + 4 * P * D * (2 * chunks) + ring
     return 8 * min(T, 256) * D
 
 

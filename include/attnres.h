@@ -76,25 +76,34 @@ typedef enum {
 #define ATTNRES_GRAD_F32 2
 /* The backward for D <= ATTNRES_SPLIT_MAX_D spreads every token over
  * ceil(D / 1024) workgroups, each taking one 1024-channel slice of
- * ATTNRES_SPLIT_TOKENS consecutive tokens side by side; the per-token sums are exchanged
- * through a ring of ATTNRES_SPLIT_RING tokens in the workspace, and every
- * workgroup writes one dw partial row slice. */
+ * ATTNRES_SPLIT_TOKENS consecutive tokens side by side (a span); the per-token sums are
+ * exchanged through a ring of ATTNRES_SPLIT_RING tokens in the workspace, and every
+ * workgroup writes one dw partial row slice.  The spans run in chunks of
+ * ATTNRES_SPLIT_CHUNK_SPANS, each followed by a fold of its partial rows, so the
+ * workspace holds the partial rows of one chunk. */
 #define ATTNRES_SPLIT_MAX_D 8192
 #define ATTNRES_SPLIT_TOKENS 4
 #define ATTNRES_SPLIT_RING 4096
+#define ATTNRES_SPLIT_CHUNK_SPANS 8192
 /* Polls of a member's ring word before the waiting workgroup recomputes that
  * member's partial sums itself (attnres_set_split_spin). */
 #define ATTNRES_SPLIT_SPIN_DEFAULT 4096
+/* Spans whose dw partial rows the split backward's workspace holds at once:
+ * ceil(T / ATTNRES_SPLIT_TOKENS), at most one chunk. */
+#define ATTNRES_SPLIT_PARTIAL_ROWS(T)                                                                              \
+  ((((T) + ATTNRES_SPLIT_TOKENS - 1) / ATTNRES_SPLIT_TOKENS) < ATTNRES_SPLIT_CHUNK_SPANS                         \
+       ? (((T) + ATTNRES_SPLIT_TOKENS - 1) / ATTNRES_SPLIT_TOKENS)                                               \
+       : ATTNRES_SPLIT_CHUNK_SPANS)
 /* Bytes of device workspace attnres_bwd / attnres_bwd_sources need for T
  * tokens, N sources and hidden size D: ATTNRES_DW_PARTIALS fp32 rows of D,
  * plus for D <= ATTNRES_SPLIT_MAX_D the exchange ring (8-byte words) and
- * ceil(T / ATTNRES_SPLIT_TOKENS) fp32 partial rows of D (at T = 131072,
- * N = 9, D = 7168: 7.3 + 4.1 + 939.5 MB). */
+ * ATTNRES_SPLIT_PARTIAL_ROWS(T) fp32 partial rows of D (at T >= 32768,
+ * N = 9, D = 7168: 7.3 + 4.1 + 234.9 MB). */
 #define ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)                                                                       \
   ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float) +                                                   \
    ((D) <= ATTNRES_SPLIT_MAX_D                                                                                   \
         ? (size_t)ATTNRES_SPLIT_RING * (size_t)(((D) + 1023) / 1024) * 2 * (size_t)(N) * 8 +                      \
-              (size_t)(((T) + ATTNRES_SPLIT_TOKENS - 1) / ATTNRES_SPLIT_TOKENS) * (size_t)(D) * sizeof(float)    \
+              (size_t)ATTNRES_SPLIT_PARTIAL_ROWS(T) * (size_t)(D) * sizeof(float)                                \
         : 0))
 
 /*

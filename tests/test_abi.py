@@ -95,12 +95,15 @@ def test_header_constants_match_binding():
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
-    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_SPIN_DEFAULT"):
+    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT"):
         assert _define("ATTNRES_" + name) == getattr(ar, name)
     # the backward's workspace: 256 partial rows, and for D <= 8192 the exchange
-    # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and
-    # ceil(T/4) partial rows
-    assert ar.workspace_bytes(131072, 9, D) == 256 * D * 4 + 4096 * 7 * 18 * 8 + 32768 * D * 4 == 950_992_896
+    # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and the
+    # partial rows of one chunk of spans (ceil(T/4) rows, at most 8192): 32768
+    # tokens and above need the same
+    assert ar.workspace_bytes(131072, 9, D) == 256 * D * 4 + 4096 * 7 * 18 * 8 + 8192 * D * 4 == 246_349_824
+    assert ar.workspace_bytes(32768, 9, D) == ar.workspace_bytes(131072, 9, D) == ar.workspace_bytes(262144, 9, D)
+    assert ar.workspace_bytes(32764, 9, D) == 256 * D * 4 + 4096 * 7 * 18 * 8 + 8191 * D * 4
     assert ar.workspace_bytes(1, 1, 8) == 256 * 8 * 4 + 4096 * 1 * 2 * 8 + 8 * 4
     assert ar.workspace_bytes(1000, 9, 12288) == 256 * 12288 * 4  # one-token-per-workgroup backward
 
@@ -476,3 +479,19 @@ def test_split_spin_setter_returns_the_previous_bound():
     assert ar.set_split_spin(ar.SPLIT_SPIN_DEFAULT) == 0
     with pytest.raises(ValueError):
         ar.set_split_spin(-1)
+
+
+def test_workspace_macro_matches_binding(tmp_path):
+    """ATTNRES_BWD_WORKSPACE_BYTES, compiled by a plain C compiler, gives the
+    binding's workspace_bytes at the chunk and split boundaries."""
+    cases = [(T, N, D_) for T in (0, 1, 3, 4, 5, 32763, 32764, 32765, 32768, 32769, 131072, 262147)
+             for N in (1, 9) for D_ in (8, 1024, 7168, 8192, 8200, 16384)]
+    src = tmp_path / "ws.c"
+    body = "\n".join(f'  printf("%zu\\n", (size_t)ATTNRES_BWD_WORKSPACE_BYTES({T}LL, {N}, {D_}));' for T, N, D_ in cases)
+    src.write_text(f'#include <stdio.h>\n#include "attnres.h"\nint main(void) {{\n{body}\n  return 0;\n}}\n')
+    exe = tmp_path / "ws"
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", inc,
+                    "-o", str(exe), str(src)], check=True, capture_output=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == [ar.workspace_bytes(T, N, D_) for T, N, D_ in cases]

@@ -47,10 +47,11 @@ def test_workspace_traffic():
     algorithmic bytes: per-group partial rows and fold rows written and read,
     the exchange ring cleared (D <= 8192); 256 partial rows otherwise."""
     D = 7168
-    # T = 131072: 32768 spans of 4 tokens, folded 128 at a time into 256 rows
-    assert bench.workspace_traffic(131072, 9, D) == 8 * 32768 * D + 8 * 256 * D + 4096 * 7 * 18 * 8
-    # T = 100: 25 spans, one per fold row
-    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 8 * 25 * 64 + 4096 * 1 * 6 * 8
+    # T = 131072: 32768 spans of 4 tokens in 4 chunks, each folded into the 256
+    # fold rows (written 4 times, re-read 3 times, read once by the final sum)
+    assert bench.workspace_traffic(131072, 9, D) == 8 * 32768 * D + 4 * 256 * D * 8 + 4096 * 7 * 18 * 8
+    # T = 100: 25 spans, one chunk, one span per fold row
+    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 4 * 25 * 64 * 2 + 4096 * 1 * 6 * 8
     assert bench.workspace_traffic(5000, 9, 12288) == 8 * 256 * 12288
     assert bench.workspace_traffic(100, 9, 12288) == 8 * 100 * 12288
 
