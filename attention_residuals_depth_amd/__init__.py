@@ -89,7 +89,9 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-SPLIT_MAX_D = 8192
+SPLIT_MAX_D = 7168
+SPLIT_ANY_N_MAX_D = 1024
+SPLIT_MIN_N = 8
 SPLIT_TOKENS = 4
 SPLIT_RING = 4096
 SPLIT_CHUNK_SPANS = 8192
@@ -104,12 +106,18 @@ def set_split_spin(polls: int) -> int:
     return int(library().attnres_set_split_spin(polls))
 
 
+def bwd_split(N: int, D: int) -> bool:
+    """ATTNRES_BWD_SPLIT: whether attnres_bwd / attnres_bwd_sources run the split
+    backward (else the one-token-per-workgroup backward) for N sources of D."""
+    return D <= SPLIT_ANY_N_MAX_D or (N >= SPLIT_MIN_N and D <= SPLIT_MAX_D)
+
+
 def workspace_bytes(T: int, N: int, D: int) -> int:
     """Bytes of device workspace attnres_bwd / attnres_bwd_sources need
-    (ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)): the dw partial rows and, for
-    D <= 8192, the split backward's exchange ring and per-group partial rows."""
+    (ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)): the dw partial rows and, where the
+    split backward runs, its exchange ring and one chunk's partial rows."""
     b = DW_PARTIALS * D * 4
-    if D <= SPLIT_MAX_D:
+    if bwd_split(N, D):
         spans = min((T + SPLIT_TOKENS - 1) // SPLIT_TOKENS, SPLIT_CHUNK_SPANS)
         b += SPLIT_RING * ((D + 1023) // 1024) * 2 * N * 8 + spans * D * 4
     return b
@@ -561,5 +569,5 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
            "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
-           "SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT", "set_split_spin",
+           "SPLIT_MAX_D", "SPLIT_ANY_N_MAX_D", "SPLIT_MIN_N", "bwd_split", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT", "set_split_spin",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

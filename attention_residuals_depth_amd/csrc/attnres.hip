@@ -1175,7 +1175,7 @@ __global__ void __launch_bounds__(kReduceThreads) dw_reduce_kernel(const float4*
 }
 
 // ---------------------------------------------------------------------------
-// Backward with tokens split over workgroups (D <= 8192)
+// Backward with tokens split over workgroups (where ATTNRES_BWD_SPLIT(N, D))
 // ---------------------------------------------------------------------------
 // Each token's D channels are cut into K slices of 128 16-byte vectors, and a
 // workgroup takes one slice of ATTNRES_SPLIT_TOKENS consecutive tokens side
@@ -1186,6 +1186,11 @@ __global__ void __launch_bounds__(kReduceThreads) dw_reduce_kernel(const float4*
 // 32K-256K tokens at N = 9, D = 7168), and 512-thread workgroups (two per CU
 // at this kernel's register use) beat 1024-thread ones, whose tails leave
 // the CU idle, and workgroups that walk two or four such spans in turn.
+// With fewer sources a token carries less work per exchange: at T = 32768
+// the one-token backward was faster for N <= 7 at D = 2048-7168 (up to 1.5x
+// at N = 1) and at D = 8192 for every N, the split one for N >= 8 up to
+// D = 7168 and for every N at D = 1024 (1.3-1.7x); ATTNRES_BWD_SPLIT in the
+// header encodes that choice, which depends on (N, D) alone.
 //
 // The per-token sums g.x_i and w.x_i then span K workgroups.  Each member
 // publishes its slice's 2N partial sums as 64-bit {tag, value} words in a
@@ -1995,14 +2000,14 @@ attnres_status bwd_common_checks(const float* w, int32_t N, int64_t T, int32_t D
   return ATTNRES_OK;
 }
 
-// split: the split-token backward (D <= ATTNRES_SPLIT_MAX_D) with the
+// split: the split-token backward (where ATTNRES_BWD_SPLIT(N, D)) with the
 // workspace layout [fold rows][ring][partial rows]; otherwise the
 // one-token-per-workgroup backward with its ATTNRES_DW_PARTIALS rows.
 attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64_t src_pitch, const float* w,
                         const float* rstd, const float* alpha, int32_t N, int64_t T, int32_t D,
                         void* const* dsrcs, int64_t dsrc_pitch, int mode, float* dw, void* workspace,
                         size_t workspace_bytes, void* stream, bool split = true) {
-  split = split && D <= ATTNRES_SPLIT_MAX_D;
+  split = split && ATTNRES_BWD_SPLIT(N, D);
   const int64_t gsize = (mode & kGradF32) ? 4 : 2;  // bytes per gradient element
   if (dout == nullptr || rstd == nullptr || alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(dout, 16) || !aligned(rstd, 4) || !aligned(alpha, 4)) return ATTNRES_ERR_INVALID_ARGUMENT;

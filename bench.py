@@ -399,10 +399,10 @@ def sweep(ar, torch, dev, reps=20):
     through the per-source calls, and the peak allocated memory of the
     stacked case (sources, dout, w, outputs, saved state, dw, workspace)."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    D = 7168
-    cases = [(9, T) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
-    cases += [(N, 32768) for N in range(2, 9)]
-    for N, T in cases:
+    cases = [(9, T, 7168) for T in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
+    cases += [(N, 32768, 7168) for N in range(2, 9)]
+    cases += [(9, 32768, D) for D in (4096, 12288, 16384)]  # other hidden sizes
+    for N, T, D in cases:
         torch.cuda.synchronize()
         held = torch.cuda.memory_allocated()  # the flush buffer and whatever the caller still holds
         g = torch.Generator(device=dev)

@@ -74,14 +74,21 @@ typedef enum {
 #define ATTNRES_GRAD_BF16 0
 #define ATTNRES_GRAD_ACCUMULATE 1
 #define ATTNRES_GRAD_F32 2
-/* The backward for D <= ATTNRES_SPLIT_MAX_D spreads every token over
- * ceil(D / 1024) workgroups, each taking one 1024-channel slice of
- * ATTNRES_SPLIT_TOKENS consecutive tokens side by side (a span); the per-token sums are
- * exchanged through a ring of ATTNRES_SPLIT_RING tokens in the workspace, and every
- * workgroup writes one dw partial row slice.  The spans run in chunks of
- * ATTNRES_SPLIT_CHUNK_SPANS, each followed by a fold of its partial rows, so the
- * workspace holds the partial rows of one chunk. */
-#define ATTNRES_SPLIT_MAX_D 8192
+/* The split backward spreads every token over ceil(D / 1024) workgroups, each
+ * taking one 1024-channel slice of ATTNRES_SPLIT_TOKENS consecutive tokens side by
+ * side (a span); the per-token sums are exchanged through a ring of
+ * ATTNRES_SPLIT_RING tokens in the workspace, and every workgroup writes one dw
+ * partial row slice.  The spans run in chunks of ATTNRES_SPLIT_CHUNK_SPANS, each
+ * followed by a fold of its partial rows, so the workspace holds the partial rows of
+ * one chunk.  It runs where it was measured faster on MI355X than the
+ * one-token-per-workgroup backward: ATTNRES_BWD_SPLIT(N, D), i.e. D <= 1024, or
+ * N >= 8 with D <= ATTNRES_SPLIT_MAX_D.  The choice depends on (N, D) only, so every
+ * call with the same N and D uses the same reduction trees. */
+#define ATTNRES_SPLIT_MAX_D 7168
+#define ATTNRES_SPLIT_ANY_N_MAX_D 1024
+#define ATTNRES_SPLIT_MIN_N 8
+#define ATTNRES_BWD_SPLIT(N, D)                                                                                    \
+  ((D) <= ATTNRES_SPLIT_ANY_N_MAX_D || ((N) >= ATTNRES_SPLIT_MIN_N && (D) <= ATTNRES_SPLIT_MAX_D))
 #define ATTNRES_SPLIT_TOKENS 4
 #define ATTNRES_SPLIT_RING 4096
 #define ATTNRES_SPLIT_CHUNK_SPANS 8192
@@ -96,12 +103,12 @@ typedef enum {
        : ATTNRES_SPLIT_CHUNK_SPANS)
 /* Bytes of device workspace attnres_bwd / attnres_bwd_sources need for T
  * tokens, N sources and hidden size D: ATTNRES_DW_PARTIALS fp32 rows of D,
- * plus for D <= ATTNRES_SPLIT_MAX_D the exchange ring (8-byte words) and
- * ATTNRES_SPLIT_PARTIAL_ROWS(T) fp32 partial rows of D (at T >= 32768,
- * N = 9, D = 7168: 7.3 + 4.1 + 234.9 MB). */
+ * plus, where the split backward runs (ATTNRES_BWD_SPLIT), the exchange ring
+ * (8-byte words) and ATTNRES_SPLIT_PARTIAL_ROWS(T) fp32 partial rows of D (at
+ * T >= 32768, N = 9, D = 7168: 7.3 + 4.1 + 234.9 MB). */
 #define ATTNRES_BWD_WORKSPACE_BYTES(T, N, D)                                                                       \
   ((size_t)ATTNRES_DW_PARTIALS * (size_t)(D) * sizeof(float) +                                                   \
-   ((D) <= ATTNRES_SPLIT_MAX_D                                                                                   \
+   (ATTNRES_BWD_SPLIT(N, D)                                                                                      \
         ? (size_t)ATTNRES_SPLIT_RING * (size_t)(((D) + 1023) / 1024) * 2 * (size_t)(N) * 8 +                      \
               (size_t)ATTNRES_SPLIT_PARTIAL_ROWS(T) * (size_t)(D) * sizeof(float)                                \
         : 0))
@@ -332,7 +339,7 @@ attnres_status attnres_bwd_noalloc(const uint16_t* dout, const uint16_t* src, co
                                    void* stream);
 
 /*
- * Poll bound of the split backward (D <= ATTNRES_SPLIT_MAX_D): a workgroup
+ * Poll bound of the split backward (ATTNRES_BWD_SPLIT(N, D)): a workgroup
  * waiting for another slice's partial sums of a token reads that member's
  * ring word at most `polls` times, then recomputes the member's partial sums
  * from HBM itself, with the member's own arithmetic and reduction tree, so

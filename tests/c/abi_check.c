@@ -2,8 +2,10 @@
  * A plain C consumer of libattnres: no Python, no torch.  Device memory comes
  * from hipMalloc, inputs from the seeded generator (libsynth), the reference
  * from the fp64 oracle (liboracle, test infrastructure).  It runs the stacked
- * forward/backward and the per-source forward on a small workload (N = 3,
- * T = 130, D = 7168, source scales 1, 2, 4), compares against the oracle with
+ * forward/backward and the per-source forward on a small workload (N = 8,
+ * T = 130, D = 7168, source scales 1, 2, 4 repeated; N = 8 takes the split
+ * backward, whose exchange is also run on its recompute route), compares
+ * against the oracle with
  * the operator's tolerances, checks that a bad argument is refused with
  * ATTNRES_ERR_INVALID_ARGUMENT, and exits 0 only if everything holds.
  */
@@ -64,11 +66,11 @@ static double rel_l2_f32(const float* got, const double* ref, size_t n) {
 }
 
 int main(void) {
-  const int N = 3;
+  const int N = 8;
   const int64_t T = 130, D = 7168;
   const float eps = 1e-6f;
   const size_t nsrc = (size_t)N * T * D, nTD = (size_t)T * D, nTN = (size_t)T * N;
-  const float scales[3] = {1.f, 2.f, 4.f};
+  const float scales[8] = {1.f, 2.f, 4.f, 1.f, 2.f, 4.f, 1.f, 2.f};
 
   uint16_t* src = malloc(nsrc * 2);
   uint16_t* dout = malloc(nTD * 2);
@@ -102,7 +104,8 @@ int main(void) {
   if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd returned %d\n", (int)st); return 1; }
   st = attnres_bwd(d_dout, d_src, d_w, d_rstd, d_alpha, N, T, (int32_t)D, d_dsrc, d_dw, d_ws, ws_bytes, NULL);
   if (st != ATTNRES_OK) { fprintf(stderr, "attnres_bwd returned %d\n", (int)st); return 1; }
-  const uint16_t* srcs[3] = {d_src, d_src + nTD, d_src + 2 * nTD};
+  const uint16_t* srcs[8];
+  for (int i = 0; i < N; ++i) srcs[i] = d_src + (size_t)i * nTD;
   st = attnres_fwd_sources(srcs, D, d_w, eps, N, T, (int32_t)D, d_out2, d_rstd2, d_alpha2, NULL);
   if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd_sources returned %d\n", (int)st); return 1; }
   st = attnres_fwd(d_src, d_w, eps, 10, T, (int32_t)D, d_out, d_rstd, d_alpha, NULL);

@@ -95,8 +95,12 @@ def test_header_constants_match_binding():
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
-    for name in ("SPLIT_MAX_D", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT"):
+    for name in ("SPLIT_MAX_D", "SPLIT_ANY_N_MAX_D", "SPLIT_MIN_N", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS",
+                 "SPLIT_SPIN_DEFAULT"):
         assert _define("ATTNRES_" + name) == getattr(ar, name)
+    # the split backward where it measured faster: every N up to D = 1024, N >= 8 up to D = 7168
+    assert ar.bwd_split(1, 8) and ar.bwd_split(3, 1024) and ar.bwd_split(8, 7168) and ar.bwd_split(9, 2048)
+    assert not ar.bwd_split(7, 7168) and not ar.bwd_split(9, 7176) and not ar.bwd_split(2, 1032)
     # the backward's workspace: 256 partial rows, and for D <= 8192 the exchange
     # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and the
     # partial rows of one chunk of spans (ceil(T/4) rows, at most 8192): 32768
@@ -106,6 +110,7 @@ def test_header_constants_match_binding():
     assert ar.workspace_bytes(32764, 9, D) == 256 * D * 4 + 4096 * 7 * 18 * 8 + 8191 * D * 4
     assert ar.workspace_bytes(1, 1, 8) == 256 * 8 * 4 + 4096 * 1 * 2 * 8 + 8 * 4
     assert ar.workspace_bytes(1000, 9, 12288) == 256 * 12288 * 4  # one-token-per-workgroup backward
+    assert ar.workspace_bytes(131072, 7, D) == 256 * D * 4  # one-token backward for N <= 7 at D = 7168
 
 
 def _fwd(src=A, w=2 * A, eps=1e-6, N=9, T=16, D_=D, out=None, rstd=None, alpha=None):
@@ -485,7 +490,7 @@ def test_workspace_macro_matches_binding(tmp_path):
     """ATTNRES_BWD_WORKSPACE_BYTES, compiled by a plain C compiler, gives the
     binding's workspace_bytes at the chunk and split boundaries."""
     cases = [(T, N, D_) for T in (0, 1, 3, 4, 5, 32763, 32764, 32765, 32768, 32769, 131072, 262147)
-             for N in (1, 9) for D_ in (8, 1024, 7168, 8192, 8200, 16384)]
+             for N in (1, 7, 8, 9) for D_ in (8, 1024, 1032, 7168, 7176, 8192, 8200, 16384)]
     src = tmp_path / "ws.c"
     body = "\n".join(f'  printf("%zu\\n", (size_t)ATTNRES_BWD_WORKSPACE_BYTES({T}LL, {N}, {D_}));' for T, N, D_ in cases)
     src.write_text(f'#include <stdio.h>\n#include "attnres.h"\nint main(void) {{\n{body}\n  return 0;\n}}\n')

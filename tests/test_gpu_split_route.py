@@ -44,11 +44,18 @@ def _inputs(N, T, D, seed):
     return src, w, dout, rstd, alpha
 
 
-# (N, T, D): the full width (7 slices), a ragged last slice (D/8 = 513 vectors,
-# the fifth slice has one), one slice, and token counts that leave the last
-# 4-token span ragged
-@pytest.mark.parametrize("N,T,D", [(9, 131, 7168), (3, 66, 4104), (1, 5, 8), (9, 4, 1024), (5, 257, 8192)],
-                         ids=lambda v: str(v))
+# (N, T, D), all where the split backward runs (ATTNRES_BWD_SPLIT): the full
+# width (7 slices), a ragged last slice (D/8 = 513 vectors, the fifth slice has
+# one; 895 vectors, the seventh has 127), one slice, and token counts that
+# leave the last 4-token span ragged
+SHAPES = [(9, 131, 7168), (8, 66, 4104), (1, 5, 8), (9, 4, 1024), (8, 257, 7160), (3, 70, 1024)]
+
+
+def test_shapes_take_the_split_backward():
+    assert all(ar.bwd_split(N, D) for N, _, D in SHAPES)
+
+
+@pytest.mark.parametrize("N,T,D", SHAPES, ids=lambda v: str(v))
 @pytest.mark.parametrize("polls", [0, 1])
 def test_recompute_route_is_bitwise_the_exchange(N, T, D, polls, spin):
     src, w, dout, rstd, alpha = _inputs(N, T, D, 0)
