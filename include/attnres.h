@@ -153,7 +153,12 @@ attnres_status attnres_fwd(const uint16_t* src, const float* w, float eps, int32
  *   workspace              device scratch of at least
  *                          ATTNRES_BWD_WORKSPACE_BYTES(T, N, D) bytes, 16-byte
  *                          aligned; contents on entry are ignored and on exit
- *                          unspecified.  May be NULL when T == 0.
+ *                          unspecified.  May be NULL when T == 0.  It holds the
+ *                          call's dw partial rows and, for the split backward,
+ *                          its exchange ring: calls that can run at the same
+ *                          time (on different streams) need different
+ *                          workspaces; calls in order on one stream can share
+ *                          one.
  * Alignment: dout, src, w, dsrc, dw, workspace 16-byte aligned; rstd, alpha
  * 4-byte aligned.  dsrc, dw and the workspace must not overlap each other or
  * any input.  Status ATTNRES_ERR_WORKSPACE if the workspace is NULL or
