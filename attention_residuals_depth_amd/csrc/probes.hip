@@ -143,6 +143,49 @@ __global__ void __launch_bounds__(1024) bwd_pattern_kernel(Rows src, const uint1
   }
 }
 
+
+// Split backward pattern: a workgroup of 4 x 128 threads takes one
+// 1024-channel slice (128 16-byte vectors) of 4 consecutive tokens side by
+// side (workgroup b = span * K + slice, K = ceil(D / 1024)); each thread reads
+// its vector of dout and of the N source rows of its token, writes its vector
+// of the N gradient rows, and side 0 writes the span's fp32 partial row slice
+// (2 x 16 bytes per thread) into `partial`, whose rows are reused every
+// kSplitChunk spans as the operator's chunked workspace is.  No exchange and
+// no arithmetic beyond an OR.
+constexpr int kSplitSide = 4;
+constexpr int kSplitSlice = 128;
+constexpr int64_t kSplitChunk = 8192;
+
+__global__ void __launch_bounds__(kSplitSide * kSplitSlice) split_bwd_pattern_kernel(Rows src,
+                                                                                     const uint16_t* __restrict__ dout,
+                                                                                     WRows dst, int32_t N, int64_t T,
+                                                                                     int32_t D, int32_t K,
+                                                                                     float* __restrict__ partial) {
+  const int side = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kSplitSlice);
+  const int tl = (int)threadIdx.x % kSplitSlice;
+  const int64_t span = blockIdx.x / K;
+  const int k = (int)(blockIdx.x % K);
+  const int v = k * kSplitSlice + tl;
+  const uint32_t off = v < D / 8 ? (uint32_t)v * 16u : 0xFFFFFFF0u;  // past the row: zeros, stores dropped
+  const int64_t t = span * kSplitSide + side;
+  const bool valid = t < T;
+  const int64_t tt = valid ? t : 0;
+  const uint32_t bytes = valid ? (uint32_t)D * 2u : 0u;
+  const u32x4_t g = ld(rsrc(dout + tt * D, bytes), off);
+  u32x4_t x[kMaxN];
+#pragma unroll
+  for (int i = 0; i < kMaxN; ++i)
+    if (i < N) x[i] = ld(rsrc(src.p[i] + tt * D, bytes), off);
+#pragma unroll
+  for (int i = 0; i < kMaxN; ++i)
+    if (i < N) st(rsrc(dst.p[i] + tt * D, bytes), off, x[i] | g);
+  if (side == 0) {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(partial + (span % kSplitChunk) * D, (uint32_t)D * 4u);
+    __builtin_amdgcn_raw_buffer_store_b128(g, rp, 2u * off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(g, rp, 2u * off + 16u, 0, 0);
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int launched() { return hipGetLastError() == hipSuccess ? 0 : 3; }
@@ -221,5 +264,25 @@ extern "C" int attnres_probe_bwd_pattern(const uint16_t* const* srcs, const uint
   const int P = T < kPersistent ? (int)T : kPersistent;
   hipLaunchKernelGGL(bwd_pattern_kernel, dim3((unsigned)P), dim3(threads_for(D, 1)), 0, (hipStream_t)stream, r, dout,
                      w, N, T, D, P);
+  return launched();
+}
+
+extern "C" int attnres_probe_split_bwd_pattern(const uint16_t* const* srcs, const uint16_t* dout, int32_t N, int64_t T,
+                                               int32_t D, uint16_t* const* dsrcs, float* partial, void* stream) {
+  if (!pattern_sizes_ok(N, T, D) || srcs == nullptr || dsrcs == nullptr) return 1;
+  if (T == 0) return 0;
+  if (dout == nullptr || !aligned16(dout) || partial == nullptr || !aligned16(partial)) return 1;
+  Rows r{};
+  WRows w{};
+  for (int i = 0; i < N; ++i) {
+    if (srcs[i] == nullptr || !aligned16(srcs[i]) || dsrcs[i] == nullptr || !aligned16(dsrcs[i])) return 1;
+    r.p[i] = srcs[i];
+    w.p[i] = dsrcs[i];
+  }
+  const int K = (D / 8 + kSplitSlice - 1) / kSplitSlice;
+  const int64_t spans = (T + kSplitSide - 1) / kSplitSide;
+  if (spans * K > (int64_t)UINT32_MAX / (kSplitSide * kSplitSlice)) return 1;
+  hipLaunchKernelGGL(split_bwd_pattern_kernel, dim3((unsigned)(spans * K)), dim3(kSplitSide * kSplitSlice), 0,
+                     (hipStream_t)stream, r, dout, w, N, T, D, K, partial);
   return launched();
 }

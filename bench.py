@@ -572,6 +572,7 @@ class Probes:
         lib.attnres_probe_copy.argtypes = [vp, vp, sz, vp]
         lib.attnres_probe_fwd_pattern.argtypes = [pp, i32, i64, i32, vp, vp]
         lib.attnres_probe_bwd_pattern.argtypes = [pp, vp, i32, i64, i32, pp, vp]
+        lib.attnres_probe_split_bwd_pattern.argtypes = [pp, vp, i32, i64, i32, pp, vp, vp]
         self.lib = lib
 
     @staticmethod
@@ -584,14 +585,16 @@ def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 <<
     """Median GB/s of the probe kernels on this device: plain read, write and
     copy streams of `nbytes` (one 4 KiB chunk per workgroup, nontemporal), and
     the operator's forward and backward access patterns on the workload's own
-    buffers (same rows, same launch shapes, no arithmetic).  Overwrites out and
-    dsrc."""
+    buffers (same rows, same launch shapes, no arithmetic; the backward both as
+    the one-token kernel and as the split kernel walk the rows).  Overwrites
+    out and dsrc."""
     pr = Probes()
     stream = torch.cuda.current_stream().cuda_stream
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     N, T, D = src.shape
+    part = torch.empty((min((T + 3) // 4, 8192), D), dtype=torch.float32, device=dev)
     srcs = (ctypes.c_void_p * N)(*[src[i].data_ptr() for i in range(N)])
     dsrcs = (ctypes.c_void_p * N)(*[dsrc[i].data_ptr() for i in range(N)])
     calls = {
@@ -605,6 +608,10 @@ def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 <<
         "bwd_pattern": (lambda: pr.check(pr.lib.attnres_probe_bwd_pattern(srcs, dout.data_ptr(), N, T, D, dsrcs,
                                                                           stream), "bwd_pattern"),
                         T * (4 * N * D + 2 * D)),
+        # the split backward's pattern, counted at the same bytes (its partial rows are not counted)
+        "split_bwd_pattern": (lambda: pr.check(pr.lib.attnres_probe_split_bwd_pattern(
+            srcs, dout.data_ptr(), N, T, D, dsrcs, part.data_ptr(), stream), "split_bwd_pattern"),
+                              T * (4 * N * D + 2 * D)),
     }
     res = {}
     ev = TimingEvents(2)
@@ -621,7 +628,7 @@ def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 <<
                 ms.append(ev.ms(0, 1))
         res[name] = moved / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
     ev.close()
-    del a, b
+    del a, b, part
     torch.cuda.empty_cache()
     return res
 

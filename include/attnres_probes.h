@@ -62,6 +62,18 @@ int attnres_probe_fwd_pattern(const uint16_t* const* srcs, int32_t N, int64_t T,
 int attnres_probe_bwd_pattern(const uint16_t* const* srcs, const uint16_t* dout, int32_t N, int64_t T, int32_t D,
                               uint16_t* const* dsrcs, void* stream);
 
+/*
+ * The split backward's access pattern without its arithmetic or its exchange:
+ * a workgroup of 4 x 128 threads reads one 1024-channel slice of 4
+ * consecutive tokens' dout and N source rows and writes that slice of their N
+ * gradient rows (row i's value: row i OR dout's row), and writes one fp32
+ * partial row slice per 4 tokens into `partial` ([min(ceil(T/4), 8192)][D]
+ * fp32, 16-byte aligned; rows reused every 8192 spans, as the operator's
+ * chunked workspace is).  Same limits as attnres_probe_fwd_pattern.
+ */
+int attnres_probe_split_bwd_pattern(const uint16_t* const* srcs, const uint16_t* dout, int32_t N, int64_t T,
+                                    int32_t D, uint16_t* const* dsrcs, float* partial, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -438,7 +438,7 @@ PROBE_LIB = os.path.join(ROOT, "attention_residuals_depth_amd", "libattnres_prob
 def test_probe_library_exports_declared_symbols_and_refuses_bad_arguments():
     names = re.findall(r"^int\s+(attnres_probe_\w+)\s*\(", open(PROBE_HEADER).read(), re.M)
     assert names == ["attnres_probe_read", "attnres_probe_write", "attnres_probe_copy", "attnres_probe_fwd_pattern",
-                     "attnres_probe_bwd_pattern"]
+                     "attnres_probe_bwd_pattern", "attnres_probe_split_bwd_pattern"]
     lib = ctypes.CDLL(PROBE_LIB)
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -455,6 +455,9 @@ def test_probe_library_exports_declared_symbols_and_refuses_bad_arguments():
     ptrs = (ctypes.c_void_p * 9)(*([A] * 9))
     assert lib.attnres_probe_fwd_pattern(ptrs, 10, 16, D, A, None) == 1   # N > 9
     assert lib.attnres_probe_fwd_pattern(ptrs, 9, 16, 8200, A, None) == 1  # D > 8192
+    lib.attnres_probe_split_bwd_pattern.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp]
+    assert lib.attnres_probe_split_bwd_pattern(ptrs, A, 9, 16, D, ptrs, None, None) == 1      # no partial rows
+    assert lib.attnres_probe_split_bwd_pattern(ptrs, A, 9, 16, D, ptrs, A + 4, None) == 1     # misaligned
     assert lib.attnres_probe_read(A, 0, A, None) == 0              # empty: nothing to do
 
 
