@@ -1496,7 +1496,23 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
     }
     if (valid) {
       const __amdgpu_buffer_rsrc_t rd = grad_row<F32>(a.dsrc, i, t, D);
-      if constexpr (F32) {
+      if constexpr (F32 && !ACC) {
+        // written fp32 gradients: the wave's 64 x 32 bytes pass through an LDS
+        // stage (the wave's part of dws, free until the dw sums) so that each
+        // store writes one contiguous KiB with the streaming hint, as in the
+        // one-token backward; wave barriers order the lanes' exchange
+        const int lane = lane_id();
+        float4* st = &dws[side][kWave * half][0];
+        st[2 * lane] = make_float4(d[0], d[1], d[2], d[3]);
+        st[2 * lane + 1] = make_float4(d[4], d[5], d[6], d[7]);
+        wave_sync();
+        const float4 lo = st[lane], hi = st[kWave + lane];
+        wave_sync();
+        // the wave's first vector in fp32 bytes; lanes past the row store past D * 4: dropped
+        const uint32_t wbase = (uint32_t)(k * kSpSliceVectors + kWave * half) * 32u;
+        bstore<kAuxStreamStore>(rd, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
+        bstore<kAuxStreamStore>(rd, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
+      } else if constexpr (F32) {
         bstore(rd, 2u * off, make_uint4(__builtin_bit_cast(uint32_t, d[0]), __builtin_bit_cast(uint32_t, d[1]),
                                         __builtin_bit_cast(uint32_t, d[2]), __builtin_bit_cast(uint32_t, d[3])));
         bstore(rd, 2u * off + 16u, make_uint4(__builtin_bit_cast(uint32_t, d[4]), __builtin_bit_cast(uint32_t, d[5]),
@@ -1506,7 +1522,9 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
       }
     }
   }
-  // dw: this slice's sum over the workgroup's tokens, in side order
+  // dw: this slice's sum over the workgroup's tokens, in side order (each
+  // lane writes only its own slots, which its wave's last stage reads, if any,
+  // have passed: the wave barrier after them)
   dws[side][tl][0] = make_float4(dwr[0], dwr[1], dwr[2], dwr[3]);
   dws[side][tl][1] = make_float4(dwr[4], dwr[5], dwr[6], dwr[7]);
   __syncthreads();
