@@ -85,3 +85,46 @@ def test_recompute_route_across_chunks():
         ar.set_split_spin(ar.SPLIT_SPIN_DEFAULT)
     assert torch.equal(d.view(torch.int16), ref_d.view(torch.int16))
     assert torch.equal(dw.view(torch.int32), ref_w.view(torch.int32))
+
+
+@pytest.mark.parametrize("accumulate,gdt", [(True, torch.bfloat16), (False, torch.float32), (True, torch.float32)],
+                         ids=["acc_bf16", "f32", "acc_f32"])
+def test_gradient_modes_across_chunks(accumulate, gdt):
+    """The per-source backward's other gradient modes across a chunk boundary, on
+    an interleaved [T][N][D] cache: the written or accumulated gradients minus
+    their prior contents against the oracle's, element by element within the
+    overwriting backward's derived bound (tests/parity.py) plus, when a bf16
+    sum is rounded, half an ulp of that sum; dw over the whole batch."""
+    import oracle
+    from parity import bf16_ulp, dsrc_bound
+    N, T, D = 8, CHUNK_TOKENS + 5, 1040
+    assert ar.bwd_split(N, D)
+    wl = synth.Workload("chunks_modes", T=T, N=N, D=D, seed=7)
+    src_h, w_h, dout_h = wl.sources(), wl.w(), wl.dout()
+    cache = to_dev_bf16(np.ascontiguousarray(src_h.transpose(1, 0, 2)))  # [T][N][D]
+    views = [cache[:, i] for i in range(N)]
+    w = torch.from_numpy(w_h).to(DEV)
+    dout = to_dev_bf16(dout_h)
+    _, rstd, alpha = ar.attnres_fwd_sources(views, w, wl.eps)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    prior = (torch.randn((T, N, D), generator=g, device=DEV) * 0.01).to(gdt)
+    grads = prior.clone()
+    _, dw = ar.attnres_bwd_sources(dout, views, w, rstd, alpha, dsrcs=[grads[:, i] for i in range(N)],
+                                   accumulate=accumulate)
+    torch.cuda.synchronize()
+    _, o_rstd, o_alpha = oracle.fwd(src_h, w_h, wl.eps)
+    o_dsrc, o_dw = oracle.bwd(src_h, w_h, wl.eps, dout_h)
+    res = grads.double().permute(1, 0, 2)                                    # [N][T][D] on the device
+    got = res - (prior.double().permute(1, 0, 2) if accumulate else 0.0)
+    ref = torch.from_numpy(o_dsrc).to(DEV)
+    x = cache.double().permute(1, 0, 2)
+    bound = dsrc_bound(x, dout.double(), w.double(), torch.from_numpy(o_rstd).to(DEV), rstd.double(),
+                       torch.from_numpy(o_alpha).to(DEV), alpha.double(), ref, got)
+    if accumulate and gdt == torch.bfloat16:
+        bound = bound + 0.5 * bf16_ulp(res.abs())
+    ratio = float(((got - ref).abs() / bound).max())
+    print(f"[chunks] {gdt} accumulate={accumulate}: max err / bound {ratio:.3f}", flush=True)
+    assert ratio <= 1.0
+    dw_rel = float(np.linalg.norm(dw.cpu().double().numpy() - o_dw) / np.linalg.norm(o_dw))
+    assert dw_rel <= 1e-5, dw_rel
