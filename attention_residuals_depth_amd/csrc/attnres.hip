@@ -2065,15 +2065,18 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
   float* ws = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int D4 = D / 4;
-  int32_t P = 0;  // rows dw_reduce_kernel sums
+  int32_t P = 0;            // rows dw_reduce_kernel sums
+  const float* reduce_rows = ws;  // where they are
   if (split) {
     const int K = (D / 8 + kSpSliceVectors - 1) / kSpSliceVectors;
     const int64_t groups = (T + kSpSide - 1) / kSpSide;  // token spans
     uint64_t* ring = reinterpret_cast<uint64_t*>(ws + (size_t)ATTNRES_DW_PARTIALS * D);
     const size_t ring_words = (size_t)kSpRing * K * 2 * N;
     float* partial = reinterpret_cast<float*>(ring + ring_words);
-    // tags are token + 1: a zeroed ring holds no valid word
-    const int ring4 = (int)(ring_words / 2);
+    // tags are token + 1: a zeroed ring holds no valid word.  Token t uses
+    // slot t mod kSpRing, so a batch of fewer tokens clears only its slots.
+    const int64_t slots = T < kSpRing ? T : kSpRing;
+    const int ring4 = (int)((size_t)slots * K * 2 * N / 2);
     hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
                        ring4);
     if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
@@ -2084,6 +2087,12 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
       const int64_t n = groups - c0 < kSpChunk ? groups - c0 : kSpChunk;
       const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, c0, c0, spin};
       if (run_split(N, mode, st, sa, n) != hipSuccess) return ATTNRES_ERR_HIP;
+      if (groups <= ATTNRES_DW_PARTIALS) {
+        // one span per fold row: the fold would copy the partial rows as they
+        // are, so the final sum reads them directly (the same bits)
+        reduce_rows = partial;
+        break;
+      }
       hipLaunchKernelGGL(dw_fold_kernel, dim3((unsigned)P, (unsigned)((D4 + kFoldCols - 1) / kFoldCols)),
                          dim3(kFoldCols), 0, st, reinterpret_cast<const float4*>(partial), c0, n, P, D4,
                          c0 == 0 ? 1 : 0, reinterpret_cast<float4*>(ws));
@@ -2096,7 +2105,7 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
     if (run_bwd(N, s, mode, st, args) != hipSuccess) return ATTNRES_ERR_HIP;
   }
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((D4 + kReduceCols - 1) / kReduceCols), dim3(kReduceThreads), 0, st,
-                     reinterpret_cast<const float4*>(ws), P, D4, reinterpret_cast<float4*>(dw));
+                     reinterpret_cast<const float4*>(reduce_rows), P, D4, reinterpret_cast<float4*>(dw));
   return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
