@@ -2088,8 +2088,9 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
       const SplitArgs sa{dout, rows, w, rstd, alpha, T, D, K, drows, ring, partial, c0, c0, spin};
       if (run_split(N, mode, st, sa, n) != hipSuccess) return ATTNRES_ERR_HIP;
       if (groups <= ATTNRES_DW_PARTIALS) {
-        // one span per fold row: the fold would copy the partial rows as they
-        // are, so the final sum reads them directly (the same bits)
+        // one span per fold row: the fold would add each partial row to +0,
+        // which returns it unchanged (a partial row holds no -0: its sums
+        // start from +0), so the final sum reads the partial rows directly
         reduce_rows = partial;
         break;
       }
