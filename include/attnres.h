@@ -32,8 +32,11 @@
  *   - Every pointer is a device pointer owned by the caller (the per-source
  *     calls take a host array of device pointers).  The library allocates no
  *     device memory, frees nothing and never synchronises; its only state is
- *     a mutex-guarded host cache of kernel occupancy per device, so calls are
- *     thread-safe and reentrant.  All work is enqueued on `stream`
+ *     a mutex-guarded host cache of kernel occupancy per device, the split
+ *     backward's poll bound (attnres_set_split_spin, an atomic) and the static
+ *     scratch array of attnres_bwd_noalloc, so calls are thread-safe and
+ *     reentrant (apart from that array: see attnres_bwd_noalloc).  All work
+ *     is enqueued on `stream`
  *     (a hipStream_t; NULL selects the null stream) and the call returns once
  *     the work is enqueued.
  *   - Outputs are overwritten, never accumulated (except by the
@@ -44,7 +47,10 @@
  *     any error the call returns a non-zero status and enqueues nothing.
  *   - Results for one token depend only on that token's inputs (and w): they
  *     are bitwise independent of T, of the token's position in the batch and
- *     of the run.  dw is bitwise reproducible for a given (T, N, D).
+ *     of the run, for every call with the same (N, D).  dw is bitwise
+ *     reproducible for a given (T, N, D).  (attnres_bwd_noalloc runs the
+ *     one-token backward also where attnres_bwd runs the split one,
+ *     ATTNRES_BWD_SPLIT; the two agree within rounding, not bit for bit.)
  */
 #ifndef ATTNRES_H
 #define ATTNRES_H
@@ -67,8 +73,10 @@ typedef enum {
 #define ATTNRES_MAX_SOURCES 9
 /* Largest hidden size the kernels accept (a row group lives on chip). */
 #define ATTNRES_MAX_D 16384
-/* Rows of dw partial sums in the backward workspace: with P = min(T, 256)
- * backward workgroups, row c holds the sum over tokens c, c+P, c+2P, ... */
+/* Rows of dw partial sums the backward's final sum reads (P <= 256 of them,
+ * at the start of the workspace): for the one-token backward, workgroup c of
+ * P = min(T, 256) sums tokens c, c+P, c+2P, ...; for the split backward, fold
+ * row b sums the 4-token spans b, b+P, b+2P, ... with P = min(spans, 256). */
 #define ATTNRES_DW_PARTIALS 256
 /* grad_mode flags of attnres_bwd_sources. */
 #define ATTNRES_GRAD_BF16 0
