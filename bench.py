@@ -73,17 +73,22 @@ def algo_bytes(T: int, N: int, D: int):
 def workspace_traffic(T: int, N: int, D: int) -> int:
     """Bytes one attnres_bwd call moves through its workspace (written plus
     read; not HBM bytes: a chunk's partial rows mostly stay in the Infinity
-    Cache).  For D <= 8192: the per-span dw partial rows (ceil(T/4) rows of D
-    fp32) written and read back, the P = min(spans, 256) fold rows written by
-    every chunk's fold, re-read by every later one and read by the final sum,
-    and the exchange ring cleared; otherwise the 256 partial rows written and
+    Cache).  Where the split backward runs (ATTNRES_BWD_SPLIT(N, D)): the
+    per-span dw partial rows (ceil(T/4) rows of D fp32) written and read back,
+    the P = min(spans, 256) fold rows written by every chunk's fold, re-read by
+    every later one and read by the final sum (no fold when P spans fill the
+    rows: then the final sum reads the partial rows), and the ring slots the
+    batch uses cleared; otherwise the min(T, 256) partial rows written and
     read."""
-    if D <= 8192:
+    import attention_residuals_depth_amd as ar
+
+    if ar.bwd_split(N, D):
         groups = (T + 3) // 4
         chunks = (groups + 8191) // 8192
         P = min(groups, 256)
-        ring = 4096 * ((D + 1023) // 1024) * 2 * N * 8
-        return 8 * groups * D + 4 * P * D * (2 * chunks) + ring
+        ring = min(T, 4096) * ((D + 1023) // 1024) * 2 * N * 8
+        fold = 4 * P * D * (2 * chunks) if groups > 256 else 0
+        return 8 * groups * D + fold + ring
     return 8 * min(T, 256) * D
 
 

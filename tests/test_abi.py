@@ -101,7 +101,7 @@ def test_header_constants_match_binding():
     # the split backward where it measured faster: every N up to D = 1024, N >= 8 up to D = 7168
     assert ar.bwd_split(1, 8) and ar.bwd_split(3, 1024) and ar.bwd_split(8, 7168) and ar.bwd_split(9, 2048)
     assert not ar.bwd_split(7, 7168) and not ar.bwd_split(9, 7176) and not ar.bwd_split(2, 1032)
-    # the backward's workspace: 256 partial rows, and for D <= 8192 the exchange
+    # the backward's workspace: 256 partial rows, and where the split backward runs the exchange
     # ring (4096 tokens x ceil(D/1024) slices x 2N words of 8 bytes) and the
     # partial rows of one chunk of spans (ceil(T/4) rows, at most 8192): 32768
     # tokens and above need the same

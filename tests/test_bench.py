@@ -44,14 +44,18 @@ def test_algorithmic_bytes_of_the_default_workload():
 
 def test_workspace_traffic():
     """The backward's workspace traffic, reported next to (not inside) the
-    algorithmic bytes: per-group partial rows and fold rows written and read,
-    the exchange ring cleared (D <= 8192); 256 partial rows otherwise."""
+    algorithmic bytes: per-span partial rows and fold rows written and read,
+    the exchange ring cleared (where the split backward runs); the one-token
+    backward's partial rows otherwise."""
     D = 7168
     # T = 131072: 32768 spans of 4 tokens in 4 chunks, each folded into the 256
     # fold rows (written 4 times, re-read 3 times, read once by the final sum)
     assert bench.workspace_traffic(131072, 9, D) == 8 * 32768 * D + 4 * 256 * D * 8 + 4096 * 7 * 18 * 8
-    # T = 100: 25 spans, one chunk, one span per fold row
-    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 4 * 25 * 64 * 2 + 4096 * 1 * 6 * 8
+    # T = 100: 25 spans, one per fold row: no fold, the final sum reads the partial rows;
+    # the ring slots of 100 tokens cleared
+    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 100 * 1 * 6 * 8
+    # N = 7 at D = 7168 takes the one-token backward: 256 partial rows
+    assert bench.workspace_traffic(131072, 7, D) == 8 * 256 * D
     assert bench.workspace_traffic(5000, 9, 12288) == 8 * 256 * 12288
     assert bench.workspace_traffic(100, 9, 12288) == 8 * 100 * 12288
 
