@@ -1339,10 +1339,15 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
   __syncthreads();
   uint64_t* ring = a.ring + (t % kSpRing) * (int64_t)K * (2 * N);
   const uint32_t tag = (uint32_t)t + 1u;
+  const bool alone = K == 1;  // one slice per row (D <= 1024): no other member to wait for
   if (valid && tl < 2 * N) {
     const float p = red[side][0][tl] + red[side][1][tl];
-    const uint64_t word = ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, p);
-    __hip_atomic_store(ring + k * (2 * N) + tl, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (alone) {
+      words[side][0][tl] = p;  // the value the ring would carry
+    } else {
+      const uint64_t word = ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, p);
+      __hip_atomic_store(ring + k * (2 * N) + tl, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // the K members' words, member by member (this one's included).  The
   // members start within about a microsecond of each other, so the first poll
@@ -1350,7 +1355,7 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
   // and those device-coherent reads compete with the row traffic (measured on
   // MI355X at N = 9, D = 7168: 2-3% faster at T = 4K-128K than polling at
   // once; longer waits were slower again).
-  if (valid) {
+  if (valid && !alone) {
     if (a.spin > 0) __builtin_amdgcn_s_sleep(kSpFirstPollSleep);
     for (int q = tl; q < K * 2 * N; q += kSpSliceVectors) {
       uint64_t word = 0;
@@ -2075,11 +2080,14 @@ attnres_status bwd_impl(const uint16_t* dout, const uint16_t* const* srcs, int64
     float* partial = reinterpret_cast<float*>(ring + ring_words);
     // tags are token + 1: a zeroed ring holds no valid word.  Token t uses
     // slot t mod kSpRing, so a batch of fewer tokens clears only its slots.
+    // With one slice per row (K = 1) the ring is not used.
     const int64_t slots = T < kSpRing ? T : kSpRing;
     const int ring4 = (int)((size_t)slots * K * 2 * N / 2);
-    hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
-                       ring4);
-    if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+    if (K > 1) {
+      hipLaunchKernelGGL(zero_kernel, dim3((ring4 + 255) / 256), dim3(256), 0, st, reinterpret_cast<float4*>(ring),
+                         ring4);
+      if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
+    }
     // chunks of spans, each folded into the P rows dw_reduce_kernel sums
     P = (int32_t)(groups < ATTNRES_DW_PARTIALS ? groups : ATTNRES_DW_PARTIALS);
     const uint32_t spin = g_split_spin.load(std::memory_order_relaxed);

@@ -86,7 +86,8 @@ def workspace_traffic(T: int, N: int, D: int) -> int:
         groups = (T + 3) // 4
         chunks = (groups + 8191) // 8192
         P = min(groups, 256)
-        ring = min(T, 4096) * ((D + 1023) // 1024) * 2 * N * 8
+        K = (D + 1023) // 1024
+        ring = min(T, 4096) * K * 2 * N * 8 if K > 1 else 0  # one slice per row: no ring
         fold = 4 * P * D * (2 * chunks) if groups > 256 else 0
         return 8 * groups * D + fold + ring
     return 8 * min(T, 256) * D

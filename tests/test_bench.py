@@ -52,8 +52,9 @@ def test_workspace_traffic():
     # fold rows (written 4 times, re-read 3 times, read once by the final sum)
     assert bench.workspace_traffic(131072, 9, D) == 8 * 32768 * D + 4 * 256 * D * 8 + 4096 * 7 * 18 * 8
     # T = 100: 25 spans, one per fold row: no fold, the final sum reads the partial rows;
-    # the ring slots of 100 tokens cleared
-    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64 + 100 * 1 * 6 * 8
+    # one slice per row (D = 64): no ring; two slices (D = 2048): the ring slots of 100 tokens cleared
+    assert bench.workspace_traffic(100, 3, 64) == 8 * 25 * 64
+    assert bench.workspace_traffic(100, 9, 2048) == 8 * 25 * 2048 + 100 * 2 * 18 * 8
     # N = 7 at D = 7168 takes the one-token backward: 256 partial rows
     assert bench.workspace_traffic(131072, 7, D) == 8 * 256 * D
     assert bench.workspace_traffic(5000, 9, 12288) == 8 * 256 * 12288
