@@ -534,10 +534,10 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
 // 6.9 vs 7.8 us kernel time).  The w slice is requested first and the row
 // group right behind it, so both latencies overlap; w then goes to the
 // thread's LDS slots while the rows arrive.
-// VPT = 4 (D <= 8192: 256 threads at D = 7168 -- 224 are needed for its 896
-// vectors, rounded up to four waves, of which waves 2 and 3 own only three
-// vectors and skip the fourth; 192 VGPRs at N = 9, two waves per SIMD) or 2
-// (larger D: up to 1024 threads, 113-114 VGPRs).  At D = 7168
+// VPT = 4 (512 < D <= 8192: 256 threads at D = 7168 -- 224 are needed for its
+// 896 vectors, rounded up to four waves, of which waves 2 and 3 own only three
+// vectors and skip the fourth; 190 VGPRs at N = 9, two waves per SIMD) or 2
+// (larger D: up to 1024 threads, 113 VGPRs; and D <= 512).  At D = 7168
 // four vectors per thread measured 3-5% faster than two at T = 2K-8K, the same
 // at T >= 16K, and 0.4 us slower for one token (fewer waves share its work);
 // one vector per thread (896 threads) was 12-20% slower.
@@ -1594,10 +1594,11 @@ struct LaunchShape {
   size_t lds;   // dynamic LDS bytes per forward workgroup (backward: twice this)
 };
 
-// forward: four vectors per thread up to D = 8192 (256 threads at D = 7168:
-// ceil(896 / 4) = 224 rounded up to whole waves), two above (at most 1024
-// threads)
-constexpr int kFwdVptMaxV4 = 1024;  // largest D/8 taking four vectors per thread
+// forward: four vectors per thread for 512 < D <= 8192 (256 threads at
+// D = 7168: ceil(896 / 4) = 224 rounded up to whole waves), two above (at
+// most 1024 threads) and at D <= 512
+constexpr int kFwdVptMaxV4 = 1024;      // largest D/8 taking four vectors per thread
+constexpr int kFwdVptMaxV2Small = 64;   // D/8 up to this takes two
 
 LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
   const int V = D / 8;
@@ -1614,9 +1615,16 @@ LaunchShape make_shape(int32_t D, int vpt, bool pipe) {
 // with T or with the call: every forward call gives bitwise the same
 // per-token results, and so does every backward call (with or without
 // accumulation, stacked or per source).
-// Forward: four vectors per thread for D <= 8192, else two; blockDim = D/(8*VPT)
-// rounded up to whole waves.
-LaunchShape fwd_shape(int32_t D) { return make_shape(D, D / 8 <= kFwdVptMaxV4 ? 4 : 2, false); }
+// Forward: four vectors per thread for 512 < D <= 8192, else two; blockDim =
+// D/(8*VPT) rounded up to whole waves.
+// At D <= 512 four vectors per thread leave most lanes of the token's single
+// wave idle and a 190-VGPR wave per token; two vectors measured 1.3-1.4x
+// faster there (T = 65536, N = 3 and 9), while at D = 1024-2048 the shapes
+// were within a few percent of each other.
+LaunchShape fwd_shape(int32_t D) {
+  const int V = D / 8;
+  return make_shape(D, V <= kFwdVptMaxV2Small ? 2 : V <= kFwdVptMaxV4 ? 4 : 2, false);
+}
 
 // Backward: D <= 8192 takes one vector per thread (896 threads, 14 waves at
 // D = 7168) with a two-token prefetch; measured 1-2% faster on MI355X than
