@@ -175,11 +175,18 @@ def test_concurrent_calls_on_two_streams():
                 assert torch.equal(_bits(x), _bits(y)), (cases[j].name, k, name)
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("case", ["depth_T300", "two_chunks"])
+def test_graph_capture_replays_match_eager(case):
     """fwd, bwd and the decoding forward captured in one HIP graph (the library
     enqueues no memsets and allocates nothing): every replay, with new input
-    contents copied in and eager work in between, matches eager calls bit for bit."""
-    wl = synth.workload(1, T=300)
+    contents copied in and eager work in between, matches eager calls bit for
+    bit -- for a small depth batch, and for a batch whose split backward runs
+    two chunks (two split launches, two folds, the ring in use)."""
+    if case == "depth_T300":
+        wl = synth.workload(1, T=300)
+    else:
+        wl = synth.Workload("graph_chunks", T=ar.SPLIT_CHUNK_SPANS * ar.SPLIT_TOKENS + 20, N=8, D=1032)
+        assert ar.bwd_split(wl.N, wl.D)
     src, w, dout = _inputs(wl)
     N, T, D = src.shape
     s_src, s_dout = src.clone(), dout.clone()
@@ -205,7 +212,7 @@ def test_graph_capture_replays_match_eager():
     with torch.cuda.graph(graph):
         step()
     for k in range(3):
-        wk = synth.Workload(f"graph_{k}", T=T, N=N, D=D, seed=20 + k)
+        wk = synth.Workload(f"graph_{k}", T=T, N=N, D=D, seed=20 + k, kind=wl.kind)
         src_k, dout_k = to_dev_bf16(wk.sources()), to_dev_bf16(wk.dout())
         s_src.copy_(src_k)
         s_dout.copy_(dout_k)
