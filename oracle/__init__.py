@@ -19,7 +19,9 @@ update (``add_bf16``) against exact rational arithmetic and hand-worked
 rounding cases; the block-batched scores (``block_scores``) against PyTorch's
 fp64 ``rms_norm`` and matmul and hand-derived constant-row cases, and the
 forward from given scores (``fwd_scored``) against the plain forward and the
-two-source sigmoid closed form.
+two-source sigmoid closed form; the block-batched shared sums (``block_sums``)
+and the forward from them (``fwd_merged``) against hand-worked sums, the plain
+forward, and the limits where one side of the softmax takes all the weight.
 """
 from __future__ import annotations
 
@@ -52,6 +54,10 @@ class Oracle:
         lib.oracle_block_scores.restype = None
         lib.oracle_fwd_scored.argtypes = [i32, i64, i64, vp, vp, vp, vp, f64, vp, vp, vp]
         lib.oracle_fwd_scored.restype = None
+        lib.oracle_block_sums.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        lib.oracle_block_sums.restype = None
+        lib.oracle_fwd_merged.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, f64, vp, vp, vp]
+        lib.oracle_fwd_merged.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -132,6 +138,41 @@ class Oracle:
                                    _p(rstd), _p(alpha))
         return out, rstd, alpha
 
+    def block_sums(self, src_bits: np.ndarray, z: np.ndarray):
+        """Block-batched shared sums: for the n shared sources src [n][T][D] (bf16
+        bits) and the block's scores z [L][T][n], returns U [L][T][D] in float64,
+        U[l][t] = sum_i exp(z[l][t][i] - max_i z[l][t][i]) x_i[t]."""
+        src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        n, T, D = _shape(src_bits)
+        z = np.ascontiguousarray(z, dtype=np.float64)
+        L = z.shape[0]
+        assert z.shape == (L, T, n)
+        U = np.empty((L, T, D))
+        self.lib.oracle_block_sums(n, T, D, L, _p(src_bits), _p(z), _p(U))
+        return U
+
+    def fwd_merged(self, U: np.ndarray, p_bits: np.ndarray, z_given: np.ndarray, r_given: np.ndarray, w: np.ndarray,
+                   eps: float):
+        """Forward of one sub-layer from its shared sum U [T][D] (float64), the
+        partial sum p [T][D] (bf16 bits, the last source), and the given scores
+        and rstd [T][N-1] of the shared sources.  Returns (out, rstd [T][N],
+        alpha [T][N])."""
+        U = np.ascontiguousarray(U, dtype=np.float64)
+        p_bits = np.ascontiguousarray(p_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        T, D = p_bits.shape
+        assert U.shape == (T, D) and w.shape == (D,)
+        z_given = np.ascontiguousarray(z_given, dtype=np.float64).reshape(T, -1)
+        N = z_given.shape[1] + 1
+        assert 2 <= N <= MAX_SOURCES
+        r_given = np.ascontiguousarray(r_given, dtype=np.float64).reshape(T, N - 1)
+        out = np.empty((T, D))
+        rstd = np.empty((T, N))
+        alpha = np.empty((T, N))
+        self.lib.oracle_fwd_merged(N, T, D, _p(U), _p(p_bits), _p(z_given), _p(r_given), _p(w), float(eps), _p(out),
+                                   _p(rstd), _p(alpha))
+        return out, rstd, alpha
+
     def fwd_f64(self, x: np.ndarray, w: np.ndarray, eps: float):
         """Forward on float64 sources x [N][T][D] and float64 w [D]."""
         x = np.ascontiguousarray(x, dtype=np.float64)
@@ -203,6 +244,14 @@ def block_scores(src_bits, W, eps):
 
 def fwd_scored(src_bits, z_given, r_given, w, eps):
     return default().fwd_scored(src_bits, z_given, r_given, w, eps)
+
+
+def block_sums(src_bits, z):
+    return default().block_sums(src_bits, z)
+
+
+def fwd_merged(U, p_bits, z_given, r_given, w, eps):
+    return default().fwd_merged(U, p_bits, z_given, r_given, w, eps)
 
 
 def add_bf16(p_bits, y_bits):

@@ -282,6 +282,82 @@ void oracle_fwd_scored(int N, int64_t T, int64_t D, const uint16_t* src, const d
   }
 }
 
+/* ---- block-batched shared sums ----------------------------------------- */
+/* The weighted sum of a sub-layer is linear in the sources, and within a
+ * block only the last source (the current partial sum) changes from one
+ * sub-layer to the next (architecture figure of "Kimi K3 模型结构（10）：RL
+ * 与服务中的状态管理").  So the part of sub-layer l's weighted sum that the n
+ * shared sources contribute can be formed once for the whole block, from the
+ * block-batched scores, up to the softmax normaliser, which also depends on
+ * the partial sum's score:
+ *
+ *   m_{l,t}   = max_i zb_{l,t,i}
+ *   U_{l,t,d} = sum_i exp(zb_{l,t,i} - m_{l,t}) x_tid        (raw sources)
+ *
+ * src: bf16 bits [n][T][D]; z: [L][T][n]; U: [L][T][D]. */
+void oracle_block_sums(int n, int64_t T, int64_t D, int L, const uint16_t* src, const double* z, double* U) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int l = 0; l < L; ++l) {
+      const double* zt = z + ((int64_t)l * T + t) * n;
+      double m = zt[0];
+      for (int i = 1; i < n; ++i)
+        if (zt[i] > m) m = zt[i];
+      double* u = U + ((int64_t)l * T + t) * D;
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int i = 0; i < n; ++i) acc += exp(zt[i] - m) * bf16_to_f64(src[((int64_t)i * T + t) * D + d]);
+        u[d] = acc;
+      }
+    }
+  }
+}
+
+/* The forward of one sub-layer from its shared sum (oracle_block_sums) and
+ * the current partial sum p, the last of its N sources.  The partial sum is
+ * normalised and scored with the sub-layer's w as in the plain forward; the
+ * other N-1 scores and rstd are given.  With M the largest of all N scores
+ * and m the largest of the N-1 given ones:
+ *
+ *   den     = sum_i exp(z_i - M)                  over all N sources
+ *   alpha_i = exp(z_i - M) / den
+ *   out_d   = (exp(m - M) U_d + exp(z_p - M) p_d) / den
+ *
+ * which is the plain forward's weighted sum, as exp(m - M) exp(z_i - m) =
+ * exp(z_i - M) for every shared source.
+ * U: [T][D] (the sub-layer's rows of the shared sum); p: bf16 bits [T][D];
+ * zg, rg: [T][N-1]; outputs as oracle_fwd. */
+void oracle_fwd_merged(int N, int64_t T, int64_t D, const double* U, const uint16_t* p, const double* zg,
+                       const double* rg, const float* w, double eps, double* out, double* rstd, double* alpha) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    double zs[16], rs[16];
+    for (int i = 0; i + 1 < N; ++i) {
+      zs[i] = zg[t * (N - 1) + i];
+      rs[i] = rg[t * (N - 1) + i];
+    }
+    const uint16_t* pt = p + t * D;
+    double sq = 0.0;
+    for (int64_t d = 0; d < D; ++d) sq += bf16_to_f64(pt[d]) * bf16_to_f64(pt[d]);
+    rs[N - 1] = 1.0 / sqrt(sq / (double)D + eps);
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += (double)w[d] * (rs[N - 1] * bf16_to_f64(pt[d]));
+    zs[N - 1] = dot;
+    double m = zs[0];
+    for (int i = 1; i + 1 < N; ++i)
+      if (zs[i] > m) m = zs[i];
+    const double top = zs[N - 1] > m ? zs[N - 1] : m;
+    double den = 0.0;
+    for (int i = 0; i < N; ++i) den += exp(zs[i] - top);
+    const double shared = exp(m - top), own = exp(zs[N - 1] - top);
+    for (int64_t d = 0; d < D; ++d) out[t * D + d] = (shared * U[t * D + d] + own * bf16_to_f64(pt[d])) / den;
+    for (int i = 0; i < N; ++i) {
+      rstd[t * N + i] = rs[i];
+      alpha[t * N + i] = exp(zs[i] - top) / den;
+    }
+  }
+}
+
 /* ---- partial-sum update ------------------------------------------------- */
 /* The architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理" lists
  * the current block's partial sum (the sum of the sub-layer outputs already

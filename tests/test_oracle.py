@@ -396,8 +396,94 @@ def pin_fwd_scored(orc):
     return fails
 
 
+def pin_block_sums(orc):
+    """Block-batched shared sums: hand-worked sums; one shared source gives the
+    source itself exactly; adding a constant to a sub-layer's scores leaves its
+    sum unchanged; each sum divided by its weights' total is the plain forward
+    on the shared sources alone for that sub-layer's pseudo-query."""
+    fails = []
+    for c in json.load(open(GOLDEN_BLOCK))["block_sums"]:
+        x = _bits_of(c["x"])[:, None, :]                      # [n][1][D]
+        z = np.array(_ev(c["z"]))[:, None, :]                 # [L][1][n]
+        U = orc.block_sums(x, z)
+        want = np.array(_ev(c["expect"]))                     # [L][D]
+        if not np.allclose(U[:, 0, :], want, rtol=1e-13, atol=1e-13):
+            fails.append(f"sums golden {c['name']}: {U[:, 0, :]} vs {want}")
+    r = _rng(500)
+    bits = _random_bits(r, (1, 5, 24), [3.0])
+    z1 = r.standard_normal((4, 5, 1)) * 7.0
+    if not np.array_equal(orc.block_sums(bits, z1), np.broadcast_to(oracle.bf16_to_f64(bits), (4, 5, 24))):
+        fails.append("one shared source: the sum is not the source itself")
+    for seed, (n, T, D, L, eps) in enumerate([(2, 3, 16, 2, 1e-6), (5, 6, 32, 4, 0.05), (8, 7, 64, 24, 1e-6)]):
+        r = _rng(510 + seed)
+        bits = _random_bits(r, (n, T, D), np.sqrt(1.0 + 12.0 * np.arange(n)))
+        W = (r.standard_normal((L, D)) * 0.5).astype(np.float32)
+        rb, zb = orc.block_scores(bits, W, eps)
+        U = orc.block_sums(bits, zb)
+        e = _rel(orc.block_sums(bits, zb + 3.75), U)
+        if not e < 1e-13:
+            fails.append(f"sums not shift invariant n={n}: rel {e:.3e}")
+        tot = np.exp(zb - zb.max(axis=2, keepdims=True)).sum(axis=2)  # [L][T]
+        for l in range(L):
+            out, _, _ = orc.fwd(bits, W[l], eps)
+            e = _rel(U[l] / tot[l][:, None], out)
+            if not e < 1e-12:
+                fails.append(f"sums / weights vs plain forward on the shared sources n={n} l={l}: rel {e:.3e}")
+                break
+    return fails
+
+
+def pin_fwd_merged(orc):
+    """Forward from the shared sum: hand-worked cases with the given or the
+    partial sum's score the largest; through block_scores and block_sums it
+    reproduces the plain forward on all N sources; shared scores far below the
+    partial sum's give out = p and alpha = (0, .., 0, 1) exactly, far above it
+    the shared sums normalised by their own weights."""
+    fails = []
+    for c in json.load(open(GOLDEN_BLOCK))["fwd_merged"]:
+        U = np.array(_ev(c["U"]))[None, :]
+        p = _bits_of(c["p"])[None, :]
+        zg = np.array(_ev(c["z_given"]))[None, :]
+        rg = np.array(_ev(c["r_given"]))[None, :]
+        out, rstd, alpha = orc.fwd_merged(U, p, zg, rg, np.array(c["w"], dtype=np.float32), c["eps"])
+        for key, got in (("alpha", alpha[0]), ("out", out[0]), ("rstd", rstd[0])):
+            want = np.array(_ev(c["expect"][key]))
+            if not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+                fails.append(f"merged golden {c['name']} {key}: {got} vs {want}")
+    for seed, (N, T, D, eps, wstd) in enumerate([(2, 3, 16, 1e-6, 0.5), (5, 6, 32, 0.05, 0.5), (9, 9, 64, 1e-6, 0.5),
+                                                (9, 5, 32, 0.0, 4.0)]):
+        r = _rng(520 + seed)
+        bits = _random_bits(r, (N, T, D), np.sqrt(1.0 + 12.0 * np.arange(N)))
+        W = (r.standard_normal((3, D)) * wstd).astype(np.float32)
+        rb, zb = orc.block_scores(bits[:N - 1], W, eps)
+        U = orc.block_sums(bits[:N - 1], zb)
+        for l in range(3):
+            got = orc.fwd_merged(U[l], bits[N - 1], zb[l], rb, W[l], eps)
+            want = orc.fwd(bits, W[l], eps)
+            for name, a, b in zip(("out", "rstd", "alpha"), got, want):
+                e = _rel(a, b)
+                if not e < 1e-12:
+                    fails.append(f"merged vs plain N={N} T={T} D={D} l={l} {name}: rel {e:.3e}")
+    r = _rng(530)
+    N, T, D = 4, 3, 16
+    bits = _random_bits(r, (N, T, D), [1.0, 2.0, 3.0, 4.0])
+    w = (r.standard_normal(D) * 0.1).astype(np.float32)
+    rg = np.ones((T, N - 1))
+    U = r.standard_normal((T, D))
+    out, _, alpha = orc.fwd_merged(U, bits[N - 1], np.full((T, N - 1), -1000.0), rg, w, 1e-6)
+    if not (np.array_equal(out, oracle.bf16_to_f64(bits[N - 1])) and np.array_equal(alpha[:, N - 1], np.ones(T))
+            and not alpha[:, :N - 1].any()):
+        fails.append("shared scores far below the partial sum's: out is not p")
+    zg = 1000.0 + r.standard_normal((T, N - 1))
+    out, _, _ = orc.fwd_merged(U, bits[N - 1], zg, rg, w, 1e-6)
+    want = U / np.exp(zg - zg.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)
+    if not np.allclose(out, want, rtol=1e-13, atol=1e-13):
+        fails.append("shared scores far above the partial sum's: out is not the normalised shared sum")
+    return fails
+
+
 PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update,
-        pin_block_scores, pin_fwd_scored]
+        pin_block_scores, pin_fwd_scored, pin_block_sums, pin_fwd_merged]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -459,6 +545,24 @@ MUTANTS = {
     "scored_last_is_first_source": ("const uint16_t* last = src + ((int64_t)(N - 1) * T + t) * D;",
                                     "const uint16_t* last = src + t * D;"),
     "scored_sum_skips_last": ("for (int i = 0; i < N; ++i) o += as[i]", "for (int i = 0; i + 1 < N; ++i) o += as[i]"),
+    # block-batched shared sums and the forward from them
+    "sums_no_max_subtraction": ("acc += exp(zt[i] - m) * bf16_to_f64", "acc += exp(zt[i]) * bf16_to_f64"),
+    "sums_skip_first_source": ("for (int i = 0; i < n; ++i) acc += exp(zt[i] - m)",
+                               "for (int i = 1; i < n; ++i) acc += exp(zt[i] - m)"),
+    "sums_max_of_first_score": ("for (int i = 1; i < n; ++i)\n        if (zt[i] > m) m = zt[i];", ""),
+    "sums_z_token_major": ("const double* zt = z + ((int64_t)l * T + t) * n;",
+                           "const double* zt = z + ((int64_t)t * L + l) * n;"),
+    "sums_normalised_rows": ("acc += exp(zt[i] - m) * bf16_to_f64(src[((int64_t)i * T + t) * D + d]);",
+                             "acc += exp(zt[i] - m) * bf16_to_f64(src[((int64_t)i * T + t) * D + d]) / (1.0 + i);"),
+    "merged_no_rescale": ("const double shared = exp(m - top)", "const double shared = 1.0"),
+    "merged_den_skips_partial": ("for (int i = 0; i < N; ++i) den += exp(zs[i] - top);",
+                                 "for (int i = 0; i + 1 < N; ++i) den += exp(zs[i] - top);"),
+    "merged_partial_unweighted": ("own * bf16_to_f64(pt[d])", "bf16_to_f64(pt[d])"),
+    "merged_partial_unnormalised": ("dot += (double)w[d] * (rs[N - 1] * bf16_to_f64(pt[d]));",
+                                    "dot += (double)w[d] * bf16_to_f64(pt[d]);"),
+    "merged_alpha_shifted_by_given_max": ("alpha[t * N + i] = exp(zs[i] - top) / den;",
+                                          "alpha[t * N + i] = exp(zs[i] - m) / den;"),
+    "merged_shared_of_token_zero": ("shared * U[t * D + d]", "shared * U[d]"),
 }
 
 
