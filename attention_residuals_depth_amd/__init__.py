@@ -28,6 +28,11 @@ The C entry points, declared in ``include/attnres.h``:
                 all L pseudo-queries of a block against the sources its
                 sub-layers share, in one MFMA pass; then each sub-layer's
                 forward from its slice of those scores.
+    attnres_block_sums / attnres_fwd_merged: from those scores, the part of
+                every sub-layer's weighted sum that the shared sources
+                contribute (fp32, before the softmax normaliser), in one
+                pass; then each sub-layer's forward from its shared sum and
+                the partial sum alone.
 """
 from __future__ import annotations
 
@@ -83,6 +88,10 @@ def library() -> ctypes.CDLL:
         lib.attnres_block_scores.restype = ctypes.c_int
         lib.attnres_fwd_scored.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_scored.restype = ctypes.c_int
+        lib.attnres_block_sums.argtypes = [pp, i64, vp, i32, i32, i64, i32, vp, i64, i64, vp]
+        lib.attnres_block_sums.restype = ctypes.c_int
+        lib.attnres_fwd_merged.argtypes = [vp, i64, vp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_merged.restype = ctypes.c_int
         lib.attnres_set_split_spin.argtypes = [ctypes.c_uint32]
         lib.attnres_set_split_spin.restype = ctypes.c_uint32
         _lib = lib
@@ -487,6 +496,76 @@ def attnres_fwd_scored(srcs, z_given: torch.Tensor, rstd_given: torch.Tensor, w:
     return out, rstd, alpha
 
 
+def attnres_block_sums(srcs, z: torch.Tensor, U=None, token_major: bool = False, stream=None):
+    """Block-batched shared sums of the n sources a block's sub-layers share (n
+    [T][D] bf16 tensors or views with one row pitch), from the block's scores z
+    [L][T][n] fp32 (attnres_block_scores): U[l][t] = sum_i exp(z[l][t][i] -
+    max_i z[l][t][i]) srcs[i][t] in fp32.  Returns U as [L][T][D], or as
+    [T][L][D] with token_major (sub-layer l's rows are then U[:, l]); a given U
+    must have that shape and be contiguous."""
+    srcs, T, D, pitch = _sources(srcs, "srcs")
+    n = len(srcs)
+    if z.dim() != 3:
+        raise ValueError("z must be [L][T][n]")
+    L = z.shape[0]
+    _check(z, "z", torch.float32, (L, T, n))
+    dev = srcs[0].device
+    shape = (T, L, D) if token_major else (L, T, D)
+    if U is None:
+        U = torch.empty(shape, dtype=torch.float32, device=dev)
+    _check(U, "U", torch.float32, shape)
+    lstride, tpitch = (D, L * D) if token_major else (T * D, D)
+    _same_device(dev, z=z, U=U, **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
+    with _device(dev):
+        code = library().attnres_block_sums(_ptr_array(srcs), pitch, z.data_ptr(), L, n, T, D, U.data_ptr(), lstride,
+                                            tpitch, _stream_handle(stream, dev))
+    if code != 0:
+        raise AttnResError("attnres_block_sums", code)
+    return U
+
+
+def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.Tensor, rstd_given: torch.Tensor,
+                       w: torch.Tensor, eps: float, out=None, rstd=None, alpha=None, stream=None):
+    """Forward of one sub-layer from its block-batched shared sum: U_l [T][D]
+    fp32 (U[l] or U[:, l] of attnres_block_sums; rows may be spaced apart),
+    partial [T][D] bf16 the current partial sum (the last of the N sources),
+    z_given and rstd_given [T][N-1] the shared sources' scores for this
+    sub-layer and their rstd (attnres_block_scores).  Returns (out, rstd [T][N],
+    alpha [T][N]) as attnres_fwd_scored would for the same sources."""
+    if not isinstance(z_given, torch.Tensor) or z_given.dim() != 2:
+        raise ValueError("z_given must be a [T][N-1] tensor")
+    T, n = z_given.shape
+    N = n + 1
+    if not 2 <= N <= MAX_SOURCES:
+        raise ValueError(f"N = {N} sources: the merged forward takes 2..{MAX_SOURCES}")
+    if not isinstance(partial, torch.Tensor) or partial.dim() != 2:
+        raise ValueError("partial must be [T][D]")
+    D = partial.shape[1]
+    p_pitch = _rows(partial, "partial", T, D)
+    u_pitch = _rows(U_l, "U_l", T, D, torch.float32)
+    _check(z_given, "z_given", torch.float32, (T, N - 1))
+    _check(rstd_given, "rstd_given", torch.float32, (T, N - 1))
+    _check(w, "w", torch.float32, (D,))
+    dev = partial.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if rstd is None:
+        rstd = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, (T, D))
+    _check(rstd, "rstd", torch.float32, (T, N))
+    _check(alpha, "alpha", torch.float32, (T, N))
+    _same_device(dev, U_l=U_l, z_given=z_given, rstd_given=rstd_given, w=w, out=out, rstd=rstd, alpha=alpha)
+    with _device(dev):
+        code = library().attnres_fwd_merged(U_l.data_ptr(), u_pitch, partial.data_ptr(), p_pitch, z_given.data_ptr(),
+                                            rstd_given.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
+                                            rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream, dev))
+    if code != 0:
+        raise AttnResError("attnres_fwd_merged", code)
+    return out, rstd, alpha
+
+
 GRAD_ACCUMULATE = 1  # grad_mode bits of attnres_bwd_sources
 GRAD_F32 = 2
 
@@ -568,6 +647,6 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
-           "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
+           "attnres_block_sums", "attnres_fwd_merged", "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
            "SPLIT_MAX_D", "SPLIT_ANY_N_MAX_D", "SPLIT_MIN_N", "bwd_split", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT", "set_split_spin",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

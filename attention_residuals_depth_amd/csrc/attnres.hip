@@ -658,7 +658,7 @@ constexpr int kBsWaves = 4;
 constexpr int kBsTiles = ATTNRES_BS_TILES;        // 16-row tiles per wave
 constexpr int kBsWaveRows = kBsTiles * 16;        // 64
 constexpr int kBsRows = kBsWaves * kBsWaveRows;   // 256 tokens per workgroup
-constexpr int kBsChunk = 16;                      // k-steps per fresh accumulator
+constexpr int kBsChunk = 4;                       // k-steps per fresh accumulator (even: see the loop)
 
 __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restrict__ W, int32_t L, int32_t D,
                                                             int32_t Lpad, int32_t Dpad, uint16_t* __restrict__ Wp) {
@@ -693,28 +693,39 @@ __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3],
 }
 
 // One k-step: squares of the rows (exact products, fp32 sums) and the three
-// query parts into the chunk accumulators.
-template <int CT>
+// query parts into the chunk accumulators.  With SEP the hi part has an
+// accumulator of its own: the lo and mid products are 2^-8 and 2^-16 of the
+// hi ones, so the roundings of their accumulator are negligible, and the hi
+// accumulator takes one rounding per k-step instead of three.
+template <int CT, bool SEP>
 __device__ __forceinline__ void bs_step(const uint4 (&a)[kBsTiles], const uint4 (&b)[CT][3],
-                                        f32x4_t (&acc)[kBsTiles][CT], float (&ss)[kBsTiles]) {
+                                        f32x4_t (&acc)[kBsTiles][CT], f32x4_t (&acch)[kBsTiles][CT],
+                                        float (&ss)[kBsTiles]) {
 #pragma unroll
   for (int m = 0; m < kBsTiles; ++m) {
     ss[m] += dot8_bf16(a[m], a[m], 0.f);
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[m]);
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int p = 2; p >= 0; --p)  // lo, mid, hi
-        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][p]), acc[m][c], 0, 0,
-                                                            0);
+    for (int c = 0; c < CT; ++c) {
+      acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][2]), acc[m][c], 0, 0, 0);
+      acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][1]), acc[m][c], 0, 0, 0);
+      if constexpr (SEP)
+        acch[m][c] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][0]), acch[m][c], 0, 0, 0);
+      else
+        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b[c][0]), acc[m][c], 0, 0, 0);
+    }
   }
 }
 
 // Accuracy: the scores of a peaked softmax reach |z| ~ 150, where one ulp of
-// relative error in z moves a weight by ~4e-6.  So the chunk sums (16 k-steps
-// each, fp32 MFMA accumulation) are added into fp64 running sums, the rstd
-// comes from a double-precision reciprocal square root of the fp32 sum of
-// squares, and z = rstd * dot is formed in fp64 and rounded once.
+// relative error in z moves a weight by ~4e-6.  So the chunk sums (4 k-steps
+// each, fp32 MFMA accumulation, the hi query part in its own accumulator
+// where the registers allow: L <= 32) are added into fp64 running sums, the
+// rstd comes from a double-precision reciprocal square root of the fp32 sum
+// of squares, and z = rstd * dot is formed in fp64 and rounded once.  With
+// chunks of 16 k-steps and one accumulator the scores of a peaked block were
+// off by up to ~5e-5 (a few ulps), enough to move a weight by 1e-5.
 template <int CT>  // query column tiles: L <= 16 * CT
 __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t T, int32_t D, float eps, int32_t n,
                                                            const uint16_t* __restrict__ Wp, int32_t L, int32_t Lpad,
@@ -734,7 +745,8 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
   uint32_t roff[kBsTiles];
 #pragma unroll
   for (int m = 0; m < kBsTiles; ++m) roff[m] = (uint32_t)((16 * m + r) * pitch_b);
-  f32x4_t acc[kBsTiles][CT];
+  constexpr bool SEP = CT <= 2;
+  f32x4_t acc[kBsTiles][CT], acch[kBsTiles][CT];
   double run[kBsTiles][CT][4];
   float ss_acc[kBsTiles];
   double ss_run[kBsTiles];
@@ -745,6 +757,7 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acch[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) run[m][c][j] = 0.0;
     }
@@ -757,8 +770,9 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) run[m][c][j] += (double)acc[m][c][j];
+        for (int j = 0; j < 4; ++j) run[m][c][j] += SEP ? (double)acch[m][c][j] + (double)acc[m][c][j] : (double)acc[m][c][j];
         acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acch[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
@@ -769,7 +783,7 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
   for (int s = 0; s < S; ++s) {
     uint4 a[kBsTiles], b[CT][3];
     bs_load<CT>(a, b, ra, rb, roff, s, q, r, D, Lpad, Dpad);
-    bs_step<CT>(a, b, acc, ss_acc);
+    bs_step<CT, SEP>(a, b, acc, acch, ss_acc);
     if (s % kBsChunk == kBsChunk - 1 || s + 1 >= S) fold();
   }
 #else
@@ -778,12 +792,12 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
   for (int s = 0; s < S; s += 2) {
     if (s + 1 < S) bs_load<CT>(a1, b1, ra, rb, roff, s + 1, q, r, D, Lpad, Dpad);
     sched_fence();
-    bs_step<CT>(a0, b0, acc, ss_acc);  // s is even: a chunk never ends here except at the last step
+    bs_step<CT, SEP>(a0, b0, acc, acch, ss_acc);  // s is even: a chunk never ends here except at the last step
     if (s + 1 >= S) fold();
     if (s + 1 >= S) break;
     if (s + 2 < S) bs_load<CT>(a0, b0, ra, rb, roff, s + 2, q, r, D, Lpad, Dpad);
     sched_fence();
-    bs_step<CT>(a1, b1, acc, ss_acc);
+    bs_step<CT, SEP>(a1, b1, acc, acch, ss_acc);
     if ((s + 1) % kBsChunk == kBsChunk - 1 || s + 2 >= S) fold();
   }
 #endif
@@ -806,6 +820,214 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
         if (col < L && row < rows) z_out[((int64_t)col * T + tw + row) * n + i] = (float)(rr * run[m][c][j]);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-batched shared sums
+// ---------------------------------------------------------------------------
+// The weighted sum is linear in the sources, and within a block only the
+// last source -- the current partial sum -- changes from one sub-layer to the
+// next (architecture figure of "Kimi K3 模型结构（10）：RL 与服务中的状态管理").
+// So the part of sub-layer l's weighted sum that the n shared sources
+// contribute is formed for all L sub-layers of the block in one pass over
+// those sources, from the block-batched scores, up to the softmax normaliser
+// (which also depends on the partial sum's score):
+//     m_l = max_i z[l][t][i],   U[l][t] = sum_i exp(z[l][t][i] - m_l) x_i[t]   (fp32)
+// Each sub-layer's forward (fwd_merged_kernel) then reads its U row and the
+// partial sum instead of all N source rows.
+//
+// One workgroup per token, the shared rows in registers as in the forward
+// (thread j owns vectors j + k*blockDim.x).  The first L threads form one
+// sub-layer's n weights each into LDS while the rows arrive; then each thread
+// unpacks one vector of every shared row and runs the L weighted sums over it
+// (8n fp32 FMAs and 32 bytes of fp32 stores per sub-layer).  The weights are
+// read from LDS at a wave-uniform address (a broadcast).  One vector per
+// thread up to D = 8192 (896 threads at D = 7168, 87 VGPRs at n = 8), two
+// above: 2-3% faster than four or two per thread at D = 7168 on MI355X.
+// Without the weighted sums (timing only) the same loads and stores took
+// 4.44 ms against 5.2-5.3 ms at T = 32768, n = 8, L = 24: the arithmetic is
+// only partly hidden behind the stores.
+template <int NS, int VPT>
+__global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const float* __restrict__ z,
+                                                                         int32_t L, int64_t T, int32_t D, int64_t t0,
+                                                                         float* __restrict__ U, int64_t u_lstride,
+                                                                         int64_t u_pitch) {
+  constexpr int NS4 = (NS + 3) / 4;
+  __shared__ float4 ew[ATTNRES_MAX_QUERIES][NS4];
+  __shared__ float4 stage[kMaxWaves * 2 * kWave];  // 2 KiB per wave
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const Slice<VPT> sl(tid, blockDim.x, D);
+  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
+  float zz[NS];
+  if (tid < L) {  // requested first: the weights can form while the rows are in flight
+    const float* zt = z + ((int64_t)tid * T + t) * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) zz[i] = zt[i];
+  }
+  sched_fence();
+  uint4 x[NS][VPT];
+  load_rows<NS, VPT>(x, src, t, D, sl);
+  sched_fence();
+  if (tid < L) {
+    float m = zz[0];
+#pragma unroll
+    for (int i = 1; i < NS; ++i) m = fmaxf(m, zz[i]);
+    float e[4 * NS4];
+#pragma unroll
+    for (int i = 0; i < 4 * NS4; ++i) e[i] = i < NS ? __expf(zz[i] - m) : 0.f;
+#pragma unroll
+    for (int q = 0; q < NS4; ++q) ew[tid][q] = make_float4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (!sl.has(k)) continue;  // wave-uniform: no lane of this wave owns a vector k
+    float f[NS][8];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) unpack8(x[i][k], f[i]);
+    const uint32_t wbase = 2u * sl.off[k] - 32u * (uint32_t)lane;  // the wave's first vector k, fp32 bytes
+    for (int l = 0; l < L; ++l) {
+      float e[4 * NS4];
+#pragma unroll
+      for (int q = 0; q < NS4; ++q) {
+        const float4 v = ew[l][q];
+        e[4 * q] = v.x; e[4 * q + 1] = v.y; e[4 * q + 2] = v.z; e[4 * q + 3] = v.w;
+      }
+      float acc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = e[0] * f[0][c];
+#pragma unroll
+      for (int i = 1; i < NS; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(e[i], f[i][c], acc[c]);
+      // the wave's 64 x 32 bytes pass through its LDS stage so that each store
+      // writes one contiguous KiB with the streaming hint (lane j: bytes
+      // [16 j, 16 j + 16) and [1024 + 16 j, ...) of the wave's 2 KiB); the
+      // wave barriers order the stage's writes before other lanes' reads, and
+      // those reads before the next sub-layer's writes.  Two half-vector
+      // streaming stores per lane ran at 2.7 TB/s, the same with the default
+      // policy at 3.1, staged at 4.9 (T = 32768, n = 8, L = 24).
+      float4* st = stage + wave * (2 * kWave);
+      st[2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      st[2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      wave_sync();
+      const float4 lo = st[lane], hi = st[kWave + lane];
+      wave_sync();
+      const __amdgpu_buffer_rsrc_t ru = rsrc(U + (int64_t)l * u_lstride + t * u_pitch, (uint32_t)D * 4u);
+      bstore<kAuxStreamStore>(ru, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
+      bstore<kAuxStreamStore>(ru, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
+    }
+  }
+}
+
+// Forward of one sub-layer from its block-batched shared sum U (above) and the
+// current partial sum p, the last of its N sources.  p is normalised and
+// scored here exactly as the scored forward scores its last source, and the
+// given rstd and scores of the N-1 shared sources arrive the same way, so the
+// softmax below is that forward's (the same instructions: alpha is bitwise
+// the scored forward's).  Then, with m the largest given score and M the
+// largest of all N,
+//     out = exp(m - M) / den * U + alpha_p * p
+// since exp(m - M) exp(z_i - m) = exp(z_i - M): the plain weighted sum, from
+// one fp32 row and one bf16 row instead of N bf16 rows.  w stays in
+// registers (the row data per thread is small here).
+template <int N, int VPT>
+__global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_merged_kernel(
+    const float* __restrict__ U, int64_t u_pitch, const uint16_t* __restrict__ p, int64_t p_pitch,
+    const float* __restrict__ zg, const float* __restrict__ rg, const float* __restrict__ w, float eps, int64_t t0,
+    int32_t D, uint16_t* __restrict__ out, float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
+  static_assert(N >= 2, "the shared sources and the partial sum");
+  __shared__ __attribute__((aligned(16))) float red[1][2][kMaxWaves];
+  const int tid = threadIdx.x;
+  const Slice<VPT> sl(tid, blockDim.x, D);
+  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
+  uint4 wv[VPT][2];
+  load_w<VPT>(wv, w, D, sl);
+  sched_fence();
+  uint4 pv[VPT], uv[VPT][2];
+  {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(p + t * p_pitch, (uint32_t)D * 2u);
+    const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) pv[k] = bload<kAuxStreamLoad>(rp, sl.off[k]);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      uv[k][0] = bload<kAuxStreamLoad>(ru, 2u * sl.off[k]);
+      uv[k][1] = bload<kAuxStreamLoad>(ru, 2u * sl.off[k] + 16u);
+    }
+  }
+  float zgv, rgv;
+  {  // lane i: shared source i's given score and rstd (lanes >= N-1 read zeros)
+    const int lane = lane_id();
+    constexpr uint32_t gb = (uint32_t)(N - 1) * 4u;
+    zgv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(zg + t * (N - 1), gb), lane * 4, 0, 0));
+    rgv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(rg + t * (N - 1), gb), lane * 4, 0, 0));
+  }
+  sched_fence();
+  clear_absent<2>(red);
+  // the partial sum's sum of squares and w.p, as the scored forward forms them
+  float part[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (!sl.has(k)) continue;
+    const float4 wa = __builtin_bit_cast(float4, wv[k][0]), wb = __builtin_bit_cast(float4, wv[k][1]);
+    const float wr[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    float f[8];
+    unpack8(pv[k], f);
+    part[0] = dot8_bf16(pv[k], pv[k], part[0]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[1] = fmaf(wr[e], f[e], part[1]);
+  }
+  block_sums<2>(part, red[0]);
+
+  // rstd, scores and softmax: the scored forward's sequence
+  float r[N], a[N];
+  float m = -INFINITY, ms = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < N - 1) {
+      r[i] = uniform(lane_value(rgv, i));
+      a[i] = uniform(lane_value(zgv, i));
+      ms = fmaxf(ms, a[i]);
+    } else {
+      r[i] = uniform(__builtin_amdgcn_rsqf(part[0] * (1.0f / (float)D) + eps));
+      a[i] = r[i] * part[1];
+    }
+    m = fmaxf(m, a[i]);
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a[i] = __expf(a[i] - m);
+    den += a[i];
+  }
+  const float inv_den = 1.0f / den;
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = uniform(a[i] * inv_den);
+  const float cs = uniform(__expf(ms - m) * inv_den);
+
+  const __amdgpu_buffer_rsrc_t ro = rsrc(out + t * D, (uint32_t)D * 2u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (!sl.has(k)) continue;
+    const float4 ua = __builtin_bit_cast(float4, uv[k][0]), ub = __builtin_bit_cast(float4, uv[k][1]);
+    const float u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+    float f[8], acc[8];
+    unpack8(pv[k], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(a[N - 1], f[e], cs * u[e]);
+    bstore<kAuxStreamStore>(ro, sl.off[k], pack8(acc));
+  }
+  if (tid < N) {
+    float rv = r[0], av = a[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      rv = tid == i ? r[i] : rv;
+      av = tid == i ? a[i] : av;
+    }
+    rstd_out[t * N + tid] = rv;
+    alpha_out[t * N + tid] = av;
   }
 }
 
@@ -2010,6 +2232,157 @@ attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, con
   return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
+// One workgroup per token for the block sums and the merged forward; the
+// dispatch packet counts work-items in 32 bits, so very large T is split over
+// several launches.
+int threads_for(int32_t D, int vpt) { return ((D / 8 + vpt - 1) / vpt + kWave - 1) / kWave * kWave; }
+
+template <int NS, int VPT>
+hipError_t run_sums_vpt(hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T, int32_t D, float* U,
+                        int64_t ls, int64_t tp) {
+  const int threads = threads_for(D, VPT);
+  int64_t res = 0;
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&block_sums_kernel<NS, VPT>), threads, 0, &res);
+  if (e != hipSuccess) return e;  // validates the launch shape
+  const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
+  for (int64_t t0 = 0; t0 < T; t0 += per_launch) {
+    const int64_t n = T - t0 < per_launch ? T - t0 : per_launch;
+    hipLaunchKernelGGL((block_sums_kernel<NS, VPT>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, rows, z, L, T,
+                       D, t0, U, ls, tp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int NS>
+hipError_t run_sums_n(int vpt, hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T, int32_t D,
+                      float* U, int64_t ls, int64_t tp) {
+  return vpt == 1 ? run_sums_vpt<NS, 1>(st, rows, z, L, T, D, U, ls, tp)
+                  : run_sums_vpt<NS, 2>(st, rows, z, L, T, D, U, ls, tp);
+}
+
+// The sums' vectors per thread: one while a token's vectors fit 1024 threads.
+int sums_vpt(int32_t D) { return D / 8 <= 1024 ? 1 : 2; }
+
+attnres_status block_sums_impl(const uint16_t* const* srcs, int64_t pitch, const float* z, int32_t L, int32_t n,
+                               int64_t T, int32_t D, float* U, int64_t ls, int64_t tp, void* stream) {
+  if (!sizes_ok(n, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (L < 1 || L > ATTNRES_MAX_QUERIES) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (T == 0) return ATTNRES_OK;
+  if (srcs == nullptr || z == nullptr || U == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(z, 4) || !aligned(U, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  // U rows start on 16-byte boundaries and never overlap: sub-layer-major
+  // (tp >= D, ls past the last token's row) or token-major (ls >= D, tp past
+  // the last sub-layer's row); every offset stays far inside int64.
+  if (ls < D || tp < D || ls % 4 != 0 || tp % 4 != 0) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (ls > (INT64_C(1) << 40) || tp > (INT64_C(1) << 40) / T) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const bool l_major = ls >= (T - 1) * tp + D, t_major = tp >= (int64_t)(L - 1) * ls + D;
+  if (!l_major && !t_major) return ATTNRES_ERR_INVALID_ARGUMENT;
+  Range ins[ATTNRES_MAX_SOURCES + 1];
+  SrcRows rows{};
+  rows.pitch = pitch;
+  for (int i = 0; i < n; ++i) {
+    if (srcs[i] == nullptr || !aligned(srcs[i], 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+    rows.p[i] = srcs[i];
+    ins[i] = rows_of(srcs[i], T, (int64_t)D * 2, pitch * 2);
+  }
+  ins[n] = range_of(z, (size_t)L * (size_t)T * (size_t)n * 4);
+  const Range out = range_of(U, (size_t)((int64_t)(L - 1) * ls + (T - 1) * tp + D) * 4);
+  for (int b = 0; b <= n; ++b)
+    if (overlap(out, ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int vpt = sums_vpt(D);
+  hipError_t e;
+  switch (n) {
+    case 1: e = run_sums_n<1>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 2: e = run_sums_n<2>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 3: e = run_sums_n<3>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 4: e = run_sums_n<4>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 5: e = run_sums_n<5>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 6: e = run_sums_n<6>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 7: e = run_sums_n<7>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 8: e = run_sums_n<8>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 9: e = run_sums_n<9>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    default: return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
+struct MergedArgs {
+  const float* U;
+  int64_t u_pitch;
+  const uint16_t* p;
+  int64_t p_pitch;
+  const float* zg;
+  const float* rg;
+  const float* w;
+  float eps;
+  int64_t T;
+  int32_t D;
+  uint16_t* out;
+  float* rstd;
+  float* alpha;
+};
+
+template <int N, int VPT>
+hipError_t run_merged_vpt(hipStream_t st, const MergedArgs& a) {
+  const int threads = threads_for(a.D, VPT);
+  int64_t res = 0;
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N, VPT>), threads, 0, &res);
+  if (e != hipSuccess) return e;  // validates the launch shape
+  const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
+  for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
+    const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
+    hipLaunchKernelGGL((fwd_merged_kernel<N, VPT>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U, a.u_pitch,
+                       a.p, a.p_pitch, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int N>
+hipError_t run_merged_n(int vpt, hipStream_t st, const MergedArgs& a) {
+  return vpt == 4 ? run_merged_vpt<N, 4>(st, a) : run_merged_vpt<N, 2>(st, a);
+}
+
+attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
+  const size_t nTD = (size_t)a.T * (size_t)a.D, nTN = (size_t)a.T * (size_t)N, nTG = (size_t)a.T * (size_t)(N - 1);
+  if (a.U == nullptr || a.p == nullptr || a.zg == nullptr || a.rg == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (a.out == nullptr || a.rstd == nullptr || a.alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(a.U, 16) || !aligned(a.p, 16) || !aligned(a.out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(a.zg, 4) || !aligned(a.rg, 4) || !aligned(a.rstd, 4) || !aligned(a.alpha, 4))
+    return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!pitch_ok(a.p_pitch, a.T, a.D)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (a.u_pitch < a.D || a.u_pitch % 4 != 0 || a.u_pitch > (INT64_C(1) << 40) / a.T) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const Range ins[5] = {rows_of(a.U, a.T, (int64_t)a.D * 4, a.u_pitch * 4), rows_of(a.p, a.T, (int64_t)a.D * 2, a.p_pitch * 2),
+                        range_of(a.zg, nTG * 4), range_of(a.rg, nTG * 4), range_of(a.w, (size_t)a.D * 4)};
+  const Range outs[3] = {range_of(a.out, nTD * 2), range_of(a.rstd, nTN * 4), range_of(a.alpha, nTN * 4)};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], ins[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int vpt = fwd_shape(a.D).vpt;
+  hipError_t e;
+  switch (N) {
+    case 2: e = run_merged_n<2>(vpt, st, a); break;
+    case 3: e = run_merged_n<3>(vpt, st, a); break;
+    case 4: e = run_merged_n<4>(vpt, st, a); break;
+    case 5: e = run_merged_n<5>(vpt, st, a); break;
+    case 6: e = run_merged_n<6>(vpt, st, a); break;
+    case 7: e = run_merged_n<7>(vpt, st, a); break;
+    case 8: e = run_merged_n<8>(vpt, st, a); break;
+    case 9: e = run_merged_n<9>(vpt, st, a); break;
+    default: return ATTNRES_ERR_INVALID_ARGUMENT;
+  }
+  return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
+}
+
 attnres_status fwd_common_checks(const float* w, float eps, int32_t N, int64_t T, int32_t D) {
   if (!sizes_ok(N, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -2223,6 +2596,24 @@ extern "C" attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_
   if (srcs == nullptr || z_given == nullptr || rstd_given == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   return fwd_impl(srcs, src_pitch, w, eps, N, T, D, out, rstd, alpha, false, nullptr, nullptr, stream, z_given,
                   rstd_given);
+}
+
+extern "C" attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch, const float* z,
+                                             int32_t L, int32_t n, int64_t T, int32_t D, float* U, int64_t u_lstride,
+                                             int64_t u_pitch, void* stream) {
+  return block_sums_impl(srcs, src_pitch, z, L, n, T, D, U, u_lstride, u_pitch, stream);
+}
+
+extern "C" attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial,
+                                             int64_t partial_pitch, const float* z_given, const float* rstd_given,
+                                             const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                                             uint16_t* out, float* rstd, float* alpha, void* stream) {
+  const attnres_status st = fwd_common_checks(w, eps, N, T, D);
+  if (st != ATTNRES_OK) return st;
+  if (N < 2) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (T == 0) return ATTNRES_OK;
+  const MergedArgs a{U, u_pitch, partial, partial_pitch, z_given, rstd_given, w, eps, T, D, out, rstd, alpha};
+  return fwd_merged_impl(a, N, stream);
 }
 
 extern "C" attnres_status attnres_bwd(const uint16_t* dout, const uint16_t* src, const float* w, const float* rstd,

@@ -23,7 +23,9 @@ peak memory -- in bf16 storage with fp32 arithmetic.  Prints one JSON line
                 the whole batch
 
   block_batched_scores  one block's 24 sub-layer forwards the plain way vs
-                one block-scores pass (MFMA) plus 24 forwards from its scores
+                one block-scores pass (MFMA) plus 24 forwards from its scores,
+                and vs block scores + one block-sums pass (the shared sources'
+                part of every sub-layer's weighted sum) + 24 merged forwards
 
 Flags: --gpus (1 only), --steps, --warmup, --workload (0..4, default 3),
 --sweep (extra per-T / per-N lines with fwd and bwd timed separately and
@@ -640,10 +642,13 @@ def ceilings(torch, dev, src, dout, out, dsrc, reps: int = 5, nbytes: int = 4 <<
 
 
 def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: int = 7168, reps: int = 5):
-    """One block's forwards two ways (the model's last block: n = 8 shared
+    """One block's forwards three ways (the model's last block: n = 8 shared
     sources -- embedding and 7 completed block sums -- plus the partial sum,
-    L = 24 sub-layers): L plain per-source forwards, against one block-scores
-    pass (MFMA) followed by L forwards from those scores.  Median of `reps`
+    L = 24 sub-layers): L plain per-source forwards; one block-scores pass
+    (MFMA) followed by L forwards from those scores; and block scores, one
+    block-sums pass (the shared sources' part of every sub-layer's weighted
+    sum, fp32, sub-layer-major and token-major) and L merged forwards that
+    read only the shared sum and the partial sum.  Median of `reps`
     whole-block timings, each preceded by a 512 MiB cache flush; per-call
     times from the same runs.  Device-side random inputs of the workload's
     scales (values do not change the timing)."""
@@ -660,7 +665,8 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
     ws = torch.empty((ar.block_scores_workspace_bytes(L, D),), dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    ev = TimingEvents(L + 2)
+    ev = TimingEvents(L + 3)
+    U = None
 
     def plain():
         ev.record(0, stream)
@@ -676,33 +682,65 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
             ar.attnres_fwd_scored(srcs, zb[l], rb, W[l], 1e-6, out=out, rstd=rstd, alpha=alpha)
             ev.record(l + 2, stream)
 
-    res = {}
-    for name, fn, last in (("plain", plain, L), ("batched", batched, L + 1)):
-        tot, first = [], []
+    def merged(token_major):
+        def run():
+            ev.record(0, stream)
+            ar.attnres_block_scores(srcs[:n], W, 1e-6, rstd=rb, z=zb, workspace=ws)
+            ev.record(1, stream)
+            ar.attnres_block_sums(srcs[:n], zb, U=U, token_major=token_major)
+            ev.record(2, stream)
+            for l in range(L):
+                ar.attnres_fwd_merged(U[:, l] if token_major else U[l], srcs[n], zb[l], rb, W[l], 1e-6, out=out,
+                                      rstd=rstd, alpha=alpha)
+                ev.record(l + 3, stream)
+        return run
+
+    def timed(fn, last, marks):
+        tot, parts = [], {m: [] for m in marks}
         for r in range(reps + 2):
             flush.zero_()
             fn()
             torch.cuda.synchronize()
             if r >= 2:
                 tot.append(ev.ms(0, last))
-                first.append(ev.ms(0, 1))
-        res[name] = (sorted(tot)[len(tot) // 2], sorted(first)[len(first) // 2])
+                for m in marks:
+                    parts[m].append(ev.ms(m[0], m[1]))
+        med = lambda v: sorted(v)[len(v) // 2]
+        return med(tot), {m: med(v) for m, v in parts.items()}
+
+    plain_ms, pp = timed(plain, L, [(0, 1)])
+    batched_ms, bp = timed(batched, L + 1, [(0, 1)])
+    scores_ms = bp[(0, 1)]
+    merged_res = {}
+    for tm in (False, True):
+        U = torch.empty((T, L, D) if tm else (L, T, D), dtype=torch.float32, device=dev)
+        ms, mp = timed(merged(tm), L + 2, [(1, 2), (2, L + 2)])
+        merged_res[tm] = (ms, mp[(1, 2)], mp[(2, L + 2)] / L)
+        del U
+        U = None
+        torch.cuda.empty_cache()
     ev.close()
-    plain_ms, plain_first = res["plain"]
-    batched_ms, scores_ms = res["batched"]
     scored_ms = (batched_ms - scores_ms) / L
     scores_bytes = T * n * (2 * D + 4) + L * T * n * 4 + 4 * L * D  # sources read; rstd, z written; W read
     fwd_bytes = T * (2 * N * D + 2 * D + 8 * N) + 4 * D
     scored_bytes = fwd_bytes + T * (N - 1) * 8  # + the given scores and rstd
+    sums_bytes = T * n * 2 * D + L * T * n * 4 + L * T * D * 4  # shared sources and z read; U written
+    merged_bytes = T * (4 * D + 2 * D + 2 * D + 8 * (N - 1) + 8 * N) + 4 * D  # U, p read; out written; scores, state
     rec = {"T": T, "n_shared": n, "N": N, "L": L, "D": D,
            "plain_block_ms": plain_ms, "batched_block_ms": batched_ms, "batched_vs_plain": plain_ms / batched_ms,
-           "plain_fwd_ms": plain_ms / L, "first_plain_fwd_ms": plain_first,
+           "plain_fwd_ms": plain_ms / L, "first_plain_fwd_ms": pp[(0, 1)],
            "block_scores_ms": scores_ms, "block_scores_GBps": scores_bytes / scores_ms / 1e6,
            "block_scores_TFLOPs": 2.0 * T * n * D * L / scores_ms / 1e9,
            "block_scores_mfma_TFLOPs": 2.0 * T * n * D * (16 * ((L + 15) // 16)) * 3 / scores_ms / 1e9,
            "scored_fwd_ms": scored_ms, "scored_fwd_GBps": scored_bytes / scored_ms / 1e6,
            "plain_fwd_GBps": fwd_bytes / (plain_ms / L) / 1e6,
-           "reps": f"median of {reps}, 512 MiB flush before each block"}
+           "U_GiB": L * T * D * 4 / 2 ** 30}
+    for tm, key in ((False, "l_major"), (True, "t_major")):
+        ms, sums_ms, mfwd_ms = merged_res[tm]
+        rec[f"merged_{key}"] = {"block_ms": ms, "vs_plain": plain_ms / ms, "block_sums_ms": sums_ms,
+                                "block_sums_GBps": sums_bytes / sums_ms / 1e6, "merged_fwd_ms": mfwd_ms,
+                                "merged_fwd_GBps": merged_bytes / mfwd_ms / 1e6}
+    rec["reps"] = f"median of {reps}, 512 MiB flush before each block"
     del srcs, W, out, rstd, alpha, rb, zb, ws, flush
     torch.cuda.empty_cache()
     return rec
@@ -734,8 +772,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="only the decoding-size forward calls (T = 1..1024), for latency profiles")
     ap.add_argument("--block", action="store_true",
-                    help="only the block-batched scores measurement (one JSON line), for profiles")
-    ap.add_argument("--no-block", action="store_true", help="skip the block-batched scores measurement")
+                    help="only the block-batched measurement (one JSON line), for profiles")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-batched measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the operator is token-local and the library has no "
@@ -789,7 +827,7 @@ def main():
         ceil = ceilings(torch, dev, src, dout, out, dsrc)
     blk = None
     if not args.no_block:
-        log("block-batched scores vs plain forwards (T=32768, 8 shared sources, 24 sub-layers)")
+        log("block-batched scores and sums vs plain forwards (T=32768, 8 shared sources, 24 sub-layers)")
         blk = block_batched(ar, torch, dev)
 
     ms_step = total_ms / args.steps

@@ -326,6 +326,59 @@ attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch
                                   uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
+ * Block-batched shared sums.  The weighted sum is linear in the sources, and
+ * while a block runs only its last source, the current partial sum, changes
+ * from one sub-layer to the next (architecture figure of "Kimi K3
+ * 模型结构（10）：RL 与服务中的状态管理").  So the part of sub-layer l's weighted
+ * sum that the n shared sources contribute is formed here for all L
+ * sub-layers in one pass over them, from the scores of attnres_block_scores,
+ * up to the softmax normaliser:
+ *     m[l][t]    = max_i z[l][t][i]
+ *     U[l][t][d] = sum_i exp(z[l][t][i] - m[l][t]) x[i][t][d]       (fp32)
+ * and each sub-layer's forward then runs attnres_fwd_merged, which reads its
+ * U rows and the partial sum instead of all N source rows.
+ *   srcs, src_pitch  the n shared sources as in attnres_block_scores
+ *                    (n = 1 .. ATTNRES_MAX_SOURCES)
+ *   z      [L][T][n] fp32, 4-byte aligned: attnres_block_scores' z (any
+ *          finite scores)
+ *   L      1 .. ATTNRES_MAX_QUERIES; T, D as attnres_fwd
+ *   U      fp32 output, 16-byte aligned: row (l, t) of D values at
+ *          U + l*u_lstride + t*u_pitch elements.  u_lstride and u_pitch are
+ *          multiples of 4, at least D, and lay the rows out sub-layer-major
+ *          (u_lstride >= (T-1)*u_pitch + D, e.g. u_lstride = T*D, u_pitch = D)
+ *          or token-major (u_pitch >= (L-1)*u_lstride + D, e.g. u_lstride =
+ *          D, u_pitch = L*D); other layouts are rejected.  L*T*D*4 bytes in
+ *          the dense layouts.
+ * U must not overlap the sources or z.  T == 0: nothing is enqueued.  The
+ * weights are fp32 (exp on the hardware exp2), the sums fp32 in source order.
+ */
+attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch, const float* z, int32_t L,
+                                  int32_t n, int64_t T, int32_t D, float* U, int64_t u_lstride, int64_t u_pitch,
+                                  void* stream);
+
+/*
+ * Forward of one sub-layer from its block-batched shared sum: U holds the
+ * sub-layer's rows of attnres_block_sums (U + l*u_lstride for sub-layer l,
+ * row t at + t*u_pitch floats; u_pitch a multiple of 4, >= D, 16-byte
+ * aligned base), partial [T][D] bf16 (row pitch partial_pitch, a multiple of
+ * 8 elements, 16-byte aligned) the current partial sum, the last of the N
+ * sources.  z_given and rstd_given ([T][N-1] fp32, 4-byte aligned) are the
+ * shared sources' scores for this sub-layer and their rstd, as for
+ * attnres_fwd_scored (z + l*T*(N-1) and rstd of attnres_block_scores).  The
+ * partial sum is normalised and scored with w, the softmax runs over all N
+ * scores exactly as in attnres_fwd_scored (alpha and rstd bitwise equal to
+ * that call's), and with m the largest given score and M the largest of all,
+ *     out = exp(m - M) / den * U + alpha[N-1] * partial
+ * which is the weighted sum of all N sources to within fp32 rounding.
+ * N = 2 .. ATTNRES_MAX_SOURCES; w, eps, T, D, out, rstd, alpha as
+ * attnres_fwd_sources.  Outputs must not overlap any input or each other.
+ * The backward is attnres_bwd_sources on all N sources with these outputs.
+ */
+attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial, int64_t partial_pitch,
+                                  const float* z_given, const float* rstd_given, const float* w, float eps, int32_t N,
+                                  int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+
+/*
  * Backward without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments, contract and errors as attnres_bwd,

@@ -147,6 +147,41 @@ def out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
     return 0.5 * bf16_ulp(torch.maximum(out_ref.abs(), out_gpu.abs())) + b
 
 
+def merged_out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
+    """Per-element bound on |out_gpu - out_ref| for the forward from block sums
+    (out' = bf16(fma(a'_p, p, c' U')), c' = exp(m - M) / den): out_bound plus
+    the difference between the weight a shared source gets through c' and its
+    exponential inside U' and the saved a'_i, which both approximate
+    exp(z_i - M) / den.  Each exponential of an argument of size |z_i - M|
+    formed in fp32 (one rounding of the argument, scaled by log2 e, then the
+    hardware exp2 within a few ulps) is off by at most u (2 |z_i - M| + 4)
+    relative, and |z_i - M| = log(max_j a_j / a_i) from the reference
+    weights; the shared sum's n fp32 terms and c' U' + a'_p p add (N + 3) u.
+    Doubled.  x [N][n][D], alpha [n][N]; float64 tensors."""
+    N = x.shape[0]
+    ar_ = a_ref.T[:, :, None].clamp_min(1e-300)           # [N][n][1]
+    spread = torch.log(ar_.max(0, keepdim=True).values / ar_)
+    k = U32 * (2 * spread + 4 + N + 3)
+    k[N - 1] = 0.0                                        # the partial sum's weight is a'_p itself
+    extra = (k * a_gpu.abs().T[:, :, None] * x.abs()).sum(0)
+    return out_bound(x, a_gpu, a_ref, out_ref, out_gpu) + 2.0 * extra
+
+
+def sums_bound(x, z) -> torch.Tensor:
+    """Per-element bound on |U_gpu - U_ref| for the block sums from the same
+    fp32 scores on both sides: each weight exp(z_i - m) formed in fp32 is off
+    by at most u (2 |z_i - m| + 4) relative (argument rounding and the
+    hardware exp2), and the n-term fp32 sum adds n u of the sum of |terms|;
+    doubled.  x [n][T][D], z [L][T][n]; returns [L][T][D]; float64 tensors."""
+    n = x.shape[0]
+    zm = z - z.max(2, keepdim=True).values                # [L][T][n]
+    c = torch.exp(zm) * U32 * (2 * zm.abs() + 4 + n)
+    b = torch.zeros((z.shape[0],) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    for i in range(n):
+        b += c[:, :, i:i + 1] * x[i].abs()[None]
+    return 2.0 * b
+
+
 def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu) -> torch.Tensor:
     """Per-element bound on |dsrc_gpu - dsrc_ref| for the overwriting backward.
     x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors."""
@@ -206,7 +241,8 @@ class Accum:
     def update(self, x, g, w, gpu: dict, ref: dict):
         """x [N][n][D] and g [n][D]: the chunk's inputs (bf16 bits or tensors);
         w [D]; gpu / ref: dicts of out [n][D], rstd and alpha [n][N] and
-        optionally dsrc [N][n][D] (tensors or arrays)."""
+        optionally dsrc [N][n][D] (tensors or arrays); ref["merged"] true
+        when out came from the block sums (merged_out_bound)."""
         d = self.dev
         go, ro = _t(gpu["out"], d), _t(ref["out"], d)
         ga, ra = _t(gpu["alpha"], d), _t(ref["alpha"], d)
@@ -219,7 +255,11 @@ class Accum:
         tok_num = (go - ro).square().sum(1).sqrt()
         tok_den = ro.square().sum(1).sqrt()
         self._max("out_token_rel_l2", (tok_num / torch.where(tok_den > 0, tok_den, torch.ones_like(tok_den))).max())
-        self._max("out_elem_ratio", ((go - ro).abs() / out_bound(xx, ga, ra, ro, go)).max())
+        if ref.get("merged"):  # the forward from block sums
+            bo = merged_out_bound(xx, ga, ra, ro, go)
+        else:
+            bo = out_bound(xx, ga, ra, ro, go)
+        self._max("out_elem_ratio", ((go - ro).abs() / bo).max())
         del go, ro
         if "dsrc" in ref:
             gd, rd = _t(gpu["dsrc"], d), _t(ref["dsrc"], d)

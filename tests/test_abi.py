@@ -37,7 +37,7 @@ def test_library_loads_and_exports_declared_symbols():
     names = _declared()
     assert names == ["attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_fwd_decode",
                      "attnres_fwd_update", "attnres_bwd_sources", "attnres_block_scores", "attnres_fwd_scored",
-                     "attnres_bwd_noalloc"]
+                     "attnres_block_sums", "attnres_fwd_merged", "attnres_bwd_noalloc"]
     others = re.findall(r"^uint32_t\s+(attnres_\w+)\s*\(", open(HEADER).read(), re.M)
     assert others == ["attnres_set_split_spin"]
     names += others
@@ -88,6 +88,51 @@ def test_block_scores_refuses_on_the_host():
     assert scored(zg=30 * g + 2) == INVALID                # misaligned
     assert scored(out=30 * g) == INVALID                   # out overlaps the given scores
     assert scored(rstd=31 * g) == INVALID                  # rstd overlaps the given rstd
+
+
+def test_block_sums_and_merged_forward_refuse_on_the_host():
+    """attnres_block_sums / attnres_fwd_merged: every call below has one bad
+    argument (or, last, nothing to do) and returns its status before anything
+    reaches the GPU."""
+    lib = ar.library()
+    g = 1 << 30
+    srcs = (ctypes.c_void_p * 9)(*[(i + 1) * g for i in range(9)])
+    T_, L_ = 16, 24
+
+    def sums(n=8, T=T_, D_=D, L=L_, z=20 * g, U=21 * g, ls=None, tp=None, pitch=None, s=srcs):
+        ls = T * D_ if ls is None else ls
+        tp = D_ if tp is None else tp
+        return lib.attnres_block_sums(s, D_ if pitch is None else pitch, z, L, n, T, D_, U, ls, tp, None)
+
+    assert sums(L=0) == INVALID and sums(L=65) == INVALID
+    assert sums(n=0) == INVALID and sums(n=10) == INVALID
+    assert sums(D_=7170) == INVALID and sums(pitch=D - 8) == INVALID
+    assert sums(z=0) == INVALID and sums(U=0) == INVALID
+    assert sums(z=20 * g + 2) == INVALID and sums(U=21 * g + 8) == INVALID   # misaligned
+    assert sums(ls=D, tp=D) == INVALID                     # rows of one sub-layer's tokens would collide
+    assert sums(ls=T_ * D - 4, tp=D) == INVALID            # sub-layer-major, one float short
+    assert sums(ls=D, tp=(L_ - 1) * D + D - 4) == INVALID  # token-major, one float short
+    assert sums(ls=T_ * D + 2) == INVALID                  # not a multiple of 4 floats
+    assert sums(tp=D - 4, ls=T_ * D) == INVALID            # pitch below a row
+    assert sums(U=1 * g) == INVALID                        # U overlaps source 0
+    assert sums(U=20 * g - 1024) == INVALID                # U runs into z
+    assert sums(T=0, s=None, z=0, U=0) == OK               # empty: nothing to do
+
+    def merged(N=9, T=T_, D_=D, U=40 * g, up=None, p=41 * g, pp=None, zg=42 * g, rg=43 * g, w=44 * g, eps=1e-6,
+               out=45 * g, rstd=46 * g, alpha=47 * g):
+        return lib.attnres_fwd_merged(U, D_ if up is None else up, p, D_ if pp is None else pp, zg, rg, w, eps, N, T,
+                                      D_, out, rstd, alpha, None)
+
+    assert merged(N=1) == INVALID and merged(N=10) == INVALID
+    assert merged(U=0) == INVALID and merged(p=0) == INVALID and merged(zg=0) == INVALID and merged(rg=0) == INVALID
+    assert merged(out=0) == INVALID and merged(rstd=0) == INVALID and merged(alpha=0) == INVALID
+    assert merged(w=0) == INVALID and merged(eps=-1.0) == INVALID and merged(D_=7170) == INVALID
+    assert merged(U=40 * g + 8) == INVALID and merged(p=41 * g + 2) == INVALID    # misaligned
+    assert merged(up=D - 4) == INVALID and merged(up=D + 2) == INVALID and merged(pp=D + 4) == INVALID
+    assert merged(out=40 * g) == INVALID                   # out overlaps U
+    assert merged(rstd=42 * g) == INVALID                  # rstd overlaps the given scores
+    assert merged(alpha=46 * g) == INVALID                 # alpha overlaps rstd
+    assert merged(T=0, U=0, p=0, zg=0, rg=0, out=0, rstd=0, alpha=0) == OK
 
 
 def test_header_constants_match_binding():

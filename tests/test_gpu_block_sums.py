@@ -1,0 +1,205 @@
+"""Block-batched shared sums (attnres_block_sums) and the forward from them
+(attnres_fwd_merged) against the fp64 oracle, through the C ABI.
+
+Within a block only the last source, the current partial sum, changes from one
+sub-layer to the next (architecture figure of "Kimi K3 模型结构（10）"), and the
+weighted sum is linear in the sources: the shared sources' part of every
+sub-layer's weighted sum is formed once per block, and each sub-layer's
+forward then reads its shared sum and the partial sum alone.
+
+Tolerances.  U: element by element within ``parity.sums_bound`` (the fp32
+weights' exponentials and the n-term fp32 sum, doubled), both sides given the
+same fp32 scores.  The merged forward meets the operator's own bars against
+the plain oracle forward on all N sources (out rel-L2 5e-3, alpha 1e-5
+absolute, rstd 1e-5 relative) and, element by element, ``merged_out_bound``:
+the plain forward's bound plus the difference between a shared source's
+weight through the rescaled sum and the saved alpha.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_residuals_depth_amd as ar
+import oracle
+import synth
+from parity import DEV, Accum, TOL_ALPHA_ABS, _t, sums_bound, to_dev_bf16, within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ar.library()
+
+
+def _queries(D, L, seed, std=None):
+    """L pseudo-queries [L][D] fp32 from the seeded generator."""
+    std = 1.0 / np.sqrt(D) if std is None else std
+    return np.stack([synth.normal_f32(D, seed, 60 + l, std) for l in range(L)])
+
+
+def _sources(n, T, D, seed=0):
+    wl = synth.Workload(f"sums_n{n}_T{T}_D{D}", T=T, N=n, D=D, seed=seed)
+    return wl, wl.sources()
+
+
+def _u_rows(U, token_major):
+    """U as [L][T][D] (a view)."""
+    return U.transpose(0, 1) if token_major else U
+
+
+@pytest.mark.parametrize("n,T,D,L,tmaj,w_std", [(8, 300, 7168, 24, False, None), (8, 130, 7168, 24, True, None),
+                                                 (3, 70, 1000, 5, False, None), (1, 17, 64, 1, False, None),
+                                                 (9, 40, 7176, 33, True, None), (4, 257, 16384, 16, False, None),
+                                                 (2, 1, 7168, 64, False, None), (5, 33, 512, 7, True, None),
+                                                 (8, 200, 7168, 24, False, 0.5)],
+                         ids=lambda v: str(v))
+def test_block_sums_against_oracle(n, T, D, L, tmaj, w_std):
+    """Every element of U against the oracle's sums of the same fp32 scores
+    (the oracle's own block scores, rounded to fp32, given to both sides)."""
+    wl, bits = _sources(n, T, D)
+    W = _queries(D, L, 1, w_std)
+    _, zo = oracle.block_scores(bits, W, wl.eps)
+    z32 = zo.astype(np.float32)
+    srcs = [to_dev_bf16(bits[i]) for i in range(n)]
+    print(f"[sums] n={n} T={T} D={D} L={L} token_major={tmaj} w_std={w_std}", flush=True)
+    U = ar.attnres_block_sums(srcs, torch.from_numpy(z32).to(DEV), token_major=tmaj)
+    torch.cuda.synchronize()
+    Uo = oracle.block_sums(bits, z32.astype(np.float64))
+    Ug = _u_rows(U, tmaj).double()
+    Ur = torch.from_numpy(Uo).to(DEV)
+    x = _t(bits, DEV)
+    bound = sums_bound(x, torch.from_numpy(z32.astype(np.float64)).to(DEV))
+    ratio = float(((Ug - Ur).abs() / (bound + 1e-300)).max())
+    rel = float((Ug - Ur).norm() / Ur.norm())
+    print(f"[sums]   max err/bound {ratio:.3e}, rel-L2 {rel:.3e}", flush=True)
+    assert ratio <= 1.0
+
+
+def test_block_sums_layouts_and_batch_agree_bitwise():
+    """Token-major and sub-layer-major U hold the same bits; a token's rows do
+    not depend on the batch it is in; interleaved [T][n][D] sources give the
+    same bits as separate ones."""
+    n, T, D, L = 6, 200, 7168, 24
+    wl, bits = _sources(n, T, D, seed=3)
+    W = _queries(D, L, 2)
+    srcs = [to_dev_bf16(bits[i]) for i in range(n)]
+    _, z = ar.attnres_block_scores(srcs, torch.from_numpy(W).to(DEV), wl.eps)
+    U1 = ar.attnres_block_sums(srcs, z)
+    U2 = ar.attnres_block_sums(srcs, z, token_major=True)
+    cache = torch.empty((T, n, D), dtype=torch.bfloat16, device=DEV)
+    for i in range(n):
+        cache[:, i].copy_(srcs[i])
+    U3 = ar.attnres_block_sums([cache[:, i] for i in range(n)], z)
+    U4 = ar.attnres_block_sums([s[37:101] for s in srcs], z[:, 37:101].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(U1, U2.transpose(0, 1))
+    assert torch.equal(U1, U3)
+    assert torch.equal(U1[:, 37:101], U4)
+
+
+def _chain(N, T, D, L, w_std=None, subs=(0,), seed=0, chunk=2048):
+    """GPU: block scores -> block sums -> each listed sub-layer's merged forward,
+    all on the device; compared with the plain oracle forward on all N
+    sources (the shared ones first, the partial sum last), every token."""
+    wl = synth.workload(1, N=N, T=T) if D == synth.D_MODEL else synth.Workload("merged", T=T, N=N, D=D, seed=seed)
+    bits = wl.sources()
+    W = _queries(D, L, 3 + seed, w_std)
+    srcs = [to_dev_bf16(bits[i]) for i in range(N)]
+    Wd = torch.from_numpy(W).to(DEV)
+    rb, zb = ar.attnres_block_scores(srcs[:-1], Wd, wl.eps)
+    U = ar.attnres_block_sums(srcs[:-1], zb)
+    errs = []
+    for l in subs:
+        print(f"[merged] N={N} T={T} D={D} sub-layer {l} w_std={w_std}", flush=True)
+        out, rstd, alpha = ar.attnres_fwd_merged(U[l], srcs[-1], zb[l], rb, Wd[l], wl.eps)
+        torch.cuda.synchronize()
+        acc = Accum(DEV)
+        for t0 in range(0, T, chunk):
+            t1 = min(T, t0 + chunk)
+            xs = np.ascontiguousarray(bits[:, t0:t1])
+            o_out, o_rstd, o_alpha = oracle.fwd(xs, W[l], wl.eps)
+            acc.update(xs, None, W[l], dict(out=out[t0:t1], rstd=rstd[t0:t1], alpha=alpha[t0:t1]),
+                       dict(out=o_out, rstd=o_rstd, alpha=o_alpha, merged=True))
+        e = acc.result()
+        print(f"[merged]   " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+        errs.append(e)
+    return errs
+
+
+@pytest.mark.parametrize("N,T,D", [(9, 300, 7168), (2, 65, 1000), (5, 129, 12288), (9, 77, 512), (4, 1, 7168)],
+                         ids=lambda v: str(v))
+def test_merged_forward_against_oracle(N, T, D):
+    for e in _chain(N, T, D, L=24, subs=(0, 7, 23)):
+        assert within_tolerance(e), e
+
+
+def test_merged_forward_peaked_softmax():
+    """Pseudo-queries ~ N(0, 0.5): scores of std ~40, nearly one-hot weights,
+    so the rescaling exp(m - M) often underflows or is exactly 1."""
+    for e in _chain(9, 4096, 7168, L=24, w_std=0.5, subs=(0, 23)):
+        assert within_tolerance(e), e
+        assert e["alpha_max_abs"] <= TOL_ALPHA_ABS
+
+
+def test_merged_matches_scored_weights_bitwise():
+    """alpha and rstd of the merged forward are the scored forward's bits (the
+    same softmax on the same given scores); out agrees within its bound and is
+    independent of the U layout and of the partial sum's row pitch."""
+    N, T, D, L = 9, 300, 7168, 24
+    wl = synth.workload(1, N=N, T=T)
+    bits = wl.sources()
+    W = torch.from_numpy(_queries(D, L, 4)).to(DEV)
+    srcs = [to_dev_bf16(bits[i]) for i in range(N)]
+    rb, zb = ar.attnres_block_scores(srcs[:-1], W, wl.eps)
+    U = ar.attnres_block_sums(srcs[:-1], zb)
+    Ut = ar.attnres_block_sums(srcs[:-1], zb, token_major=True)
+    cache = torch.empty((T, 2, D), dtype=torch.bfloat16, device=DEV)
+    cache[:, 1].copy_(srcs[-1])
+    for l in (0, 11, 23):
+        o_s, r_s, a_s = ar.attnres_fwd_scored(srcs, zb[l], rb, W[l], wl.eps)
+        o_m, r_m, a_m = ar.attnres_fwd_merged(U[l], srcs[-1], zb[l], rb, W[l], wl.eps)
+        o_t, r_t, a_t = ar.attnres_fwd_merged(Ut[:, l], cache[:, 1], zb[l], rb, W[l], wl.eps)
+        torch.cuda.synchronize()
+        assert torch.equal(a_m, a_s) and torch.equal(r_m, r_s)
+        assert torch.equal(o_t, o_m) and torch.equal(a_t, a_m) and torch.equal(r_t, r_m)
+        diff = (o_m.float() - o_s.float()).abs()
+        print(f"[merged vs scored] l={l}: out max |diff| {float(diff.max()):.3e}, "
+              f"differing elements {int((diff > 0).sum())} of {o_m.numel()}", flush=True)
+
+
+def test_merged_saved_state_drives_the_backward():
+    """The merged forward's saved rstd and alpha, given to the backward with all
+    N sources, give the gradients of the scored forward's saved state (bitwise:
+    the same saved bits)."""
+    N, T, D, L = 9, 129, 7168, 24
+    wl = synth.workload(1, N=N, T=T)
+    bits = wl.sources()
+    W = torch.from_numpy(_queries(D, L, 5)).to(DEV)
+    srcs = [to_dev_bf16(bits[i]) for i in range(N)]
+    dout = to_dev_bf16(wl.dout())
+    rb, zb = ar.attnres_block_scores(srcs[:-1], W, wl.eps)
+    U = ar.attnres_block_sums(srcs[:-1], zb)
+    _, r_m, a_m = ar.attnres_fwd_merged(U[5], srcs[-1], zb[5], rb, W[5], wl.eps)
+    _, r_s, a_s = ar.attnres_fwd_scored(srcs, zb[5], rb, W[5], wl.eps)
+    d_m, dw_m = ar.attnres_bwd_sources(dout, srcs, W[5], r_m, a_m)
+    d_s, dw_s = ar.attnres_bwd_sources(dout, srcs, W[5], r_s, a_s)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(d_m, d_s)) and torch.equal(dw_m, dw_s)
+
+
+def test_empty_batch_is_a_no_op():
+    D, L = 7168, 4
+    srcs = [torch.empty((0, D), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    z = torch.empty((L, 0, 3), dtype=torch.float32, device=DEV)
+    U = ar.attnres_block_sums(srcs, z)
+    assert U.shape == (L, 0, D)
+    out, rstd, alpha = ar.attnres_fwd_merged(U[0], torch.empty((0, D), dtype=torch.bfloat16, device=DEV),
+                                             torch.empty((0, 3), device=DEV), torch.empty((0, 3), device=DEV),
+                                             torch.zeros(D, device=DEV), 1e-6)
+    torch.cuda.synchronize()
+    assert out.shape == (0, D) and rstd.shape == (0, 4) and alpha.shape == (0, 4)
