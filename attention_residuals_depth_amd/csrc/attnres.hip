@@ -923,40 +923,60 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
 
 // Forward of one sub-layer from its block-batched shared sum U (above) and the
 // current partial sum p, the last of its N sources.  p is normalised and
-// scored here exactly as the scored forward scores its last source, and the
-// given rstd and scores of the N-1 shared sources arrive the same way, so the
-// softmax below is that forward's (the same instructions: alpha is bitwise
-// the scored forward's).  Then, with m the largest given score and M the
-// largest of all N,
+// scored here with w; the given rstd and scores of the N-1 shared sources
+// arrive as in the scored forward (lane i of each wave loads source i's), and
+// the softmax over all N scores is that forward's sequence.  Then, with m the
+// largest given score and M the largest of all N,
 //     out = exp(m - M) / den * U + alpha_p * p
 // since exp(m - M) exp(z_i - m) = exp(z_i - M): the plain weighted sum, from
-// one fp32 row and one bf16 row instead of N bf16 rows.  w stays in
-// registers (the row data per thread is small here).
-template <int N, int VPT>
-__global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_merged_kernel(
+// one fp32 row and one bf16 row instead of N bf16 rows.
+// Thread j owns the channel quads j + k*blockDim.x (k < kMergedQuads): 16
+// contiguous bytes of U and of w and 8 of p and out per quad, so every load
+// and store instruction of a wave covers one contiguous run (1 KiB of U,
+// 512 bytes of p).  Eight-channel vectors, whose 32 bytes of U take two
+// loads with a 32-byte lane stride, ran 11% slower (5.57 against 6.20 TB/s at
+// T = 32768, D = 7168); 256 threads (7 quads each) beat 448 (4) and 896 (2).
+// The partial sum's dots are therefore summed in another order than in the
+// scored forward: its rstd and score, and so alpha, agree with that forward's
+// to within fp32 rounding, not bit for bit.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kMergedQuads = 7;
+
+__device__ __forceinline__ void unpack4(const u32x2_t& q, float (&f)[4]) {
+  f[0] = __builtin_bit_cast(float, q.x << 16);
+  f[1] = __builtin_bit_cast(float, q.x & 0xFFFF0000u);
+  f[2] = __builtin_bit_cast(float, q.y << 16);
+  f[3] = __builtin_bit_cast(float, q.y & 0xFFFF0000u);
+}
+
+template <int N>
+__global__ void __launch_bounds__(1024) fwd_merged_kernel(
     const float* __restrict__ U, int64_t u_pitch, const uint16_t* __restrict__ p, int64_t p_pitch,
     const float* __restrict__ zg, const float* __restrict__ rg, const float* __restrict__ w, float eps, int64_t t0,
     int32_t D, uint16_t* __restrict__ out, float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
   static_assert(N >= 2, "the shared sources and the partial sum");
+  constexpr int Q = kMergedQuads;
   __shared__ __attribute__((aligned(16))) float red[1][2][kMaxWaves];
   const int tid = threadIdx.x;
-  const Slice<VPT> sl(tid, blockDim.x, D);
   const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
-  uint4 wv[VPT][2];
-  load_w<VPT>(wv, w, D, sl);
-  sched_fence();
-  uint4 pv[VPT], uv[VPT][2];
-  {
-    const __amdgpu_buffer_rsrc_t rp = rsrc(p + t * p_pitch, (uint32_t)D * 2u);
-    const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);
+  const int V4 = D / 4;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
+  const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);
+  const __amdgpu_buffer_rsrc_t rp = rsrc(p + t * p_pitch, (uint32_t)D * 2u);
+  uint4 wq[Q], uq[Q];
+  u32x2_t pq[Q];
+  uint32_t o16[Q];  // the quad's byte offset in an fp32 row (past the row end: reads zeros, stores dropped)
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) pv[k] = bload<kAuxStreamLoad>(rp, sl.off[k]);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      uv[k][0] = bload<kAuxStreamLoad>(ru, 2u * sl.off[k]);
-      uv[k][1] = bload<kAuxStreamLoad>(ru, 2u * sl.off[k] + 16u);
-    }
+  for (int k = 0; k < Q; ++k) {
+    const int q = tid + k * (int)blockDim.x;
+    o16[k] = q < V4 ? (uint32_t)q * 16u : 0xFFFFFFF0u;
+    wq[k] = bload(rw, o16[k]);
   }
+  sched_fence();
+#pragma unroll
+  for (int k = 0; k < Q; ++k) pq[k] = __builtin_amdgcn_raw_buffer_load_b64(rp, o16[k] / 2u, 0, kAuxStreamLoad);
+#pragma unroll
+  for (int k = 0; k < Q; ++k) uq[k] = bload<kAuxStreamLoad>(ru, o16[k]);
   float zgv, rgv;
   {  // lane i: shared source i's given score and rstd (lanes >= N-1 read zeros)
     const int lane = lane_id();
@@ -966,18 +986,21 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_merged_kernel(
   }
   sched_fence();
   clear_absent<2>(red);
-  // the partial sum's sum of squares and w.p, as the scored forward forms them
+  // the partial sum's sum of squares and w.p
   float part[2] = {0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    if (!sl.has(k)) continue;
-    const float4 wa = __builtin_bit_cast(float4, wv[k][0]), wb = __builtin_bit_cast(float4, wv[k][1]);
-    const float wr[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-    float f[8];
-    unpack8(pv[k], f);
-    part[0] = dot8_bf16(pv[k], pv[k], part[0]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[1] = fmaf(wr[e], f[e], part[1]);
+  for (int k = 0; k < Q; ++k) {
+    const float4 wv = __builtin_bit_cast(float4, wq[k]);
+    float f[4];
+    unpack4(pq[k], f);
+    part[0] = fmaf(f[0], f[0], part[0]);
+    part[0] = fmaf(f[1], f[1], part[0]);
+    part[0] = fmaf(f[2], f[2], part[0]);
+    part[0] = fmaf(f[3], f[3], part[0]);
+    part[1] = fmaf(wv.x, f[0], part[1]);
+    part[1] = fmaf(wv.y, f[1], part[1]);
+    part[1] = fmaf(wv.z, f[2], part[1]);
+    part[1] = fmaf(wv.w, f[3], part[1]);
   }
   block_sums<2>(part, red[0]);
 
@@ -1009,15 +1032,17 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_merged_kernel(
 
   const __amdgpu_buffer_rsrc_t ro = rsrc(out + t * D, (uint32_t)D * 2u);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    if (!sl.has(k)) continue;
-    const float4 ua = __builtin_bit_cast(float4, uv[k][0]), ub = __builtin_bit_cast(float4, uv[k][1]);
-    const float u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-    float f[8], acc[8];
-    unpack8(pv[k], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(a[N - 1], f[e], cs * u[e]);
-    bstore<kAuxStreamStore>(ro, sl.off[k], pack8(acc));
+  for (int k = 0; k < Q; ++k) {
+    const float4 u = __builtin_bit_cast(float4, uq[k]);
+    float f[4];
+    unpack4(pq[k], f);
+    const float acc[8] = {fmaf(a[N - 1], f[0], cs * u.x), fmaf(a[N - 1], f[1], cs * u.y),
+                          fmaf(a[N - 1], f[2], cs * u.z), fmaf(a[N - 1], f[3], cs * u.w), 0.f, 0.f, 0.f, 0.f};
+    const uint4 pk = pack8(acc);
+    u32x2_t o;
+    o.x = pk.x;
+    o.y = pk.y;
+    __builtin_amdgcn_raw_buffer_store_b64(o, ro, o16[k] / 2u, 0, kAuxStreamStore);
   }
   if (tid < N) {
     float rv = r[0], av = a[0];
@@ -2326,26 +2351,23 @@ struct MergedArgs {
   float* alpha;
 };
 
-template <int N, int VPT>
-hipError_t run_merged_vpt(hipStream_t st, const MergedArgs& a) {
-  const int threads = threads_for(a.D, VPT);
+// kMergedQuads channel quads per thread, whole waves: 256 threads at D = 7168,
+// 640 at D = 16384.
+template <int N>
+hipError_t run_merged_n(hipStream_t st, const MergedArgs& a) {
+  const int threads = ((a.D / 4 + kMergedQuads - 1) / kMergedQuads + kWave - 1) / kWave * kWave;
   int64_t res = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N, VPT>), threads, 0, &res);
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N>), threads, 0, &res);
   if (e != hipSuccess) return e;  // validates the launch shape
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_merged_kernel<N, VPT>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U, a.u_pitch,
-                       a.p, a.p_pitch, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    hipLaunchKernelGGL((fwd_merged_kernel<N>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U, a.u_pitch, a.p,
+                       a.p_pitch, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-template <int N>
-hipError_t run_merged_n(int vpt, hipStream_t st, const MergedArgs& a) {
-  return vpt == 4 ? run_merged_vpt<N, 4>(st, a) : run_merged_vpt<N, 2>(st, a);
 }
 
 attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
@@ -2367,17 +2389,16 @@ attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
       if (overlap(outs[i], outs[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int vpt = fwd_shape(a.D).vpt;
   hipError_t e;
   switch (N) {
-    case 2: e = run_merged_n<2>(vpt, st, a); break;
-    case 3: e = run_merged_n<3>(vpt, st, a); break;
-    case 4: e = run_merged_n<4>(vpt, st, a); break;
-    case 5: e = run_merged_n<5>(vpt, st, a); break;
-    case 6: e = run_merged_n<6>(vpt, st, a); break;
-    case 7: e = run_merged_n<7>(vpt, st, a); break;
-    case 8: e = run_merged_n<8>(vpt, st, a); break;
-    case 9: e = run_merged_n<9>(vpt, st, a); break;
+    case 2: e = run_merged_n<2>(st, a); break;
+    case 3: e = run_merged_n<3>(st, a); break;
+    case 4: e = run_merged_n<4>(st, a); break;
+    case 5: e = run_merged_n<5>(st, a); break;
+    case 6: e = run_merged_n<6>(st, a); break;
+    case 7: e = run_merged_n<7>(st, a); break;
+    case 8: e = run_merged_n<8>(st, a); break;
+    case 9: e = run_merged_n<9>(st, a); break;
     default: return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;

@@ -366,8 +366,9 @@ attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch
  * shared sources' scores for this sub-layer and their rstd, as for
  * attnres_fwd_scored (z + l*T*(N-1) and rstd of attnres_block_scores).  The
  * partial sum is normalised and scored with w, the softmax runs over all N
- * scores exactly as in attnres_fwd_scored (alpha and rstd bitwise equal to
- * that call's), and with m the largest given score and M the largest of all,
+ * scores as in attnres_fwd_scored (rstd and alpha within fp32 rounding of
+ * that call's: the partial sum's dots are summed in another order), and with
+ * m the largest given score and M the largest of all,
  *     out = exp(m - M) / den * U + alpha[N-1] * partial
  * which is the weighted sum of all N sources to within fp32 rounding.
  * N = 2 .. ATTNRES_MAX_SOURCES; w, eps, T, D, out, rstd, alpha as
