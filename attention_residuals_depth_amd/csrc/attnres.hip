@@ -684,8 +684,12 @@ __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3],
                                         int r, int32_t D, int32_t Lpad, int32_t Dpad) {
   const int ch = 32 * s + 8 * q;  // this lane's first channel
   const uint32_t kb = (uint32_t)ch * 2u;
+  // default policy: a k-step reads 64 of a row's 128-byte line, and the L2
+  // keeps the line for the next k-step; with the streaming hint it was often
+  // gone by then and fetched again (1.67x the algorithmic bytes, 1.50 against
+  // 1.37 ms at T = 32768, n = 8, L = 24)
 #pragma unroll
-  for (int m = 0; m < kBsTiles; ++m) a[m] = bload<kAuxStreamLoad>(ra, ch < D ? roff[m] + kb : 0xFFFFFFF0u);
+  for (int m = 0; m < kBsTiles; ++m) a[m] = bload(ra, ch < D ? roff[m] + kb : 0xFFFFFFF0u);
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
