@@ -7,7 +7,10 @@
  * backward, whose exchange is also run on its recompute route), compares
  * against the oracle with
  * the operator's tolerances, checks that a bad argument is refused with
- * ATTNRES_ERR_INVALID_ARGUMENT, and exits 0 only if everything holds.
+ * ATTNRES_ERR_INVALID_ARGUMENT, runs the block-level route (block scores of
+ * the first seven sources for four pseudo-queries, block sums, the merged
+ * forward of one sub-layer with the eighth source as its partial sum) against
+ * the oracle's plain forward, and exits 0 only if everything holds.
  */
 #include <hip/hip_runtime_api.h>
 
@@ -160,5 +163,48 @@ int main(void) {
   const int same0 = memcmp(dsrc, dsrc0, nsrc * 2) == 0 && memcmp(dw, dw0, D * 4) == 0;
   printf("recomputed exchange == ring exchange: %s\n", same0 ? "yes" : "no");
   if (prev != ATTNRES_SPLIT_SPIN_DEFAULT || !same0) ++fails;
+
+  /* the block-level route: sources 0..6 shared, source 7 the partial sum, sub-layer 2 of 4 */
+  {
+    const int L = 4, n = N - 1, l = 2;
+    float* W = malloc((size_t)L * D * 4);
+    synth_normal_f32(W, (int64_t)L * D, 0, 3, 0, 1.f / sqrtf((float)D));
+    float *d_W, *d_rb, *d_zb, *d_U, *d_rstd3, *d_alpha3;
+    uint16_t* d_out3;
+    void* d_bws;
+    const size_t bws = ATTNRES_BLOCK_SCORES_WORKSPACE_BYTES(L, D);
+    CHECK_HIP(hipMalloc((void**)&d_W, (size_t)L * D * 4));
+    CHECK_HIP(hipMalloc((void**)&d_rb, (size_t)T * n * 4));
+    CHECK_HIP(hipMalloc((void**)&d_zb, (size_t)L * T * n * 4));
+    CHECK_HIP(hipMalloc((void**)&d_U, (size_t)L * T * D * 4));
+    CHECK_HIP(hipMalloc((void**)&d_out3, nTD * 2));
+    CHECK_HIP(hipMalloc((void**)&d_rstd3, nTN * 4));
+    CHECK_HIP(hipMalloc((void**)&d_alpha3, nTN * 4));
+    CHECK_HIP(hipMalloc(&d_bws, bws));
+    CHECK_HIP(hipMemcpy(d_W, W, (size_t)L * D * 4, hipMemcpyHostToDevice));
+    st = attnres_block_scores(srcs, D, d_W, L, eps, n, T, (int32_t)D, d_rb, d_zb, d_bws, bws, NULL);
+    if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_scores returned %d\n", (int)st); return 1; }
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, T * D, D, NULL);
+    if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_sums returned %d\n", (int)st); return 1; }
+    st = attnres_fwd_merged(d_U + (size_t)l * T * D, D, srcs[n], D, d_zb + (size_t)l * T * n, d_rb, d_W + (size_t)l * D,
+                            eps, N, T, (int32_t)D, d_out3, d_rstd3, d_alpha3, NULL);
+    if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd_merged returned %d\n", (int)st); return 1; }
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, D, D, NULL);  /* rows would collide */
+    if (st != ATTNRES_ERR_INVALID_ARGUMENT) { fprintf(stderr, "colliding U rows not refused (%d)\n", (int)st); ++fails; }
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(out, d_out3, nTD * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(rstd, d_rstd3, nTN * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(alpha, d_alpha3, nTN * 4, hipMemcpyDeviceToHost));
+    oracle_fwd(N, T, D, src, W + (size_t)l * D, eps, r_out, r_rstd, r_alpha);
+    double a3 = 0, r3 = 0;
+    for (size_t i = 0; i < nTN; ++i) {
+      a3 = fmax(a3, fabs((double)alpha[i] - r_alpha[i]));
+      r3 = fmax(r3, fabs((double)rstd[i] / r_rstd[i] - 1.0));
+    }
+    const double o3 = rel_l2_bf16(out, r_out, nTD);
+    printf("block route (scores, sums, merged forward): out rel_l2 %.3e  alpha max abs %.3e  rstd max rel %.3e\n", o3,
+           a3, r3);
+    if (!(o3 <= 5e-3 && a3 <= 1e-5 && r3 <= 1e-5)) ++fails;
+  }
   return fails == 0 ? 0 : 1;
 }
