@@ -47,6 +47,9 @@ void oracle_block_scores(int n, int64_t T, int64_t D, int L, const uint16_t* src
                          double* rstd, double* z);
 void oracle_fwd_scored(int N, int64_t T, int64_t D, const uint16_t* src, const double* zg, const double* rg,
                        const float* w, double eps, double* out, double* rstd, double* alpha);
+void oracle_block_sums(int n, int64_t T, int64_t D, int L, const uint16_t* src, const double* z, double* U);
+void oracle_fwd_merged(int N, int64_t T, int64_t D, const double* U, const uint16_t* p, const double* zg,
+                       const double* rg, const float* w, double eps, double* out, double* rstd, double* alpha);
 
 static double bf(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
@@ -118,6 +121,14 @@ static void run_oracle(void) {
     oracle_fwd_scored(N, T, D, src, zb + (size_t)(L - 1) * T * (N - 1), rb, w, 1e-6, out3, rstd3, alpha3);
     for (size_t k = 0; k < (size_t)T * D; ++k) EXPECT(fabs(out3[k] - out[k]) <= 1e-12 * (1.0 + fabs(out[k])));
     for (size_t k = 0; k < (size_t)T * N; ++k) EXPECT(fabs(alpha3[k] - alpha[k]) <= 1e-12);
+    /* the shared sums of those sources, then the last sub-layer's forward from its sum */
+    double* U = malloc(sizeof(double) * L * T * D);
+    oracle_block_sums(N - 1, T, D, L, src, zb, U);
+    oracle_fwd_merged(N, T, D, U + (size_t)(L - 1) * T * D, src + (size_t)(N - 1) * T * D,
+                      zb + (size_t)(L - 1) * T * (N - 1), rb, w, 1e-6, out3, rstd3, alpha3);
+    for (size_t k = 0; k < (size_t)T * D; ++k) EXPECT(fabs(out3[k] - out[k]) <= 1e-12 * (1.0 + fabs(out[k])));
+    for (size_t k = 0; k < (size_t)T * N; ++k) EXPECT(fabs(alpha3[k] - alpha[k]) <= 1e-12);
+    free(U);
     free(W); free(rb); free(zb); free(out3); free(rstd3); free(alpha3);
   }
 
@@ -203,6 +214,20 @@ static void run_abi(void) {
   for (int i = 0; i < N; ++i) bad[i] = (void*)srcs[i];
   EXPECT(attnres_bwd_sources(dout, srcs, (int64_t)N * D, w, rstd, alpha, N, T, D, bad, (int64_t)N * D, 0, dw, ws,
                              wsb, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  /* block sums: colliding U rows, U on top of a source; merged forward: out on top of U, misaligned partial sum */
+  float* U = (float*)ws;
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, U, D, D, NULL) ==
+         ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, (float*)srcs[0], (int64_t)T * D, D, NULL) ==
+         ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 0, N - 1, T, D, U, (int64_t)T * D, D, NULL) ==
+         ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, rstd, alpha, w, 1e-6f, N, T, D, (uint16_t*)U, rstd,
+                            alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1] + 1, (int64_t)N * D, rstd, alpha, w, 1e-6f, N, T, D, out, rstd, alpha,
+                            NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, rstd, alpha, w, 1e-6f, 1, T, D, out, rstd, alpha,
+                            NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
 }
 #endif
 
