@@ -5,7 +5,8 @@ buffers, interleaved by token, padded rows) and a call mix (overwriting or
 accumulating backward with bf16 or fp32 gradients, decoding forward, fused
 partial-sum update), runs it
 on the GPU and compares every output with the oracle at the operator's
-tolerances.  The cases are fixed by their seeds, so a failure names a
+tolerances.  A second set of cases runs the block-level route (block scores,
+block sums, merged forwards) the same way.  The cases are fixed by their seeds, so a failure names a
 reproducible configuration."""
 from __future__ import annotations
 
@@ -144,3 +145,37 @@ def test_random_configuration(seed):
             assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
         else:
             assert float(np.max(np.abs(dw.cpu().double().numpy()))) <= 1e-6
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_block_route(seed):
+    """The block-level route on seeded random configurations: block scores of
+    n shared sources for L pseudo-queries, block sums (either U layout), and
+    the merged forward of a few sub-layers with the partial sum as the last
+    source, against the oracle's plain forward on all n + 1 sources."""
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(1, 9))
+    N = n + 1
+    T = int(rng.integers(1, 200))
+    D = 8 * int(rng.choice([1, 2, 7, 64, 125, 513, 896, 1024, 1025, 1536, 2048]))
+    L = int(rng.integers(1, 41))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3]))
+    w_std = float(rng.choice([1.0 / np.sqrt(D), 0.5]))
+    layout = str(rng.choice(["separate", "interleaved", "padded"]))
+    token_major = bool(rng.integers(0, 2))
+    wl = synth.Workload(f"fuzzb{seed}", T=T, N=N, D=D, eps=eps, seed=seed, kind="depth")
+    src_h = wl.sources()
+    W_h = np.stack([synth.normal_f32(D, seed, 300 + l, w_std) for l in range(L)])
+    print(f"[fuzz block] seed={seed} n={n} T={T} D={D} L={L} eps={eps} w_std={w_std:.3g} layout={layout} "
+          f"token_major={token_major}", flush=True)
+    views = _place(to_dev_bf16(src_h), layout, rng)
+    W = torch.from_numpy(W_h).to(DEV)
+    rb, zb = ar.attnres_block_scores(views[:n], W, eps)
+    U = ar.attnres_block_sums(views[:n], zb, token_major=token_major)
+    for l in sorted({0, L - 1, int(rng.integers(0, L))}):
+        out, rstd, alpha = ar.attnres_fwd_merged(U[:, l] if token_major else U[l], views[n], zb[l], rb, W[l], eps)
+        torch.cuda.synchronize()
+        o_out, o_rstd, o_alpha = oracle.fwd(src_h, W_h[l], eps)
+        assert rel_l2(bf16_dev_to_f64(out), o_out) <= TOL_OUT_REL_L2
+        assert float(np.max(np.abs(alpha.cpu().double().numpy() - o_alpha))) <= TOL_ALPHA_ABS
+        assert float(np.max(np.abs(rstd.cpu().double().numpy() / o_rstd - 1))) <= TOL_RSTD_REL
