@@ -223,3 +223,61 @@ def test_graph_capture_replays_match_eager(case):
         for name, x, y in zip(("out", "rstd", "alpha", "dsrc", "dw"), ref, (out, rstd, alpha, dsrc, dw)):
             assert torch.equal(_bits(x), _bits(y)), (k, name)
         assert torch.equal(_bits(ref[0]), _bits(dec)), k
+
+
+def test_graph_capture_block_route_replays_match_eager():
+    """The block-level route (block scores with its query split, block sums,
+    three merged forwards) captured in one HIP graph: every replay, with new
+    sources and queries copied in and eager work in between, matches eager
+    calls in fresh buffers bit for bit."""
+    n, T, D, L = 8, 300, 7168, 24
+    N = n + 1
+    s_src = torch.empty((N, T, D), dtype=torch.bfloat16, device=DEV)
+    s_W = torch.empty((L, D), dtype=torch.float32, device=DEV)
+    rb = torch.empty((T, n), dtype=torch.float32, device=DEV)
+    zb = torch.empty((L, T, n), dtype=torch.float32, device=DEV)
+    ws = torch.empty((ar.block_scores_workspace_bytes(L, D),), dtype=torch.uint8, device=DEV)
+    U = torch.empty((L, T, D), dtype=torch.float32, device=DEV)
+    subs = (0, 11, 23)
+    outs = [(torch.empty((T, D), dtype=torch.bfloat16, device=DEV), torch.empty((T, N), device=DEV),
+             torch.empty((T, N), device=DEV)) for _ in subs]
+    eps = 1e-6
+
+    def step():
+        srcs = [s_src[i] for i in range(N)]
+        ar.attnres_block_scores(srcs[:n], s_W, eps, rstd=rb, z=zb, workspace=ws)
+        ar.attnres_block_sums(srcs[:n], zb, U=U)
+        for l, (o, r, a) in zip(subs, outs):
+            ar.attnres_fwd_merged(U[l], srcs[n], zb[l], rb, s_W[l], eps, out=o, rstd=r, alpha=a)
+
+    def inputs(k):
+        wk = synth.Workload(f"graph_block_{k}", T=T, N=N, D=D, seed=40 + k)
+        W = np.stack([synth.normal_f32(D, 40 + k, 70 + l, 1.0 / np.sqrt(D)) for l in range(L)])
+        return to_dev_bf16(wk.sources()), torch.from_numpy(W).to(DEV)
+
+    src0, W0 = inputs(0)
+    s_src.copy_(src0)
+    s_W.copy_(W0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for k in range(1, 4):
+        src_k, W_k = inputs(k)
+        s_src.copy_(src_k)
+        s_W.copy_(W_k)
+        graph.replay()
+        torch.cuda.synchronize()
+        srcs = [src_k[i] for i in range(N)]
+        r_rb, r_zb = ar.attnres_block_scores(srcs[:n], W_k, eps)  # eager, fresh buffers
+        r_U = ar.attnres_block_sums(srcs[:n], r_zb)
+        torch.cuda.synchronize()
+        assert torch.equal(r_rb, rb) and torch.equal(r_zb, zb) and torch.equal(r_U, U), k
+        for l, (o, r, a) in zip(subs, outs):
+            e_o, e_r, e_a = ar.attnres_fwd_merged(r_U[l], srcs[n], r_zb[l], r_rb, W_k[l], eps)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(e_o), _bits(o)) and torch.equal(e_r, r) and torch.equal(e_a, a), (k, l)
