@@ -525,8 +525,8 @@ __device__ __forceinline__ void fwd_token(uint4 (&x)[N][VPT], int64_t t, int& bu
   }
 }
 
-// One workgroup per token: workgroup b handles token t0 + b.  The hardware
-// dispatcher starts the next token as soon as a workgroup retires, two
+// One workgroup per token: workgroup b handles token t0 + xcd_chunked(b).  The
+// hardware dispatcher starts the next token as soon as a workgroup retires, two
 // workgroups share a CU, and the tokens in flight at any moment are
 // neighbours, so the rows the chip reads are close together in every source.
 // This beat a persistent kernel with a two-token software pipeline per
@@ -561,6 +561,27 @@ constexpr int kFwdPlain = 0;
 constexpr int kFwdUpdate = 1;
 constexpr int kFwdScored = 2;
 
+// The token of workgroup b in a launch of n one-token workgroups.  The
+// dispatcher deals the workgroups of a launch to the 8 XCDs in turn
+// (workgroup b runs on XCD b mod 8), so with t = b consecutive tokens land on
+// different XCDs.  Here, in groups of 8C tokens, XCD x takes the C consecutive
+// tokens x*C .. x*C + C-1 of each group (the last, partial group keeps t = b).
+// On MI355X the forward read 13% faster at T = 131072 with C = 16 (5.53 ->
+// 6.25 TB/s; 6% at T = 16384 and 32768, equal at T = 1024), C = 32 within 1%
+// of that; each token's arithmetic is unchanged, so its results are the same
+// bits.  The block sums and the merged forward use it too (2-3% and 1%); the
+// backward kernels measured no gain from it (the one-token backward's
+// workgroup-to-token stride, the split backward's spans with all slices on
+// one XCD: 10-15% slower).
+constexpr int64_t kXcdCount = 8;
+constexpr int64_t kXcdChunk = 16;
+__device__ __forceinline__ int64_t xcd_chunked(int64_t b, int64_t n) {
+  constexpr int64_t G = kXcdCount * kXcdChunk;
+  if (b >= n / G * G) return b;
+  const int64_t r = b % G;
+  return b - r + (r % kXcdCount) * kXcdChunk + r / kXcdCount;
+}
+
 template <int N, int VPT, int VARIANT>
 __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src, const uint16_t* __restrict__ delta,
                                                    uint16_t* partial_out, const float* __restrict__ zg,
@@ -583,7 +604,7 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
   c.red = &red[0][0];
   c.tid = threadIdx.x;
   const Slice<VPT> sl(c.tid, blockDim.x, D);
-  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
+  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // the host launches one workgroup per token
 
   uint4 wv[VPT][2];
   load_w<VPT>(wv, w, D, sl);
@@ -862,7 +883,7 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
   __shared__ float4 stage[kMaxWaves * 2 * kWave];  // 2 KiB per wave
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const Slice<VPT> sl(tid, blockDim.x, D);
-  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
+  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // one workgroup per token (2-3% faster than t = b)
   float zz[NS];
   if (tid < L) {  // requested first: the weights can form while the rows are in flight
     const float* zt = z + ((int64_t)tid * T + t) * NS;
@@ -962,7 +983,7 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
   constexpr int Q = kMergedQuads;
   __shared__ __attribute__((aligned(16))) float red[1][2][kMaxWaves];
   const int tid = threadIdx.x;
-  const int64_t t = t0 + blockIdx.x;  // the host launches one workgroup per token
+  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // one workgroup per token (1% faster than t = b)
   const int V4 = D / 4;
   const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);

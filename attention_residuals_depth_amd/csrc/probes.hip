@@ -70,11 +70,22 @@ struct WRows {
   uint16_t* p[kMaxN];
 };
 
-// Forward pattern: workgroup t reads row t of the N row sets (four 16-byte
-// vectors per thread, all loads issued before any use) and writes row t of out.
+// Forward pattern: one workgroup per token reads the token's row of each of
+// the N row sets (four 16-byte vectors per thread, all loads issued before any
+// use) and writes its row of out.  Tokens are dealt to workgroups as the
+// operator's forward deals them: workgroup b runs on XCD b mod 8, and in
+// groups of 128 tokens XCD x takes the 16 consecutive tokens 16x .. 16x + 15
+// (the last, partial group keeps token = b).
+__device__ __forceinline__ int64_t xcd_token(int64_t b, int64_t n) {
+  constexpr int64_t C = 16, G = 8 * C;
+  if (b >= n / G * G) return b;
+  const int64_t r = b % G;
+  return b - r + (r % 8) * C + r / 8;
+}
+
 __global__ void __launch_bounds__(256) fwd_pattern_kernel(Rows src, int32_t N, int32_t D,
                                                           uint16_t* __restrict__ out) {
-  const int64_t t = blockIdx.x;
+  const int64_t t = xcd_token(blockIdx.x, gridDim.x);
   const uint32_t bytes = (uint32_t)D * 2u;
   u32x4_t x[kMaxN][4];
 #pragma unroll
