@@ -569,10 +569,12 @@ constexpr int kFwdScored = 2;
 // On MI355X the forward read 13% faster at T = 131072 with C = 16 (5.53 ->
 // 6.25 TB/s; 6% at T = 16384 and 32768, equal at T = 1024), C = 32 within 1%
 // of that; each token's arithmetic is unchanged, so its results are the same
-// bits.  The block sums and the merged forward use it too (2-3% and 1%); the
-// backward kernels measured no gain from it (the one-token backward's
-// workgroup-to-token stride, the split backward's spans with all slices on
-// one XCD: 10-15% slower).
+// bits.  Only where two or more workgroups share a CU (D <= 8192): with one
+// workgroup of 768-1024 threads per CU (D = 12288, 16384) the same mapping
+// read 2% and 12% slower.  The block sums and the merged forward use it too
+// (2-3% and 1% at D = 7168); the backward kernels measured no gain from it
+// (the one-token backward's workgroup-to-token stride, the split backward's
+// spans with all slices on one XCD: 10-15% slower).
 constexpr int64_t kXcdCount = 8;
 constexpr int64_t kXcdChunk = 16;
 __device__ __forceinline__ int64_t xcd_chunked(int64_t b, int64_t n) {
@@ -604,7 +606,8 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
   c.red = &red[0][0];
   c.tid = threadIdx.x;
   const Slice<VPT> sl(c.tid, blockDim.x, D);
-  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // the host launches one workgroup per token
+  // the host launches one workgroup per token; VPT = 4 <=> 512 < D <= 8192
+  const int64_t t = t0 + (VPT >= 4 ? xcd_chunked(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
 
   uint4 wv[VPT][2];
   load_w<VPT>(wv, w, D, sl);
@@ -883,7 +886,8 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
   __shared__ float4 stage[kMaxWaves * 2 * kWave];  // 2 KiB per wave
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const Slice<VPT> sl(tid, blockDim.x, D);
-  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // one workgroup per token (2-3% faster than t = b)
+  // one workgroup per token; VPT = 1 <=> D <= 8192 (2-3% faster than t = b at D = 7168)
+  const int64_t t = t0 + (VPT == 1 ? xcd_chunked(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
   float zz[NS];
   if (tid < L) {  // requested first: the weights can form while the rows are in flight
     const float* zt = z + ((int64_t)tid * T + t) * NS;
@@ -983,7 +987,8 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
   constexpr int Q = kMergedQuads;
   __shared__ __attribute__((aligned(16))) float red[1][2][kMaxWaves];
   const int tid = threadIdx.x;
-  const int64_t t = t0 + xcd_chunked(blockIdx.x, gridDim.x);  // one workgroup per token (1% faster than t = b)
+  // one workgroup per token (1% faster than t = b at D = 7168; up to D = 8192)
+  const int64_t t = t0 + (D <= 8192 ? xcd_chunked(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
   const int V4 = D / 4;
   const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);

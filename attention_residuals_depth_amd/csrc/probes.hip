@@ -75,7 +75,8 @@ struct WRows {
 // use) and writes its row of out.  Tokens are dealt to workgroups as the
 // operator's forward deals them: workgroup b runs on XCD b mod 8, and in
 // groups of 128 tokens XCD x takes the 16 consecutive tokens 16x .. 16x + 15
-// (the last, partial group keeps token = b).
+// (the last, partial group keeps token = b; the operator does this for
+// 512 < D <= 8192, where this probe's four vectors per thread apply).
 __device__ __forceinline__ int64_t xcd_token(int64_t b, int64_t n) {
   constexpr int64_t C = 16, G = 8 * C;
   if (b >= n / G * G) return b;
