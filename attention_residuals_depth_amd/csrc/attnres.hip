@@ -668,7 +668,8 @@ __global__ void __launch_bounds__(VPT >= 4 ? 256 : 1024) fwd_kernel(SrcRows src,
 // channels of row l % 16 (A) and of query column l % 16 (B), both at channel
 // 32 s + 8 (l / 16), and after the loop rows 4 (l / 16) + j, column l % 16
 // of the 16 x 16 result (v_mfma_f32_16x16x32_bf16; lane layout verified on
-// the device).  Wp: the parts [3][Lpad][Dpad] bf16, zero past L and D.
+// the device).  Wp: the three parts of the queries, zero past L and D, in
+// the B operand's lane order: [k-step][part][column tile][lane] x 8 bf16.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -676,7 +677,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define ATTNRES_BS_TILES 4
 #endif
 #ifndef ATTNRES_BS_PREFETCH
-#define ATTNRES_BS_PREFETCH 1
+#define ATTNRES_BS_PREFETCH 0
 #endif
 constexpr int kBsWaves = 4;
 constexpr int kBsTiles = ATTNRES_BS_TILES;        // 16-row tiles per wave
@@ -695,9 +696,17 @@ __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restr
   const float r1 = w - (float)hi;  // exact
   const __bf16 mid = (__bf16)r1;
   const __bf16 lo = (__bf16)(r1 - (float)mid);  // exact: at most 8 significant bits remain
-  Wp[idx] = __builtin_bit_cast(uint16_t, hi);
-  Wp[total + idx] = __builtin_bit_cast(uint16_t, mid);
-  Wp[2 * total + idx] = __builtin_bit_cast(uint16_t, lo);
+  // stored in the lane order of the MFMA B operand: for k-step s, part p and
+  // column tile c, lane 16 q + r holds column 16 c + r, channels 32 s + 8 q ..
+  // 32 s + 8 q + 7, so one wave-wide load of a B operand reads 1 KiB
+  // contiguous (with [p][l][d] rows it touched 16 rows x 64 bytes, and the
+  // kernel ran 1.37 ms instead of 1.05-1.09 ms at T = 32768, n = 8, L = 24)
+  const int s = d / 32, q = (d % 32) / 8, e = d % 8, c = l / 16, r = l % 16;
+  const int64_t ctl = Lpad / 16;
+  const int64_t base = ((int64_t)s * 3 * ctl + c) * kWave + q * 16 + r;
+  Wp[base * 8 + e] = __builtin_bit_cast(uint16_t, hi);
+  Wp[(base + ctl * kWave) * 8 + e] = __builtin_bit_cast(uint16_t, mid);
+  Wp[(base + 2 * ctl * kWave) * 8 + e] = __builtin_bit_cast(uint16_t, lo);
 }
 
 // Loads of one k-step: this lane's 16 bytes of each of its four rows (A) and
@@ -714,10 +723,15 @@ __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3],
   // 1.37 ms at T = 32768, n = 8, L = 24)
 #pragma unroll
   for (int m = 0; m < kBsTiles; ++m) a[m] = bload(ra, ch < D ? roff[m] + kb : 0xFFFFFFF0u);
+  // the parts in the B operand's lane order (split_queries_kernel); column
+  // tiles past Lpad (CT > Lpad / 16) read whatever follows, or zeros past the
+  // end, and their scores are never stored
+  const int ctl = Lpad / 16;
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int p = 0; p < 3; ++p) b[c][p] = bload(rb, (uint32_t)(((p * Lpad + 16 * c + r) * Dpad) * 2) + kb);
+    for (int p = 0; p < 3; ++p)
+      b[c][p] = bload(rb, (uint32_t)((((s * 3 + p) * ctl + c) * kWave + q * 16 + r) * 16));
 }
 
 // One k-step: squares of the rows (exact products, fp32 sums) and the three
@@ -804,8 +818,11 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
       }
     }
   };
-  // two register sets alternate: the loads of step s + 1 are in flight while
-  // step s runs on the matrix cores
+  // One register set per k-step, loaded right before its matrix ops (the
+  // default): with the B operands in lane order this measured 3% faster than
+  // two sets alternating (the loads of step s + 1 in flight while step s runs,
+  // ATTNRES_BS_PREFETCH = 1), whose extra registers cost more than the
+  // overlap gained; the other waves of the CU cover the load latency.
   const int S = Dpad / 32;
 #if !ATTNRES_BS_PREFETCH
   for (int s = 0; s < S; ++s) {
