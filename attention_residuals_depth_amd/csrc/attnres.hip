@@ -714,7 +714,7 @@ __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restr
 template <int CT>
 __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3], __amdgpu_buffer_rsrc_t ra,
                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&roff)[kBsTiles], int s, int q,
-                                        int r, int32_t D, int32_t Lpad, int32_t Dpad) {
+                                        int r, int32_t D, int32_t Lpad) {
   const int ch = 32 * s + 8 * q;  // this lane's first channel
   const uint32_t kb = (uint32_t)ch * 2u;
   // default policy: a k-step reads 64 of a row's 128-byte line, and the L2
@@ -827,20 +827,20 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
 #if !ATTNRES_BS_PREFETCH
   for (int s = 0; s < S; ++s) {
     uint4 a[kBsTiles], b[CT][3];
-    bs_load<CT>(a, b, ra, rb, roff, s, q, r, D, Lpad, Dpad);
+    bs_load<CT>(a, b, ra, rb, roff, s, q, r, D, Lpad);
     bs_step<CT, SEP>(a, b, acc, acch, ss_acc);
     if (s % kBsChunk == kBsChunk - 1 || s + 1 >= S) fold();
   }
 #else
   uint4 a0[kBsTiles], a1[kBsTiles], b0[CT][3], b1[CT][3];
-  bs_load<CT>(a0, b0, ra, rb, roff, 0, q, r, D, Lpad, Dpad);
+  bs_load<CT>(a0, b0, ra, rb, roff, 0, q, r, D, Lpad);
   for (int s = 0; s < S; s += 2) {
-    if (s + 1 < S) bs_load<CT>(a1, b1, ra, rb, roff, s + 1, q, r, D, Lpad, Dpad);
+    if (s + 1 < S) bs_load<CT>(a1, b1, ra, rb, roff, s + 1, q, r, D, Lpad);
     sched_fence();
     bs_step<CT, SEP>(a0, b0, acc, acch, ss_acc);  // s is even: a chunk never ends here except at the last step
     if (s + 1 >= S) fold();
     if (s + 1 >= S) break;
-    if (s + 2 < S) bs_load<CT>(a0, b0, ra, rb, roff, s + 2, q, r, D, Lpad, Dpad);
+    if (s + 2 < S) bs_load<CT>(a0, b0, ra, rb, roff, s + 2, q, r, D, Lpad);
     sched_fence();
     bs_step<CT, SEP>(a1, b1, acc, acch, ss_acc);
     if ((s + 1) % kBsChunk == kBsChunk - 1 || s + 2 >= S) fold();
