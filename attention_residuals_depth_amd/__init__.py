@@ -90,7 +90,7 @@ def library() -> ctypes.CDLL:
         lib.attnres_fwd_scored.restype = ctypes.c_int
         lib.attnres_block_sums.argtypes = [pp, i64, vp, i32, i32, i64, i32, vp, i64, i64, vp]
         lib.attnres_block_sums.restype = ctypes.c_int
-        lib.attnres_fwd_merged.argtypes = [vp, i64, vp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_merged.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_merged.restype = ctypes.c_int
         lib.attnres_set_split_spin.argtypes = [ctypes.c_uint32]
         lib.attnres_set_split_spin.restype = ctypes.c_uint32
@@ -525,13 +525,18 @@ def attnres_block_sums(srcs, z: torch.Tensor, U=None, token_major: bool = False,
 
 
 def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.Tensor, rstd_given: torch.Tensor,
-                       w: torch.Tensor, eps: float, out=None, rstd=None, alpha=None, stream=None):
+                       w: torch.Tensor, eps: float, delta=None, partial_out=None, in_place: bool = True, out=None,
+                       rstd=None, alpha=None, stream=None):
     """Forward of one sub-layer from its block-batched shared sum: U_l [T][D]
     fp32 (U[l] or U[:, l] of attnres_block_sums; rows may be spaced apart),
     partial [T][D] bf16 the current partial sum (the last of the N sources),
     z_given and rstd_given [T][N-1] the shared sources' scores for this
-    sub-layer and their rstd (attnres_block_scores).  Returns (out, rstd [T][N],
-    alpha [T][N]) as attnres_fwd_scored would for the same sources."""
+    sub-layer and their rstd (attnres_block_scores).  With delta ([T][D] bf16,
+    the previous sub-layer's output) the partial sum is first updated to
+    bf16(partial + delta), written to partial_out (default: partial itself
+    when in_place, else a new tensor) and used as the last source, as in
+    attnres_fwd_update.  Returns (out, rstd [T][N], alpha [T][N]), plus
+    partial_out when delta is given."""
     if not isinstance(z_given, torch.Tensor) or z_given.dim() != 2:
         raise ValueError("z_given must be a [T][N-1] tensor")
     T, n = z_given.shape
@@ -547,6 +552,20 @@ def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.
     _check(rstd_given, "rstd_given", torch.float32, (T, N - 1))
     _check(w, "w", torch.float32, (D,))
     dev = partial.device
+    if delta is not None:
+        _check(delta, "delta", torch.bfloat16, (T, D))
+        if partial_out is None:
+            if in_place:
+                partial_out = partial
+            elif p_pitch == D:
+                partial_out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+            else:
+                raise ValueError("with a strided partial sum pass partial_out (a row set of the same pitch)")
+        _common_pitch([partial_out], "partial_out", T, D, p_pitch)
+        if partial_out.requires_grad:
+            raise RuntimeError("partial_out requires grad: the library cannot write it in place under autograd")
+    elif partial_out is not None:
+        raise ValueError("partial_out is only written with a delta")
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     if rstd is None:
@@ -556,14 +575,20 @@ def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.
     _check(out, "out", torch.bfloat16, (T, D))
     _check(rstd, "rstd", torch.float32, (T, N))
     _check(alpha, "alpha", torch.float32, (T, N))
-    _same_device(dev, U_l=U_l, z_given=z_given, rstd_given=rstd_given, w=w, out=out, rstd=rstd, alpha=alpha)
+    _same_device(dev, U_l=U_l, z_given=z_given, rstd_given=rstd_given, w=w, out=out, rstd=rstd, alpha=alpha,
+                 **({} if delta is None else {"delta": delta, "partial_out": partial_out}))
     with _device(dev):
-        code = library().attnres_fwd_merged(U_l.data_ptr(), u_pitch, partial.data_ptr(), p_pitch, z_given.data_ptr(),
+        code = library().attnres_fwd_merged(U_l.data_ptr(), u_pitch, partial.data_ptr(), p_pitch,
+                                            None if delta is None else delta.data_ptr(),
+                                            None if delta is None else partial_out.data_ptr(), z_given.data_ptr(),
                                             rstd_given.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
                                             rstd.data_ptr(), alpha.data_ptr(), _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_fwd_merged", code)
-    return out, rstd, alpha
+    if delta is None:
+        return out, rstd, alpha
+    torch.autograd.graph.increment_version(partial_out)
+    return out, rstd, alpha, partial_out
 
 
 GRAD_ACCUMULATE = 1  # grad_mode bits of attnres_bwd_sources

@@ -995,11 +995,19 @@ __device__ __forceinline__ void unpack4(const u32x2_t& q, float (&f)[4]) {
   f[3] = __builtin_bit_cast(float, q.y & 0xFFFF0000u);
 }
 
-template <int N>
+//
+// UPDATE: the partial sum is first advanced by the previous sub-layer's output
+// y (delta), as the fused update of the plain forward does: each thread adds
+// its quads in fp32, rounds once to bf16 (the correctly rounded sum of two
+// bf16 values), stores the new partial sum to partial_out (row pitch p_pitch;
+// may be p itself: a thread rewrites only the quads it has already read) and
+// continues with it.
+template <int N, bool UPDATE>
 __global__ void __launch_bounds__(1024) fwd_merged_kernel(
-    const float* __restrict__ U, int64_t u_pitch, const uint16_t* __restrict__ p, int64_t p_pitch,
-    const float* __restrict__ zg, const float* __restrict__ rg, const float* __restrict__ w, float eps, int64_t t0,
-    int32_t D, uint16_t* __restrict__ out, float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
+    const float* __restrict__ U, int64_t u_pitch, const uint16_t* p, int64_t p_pitch,
+    const uint16_t* __restrict__ delta, uint16_t* partial_out, const float* __restrict__ zg,
+    const float* __restrict__ rg, const float* __restrict__ w, float eps, int64_t t0, int32_t D,
+    uint16_t* __restrict__ out, float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
   static_assert(N >= 2, "the shared sources and the partial sum");
   constexpr int Q = kMergedQuads;
   __shared__ __attribute__((aligned(16))) float red[1][2][kMaxWaves];
@@ -1022,6 +1030,12 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
   sched_fence();
 #pragma unroll
   for (int k = 0; k < Q; ++k) pq[k] = __builtin_amdgcn_raw_buffer_load_b64(rp, o16[k] / 2u, 0, kAuxStreamLoad);
+  u32x2_t yq[UPDATE ? Q : 1];
+  if constexpr (UPDATE) {
+    const __amdgpu_buffer_rsrc_t ry = rsrc(delta + t * D, (uint32_t)D * 2u);
+#pragma unroll
+    for (int k = 0; k < Q; ++k) yq[k] = __builtin_amdgcn_raw_buffer_load_b64(ry, o16[k] / 2u, 0, kAuxStreamLoad);
+  }
 #pragma unroll
   for (int k = 0; k < Q; ++k) uq[k] = bload<kAuxStreamLoad>(ru, o16[k]);
   float zgv, rgv;
@@ -1032,6 +1046,20 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
     rgv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(rg + t * (N - 1), gb), lane * 4, 0, 0));
   }
   sched_fence();
+  if constexpr (UPDATE) {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(partial_out + t * p_pitch, (uint32_t)D * 2u);
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+      float a[4], b[4];
+      unpack4(pq[k], a);
+      unpack4(yq[k], b);
+      const float s8[8] = {a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3], 0.f, 0.f, 0.f, 0.f};
+      const uint4 pk = pack8(s8);
+      pq[k].x = pk.x;
+      pq[k].y = pk.y;
+      __builtin_amdgcn_raw_buffer_store_b64(pq[k], rq, o16[k] / 2u, 0, kAuxStreamStore);
+    }
+  }
   clear_absent<2>(red);
   // the partial sum's sum of squares and w.p
   float part[2] = {0.f, 0.f};
@@ -2387,6 +2415,8 @@ struct MergedArgs {
   int64_t u_pitch;
   const uint16_t* p;
   int64_t p_pitch;
+  const uint16_t* delta;  // with partial_out: the fused partial-sum update, else both NULL
+  uint16_t* partial_out;
   const float* zg;
   const float* rg;
   const float* w;
@@ -2400,21 +2430,27 @@ struct MergedArgs {
 
 // kMergedQuads channel quads per thread, whole waves: 256 threads at D = 7168,
 // 640 at D = 16384.
-template <int N>
-hipError_t run_merged_n(hipStream_t st, const MergedArgs& a) {
+template <int N, bool UPDATE>
+hipError_t run_merged_nu(hipStream_t st, const MergedArgs& a) {
   const int threads = ((a.D / 4 + kMergedQuads - 1) / kMergedQuads + kWave - 1) / kWave * kWave;
   int64_t res = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N>), threads, 0, &res);
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N, UPDATE>), threads, 0, &res);
   if (e != hipSuccess) return e;  // validates the launch shape
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_merged_kernel<N>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U, a.u_pitch, a.p,
-                       a.p_pitch, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out, a.rstd, a.alpha);
+    hipLaunchKernelGGL((fwd_merged_kernel<N, UPDATE>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U,
+                       a.u_pitch, a.p, a.p_pitch, a.delta, a.partial_out, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out,
+                       a.rstd, a.alpha);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int N>
+hipError_t run_merged_n(hipStream_t st, const MergedArgs& a) {
+  return a.delta != nullptr ? run_merged_nu<N, true>(st, a) : run_merged_nu<N, false>(st, a);
 }
 
 attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
@@ -2426,13 +2462,21 @@ attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
     return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(a.p_pitch, a.T, a.D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (a.u_pitch < a.D || a.u_pitch % 4 != 0 || a.u_pitch > (INT64_C(1) << 40) / a.T) return ATTNRES_ERR_INVALID_ARGUMENT;
-  const Range ins[5] = {rows_of(a.U, a.T, (int64_t)a.D * 4, a.u_pitch * 4), rows_of(a.p, a.T, (int64_t)a.D * 2, a.p_pitch * 2),
-                        range_of(a.zg, nTG * 4), range_of(a.rg, nTG * 4), range_of(a.w, (size_t)a.D * 4)};
-  const Range outs[3] = {range_of(a.out, nTD * 2), range_of(a.rstd, nTN * 4), range_of(a.alpha, nTN * 4)};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 5; ++j)
-      if (overlap(outs[i], ins[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
-    for (int j = i + 1; j < 3; ++j)
+  const bool update = a.delta != nullptr || a.partial_out != nullptr;
+  if (update && (a.delta == nullptr || a.partial_out == nullptr)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (!aligned(a.delta, 16) || !aligned(a.partial_out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const Range ins[6] = {rows_of(a.U, a.T, (int64_t)a.D * 4, a.u_pitch * 4), rows_of(a.p, a.T, (int64_t)a.D * 2, a.p_pitch * 2),
+                        range_of(a.zg, nTG * 4), range_of(a.rg, nTG * 4), range_of(a.w, (size_t)a.D * 4),
+                        range_of(a.delta, update ? nTD * 2 : 0)};
+  const Range outs[4] = {range_of(a.out, nTD * 2), range_of(a.rstd, nTN * 4), range_of(a.alpha, nTN * 4),
+                         rows_of(a.partial_out, update ? a.T : 0, (int64_t)a.D * 2, a.p_pitch * 2)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j) {
+      // the partial sum may be updated in place: exactly its own rows
+      const bool in_place = i == 3 && j == 1 && a.partial_out == a.p;
+      if (!in_place && overlap(outs[i], ins[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
+    }
+    for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -2673,14 +2717,16 @@ extern "C" attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_
 }
 
 extern "C" attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial,
-                                             int64_t partial_pitch, const float* z_given, const float* rstd_given,
-                                             const float* w, float eps, int32_t N, int64_t T, int32_t D,
-                                             uint16_t* out, float* rstd, float* alpha, void* stream) {
+                                             int64_t partial_pitch, const uint16_t* delta, uint16_t* partial_out,
+                                             const float* z_given, const float* rstd_given, const float* w, float eps,
+                                             int32_t N, int64_t T, int32_t D, uint16_t* out, float* rstd,
+                                             float* alpha, void* stream) {
   const attnres_status st = fwd_common_checks(w, eps, N, T, D);
   if (st != ATTNRES_OK) return st;
   if (N < 2) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (T == 0) return ATTNRES_OK;
-  const MergedArgs a{U, u_pitch, partial, partial_pitch, z_given, rstd_given, w, eps, T, D, out, rstd, alpha};
+  const MergedArgs a{U,     u_pitch, partial, partial_pitch, delta, partial_out, z_given, rstd_given, w, eps,
+                     T,     D,       out,     rstd,          alpha};
   return fwd_merged_impl(a, N, stream);
 }
 

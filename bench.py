@@ -740,6 +740,25 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
         rec[f"merged_{key}"] = {"block_ms": ms, "vs_plain": plain_ms / ms, "block_sums_ms": sums_ms,
                                 "block_sums_GBps": sums_bytes / sums_ms / 1e6, "merged_fwd_ms": mfwd_ms,
                                 "merged_fwd_GBps": merged_bytes / mfwd_ms / 1e6}
+    # one sub-layer's merged forward with the fused partial-sum update, against a
+    # separate bf16 add followed by the merged forward (median of 11 calls)
+    U = torch.empty((L, T, D), dtype=torch.float32, device=dev)
+    ar.attnres_block_scores(srcs[:n], W, 1e-6, rstd=rb, z=zb, workspace=ws)
+    ar.attnres_block_sums(srcs[:n], zb, U=U)
+    y = (torch.randn((T, D), device=dev, generator=g) * 0.3).to(torch.bfloat16)
+    p = srcs[n].clone()
+
+    def fused():
+        ar.attnres_fwd_merged(U[5], p, zb[5], rb, W[5], 1e-6, delta=y, out=out, rstd=rstd, alpha=alpha)
+
+    def unfused():
+        torch.add(p, y, out=p)
+        ar.attnres_fwd_merged(U[5], p, zb[5], rb, W[5], 1e-6, out=out, rstd=rstd, alpha=alpha)
+
+    upd_bytes = T * (4 * D + 8 * D + 8 * (N - 1) + 8 * N) + 4 * D  # U, p, y read; p, out written
+    f_ms, u_ms = _median_ms(torch, flush, fused, 11), _median_ms(torch, flush, unfused, 11)
+    rec["merged_update"] = {"fused_ms": f_ms, "fused_GBps": upd_bytes / f_ms / 1e6, "add_then_merged_ms": u_ms}
+    del U, y, p
     rec["reps"] = f"median of {reps}, 512 MiB flush before each block"
     del srcs, W, out, rstd, alpha, rb, zb, ws, flush
     torch.cuda.empty_cache()

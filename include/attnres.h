@@ -41,8 +41,8 @@
  *     the work is enqueued.
  *   - Outputs are overwritten, never accumulated (except by the
  *     accumulating modes of attnres_bwd_sources).  Inputs are not modified
- *     (except the partial sum that attnres_fwd_update updates when
- *     partial_out is the partial sum itself).
+ *     (except the partial sum that attnres_fwd_update or attnres_fwd_merged
+ *     updates when partial_out is the partial sum itself).
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error the call returns a non-zero status and enqueues nothing.
  *   - Results for one token depend only on that token's inputs (and w): they
@@ -373,11 +373,20 @@ attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch
  * which is the weighted sum of all N sources to within fp32 rounding.
  * N = 2 .. ATTNRES_MAX_SOURCES; w, eps, T, D, out, rstd, alpha as
  * attnres_fwd_sources.  Outputs must not overlap any input or each other.
- * The backward is attnres_bwd_sources on all N sources with these outputs.
+ *   delta, partial_out  both NULL, or the fused partial-sum update of
+ *               attnres_fwd_update: delta [T][D] bf16 (dense, 16-byte
+ *               aligned) is added to the partial sum first, partial_out =
+ *               bf16(partial + delta) (rounded once, ties to even; row pitch
+ *               partial_pitch; may be `partial` itself, else disjoint from
+ *               every input), and the forward then uses partial_out as the
+ *               last source.
+ * The backward is attnres_bwd_sources on all N sources (partial_out as the
+ * last, when updated) with these outputs.
  */
 attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial, int64_t partial_pitch,
-                                  const float* z_given, const float* rstd_given, const float* w, float eps, int32_t N,
-                                  int64_t T, int32_t D, uint16_t* out, float* rstd, float* alpha, void* stream);
+                                  const uint16_t* delta, uint16_t* partial_out, const float* z_given,
+                                  const float* rstd_given, const float* w, float eps, int32_t N, int64_t T, int32_t D,
+                                  uint16_t* out, float* rstd, float* alpha, void* stream);
 
 /*
  * Backward without a workspace argument, for callers that cannot allocate

@@ -186,8 +186,8 @@ int main(void) {
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_scores returned %d\n", (int)st); return 1; }
     st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, T * D, D, NULL);
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_sums returned %d\n", (int)st); return 1; }
-    st = attnres_fwd_merged(d_U + (size_t)l * T * D, D, srcs[n], D, d_zb + (size_t)l * T * n, d_rb, d_W + (size_t)l * D,
-                            eps, N, T, (int32_t)D, d_out3, d_rstd3, d_alpha3, NULL);
+    st = attnres_fwd_merged(d_U + (size_t)l * T * D, D, srcs[n], D, NULL, NULL, d_zb + (size_t)l * T * n, d_rb,
+                            d_W + (size_t)l * D, eps, N, T, (int32_t)D, d_out3, d_rstd3, d_alpha3, NULL);
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd_merged returned %d\n", (int)st); return 1; }
     st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, D, D, NULL);  /* rows would collide */
     if (st != ATTNRES_ERR_INVALID_ARGUMENT) { fprintf(stderr, "colliding U rows not refused (%d)\n", (int)st); ++fails; }

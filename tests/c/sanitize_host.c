@@ -222,12 +222,17 @@ static void run_abi(void) {
          ATTNRES_ERR_INVALID_ARGUMENT);
   EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 0, N - 1, T, D, U, (int64_t)T * D, D, NULL) ==
          ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, rstd, alpha, w, 1e-6f, N, T, D, (uint16_t*)U, rstd,
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D,
+                            (uint16_t*)U, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1] + 1, (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D, out,
+                            rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, 1, T, D, out, rstd,
                             alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1] + 1, (int64_t)N * D, rstd, alpha, w, 1e-6f, N, T, D, out, rstd, alpha,
-                            NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, rstd, alpha, w, 1e-6f, 1, T, D, out, rstd, alpha,
-                            NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  /* the update: delta without partial_out, and partial_out on top of delta */
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, dout, NULL, rstd, alpha, w, 1e-6f, N, T, D, out, rstd,
+                            alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, dout, (uint16_t*)dout, rstd, alpha, w, 1e-6f, N, T, D,
+                            out, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
 }
 #endif
 

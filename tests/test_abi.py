@@ -119,9 +119,9 @@ def test_block_sums_and_merged_forward_refuse_on_the_host():
     assert sums(T=0, s=None, z=0, U=0) == OK               # empty: nothing to do
 
     def merged(N=9, T=T_, D_=D, U=40 * g, up=None, p=41 * g, pp=None, zg=42 * g, rg=43 * g, w=44 * g, eps=1e-6,
-               out=45 * g, rstd=46 * g, alpha=47 * g):
-        return lib.attnres_fwd_merged(U, D_ if up is None else up, p, D_ if pp is None else pp, zg, rg, w, eps, N, T,
-                                      D_, out, rstd, alpha, None)
+               out=45 * g, rstd=46 * g, alpha=47 * g, y=None, po=None):
+        return lib.attnres_fwd_merged(U, D_ if up is None else up, p, D_ if pp is None else pp, y, po, zg, rg, w, eps,
+                                      N, T, D_, out, rstd, alpha, None)
 
     assert merged(N=1) == INVALID and merged(N=10) == INVALID
     assert merged(U=0) == INVALID and merged(p=0) == INVALID and merged(zg=0) == INVALID and merged(rg=0) == INVALID
@@ -132,6 +132,11 @@ def test_block_sums_and_merged_forward_refuse_on_the_host():
     assert merged(out=40 * g) == INVALID                   # out overlaps U
     assert merged(rstd=42 * g) == INVALID                  # rstd overlaps the given scores
     assert merged(alpha=46 * g) == INVALID                 # alpha overlaps rstd
+    assert merged(y=48 * g) == INVALID and merged(po=49 * g) == INVALID  # the update needs both
+    assert merged(y=48 * g + 4, po=49 * g) == INVALID                     # misaligned delta
+    assert merged(y=48 * g, po=48 * g) == INVALID                         # partial_out on top of delta
+    assert merged(y=48 * g, po=40 * g) == INVALID                         # partial_out on top of U
+    assert merged(y=48 * g, po=45 * g) == INVALID                         # partial_out on top of out
     assert merged(T=0, U=0, p=0, zg=0, rg=0, out=0, rstd=0, alpha=0) == OK
 
 

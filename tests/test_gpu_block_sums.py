@@ -205,6 +205,51 @@ def test_merged_saved_state_drives_the_backward():
     assert within_tolerance(e), e
 
 
+@pytest.mark.parametrize("in_place", [False, True], ids=["new_buffer", "in_place"])
+def test_merged_forward_with_update(in_place):
+    """The fused partial-sum update: partial_out = bf16(partial + delta) bit for
+    bit as the oracle rounds it; out, rstd and alpha bitwise those of the
+    merged forward on the separately updated partial sum, and within the
+    bounds of the oracle's plain forward on the updated sources."""
+    N, T, D, L, l = 9, 300, 7168, 24, 7
+    wl = synth.workload(1, N=N, T=T)
+    bits = wl.sources()
+    y_h = synth.Workload("merged_y", T=T, N=1, D=D, seed=9, kind="tiny", tiny_scales=(0.3,)).sources()[0]
+    W_h = _queries(D, L, 6)
+    W = torch.from_numpy(W_h).to(DEV)
+    srcs = [to_dev_bf16(bits[i]) for i in range(N)]
+    rb, zb = ar.attnres_block_scores(srcs[:-1], W, wl.eps)
+    U = ar.attnres_block_sums(srcs[:-1], zb)
+    p = srcs[-1].clone()
+    out, rstd, alpha, p_new = ar.attnres_fwd_merged(U[l], p, zb[l], rb, W[l], wl.eps, delta=to_dev_bf16(y_h),
+                                                    in_place=in_place)
+    torch.cuda.synchronize()
+    assert (p_new.data_ptr() == p.data_ptr()) == in_place
+    o_p = oracle.add_bf16(bits[-1], y_h)
+    assert np.array_equal(p_new.cpu().view(torch.int16).numpy().view(np.uint16), o_p)
+    e_out, e_rstd, e_alpha = ar.attnres_fwd_merged(U[l], to_dev_bf16(o_p), zb[l], rb, W[l], wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(out, e_out) and torch.equal(rstd, e_rstd) and torch.equal(alpha, e_alpha)
+    srcs_h = np.concatenate([bits[:-1], o_p[None]])
+    o_out, o_rstd, o_alpha = oracle.fwd(srcs_h, W_h[l], wl.eps)
+    acc = Accum(DEV)
+    acc.update(srcs_h, None, W_h[l], dict(out=out, rstd=rstd, alpha=alpha),
+               dict(out=o_out, rstd=o_rstd, alpha=o_alpha, merged=True))
+    e = acc.result()
+    print("[merged update] " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert within_tolerance(e), e
+
+
+def test_merged_update_refuses_half_an_update():
+    D = 64
+    z = torch.zeros((4, 2), device=DEV)
+    p = torch.zeros((4, D), dtype=torch.bfloat16, device=DEV)
+    U = torch.zeros((4, D), device=DEV)
+    w = torch.zeros(D, device=DEV)
+    with pytest.raises(ValueError):
+        ar.attnres_fwd_merged(U, p, z, z, w, 1e-6, partial_out=p)
+
+
 def test_empty_batch_is_a_no_op():
     D, L = 7168, 4
     srcs = [torch.empty((0, D), dtype=torch.bfloat16, device=DEV) for _ in range(3)]

@@ -152,7 +152,9 @@ def test_random_block_route(seed):
     """The block-level route on seeded random configurations: block scores of
     n shared sources for L pseudo-queries, block sums (either U layout), and
     the merged forward of a few sub-layers with the partial sum as the last
-    source, against the oracle's plain forward on all n + 1 sources."""
+    source (in half the cases with the fused update of the partial sum,
+    checked bit for bit), against the oracle's plain forward on all n + 1
+    sources."""
     rng = np.random.default_rng(5000 + seed)
     n = int(rng.integers(1, 9))
     N = n + 1
@@ -166,16 +168,29 @@ def test_random_block_route(seed):
     wl = synth.Workload(f"fuzzb{seed}", T=T, N=N, D=D, eps=eps, seed=seed, kind="depth")
     src_h = wl.sources()
     W_h = np.stack([synth.normal_f32(D, seed, 300 + l, w_std) for l in range(L)])
+    update = bool(rng.integers(0, 2))  # the fused partial-sum update, out of place
     print(f"[fuzz block] seed={seed} n={n} T={T} D={D} L={L} eps={eps} w_std={w_std:.3g} layout={layout} "
-          f"token_major={token_major}", flush=True)
+          f"token_major={token_major} update={update}", flush=True)
     views = _place(to_dev_bf16(src_h), layout, rng)
     W = torch.from_numpy(W_h).to(DEV)
     rb, zb = ar.attnres_block_scores(views[:n], W, eps)
     U = ar.attnres_block_sums(views[:n], zb, token_major=token_major)
     for l in sorted({0, L - 1, int(rng.integers(0, L))}):
-        out, rstd, alpha = ar.attnres_fwd_merged(U[:, l] if token_major else U[l], views[n], zb[l], rb, W[l], eps)
-        torch.cuda.synchronize()
-        o_out, o_rstd, o_alpha = oracle.fwd(src_h, W_h[l], eps)
+        U_l = U[:, l] if token_major else U[l]
+        if update:
+            y_h = synth.Workload(f"fuzzby{seed}_{l}", T=T, N=1, D=D, seed=seed + l, kind="tiny",
+                                 tiny_scales=(0.3,)).sources()[0]
+            p_out = _zeros_like_layout([views[n]])[0]
+            out, rstd, alpha, p_out = ar.attnres_fwd_merged(U_l, views[n], zb[l], rb, W[l], eps,
+                                                            delta=to_dev_bf16(y_h), partial_out=p_out)
+            torch.cuda.synchronize()
+            o_p = oracle.add_bf16(src_h[n], y_h)
+            assert np.array_equal(p_out.contiguous().cpu().view(torch.int16).numpy().view(np.uint16), o_p)
+            o_out, o_rstd, o_alpha = oracle.fwd(np.concatenate([src_h[:n], o_p[None]]), W_h[l], eps)
+        else:
+            out, rstd, alpha = ar.attnres_fwd_merged(U_l, views[n], zb[l], rb, W[l], eps)
+            torch.cuda.synchronize()
+            o_out, o_rstd, o_alpha = oracle.fwd(src_h, W_h[l], eps)
         assert rel_l2(bf16_dev_to_f64(out), o_out) <= TOL_OUT_REL_L2
         assert float(np.max(np.abs(alpha.cpu().double().numpy() - o_alpha))) <= TOL_ALPHA_ABS
         assert float(np.max(np.abs(rstd.cpu().double().numpy() / o_rstd - 1))) <= TOL_RSTD_REL
