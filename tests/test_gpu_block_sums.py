@@ -146,6 +146,15 @@ def test_merged_forward_peaked_softmax():
         assert e["alpha_max_abs"] <= TOL_ALPHA_ABS
 
 
+def test_block_route_full_size_T32768():
+    """The bench's block at full size: 8 shared sources and the partial sum,
+    24 sub-layers, T = 32768; scores, sums and three sub-layers' merged
+    forwards (U sub-layer-major) on every token against the oracle's plain
+    forward on all 9 sources, element by element."""
+    for e in _chain(9, 32768, 7168, L=24, subs=(0, 11, 23), chunk=4096):
+        assert within_tolerance(e), e
+
+
 def test_merged_agrees_with_scored_and_layouts_bitwise():
     """The merged forward's rstd and alpha agree with the scored forward's: the
     same softmax on the same given scores, only the partial sum's two dots
