@@ -88,9 +88,10 @@ def library() -> ctypes.CDLL:
         lib.attnres_block_scores.restype = ctypes.c_int
         lib.attnres_fwd_scored.argtypes = [pp, i64, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
         lib.attnres_fwd_scored.restype = ctypes.c_int
-        lib.attnres_block_sums.argtypes = [pp, i64, vp, i32, i32, i64, i32, vp, i64, i64, vp]
+        lib.attnres_block_sums.argtypes = [pp, i64, vp, i32, i32, i64, i32, vp, i64, i64, i32, vp]
         lib.attnres_block_sums.restype = ctypes.c_int
-        lib.attnres_fwd_merged.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp, vp]
+        lib.attnres_fwd_merged.argtypes = [vp, i64, i32, vp, i64, vp, vp, vp, vp, vp, f32, i32, i64, i32, vp, vp, vp,
+                                           vp]
         lib.attnres_fwd_merged.restype = ctypes.c_int
         lib.attnres_set_split_spin.argtypes = [ctypes.c_uint32]
         lib.attnres_set_split_spin.restype = ctypes.c_uint32
@@ -496,13 +497,35 @@ def attnres_fwd_scored(srcs, z_given: torch.Tensor, rstd_given: torch.Tensor, w:
     return out, rstd, alpha
 
 
-def attnres_block_sums(srcs, z: torch.Tensor, U=None, token_major: bool = False, stream=None):
+U_F32 = 0  # element formats of the block sums (ATTNRES_U_F32, ATTNRES_U_F24)
+U_F24 = 1
+_U_FORMATS = {"f32": U_F32, "f24": U_F24}
+
+
+def decode_u24(U: torch.Tensor) -> torch.Tensor:
+    """The fp32 values of block sums stored in the 24-bit format (a uint8
+    tensor whose last dimension holds an element's three bytes).  A plain
+    torch view for inspection; attnres_fwd_merged reads the format itself."""
+    if U.dtype != torch.uint8 or U.dim() < 1 or U.shape[-1] != 3:
+        raise ValueError("U must be a uint8 tensor with three bytes per element in its last dimension")
+    b = U.to(torch.int64)
+    bits = (b[..., 0] << 8) | (b[..., 1] << 16) | (b[..., 2] << 24)  # the fp32 bit pattern, 0 .. 2^32 - 1
+    return torch.where(bits >= 2 ** 31, bits - 2 ** 32, bits).to(torch.int32).view(torch.float32)
+
+
+def attnres_block_sums(srcs, z: torch.Tensor, U=None, token_major: bool = False, u_format: str = "f32",
+                       stream=None):
     """Block-batched shared sums of the n sources a block's sub-layers share (n
     [T][D] bf16 tensors or views with one row pitch), from the block's scores z
     [L][T][n] fp32 (attnres_block_scores): U[l][t] = sum_i exp(z[l][t][i] -
-    max_i z[l][t][i]) srcs[i][t] in fp32.  Returns U as [L][T][D], or as
-    [T][L][D] with token_major (sub-layer l's rows are then U[:, l]); a given U
-    must have that shape and be contiguous."""
+    max_i z[l][t][i]) srcs[i][t], summed in fp32.  Returns U as [L][T][D], or
+    as [T][L][D] with token_major (sub-layer l's rows are then U[:, l]); a
+    given U must have that shape and be contiguous.  u_format "f32" stores
+    fp32; "f24" stores each sum rounded to a 16-bit significand in three bytes
+    (ATTNRES_U_F24), as a uint8 tensor with one more dimension of 3."""
+    if u_format not in _U_FORMATS:
+        raise ValueError(f"u_format must be one of {sorted(_U_FORMATS)}")
+    fmt = _U_FORMATS[u_format]
     srcs, T, D, pitch = _sources(srcs, "srcs")
     n = len(srcs)
     if z.dim() != 3:
@@ -511,14 +534,17 @@ def attnres_block_sums(srcs, z: torch.Tensor, U=None, token_major: bool = False,
     _check(z, "z", torch.float32, (L, T, n))
     dev = srcs[0].device
     shape = (T, L, D) if token_major else (L, T, D)
+    dtype = torch.float32
+    if fmt == U_F24:
+        shape, dtype = shape + (3,), torch.uint8
     if U is None:
-        U = torch.empty(shape, dtype=torch.float32, device=dev)
-    _check(U, "U", torch.float32, shape)
+        U = torch.empty(shape, dtype=dtype, device=dev)
+    _check(U, "U", dtype, shape)
     lstride, tpitch = (D, L * D) if token_major else (T * D, D)
     _same_device(dev, z=z, U=U, **{f"srcs[{i}]": t for i, t in enumerate(srcs)})
     with _device(dev):
         code = library().attnres_block_sums(_ptr_array(srcs), pitch, z.data_ptr(), L, n, T, D, U.data_ptr(), lstride,
-                                            tpitch, _stream_handle(stream, dev))
+                                            tpitch, fmt, _stream_handle(stream, dev))
     if code != 0:
         raise AttnResError("attnres_block_sums", code)
     return U
@@ -528,7 +554,8 @@ def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.
                        w: torch.Tensor, eps: float, delta=None, partial_out=None, in_place: bool = True, out=None,
                        rstd=None, alpha=None, stream=None):
     """Forward of one sub-layer from its block-batched shared sum: U_l [T][D]
-    fp32 (U[l] or U[:, l] of attnres_block_sums; rows may be spaced apart),
+    fp32, or [T][D][3] uint8 in the 24-bit format (U[l] or U[:, l] of
+    attnres_block_sums; rows may be spaced apart),
     partial [T][D] bf16 the current partial sum (the last of the N sources),
     z_given and rstd_given [T][N-1] the shared sources' scores for this
     sub-layer and their rstd (attnres_block_scores).  With delta ([T][D] bf16,
@@ -547,7 +574,20 @@ def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.
         raise ValueError("partial must be [T][D]")
     D = partial.shape[1]
     p_pitch = _rows(partial, "partial", T, D)
-    u_pitch = _rows(U_l, "U_l", T, D, torch.float32)
+    if isinstance(U_l, torch.Tensor) and U_l.dtype == torch.uint8:
+        fmt = U_F24
+        if U_l.device.type != "cuda":
+            raise ValueError("U_l must be a device tensor")
+        if tuple(U_l.shape) != (T, D, 3):
+            raise ValueError(f"a 24-bit U_l must have shape {(T, D, 3)}, got {tuple(U_l.shape)}")
+        if T > 0 and D > 0 and (U_l.stride(2) != 1 or (D > 1 and U_l.stride(1) != 3)):
+            raise ValueError("U_l rows must be contiguous, three bytes per element")
+        if T > 1 and U_l.stride(0) % 3 != 0:
+            raise ValueError("U_l rows must start on element boundaries")
+        u_pitch = U_l.stride(0) // 3 if T > 1 else D
+    else:
+        fmt = U_F32
+        u_pitch = _rows(U_l, "U_l", T, D, torch.float32)
     _check(z_given, "z_given", torch.float32, (T, N - 1))
     _check(rstd_given, "rstd_given", torch.float32, (T, N - 1))
     _check(w, "w", torch.float32, (D,))
@@ -578,7 +618,7 @@ def attnres_fwd_merged(U_l: torch.Tensor, partial: torch.Tensor, z_given: torch.
     _same_device(dev, U_l=U_l, z_given=z_given, rstd_given=rstd_given, w=w, out=out, rstd=rstd, alpha=alpha,
                  **({} if delta is None else {"delta": delta, "partial_out": partial_out}))
     with _device(dev):
-        code = library().attnres_fwd_merged(U_l.data_ptr(), u_pitch, partial.data_ptr(), p_pitch,
+        code = library().attnres_fwd_merged(U_l.data_ptr(), u_pitch, fmt, partial.data_ptr(), p_pitch,
                                             None if delta is None else delta.data_ptr(),
                                             None if delta is None else partial_out.data_ptr(), z_given.data_ptr(),
                                             rstd_given.data_ptr(), w.data_ptr(), float(eps), N, T, D, out.data_ptr(),
@@ -672,6 +712,6 @@ def attnres(srcs, w: torch.Tensor, eps: float) -> torch.Tensor:
 
 __all__ = ["attnres", "attnres_fwd", "attnres_bwd", "attnres_fwd_sources", "attnres_bwd_sources", "attnres_fwd_decode",
            "attnres_fwd_update", "attnres_bwd_noalloc", "attnres_block_scores", "attnres_fwd_scored",
-           "attnres_block_sums", "attnres_fwd_merged", "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
+           "attnres_block_sums", "attnres_fwd_merged", "U_F32", "U_F24", "decode_u24", "block_scores_workspace_bytes", "MAX_QUERIES", "GRAD_ACCUMULATE", "GRAD_F32", "NOALLOC_MAX_D",
            "SPLIT_MAX_D", "SPLIT_ANY_N_MAX_D", "SPLIT_MIN_N", "bwd_split", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS", "SPLIT_SPIN_DEFAULT", "set_split_spin",
            "workspace_bytes", "library", "AttnResError", "MAX_SOURCES", "MAX_D", "DW_PARTIALS", "LIB_PATH"]

@@ -893,11 +893,41 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
 // Without the weighted sums (timing only) the same loads and stores took
 // 4.44 ms against 5.2-5.3 ms at T = 32768, n = 8, L = 24: the arithmetic is
 // only partly hidden behind the stores.
-template <int NS, int VPT>
+// The shared sums' 24-bit element format (ATTNRES_U_F24): an fp32 value
+// rounded to nearest even at bit 8 of its bit pattern (16 significant bits,
+// the fp32 exponent range), stored as the upper three bytes, little-endian,
+// three bytes per element.  Four elements take three dwords:
+//     dw0 = e0 | e1 << 24,  dw1 = e1 >> 8 | e2 << 16,  dw2 = e2 >> 16 | e3 << 8
+// with e_k the 24-bit codes.  Rounding the bit pattern is the round-to-nearest
+// of the value on a 16-bit significand (a carry into the exponent is the
+// correct result; finite values near the fp32 maximum round to infinity).
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
+
+__device__ __forceinline__ uint32_t rne24(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b + 0x7Fu + ((b >> 8) & 1u)) & 0xFFFFFF00u;
+}
+
+// four rounded values (low bytes zero) -> three dwords
+__device__ __forceinline__ void pack24(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t* d) {
+  d[0] = (r0 >> 8) | (r1 << 16);
+  d[1] = (r1 >> 16) | (r2 << 8);
+  d[2] = (r2 >> 24) | r3;
+}
+
+__device__ __forceinline__ float4 unpack24(const u32x3_t& d) {
+  return make_float4(__builtin_bit_cast(float, d.x << 8),
+                     __builtin_bit_cast(float, __builtin_amdgcn_alignbyte(d.y, d.x, 3) << 8),
+                     __builtin_bit_cast(float, __builtin_amdgcn_alignbyte(d.z, d.y, 2) << 8),
+                     __builtin_bit_cast(float, d.z & 0xFFFFFF00u));
+}
+
+template <int NS, int VPT, bool F24>
 __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const float* __restrict__ z,
                                                                          int32_t L, int64_t T, int32_t D, int64_t t0,
-                                                                         float* __restrict__ U, int64_t u_lstride,
+                                                                         void* __restrict__ U, int64_t u_lstride,
                                                                          int64_t u_pitch) {
+  constexpr uint32_t EB = F24 ? 3 : 4;  // bytes per element of U
   constexpr int NS4 = (NS + 3) / 4;
   __shared__ float4 ew[ATTNRES_MAX_QUERIES][NS4];
   __shared__ float4 stage[kMaxWaves * 2 * kWave];  // 2 KiB per wave
@@ -954,15 +984,38 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
       // those reads before the next sub-layer's writes.  Two half-vector
       // streaming stores per lane ran at 2.7 TB/s, the same with the default
       // policy at 3.1, staged at 4.9 (T = 32768, n = 8, L = 24).
+      // (24-bit elements: 24 bytes per lane, 1536 per wave, stored as two
+      // runs of 768 bytes, 12 bytes per lane; 3D is a multiple of 12, so a
+      // lane's 12 bytes are wholly inside the row or wholly past its end)
+      const __amdgpu_buffer_rsrc_t ru =
+          rsrc(static_cast<uint8_t*>(U) + ((int64_t)l * u_lstride + t * u_pitch) * EB, (uint32_t)D * EB);
       float4* st = stage + wave * (2 * kWave);
-      st[2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      st[2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      wave_sync();
-      const float4 lo = st[lane], hi = st[kWave + lane];
-      wave_sync();
-      const __amdgpu_buffer_rsrc_t ru = rsrc(U + (int64_t)l * u_lstride + t * u_pitch, (uint32_t)D * 4u);
-      bstore<kAuxStreamStore>(ru, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
-      bstore<kAuxStreamStore>(ru, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
+      if constexpr (F24) {
+        uint32_t* s32 = reinterpret_cast<uint32_t*>(st);
+        uint32_t d[6];
+        pack24(rne24(acc[0]), rne24(acc[1]), rne24(acc[2]), rne24(acc[3]), d);
+        pack24(rne24(acc[4]), rne24(acc[5]), rne24(acc[6]), rne24(acc[7]), d + 3);
+        uint2* s64 = reinterpret_cast<uint2*>(s32 + 6 * lane);
+        s64[0] = make_uint2(d[0], d[1]);
+        s64[1] = make_uint2(d[2], d[3]);
+        s64[2] = make_uint2(d[4], d[5]);
+        wave_sync();
+        u32x3_t lo, hi;
+        lo.x = s32[3 * lane]; lo.y = s32[3 * lane + 1]; lo.z = s32[3 * lane + 2];
+        hi.x = s32[3 * kWave + 3 * lane]; hi.y = s32[3 * kWave + 3 * lane + 1]; hi.z = s32[3 * kWave + 3 * lane + 2];
+        wave_sync();
+        const uint32_t wb24 = (sl.off[k] >> 4) * 24u - 24u * (uint32_t)lane;  // the wave's first vector, bytes
+        __builtin_amdgcn_raw_buffer_store_b96(lo, ru, wb24 + 12u * (uint32_t)lane, 0, kAuxStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b96(hi, ru, wb24 + 768u + 12u * (uint32_t)lane, 0, kAuxStreamStore);
+      } else {
+        st[2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        st[2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        wave_sync();
+        const float4 lo = st[lane], hi = st[kWave + lane];
+        wave_sync();
+        bstore<kAuxStreamStore>(ru, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
+        bstore<kAuxStreamStore>(ru, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
+      }
     }
   }
 }
@@ -1002,9 +1055,9 @@ __device__ __forceinline__ void unpack4(const u32x2_t& q, float (&f)[4]) {
 // bf16 values), stores the new partial sum to partial_out (row pitch p_pitch;
 // may be p itself: a thread rewrites only the quads it has already read) and
 // continues with it.
-template <int N, bool UPDATE>
+template <int N, bool UPDATE, bool F24>
 __global__ void __launch_bounds__(1024) fwd_merged_kernel(
-    const float* __restrict__ U, int64_t u_pitch, const uint16_t* p, int64_t p_pitch,
+    const void* __restrict__ U, int64_t u_pitch, const uint16_t* p, int64_t p_pitch,
     const uint16_t* __restrict__ delta, uint16_t* partial_out, const float* __restrict__ zg,
     const float* __restrict__ rg, const float* __restrict__ w, float eps, int64_t t0, int32_t D,
     uint16_t* __restrict__ out, float* __restrict__ rstd_out, float* __restrict__ alpha_out) {
@@ -1016,9 +1069,12 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
   const int64_t t = t0 + (D <= 8192 ? xcd_chunked(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
   const int V4 = D / 4;
   const __amdgpu_buffer_rsrc_t rw = rsrc(w, (uint32_t)D * 4u);
-  const __amdgpu_buffer_rsrc_t ru = rsrc(U + t * u_pitch, (uint32_t)D * 4u);
+  constexpr uint32_t EB = F24 ? 3 : 4;  // bytes per element of U
+  const __amdgpu_buffer_rsrc_t ru = rsrc(static_cast<const uint8_t*>(U) + t * u_pitch * EB, (uint32_t)D * EB);
   const __amdgpu_buffer_rsrc_t rp = rsrc(p + t * p_pitch, (uint32_t)D * 2u);
-  uint4 wq[Q], uq[Q];
+  uint4 wq[Q];
+  u32x4_t uq[F24 ? 1 : Q];
+  u32x3_t uq3[F24 ? Q : 1];
   u32x2_t pq[Q];
   uint32_t o16[Q];  // the quad's byte offset in an fp32 row (past the row end: reads zeros, stores dropped)
 #pragma unroll
@@ -1037,7 +1093,13 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
     for (int k = 0; k < Q; ++k) yq[k] = __builtin_amdgcn_raw_buffer_load_b64(ry, o16[k] / 2u, 0, kAuxStreamLoad);
   }
 #pragma unroll
-  for (int k = 0; k < Q; ++k) uq[k] = bload<kAuxStreamLoad>(ru, o16[k]);
+  for (int k = 0; k < Q; ++k) {
+    if constexpr (F24)  // 12 bytes per quad; past the row end (o16 = 0xFFFFFFF0): zeros
+      uq3[k] = __builtin_amdgcn_raw_buffer_load_b96(ru, o16[k] == 0xFFFFFFF0u ? o16[k] : o16[k] / 4u * 3u, 0,
+                                                    kAuxStreamLoad);
+    else
+      uq[k] = __builtin_amdgcn_raw_buffer_load_b128(ru, o16[k], 0, kAuxStreamLoad);
+  }
   float zgv, rgv;
   {  // lane i: shared source i's given score and rstd (lanes >= N-1 read zeros)
     const int lane = lane_id();
@@ -1108,7 +1170,11 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
   const __amdgpu_buffer_rsrc_t ro = rsrc(out + t * D, (uint32_t)D * 2u);
 #pragma unroll
   for (int k = 0; k < Q; ++k) {
-    const float4 u = __builtin_bit_cast(float4, uq[k]);
+    float4 u;
+    if constexpr (F24)
+      u = unpack24(uq3[k]);
+    else
+      u = __builtin_bit_cast(float4, uq[k]);
     float f[4];
     unpack4(pq[k], f);
     const float acc[8] = {fmaf(a[N - 1], f[0], cs * u.x), fmaf(a[N - 1], f[1], cs * u.y),
@@ -2337,17 +2403,17 @@ attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, con
 // several launches.
 int threads_for(int32_t D, int vpt) { return ((D / 8 + vpt - 1) / vpt + kWave - 1) / kWave * kWave; }
 
-template <int NS, int VPT>
-hipError_t run_sums_vpt(hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T, int32_t D, float* U,
+template <int NS, int VPT, bool F24>
+hipError_t run_sums_vpt(hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T, int32_t D, void* U,
                         int64_t ls, int64_t tp) {
   const int threads = threads_for(D, VPT);
   int64_t res = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&block_sums_kernel<NS, VPT>), threads, 0, &res);
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&block_sums_kernel<NS, VPT, F24>), threads, 0, &res);
   if (e != hipSuccess) return e;  // validates the launch shape
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
   for (int64_t t0 = 0; t0 < T; t0 += per_launch) {
     const int64_t n = T - t0 < per_launch ? T - t0 : per_launch;
-    hipLaunchKernelGGL((block_sums_kernel<NS, VPT>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, rows, z, L, T,
+    hipLaunchKernelGGL((block_sums_kernel<NS, VPT, F24>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, rows, z, L, T,
                        D, t0, U, ls, tp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2356,22 +2422,27 @@ hipError_t run_sums_vpt(hipStream_t st, const SrcRows& rows, const float* z, int
 }
 
 template <int NS>
-hipError_t run_sums_n(int vpt, hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T, int32_t D,
-                      float* U, int64_t ls, int64_t tp) {
-  return vpt == 1 ? run_sums_vpt<NS, 1>(st, rows, z, L, T, D, U, ls, tp)
-                  : run_sums_vpt<NS, 2>(st, rows, z, L, T, D, U, ls, tp);
+hipError_t run_sums_n(int vpt, bool f24, hipStream_t st, const SrcRows& rows, const float* z, int32_t L, int64_t T,
+                      int32_t D, void* U, int64_t ls, int64_t tp) {
+  if (f24)
+    return vpt == 1 ? run_sums_vpt<NS, 1, true>(st, rows, z, L, T, D, U, ls, tp)
+                    : run_sums_vpt<NS, 2, true>(st, rows, z, L, T, D, U, ls, tp);
+  return vpt == 1 ? run_sums_vpt<NS, 1, false>(st, rows, z, L, T, D, U, ls, tp)
+                  : run_sums_vpt<NS, 2, false>(st, rows, z, L, T, D, U, ls, tp);
 }
 
 // The sums' vectors per thread: one while a token's vectors fit 1024 threads.
 int sums_vpt(int32_t D) { return D / 8 <= 1024 ? 1 : 2; }
 
 attnres_status block_sums_impl(const uint16_t* const* srcs, int64_t pitch, const float* z, int32_t L, int32_t n,
-                               int64_t T, int32_t D, float* U, int64_t ls, int64_t tp, void* stream) {
+                               int64_t T, int32_t D, void* U, int64_t ls, int64_t tp, int32_t u_format, void* stream) {
   if (!sizes_ok(n, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (L < 1 || L > ATTNRES_MAX_QUERIES) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (T == 0) return ATTNRES_OK;
   if (srcs == nullptr || z == nullptr || U == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!aligned(z, 4) || !aligned(U, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (u_format != ATTNRES_U_F32 && u_format != ATTNRES_U_F24) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const bool f24 = u_format == ATTNRES_U_F24;
+  if (!aligned(z, 4) || !aligned(U, f24 ? 4 : 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
   // U rows start on 16-byte boundaries and never overlap: sub-layer-major
   // (tp >= D, ls past the last token's row) or token-major (ls >= D, tp past
@@ -2389,30 +2460,31 @@ attnres_status block_sums_impl(const uint16_t* const* srcs, int64_t pitch, const
     ins[i] = rows_of(srcs[i], T, (int64_t)D * 2, pitch * 2);
   }
   ins[n] = range_of(z, (size_t)L * (size_t)T * (size_t)n * 4);
-  const Range out = range_of(U, (size_t)((int64_t)(L - 1) * ls + (T - 1) * tp + D) * 4);
+  const Range out = range_of(U, (size_t)((int64_t)(L - 1) * ls + (T - 1) * tp + D) * (f24 ? 3 : 4));
   for (int b = 0; b <= n; ++b)
     if (overlap(out, ins[b])) return ATTNRES_ERR_INVALID_ARGUMENT;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int vpt = sums_vpt(D);
   hipError_t e;
   switch (n) {
-    case 1: e = run_sums_n<1>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 2: e = run_sums_n<2>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 3: e = run_sums_n<3>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 4: e = run_sums_n<4>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 5: e = run_sums_n<5>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 6: e = run_sums_n<6>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 7: e = run_sums_n<7>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 8: e = run_sums_n<8>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
-    case 9: e = run_sums_n<9>(vpt, st, rows, z, L, T, D, U, ls, tp); break;
+    case 1: e = run_sums_n<1>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 2: e = run_sums_n<2>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 3: e = run_sums_n<3>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 4: e = run_sums_n<4>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 5: e = run_sums_n<5>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 6: e = run_sums_n<6>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 7: e = run_sums_n<7>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 8: e = run_sums_n<8>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
+    case 9: e = run_sums_n<9>(vpt, f24, st, rows, z, L, T, D, U, ls, tp); break;
     default: return ATTNRES_ERR_INVALID_ARGUMENT;
   }
   return e == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
 
 struct MergedArgs {
-  const float* U;
+  const void* U;
   int64_t u_pitch;
+  int32_t u_format;
   const uint16_t* p;
   int64_t p_pitch;
   const uint16_t* delta;  // with partial_out: the fused partial-sum update, else both NULL
@@ -2430,16 +2502,17 @@ struct MergedArgs {
 
 // kMergedQuads channel quads per thread, whole waves: 256 threads at D = 7168,
 // 640 at D = 16384.
-template <int N, bool UPDATE>
+template <int N, bool UPDATE, bool F24>
 hipError_t run_merged_nu(hipStream_t st, const MergedArgs& a) {
   const int threads = ((a.D / 4 + kMergedQuads - 1) / kMergedQuads + kWave - 1) / kWave * kWave;
   int64_t res = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N, UPDATE>), threads, 0, &res);
+  hipError_t e =
+      resident_blocks(reinterpret_cast<const void*>(&fwd_merged_kernel<N, UPDATE, F24>), threads, 0, &res);
   if (e != hipSuccess) return e;  // validates the launch shape
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
   for (int64_t t0 = 0; t0 < a.T; t0 += per_launch) {
     const int64_t n = a.T - t0 < per_launch ? a.T - t0 : per_launch;
-    hipLaunchKernelGGL((fwd_merged_kernel<N, UPDATE>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U,
+    hipLaunchKernelGGL((fwd_merged_kernel<N, UPDATE, F24>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, a.U,
                        a.u_pitch, a.p, a.p_pitch, a.delta, a.partial_out, a.zg, a.rg, a.w, a.eps, t0, a.D, a.out,
                        a.rstd, a.alpha);
     e = hipGetLastError();
@@ -2450,14 +2523,18 @@ hipError_t run_merged_nu(hipStream_t st, const MergedArgs& a) {
 
 template <int N>
 hipError_t run_merged_n(hipStream_t st, const MergedArgs& a) {
-  return a.delta != nullptr ? run_merged_nu<N, true>(st, a) : run_merged_nu<N, false>(st, a);
+  if (a.u_format == ATTNRES_U_F24)
+    return a.delta != nullptr ? run_merged_nu<N, true, true>(st, a) : run_merged_nu<N, false, true>(st, a);
+  return a.delta != nullptr ? run_merged_nu<N, true, false>(st, a) : run_merged_nu<N, false, false>(st, a);
 }
 
 attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
   const size_t nTD = (size_t)a.T * (size_t)a.D, nTN = (size_t)a.T * (size_t)N, nTG = (size_t)a.T * (size_t)(N - 1);
   if (a.U == nullptr || a.p == nullptr || a.zg == nullptr || a.rg == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (a.out == nullptr || a.rstd == nullptr || a.alpha == nullptr) return ATTNRES_ERR_INVALID_ARGUMENT;
-  if (!aligned(a.U, 16) || !aligned(a.p, 16) || !aligned(a.out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
+  if (a.u_format != ATTNRES_U_F32 && a.u_format != ATTNRES_U_F24) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const int64_t eb = a.u_format == ATTNRES_U_F24 ? 3 : 4;  // bytes per element of U
+  if (!aligned(a.U, eb == 4 ? 16 : 4) || !aligned(a.p, 16) || !aligned(a.out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(a.zg, 4) || !aligned(a.rg, 4) || !aligned(a.rstd, 4) || !aligned(a.alpha, 4))
     return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(a.p_pitch, a.T, a.D)) return ATTNRES_ERR_INVALID_ARGUMENT;
@@ -2465,7 +2542,7 @@ attnres_status fwd_merged_impl(const MergedArgs& a, int32_t N, void* stream) {
   const bool update = a.delta != nullptr || a.partial_out != nullptr;
   if (update && (a.delta == nullptr || a.partial_out == nullptr)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!aligned(a.delta, 16) || !aligned(a.partial_out, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  const Range ins[6] = {rows_of(a.U, a.T, (int64_t)a.D * 4, a.u_pitch * 4), rows_of(a.p, a.T, (int64_t)a.D * 2, a.p_pitch * 2),
+  const Range ins[6] = {rows_of(a.U, a.T, (int64_t)a.D * eb, a.u_pitch * eb), rows_of(a.p, a.T, (int64_t)a.D * 2, a.p_pitch * 2),
                         range_of(a.zg, nTG * 4), range_of(a.rg, nTG * 4), range_of(a.w, (size_t)a.D * 4),
                         range_of(a.delta, update ? nTD * 2 : 0)};
   const Range outs[4] = {range_of(a.out, nTD * 2), range_of(a.rstd, nTN * 4), range_of(a.alpha, nTN * 4),
@@ -2711,13 +2788,14 @@ extern "C" attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_
 }
 
 extern "C" attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch, const float* z,
-                                             int32_t L, int32_t n, int64_t T, int32_t D, float* U, int64_t u_lstride,
-                                             int64_t u_pitch, void* stream) {
-  return block_sums_impl(srcs, src_pitch, z, L, n, T, D, U, u_lstride, u_pitch, stream);
+                                             int32_t L, int32_t n, int64_t T, int32_t D, void* U, int64_t u_lstride,
+                                             int64_t u_pitch, int32_t u_format, void* stream) {
+  return block_sums_impl(srcs, src_pitch, z, L, n, T, D, U, u_lstride, u_pitch, u_format, stream);
 }
 
-extern "C" attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial,
-                                             int64_t partial_pitch, const uint16_t* delta, uint16_t* partial_out,
+extern "C" attnres_status attnres_fwd_merged(const void* U, int64_t u_pitch, int32_t u_format,
+                                             const uint16_t* partial, int64_t partial_pitch,
+                                             const uint16_t* delta, uint16_t* partial_out,
                                              const float* z_given, const float* rstd_given, const float* w, float eps,
                                              int32_t N, int64_t T, int32_t D, uint16_t* out, float* rstd,
                                              float* alpha, void* stream) {
@@ -2725,8 +2803,8 @@ extern "C" attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, co
   if (st != ATTNRES_OK) return st;
   if (N < 2) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (T == 0) return ATTNRES_OK;
-  const MergedArgs a{U,     u_pitch, partial, partial_pitch, delta, partial_out, z_given, rstd_given, w, eps,
-                     T,     D,       out,     rstd,          alpha};
+  const MergedArgs a{U,   u_pitch, u_format, partial, partial_pitch, delta, partial_out, z_given, rstd_given, w,
+                     eps, T,       D,        out,     rstd,          alpha};
   return fwd_merged_impl(a, N, stream);
 }
 

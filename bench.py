@@ -25,7 +25,8 @@ peak memory -- in bf16 storage with fp32 arithmetic.  Prints one JSON line
   block_batched_scores  one block's 24 sub-layer forwards the plain way vs
                 one block-scores pass (MFMA) plus 24 forwards from its scores,
                 and vs block scores + one block-sums pass (the shared sources'
-                part of every sub-layer's weighted sum) + 24 merged forwards
+                part of every sub-layer's weighted sum, fp32 or 24-bit
+                elements) + 24 merged forwards
 
 Flags: --gpus (1 only), --steps, --warmup, --workload (0..4, default 3),
 --sweep (extra per-T / per-N lines with fwd and bwd timed separately and
@@ -647,8 +648,9 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
     L = 24 sub-layers): L plain per-source forwards; one block-scores pass
     (MFMA) followed by L forwards from those scores; and block scores, one
     block-sums pass (the shared sources' part of every sub-layer's weighted
-    sum, fp32, sub-layer-major and token-major) and L merged forwards that
-    read only the shared sum and the partial sum.  Median of `reps`
+    sum, fp32 sub-layer-major and token-major, and in the 24-bit element
+    format sub-layer-major) and L merged forwards that read only the shared
+    sum and the partial sum.  Median of `reps`
     whole-block timings, each preceded by a 512 MiB cache flush; per-call
     times from the same runs.  Device-side random inputs of the workload's
     scales (values do not change the timing)."""
@@ -682,12 +684,12 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
             ar.attnres_fwd_scored(srcs, zb[l], rb, W[l], 1e-6, out=out, rstd=rstd, alpha=alpha)
             ev.record(l + 2, stream)
 
-    def merged(token_major):
+    def merged(token_major, u_format="f32"):
         def run():
             ev.record(0, stream)
             ar.attnres_block_scores(srcs[:n], W, 1e-6, rstd=rb, z=zb, workspace=ws)
             ev.record(1, stream)
-            ar.attnres_block_sums(srcs[:n], zb, U=U, token_major=token_major)
+            ar.attnres_block_sums(srcs[:n], zb, U=U, token_major=token_major, u_format=u_format)
             ev.record(2, stream)
             for l in range(L):
                 ar.attnres_fwd_merged(U[:, l] if token_major else U[l], srcs[n], zb[l], rb, W[l], 1e-6, out=out,
@@ -712,10 +714,13 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
     batched_ms, bp = timed(batched, L + 1, [(0, 1)])
     scores_ms = bp[(0, 1)]
     merged_res = {}
-    for tm in (False, True):
-        U = torch.empty((T, L, D) if tm else (L, T, D), dtype=torch.float32, device=dev)
-        ms, mp = timed(merged(tm), L + 2, [(1, 2), (2, L + 2)])
-        merged_res[tm] = (ms, mp[(1, 2)], mp[(2, L + 2)] / L)
+    for tm, fmt in ((False, "f32"), (True, "f32"), (False, "f24")):
+        if fmt == "f24":
+            U = torch.empty((L, T, D, 3), dtype=torch.uint8, device=dev)
+        else:
+            U = torch.empty((T, L, D) if tm else (L, T, D), dtype=torch.float32, device=dev)
+        ms, mp = timed(merged(tm, fmt), L + 2, [(1, 2), (2, L + 2)])
+        merged_res[(tm, fmt)] = (ms, mp[(1, 2)], mp[(2, L + 2)] / L)
         del U
         U = None
         torch.cuda.empty_cache()
@@ -735,11 +740,14 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
            "scored_fwd_ms": scored_ms, "scored_fwd_GBps": scored_bytes / scored_ms / 1e6,
            "plain_fwd_GBps": fwd_bytes / (plain_ms / L) / 1e6,
            "U_GiB": L * T * D * 4 / 2 ** 30}
-    for tm, key in ((False, "l_major"), (True, "t_major")):
-        ms, sums_ms, mfwd_ms = merged_res[tm]
+    for tm, fmt, key in ((False, "f32", "l_major"), (True, "f32", "t_major"), (False, "f24", "l_major_f24")):
+        ms, sums_ms, mfwd_ms = merged_res[(tm, fmt)]
+        eb = 3 if fmt == "f24" else 4  # bytes per element of U
+        sb = sums_bytes - L * T * D * (4 - eb)
+        mb = merged_bytes - T * D * (4 - eb)
         rec[f"merged_{key}"] = {"block_ms": ms, "vs_plain": plain_ms / ms, "block_sums_ms": sums_ms,
-                                "block_sums_GBps": sums_bytes / sums_ms / 1e6, "merged_fwd_ms": mfwd_ms,
-                                "merged_fwd_GBps": merged_bytes / mfwd_ms / 1e6}
+                                "block_sums_GBps": sb / sums_ms / 1e6, "merged_fwd_ms": mfwd_ms,
+                                "merged_fwd_GBps": mb / mfwd_ms / 1e6}
     # one sub-layer's merged forward with the fused partial-sum update, against a
     # separate bf16 add followed by the merged forward (median of 11 calls)
     U = torch.empty((L, T, D), dtype=torch.float32, device=dev)

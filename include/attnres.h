@@ -337,30 +337,46 @@ attnres_status attnres_fwd_scored(const uint16_t* const* srcs, int64_t src_pitch
  *     U[l][t][d] = sum_i exp(z[l][t][i] - m[l][t]) x[i][t][d]       (fp32)
  * and each sub-layer's forward then runs attnres_fwd_merged, which reads its
  * U rows and the partial sum instead of all N source rows.
+ * U is stored in one of two element formats (u_format):
+ *   ATTNRES_U_F32  fp32, 4 bytes per element;
+ *   ATTNRES_U_F24  the fp32 sum rounded to nearest even on a 16-bit
+ *                  significand (fp32 exponent range), kept as the upper three
+ *                  bytes of its fp32 bit pattern, little-endian, 3 bytes per
+ *                  element: element k of a row occupies bytes 3k .. 3k+2 and
+ *                  its value is the fp32 number whose bit pattern is
+ *                  byte[3k] << 8 | byte[3k+1] << 16 | byte[3k+2] << 24.
+ *                  A quarter less traffic for the sums and the merged
+ *                  forward; the relative error of an element is at most
+ *                  2^-16 (1/128 of a bf16 unit in the last place).
  *   srcs, src_pitch  the n shared sources as in attnres_block_scores
  *                    (n = 1 .. ATTNRES_MAX_SOURCES)
  *   z      [L][T][n] fp32, 4-byte aligned: attnres_block_scores' z (any
  *          finite scores)
  *   L      1 .. ATTNRES_MAX_QUERIES; T, D as attnres_fwd
- *   U      fp32 output, 16-byte aligned: row (l, t) of D values at
- *          U + l*u_lstride + t*u_pitch elements.  u_lstride and u_pitch are
+ *   U      output, 16-byte (ATTNRES_U_F32) or 4-byte (ATTNRES_U_F24)
+ *          aligned: row (l, t) of D elements at element offset
+ *          l*u_lstride + t*u_pitch.  u_lstride and u_pitch are
  *          multiples of 4, at least D, and lay the rows out sub-layer-major
  *          (u_lstride >= (T-1)*u_pitch + D, e.g. u_lstride = T*D, u_pitch = D)
  *          or token-major (u_pitch >= (L-1)*u_lstride + D, e.g. u_lstride =
- *          D, u_pitch = L*D); other layouts are rejected.  L*T*D*4 bytes in
- *          the dense layouts.
+ *          D, u_pitch = L*D); other layouts are rejected.  L*T*D*4 (F32) or
+ *          L*T*D*3 (F24) bytes in the dense layouts.
+ *   u_format  ATTNRES_U_F32 or ATTNRES_U_F24; anything else is rejected.
  * U must not overlap the sources or z.  T == 0: nothing is enqueued.  The
  * weights are fp32 (exp on the hardware exp2), the sums fp32 in source order.
  */
+#define ATTNRES_U_F32 0
+#define ATTNRES_U_F24 1
 attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch, const float* z, int32_t L,
-                                  int32_t n, int64_t T, int32_t D, float* U, int64_t u_lstride, int64_t u_pitch,
-                                  void* stream);
+                                  int32_t n, int64_t T, int32_t D, void* U, int64_t u_lstride, int64_t u_pitch,
+                                  int32_t u_format, void* stream);
 
 /*
  * Forward of one sub-layer from its block-batched shared sum: U holds the
- * sub-layer's rows of attnres_block_sums (U + l*u_lstride for sub-layer l,
- * row t at + t*u_pitch floats; u_pitch a multiple of 4, >= D, 16-byte
- * aligned base), partial [T][D] bf16 (row pitch partial_pitch, a multiple of
+ * sub-layer's rows of attnres_block_sums in the format u_format (its element
+ * offset l*u_lstride for sub-layer l; row t at a further t*u_pitch elements;
+ * u_pitch a multiple of 4, >= D; base aligned as for attnres_block_sums),
+ * partial [T][D] bf16 (row pitch partial_pitch, a multiple of
  * 8 elements, 16-byte aligned) the current partial sum, the last of the N
  * sources.  z_given and rstd_given ([T][N-1] fp32, 4-byte aligned) are the
  * shared sources' scores for this sub-layer and their rstd, as for
@@ -383,7 +399,8 @@ attnres_status attnres_block_sums(const uint16_t* const* srcs, int64_t src_pitch
  * The backward is attnres_bwd_sources on all N sources (partial_out as the
  * last, when updated) with these outputs.
  */
-attnres_status attnres_fwd_merged(const float* U, int64_t u_pitch, const uint16_t* partial, int64_t partial_pitch,
+attnres_status attnres_fwd_merged(const void* U, int64_t u_pitch, int32_t u_format, const uint16_t* partial,
+                                  int64_t partial_pitch,
                                   const uint16_t* delta, uint16_t* partial_out, const float* z_given,
                                   const float* rstd_given, const float* w, float eps, int32_t N, int64_t T, int32_t D,
                                   uint16_t* out, float* rstd, float* alpha, void* stream);

@@ -184,13 +184,15 @@ int main(void) {
     CHECK_HIP(hipMemcpy(d_W, W, (size_t)L * D * 4, hipMemcpyHostToDevice));
     st = attnres_block_scores(srcs, D, d_W, L, eps, n, T, (int32_t)D, d_rb, d_zb, d_bws, bws, NULL);
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_scores returned %d\n", (int)st); return 1; }
-    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, T * D, D, NULL);
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, T * D, D, ATTNRES_U_F32, NULL);
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_sums returned %d\n", (int)st); return 1; }
-    st = attnres_fwd_merged(d_U + (size_t)l * T * D, D, srcs[n], D, NULL, NULL, d_zb + (size_t)l * T * n, d_rb,
-                            d_W + (size_t)l * D, eps, N, T, (int32_t)D, d_out3, d_rstd3, d_alpha3, NULL);
+    st = attnres_fwd_merged(d_U + (size_t)l * T * D, D, ATTNRES_U_F32, srcs[n], D, NULL, NULL, d_zb + (size_t)l * T * n,
+                            d_rb, d_W + (size_t)l * D, eps, N, T, (int32_t)D, d_out3, d_rstd3, d_alpha3, NULL);
     if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd_merged returned %d\n", (int)st); return 1; }
-    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, D, D, NULL);  /* rows would collide */
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, D, D, ATTNRES_U_F32, NULL);  /* rows would collide */
     if (st != ATTNRES_ERR_INVALID_ARGUMENT) { fprintf(stderr, "colliding U rows not refused (%d)\n", (int)st); ++fails; }
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U, T * D, D, 2, NULL);  /* no such format */
+    if (st != ATTNRES_ERR_INVALID_ARGUMENT) { fprintf(stderr, "U format 2 not refused (%d)\n", (int)st); ++fails; }
     CHECK_HIP(hipDeviceSynchronize());
     CHECK_HIP(hipMemcpy(out, d_out3, nTD * 2, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(rstd, d_rstd3, nTN * 4, hipMemcpyDeviceToHost));
@@ -205,6 +207,37 @@ int main(void) {
     printf("block route (scores, sums, merged forward): out rel_l2 %.3e  alpha max abs %.3e  rstd max rel %.3e\n", o3,
            a3, r3);
     if (!(o3 <= 5e-3 && a3 <= 1e-5 && r3 <= 1e-5)) ++fails;
+
+    /* the same route with U in the 24-bit format: its bytes are the fp32 sums rounded to nearest even at bit 8 */
+    uint8_t* d_U24;
+    const size_t nU = (size_t)L * T * D;
+    CHECK_HIP(hipMalloc((void**)&d_U24, nU * 3));
+    st = attnres_block_sums(srcs, D, d_zb, L, n, T, (int32_t)D, d_U24, T * D, D, ATTNRES_U_F24, NULL);
+    if (st != ATTNRES_OK) { fprintf(stderr, "attnres_block_sums (F24) returned %d\n", (int)st); return 1; }
+    st = attnres_fwd_merged(d_U24 + (size_t)l * T * D * 3, D, ATTNRES_U_F24, srcs[n], D, NULL, NULL,
+                            d_zb + (size_t)l * T * n, d_rb, d_W + (size_t)l * D, eps, N, T, (int32_t)D, d_out3, d_rstd3,
+                            d_alpha3, NULL);
+    if (st != ATTNRES_OK) { fprintf(stderr, "attnres_fwd_merged (F24) returned %d\n", (int)st); return 1; }
+    CHECK_HIP(hipDeviceSynchronize());
+    uint32_t* u32 = malloc(nU * 4);
+    uint8_t* u24 = malloc(nU * 3);
+    CHECK_HIP(hipMemcpy(u32, d_U, nU * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(u24, d_U24, nU * 3, hipMemcpyDeviceToHost));
+    size_t bad24 = 0;
+    for (size_t i = 0; i < nU; ++i) {
+      const uint32_t b = u32[i], r = b + 0x7Fu + ((b >> 8) & 1u);
+      if (u24[3 * i] != ((r >> 8) & 0xFF) || u24[3 * i + 1] != ((r >> 16) & 0xFF) || u24[3 * i + 2] != (r >> 24)) ++bad24;
+    }
+    CHECK_HIP(hipMemcpy(out, d_out3, nTD * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(alpha, d_alpha3, nTN * 4, hipMemcpyDeviceToHost));
+    double a4 = 0;
+    for (size_t i = 0; i < nTN; ++i) a4 = fmax(a4, fabs((double)alpha[i] - r_alpha[i]));
+    const double o4 = rel_l2_bf16(out, r_out, nTD);
+    printf("block route with 24-bit U: %zu of %zu elements differ from the rounded fp32 sums; out rel_l2 %.3e  "
+           "alpha max abs %.3e\n", bad24, nU, o4, a4);
+    if (!(bad24 == 0 && o4 <= 5e-3 && a4 <= 1e-5)) ++fails;
+    free(u32);
+    free(u24);
   }
   return fails == 0 ? 0 : 1;
 }

@@ -216,22 +216,35 @@ static void run_abi(void) {
                              wsb, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
   /* block sums: colliding U rows, U on top of a source; merged forward: out on top of U, misaligned partial sum */
   float* U = (float*)ws;
-  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, U, D, D, NULL) ==
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, U, D, D, ATTNRES_U_F32, NULL) ==
          ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, (float*)srcs[0], (int64_t)T * D, D, NULL) ==
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, (float*)srcs[0], (int64_t)T * D, D,
+                            ATTNRES_U_F32, NULL) ==
          ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 0, N - 1, T, D, U, (int64_t)T * D, D, NULL) ==
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 0, N - 1, T, D, U, (int64_t)T * D, D, ATTNRES_U_F32, NULL) ==
          ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D,
+  EXPECT(attnres_fwd_merged(U, D, ATTNRES_U_F32, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D,
                             (uint16_t*)U, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1] + 1, (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D, out,
+  EXPECT(attnres_fwd_merged(U, D, ATTNRES_U_F32, srcs[N - 1] + 1, (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D, out,
                             rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, 1, T, D, out, rstd,
+  EXPECT(attnres_fwd_merged(U, D, ATTNRES_U_F32, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, 1, T, D, out, rstd,
                             alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  /* the 24-bit U format: another format number, U bases that are not 4-byte aligned, and 3-byte rows on top of
+   * a source */
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, U, (int64_t)T * D, D, 2, NULL) ==
+         ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, (uint8_t*)U + 2, (int64_t)T * D, D,
+                            ATTNRES_U_F24, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_block_sums(srcs, (int64_t)N * D, rstd, 4, N - 1, T, D, (void*)srcs[1], (int64_t)T * D, D,
+                            ATTNRES_U_F24, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged((uint8_t*)U + 2, D, ATTNRES_U_F24, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w,
+                            1e-6f, N, T, D, out, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
+  EXPECT(attnres_fwd_merged(U, D, -1, srcs[N - 1], (int64_t)N * D, NULL, NULL, rstd, alpha, w, 1e-6f, N, T, D, out,
+                            rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
   /* the update: delta without partial_out, and partial_out on top of delta */
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, dout, NULL, rstd, alpha, w, 1e-6f, N, T, D, out, rstd,
+  EXPECT(attnres_fwd_merged(U, D, ATTNRES_U_F32, srcs[N - 1], (int64_t)N * D, dout, NULL, rstd, alpha, w, 1e-6f, N, T, D, out, rstd,
                             alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
-  EXPECT(attnres_fwd_merged(U, D, srcs[N - 1], (int64_t)N * D, dout, (uint16_t*)dout, rstd, alpha, w, 1e-6f, N, T, D,
+  EXPECT(attnres_fwd_merged(U, D, ATTNRES_U_F32, srcs[N - 1], (int64_t)N * D, dout, (uint16_t*)dout, rstd, alpha, w, 1e-6f, N, T, D,
                             out, rstd, alpha, NULL) == ATTNRES_ERR_INVALID_ARGUMENT);
 }
 #endif

@@ -147,7 +147,10 @@ def out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
     return 0.5 * bf16_ulp(torch.maximum(out_ref.abs(), out_gpu.abs())) + b
 
 
-def merged_out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
+U24 = 2.0 ** -16  # relative rounding error of a block sum stored in the 24-bit format
+
+
+def merged_out_bound(x, a_gpu, a_ref, out_ref, out_gpu, u_rel=0.0) -> torch.Tensor:
     """Per-element bound on |out_gpu - out_ref| for the forward from block sums
     (out' = bf16(fma(a'_p, p, c' U')), c' = exp(m - M) / den): out_bound plus
     the difference between the weight a shared source gets through c' and its
@@ -157,11 +160,13 @@ def merged_out_bound(x, a_gpu, a_ref, out_ref, out_gpu) -> torch.Tensor:
     hardware exp2 within a few ulps) is off by at most u (2 |z_i - M| + 4)
     relative, and |z_i - M| = log(max_j a_j / a_i) from the reference
     weights; the shared sum's n fp32 terms and c' U' + a'_p p add (N + 3) u.
+    u_rel: the relative error of a stored element of U' (0 for fp32, U24 for
+    the 24-bit format), which scales every shared source's part of it.
     Doubled.  x [N][n][D], alpha [n][N]; float64 tensors."""
     N = x.shape[0]
     ar_ = a_ref.T[:, :, None].clamp_min(1e-300)           # [N][n][1]
     spread = torch.log(ar_.max(0, keepdim=True).values / ar_)
-    k = U32 * (2 * spread + 4 + N + 3)
+    k = U32 * (2 * spread + 4 + N + 3) + u_rel
     k[N - 1] = 0.0                                        # the partial sum's weight is a'_p itself
     extra = (k * a_gpu.abs().T[:, :, None] * x.abs()).sum(0)
     return out_bound(x, a_gpu, a_ref, out_ref, out_gpu) + 2.0 * extra
@@ -242,7 +247,8 @@ class Accum:
         """x [N][n][D] and g [n][D]: the chunk's inputs (bf16 bits or tensors);
         w [D]; gpu / ref: dicts of out [n][D], rstd and alpha [n][N] and
         optionally dsrc [N][n][D] (tensors or arrays); ref["merged"] true
-        when out came from the block sums (merged_out_bound)."""
+        when out came from the block sums (merged_out_bound), with
+        ref["u_rel"] the relative error of their stored elements."""
         d = self.dev
         go, ro = _t(gpu["out"], d), _t(ref["out"], d)
         ga, ra = _t(gpu["alpha"], d), _t(ref["alpha"], d)
@@ -255,8 +261,8 @@ class Accum:
         tok_num = (go - ro).square().sum(1).sqrt()
         tok_den = ro.square().sum(1).sqrt()
         self._max("out_token_rel_l2", (tok_num / torch.where(tok_den > 0, tok_den, torch.ones_like(tok_den))).max())
-        if ref.get("merged"):  # the forward from block sums
-            bo = merged_out_bound(xx, ga, ra, ro, go)
+        if ref.get("merged"):  # the forward from block sums (u_rel: U's storage rounding)
+            bo = merged_out_bound(xx, ga, ra, ro, go, ref.get("u_rel", 0.0))
         else:
             bo = out_bound(xx, ga, ra, ro, go)
         self._max("out_elem_ratio", ((go - ro).abs() / bo).max())

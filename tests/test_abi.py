@@ -99,10 +99,10 @@ def test_block_sums_and_merged_forward_refuse_on_the_host():
     srcs = (ctypes.c_void_p * 9)(*[(i + 1) * g for i in range(9)])
     T_, L_ = 16, 24
 
-    def sums(n=8, T=T_, D_=D, L=L_, z=20 * g, U=21 * g, ls=None, tp=None, pitch=None, s=srcs):
+    def sums(n=8, T=T_, D_=D, L=L_, z=20 * g, U=21 * g, ls=None, tp=None, pitch=None, s=srcs, fmt=ar.U_F32):
         ls = T * D_ if ls is None else ls
         tp = D_ if tp is None else tp
-        return lib.attnres_block_sums(s, D_ if pitch is None else pitch, z, L, n, T, D_, U, ls, tp, None)
+        return lib.attnres_block_sums(s, D_ if pitch is None else pitch, z, L, n, T, D_, U, ls, tp, fmt, None)
 
     assert sums(L=0) == INVALID and sums(L=65) == INVALID
     assert sums(n=0) == INVALID and sums(n=10) == INVALID
@@ -116,12 +116,17 @@ def test_block_sums_and_merged_forward_refuse_on_the_host():
     assert sums(tp=D - 4, ls=T_ * D) == INVALID            # pitch below a row
     assert sums(U=1 * g) == INVALID                        # U overlaps source 0
     assert sums(U=20 * g - 1024) == INVALID                # U runs into z
+    assert sums(fmt=2) == INVALID and sums(fmt=-1) == INVALID  # no such element format
+    assert sums(fmt=ar.U_F24, U=21 * g + 2) == INVALID     # 24-bit elements: a 4-byte aligned base
+    # the 24-bit rows span 3 bytes per element: a U whose last 12 bytes lie on z overlaps it
+    span24 = ((L_ - 1) * T_ * D + (T_ - 1) * D + D) * 3
+    assert sums(fmt=ar.U_F24, U=20 * g - span24 + 12) == INVALID
     assert sums(T=0, s=None, z=0, U=0) == OK               # empty: nothing to do
 
     def merged(N=9, T=T_, D_=D, U=40 * g, up=None, p=41 * g, pp=None, zg=42 * g, rg=43 * g, w=44 * g, eps=1e-6,
-               out=45 * g, rstd=46 * g, alpha=47 * g, y=None, po=None):
-        return lib.attnres_fwd_merged(U, D_ if up is None else up, p, D_ if pp is None else pp, y, po, zg, rg, w, eps,
-                                      N, T, D_, out, rstd, alpha, None)
+               out=45 * g, rstd=46 * g, alpha=47 * g, y=None, po=None, fmt=ar.U_F32):
+        return lib.attnres_fwd_merged(U, D_ if up is None else up, fmt, p, D_ if pp is None else pp, y, po, zg, rg, w,
+                                      eps, N, T, D_, out, rstd, alpha, None)
 
     assert merged(N=1) == INVALID and merged(N=10) == INVALID
     assert merged(U=0) == INVALID and merged(p=0) == INVALID and merged(zg=0) == INVALID and merged(rg=0) == INVALID
@@ -137,6 +142,8 @@ def test_block_sums_and_merged_forward_refuse_on_the_host():
     assert merged(y=48 * g, po=48 * g) == INVALID                         # partial_out on top of delta
     assert merged(y=48 * g, po=40 * g) == INVALID                         # partial_out on top of U
     assert merged(y=48 * g, po=45 * g) == INVALID                         # partial_out on top of out
+    assert merged(fmt=2) == INVALID and merged(fmt=ar.U_F24, U=40 * g + 2) == INVALID
+    assert merged(fmt=ar.U_F24, out=40 * g + T_ * D * 3 - 16) == INVALID  # out overlaps the last 24-bit U row
     assert merged(T=0, U=0, p=0, zg=0, rg=0, out=0, rstd=0, alpha=0) == OK
 
 
@@ -553,3 +560,23 @@ def test_workspace_macro_matches_binding(tmp_path):
                     "-o", str(exe), str(src)], check=True, capture_output=True)
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert got == [ar.workspace_bytes(T, N, D_) for T, N, D_ in cases]
+
+
+def test_decode_u24_reads_the_24_bit_format():
+    """decode_u24 (host logic, CPU tensors here) returns the fp32 value whose
+    upper three bytes the element holds: exactly for values whose low byte is
+    zero, and within 2^-16 relative of the original for rounded values."""
+    import torch
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(1000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 1000),
+                        np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -126, 3.0e38], dtype=np.float32)]).astype(np.float32)
+    b = v.view(np.uint32).astype(np.uint64)
+    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFFFF
+    by = np.stack([(r >> 8) & 0xFF, (r >> 16) & 0xFF, r >> 24], -1).astype(np.uint8)
+    d = ar.decode_u24(torch.from_numpy(by)).numpy()
+    assert np.array_equal(d.view(np.uint32), (r & 0xFFFFFF00).astype(np.uint32))
+    fin = np.isfinite(d)
+    assert fin.all()
+    assert np.all(np.abs(d.astype(np.float64) - v) <= 2.0 ** -16 * np.abs(v.astype(np.float64)))
+    with pytest.raises(ValueError):
+        ar.decode_u24(torch.zeros((4, 2), dtype=torch.uint8))

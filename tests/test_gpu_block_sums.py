@@ -14,6 +14,13 @@ the plain oracle forward on all N sources (out rel-L2 5e-3, alpha 1e-5
 absolute, rstd 1e-5 relative) and, element by element, ``merged_out_bound``:
 the plain forward's bound plus the difference between a shared source's
 weight through the rescaled sum and the saved alpha.
+
+The 24-bit element format of U (each fp32 sum rounded to nearest even on a
+16-bit significand, three bytes kept): its bytes are checked bit for bit
+against that rounding of the fp32 sums, done here on the host from the
+definition; the merged forward on it bit for bit against the merged forward on
+the decoded values given as fp32; and the chain against the oracle within
+merged_out_bound plus the format's 2^-16 relative error on the shared part.
 """
 from __future__ import annotations
 
@@ -24,7 +31,7 @@ import torch
 import attention_residuals_depth_amd as ar
 import oracle
 import synth
-from parity import DEV, Accum, TOL_ALPHA_ABS, _t, sums_bound, to_dev_bf16, within_tolerance
+from parity import DEV, U24, Accum, TOL_ALPHA_ABS, _t, sums_bound, to_dev_bf16, within_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +109,7 @@ def test_block_sums_layouts_and_batch_agree_bitwise():
     assert torch.equal(U1[:, 37:101], U4)
 
 
-def _chain(N, T, D, L, w_std=None, subs=(0,), seed=0, chunk=2048):
+def _chain(N, T, D, L, w_std=None, subs=(0,), seed=0, chunk=2048, u_format="f32"):
     """GPU: block scores -> block sums -> each listed sub-layer's merged forward,
     all on the device; compared with the plain oracle forward on all N
     sources (the shared ones first, the partial sum last), every token."""
@@ -112,10 +119,10 @@ def _chain(N, T, D, L, w_std=None, subs=(0,), seed=0, chunk=2048):
     srcs = [to_dev_bf16(bits[i]) for i in range(N)]
     Wd = torch.from_numpy(W).to(DEV)
     rb, zb = ar.attnres_block_scores(srcs[:-1], Wd, wl.eps)
-    U = ar.attnres_block_sums(srcs[:-1], zb)
+    U = ar.attnres_block_sums(srcs[:-1], zb, u_format=u_format)
     errs = []
     for l in subs:
-        print(f"[merged] N={N} T={T} D={D} sub-layer {l} w_std={w_std}", flush=True)
+        print(f"[merged] N={N} T={T} D={D} sub-layer {l} w_std={w_std} U {u_format}", flush=True)
         out, rstd, alpha = ar.attnres_fwd_merged(U[l], srcs[-1], zb[l], rb, Wd[l], wl.eps)
         torch.cuda.synchronize()
         acc = Accum(DEV)
@@ -124,7 +131,8 @@ def _chain(N, T, D, L, w_std=None, subs=(0,), seed=0, chunk=2048):
             xs = np.ascontiguousarray(bits[:, t0:t1])
             o_out, o_rstd, o_alpha = oracle.fwd(xs, W[l], wl.eps)
             acc.update(xs, None, W[l], dict(out=out[t0:t1], rstd=rstd[t0:t1], alpha=alpha[t0:t1]),
-                       dict(out=o_out, rstd=o_rstd, alpha=o_alpha, merged=True))
+                       dict(out=o_out, rstd=o_rstd, alpha=o_alpha, merged=True,
+                            u_rel=U24 if u_format == "f24" else 0.0))
         e = acc.result()
         print(f"[merged]   " + ", ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
         errs.append(e)
@@ -138,10 +146,87 @@ def test_merged_forward_against_oracle(N, T, D):
         assert within_tolerance(e), e
 
 
-def test_merged_forward_peaked_softmax():
+@pytest.mark.parametrize("N,T,D", [(9, 300, 7168), (2, 65, 1000), (5, 129, 12288), (9, 77, 512), (3, 45, 7176)],
+                         ids=lambda v: str(v))
+def test_merged_forward_f24_against_oracle(N, T, D):
+    for e in _chain(N, T, D, L=24, subs=(0, 7, 23), u_format="f24"):
+        assert within_tolerance(e), e
+
+
+def _rne24_bytes(u32: np.ndarray) -> np.ndarray:
+    """The 24-bit format from its definition: the fp32 bit pattern plus 0x7F
+    plus bit 8 (round to nearest, ties to even, at bit 8), its upper three
+    bytes little-endian.  u32: uint32 bit patterns; returns [..., 3] uint8."""
+    b = u32.astype(np.uint64)
+    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFFFF
+    return np.stack([(r >> 8) & 0xFF, (r >> 16) & 0xFF, r >> 24], axis=-1).astype(np.uint8)
+
+
+@pytest.mark.parametrize("n,T,D,L,tmaj", [(8, 300, 7168, 24, False), (8, 130, 7168, 24, True), (9, 40, 7176, 33, True),
+                                          (4, 257, 16384, 16, False), (1, 17, 64, 1, False), (3, 70, 1000, 5, True)],
+                         ids=lambda v: str(v))
+def test_block_sums_f24_is_the_rounded_fp32(n, T, D, L, tmaj):
+    """U in the 24-bit format holds exactly the fp32 sums rounded as the format
+    defines (every byte), in both layouts; decode_u24 returns those values;
+    and the decoded sums lie within the fp32 bound plus the format's rounding
+    of the oracle's sums."""
+    wl, bits = _sources(n, T, D, seed=4)
+    W = _queries(D, L, 7)
+    srcs = [to_dev_bf16(bits[i]) for i in range(n)]
+    print(f"[sums f24] n={n} T={T} D={D} L={L} token_major={tmaj}", flush=True)
+    _, z = ar.attnres_block_scores(srcs, torch.from_numpy(W).to(DEV), wl.eps)
+    U32 = ar.attnres_block_sums(srcs, z, token_major=tmaj)
+    Ub = ar.attnres_block_sums(srcs, z, token_major=tmaj, u_format="f24")
+    torch.cuda.synchronize()
+    assert Ub.dtype == torch.uint8 and Ub.shape == U32.shape + (3,)
+    want = _rne24_bytes(U32.cpu().numpy().view(np.uint32))
+    got = Ub.cpu().numpy()
+    assert np.array_equal(got, want), f"{int((got != want).any(-1).sum())} elements differ"
+    dec = ar.decode_u24(Ub)
+    wb = want.astype(np.uint32)
+    r = (wb[..., 0] << 8) | (wb[..., 1] << 16) | (wb[..., 2] << 24)
+    assert np.array_equal(dec.cpu().numpy().view(np.uint32), r)
+    Uo = oracle.block_sums(bits, z.cpu().double().numpy())
+    Ur = torch.from_numpy(Uo).to(DEV)
+    Ug = _u_rows(dec, tmaj).double()
+    bound = sums_bound(_t(bits, DEV), z.double()) + U24 * Ug.abs()
+    ratio = float(((Ug - Ur).abs() / (bound + 1e-300)).max())
+    print(f"[sums f24]   max err/bound {ratio:.3e}", flush=True)
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("update", [False, True], ids=["plain", "update"])
+def test_merged_f24_is_the_merged_forward_on_the_decoded_sums(update):
+    """The merged forward reading 24-bit U gives bitwise the outputs of the
+    merged forward reading the decoded values as fp32 (both layouts; with the
+    fused update too): the format changes only what is stored."""
+    N, T, D, L = 9, 257, 7168, 24
+    wl = synth.workload(1, N=N, T=T)
+    bits = wl.sources()
+    W = torch.from_numpy(_queries(D, L, 8)).to(DEV)
+    srcs = [to_dev_bf16(bits[i]) for i in range(N)]
+    rb, zb = ar.attnres_block_scores(srcs[:-1], W, wl.eps)
+    Ub = ar.attnres_block_sums(srcs[:-1], zb, u_format="f24")
+    Ubt = ar.attnres_block_sums(srcs[:-1], zb, token_major=True, u_format="f24")
+    dec = ar.decode_u24(Ub).contiguous()
+    y = to_dev_bf16(synth.Workload("merged_y24", T=T, N=1, D=D, seed=11, kind="tiny",
+                                   tiny_scales=(0.3,)).sources()[0]) if update else None
+    for l in (0, 12, 23):
+        kw = {} if not update else dict(delta=y, in_place=False)
+        r24 = ar.attnres_fwd_merged(Ub[l], srcs[-1], zb[l], rb, W[l], wl.eps, **kw)
+        r24t = ar.attnres_fwd_merged(Ubt[:, l], srcs[-1], zb[l], rb, W[l], wl.eps, **kw)
+        r32 = ar.attnres_fwd_merged(dec[l], srcs[-1], zb[l], rb, W[l], wl.eps, **kw)
+        torch.cuda.synchronize()
+        print(f"[merged f24 == merged on decoded] l={l} update={update}", flush=True)
+        for a, b, c in zip(r24, r24t, r32):
+            assert torch.equal(a, c) and torch.equal(b, c)
+
+
+@pytest.mark.parametrize("u_format", ["f32", "f24"])
+def test_merged_forward_peaked_softmax(u_format):
     """Pseudo-queries ~ N(0, 0.5): scores of std ~40, nearly one-hot weights,
     so the rescaling exp(m - M) often underflows or is exactly 1."""
-    for e in _chain(9, 4096, 7168, L=24, w_std=0.5, subs=(0, 23)):
+    for e in _chain(9, 4096, 7168, L=24, w_std=0.5, subs=(0, 23), u_format=u_format):
         assert within_tolerance(e), e
         assert e["alpha_max_abs"] <= TOL_ALPHA_ABS
 
@@ -152,6 +237,12 @@ def test_block_route_full_size_T32768():
     forwards (U sub-layer-major) on every token against the oracle's plain
     forward on all 9 sources, element by element."""
     for e in _chain(9, 32768, 7168, L=24, subs=(0, 11, 23), chunk=4096):
+        assert within_tolerance(e), e
+
+
+def test_block_route_full_size_T32768_f24():
+    """The same block with U in the 24-bit format, two sub-layers on every token."""
+    for e in _chain(9, 32768, 7168, L=24, subs=(5, 17), chunk=4096, u_format="f24"):
         assert within_tolerance(e), e
 
 
@@ -263,6 +354,8 @@ def test_empty_batch_is_a_no_op():
     D, L = 7168, 4
     srcs = [torch.empty((0, D), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
     z = torch.empty((L, 0, 3), dtype=torch.float32, device=DEV)
+    U24 = ar.attnres_block_sums(srcs, z, u_format="f24")
+    assert U24.shape == (L, 0, D, 3)
     U = ar.attnres_block_sums(srcs, z)
     assert U.shape == (L, 0, D)
     out, rstd, alpha = ar.attnres_fwd_merged(U[0], torch.empty((0, D), dtype=torch.bfloat16, device=DEV),

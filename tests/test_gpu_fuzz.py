@@ -153,8 +153,8 @@ def test_random_block_route(seed):
     n shared sources for L pseudo-queries, block sums (either U layout), and
     the merged forward of a few sub-layers with the partial sum as the last
     source (in half the cases with the fused update of the partial sum,
-    checked bit for bit), against the oracle's plain forward on all n + 1
-    sources."""
+    checked bit for bit; in half U in the 24-bit format), against the
+    oracle's plain forward on all n + 1 sources."""
     rng = np.random.default_rng(5000 + seed)
     n = int(rng.integers(1, 9))
     N = n + 1
@@ -169,12 +169,13 @@ def test_random_block_route(seed):
     src_h = wl.sources()
     W_h = np.stack([synth.normal_f32(D, seed, 300 + l, w_std) for l in range(L)])
     update = bool(rng.integers(0, 2))  # the fused partial-sum update, out of place
+    u_format = str(rng.choice(["f32", "f24"]))
     print(f"[fuzz block] seed={seed} n={n} T={T} D={D} L={L} eps={eps} w_std={w_std:.3g} layout={layout} "
-          f"token_major={token_major} update={update}", flush=True)
+          f"token_major={token_major} update={update} U {u_format}", flush=True)
     views = _place(to_dev_bf16(src_h), layout, rng)
     W = torch.from_numpy(W_h).to(DEV)
     rb, zb = ar.attnres_block_scores(views[:n], W, eps)
-    U = ar.attnres_block_sums(views[:n], zb, token_major=token_major)
+    U = ar.attnres_block_sums(views[:n], zb, token_major=token_major, u_format=u_format)
     for l in sorted({0, L - 1, int(rng.integers(0, L))}):
         U_l = U[:, l] if token_major else U[l]
         if update:

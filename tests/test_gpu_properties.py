@@ -226,8 +226,9 @@ def test_graph_capture_replays_match_eager(case):
 
 
 def test_graph_capture_block_route_replays_match_eager():
-    """The block-level route (block scores with its query split, block sums,
-    three merged forwards) captured in one HIP graph: every replay, with new
+    """The block-level route (block scores with its query split, block sums in
+    both element formats, three merged forwards from the fp32 sums and one
+    from the 24-bit ones) captured in one HIP graph: every replay, with new
     sources and queries copied in and eager work in between, matches eager
     calls in fresh buffers bit for bit."""
     n, T, D, L = 8, 300, 7168, 24
@@ -238,17 +239,22 @@ def test_graph_capture_block_route_replays_match_eager():
     zb = torch.empty((L, T, n), dtype=torch.float32, device=DEV)
     ws = torch.empty((ar.block_scores_workspace_bytes(L, D),), dtype=torch.uint8, device=DEV)
     U = torch.empty((L, T, D), dtype=torch.float32, device=DEV)
+    U24 = torch.empty((L, T, D, 3), dtype=torch.uint8, device=DEV)
     subs = (0, 11, 23)
     outs = [(torch.empty((T, D), dtype=torch.bfloat16, device=DEV), torch.empty((T, N), device=DEV),
-             torch.empty((T, N), device=DEV)) for _ in subs]
+             torch.empty((T, N), device=DEV)) for _ in range(len(subs) + 1)]
+    l24 = 5
     eps = 1e-6
 
     def step():
         srcs = [s_src[i] for i in range(N)]
         ar.attnres_block_scores(srcs[:n], s_W, eps, rstd=rb, z=zb, workspace=ws)
         ar.attnres_block_sums(srcs[:n], zb, U=U)
+        ar.attnres_block_sums(srcs[:n], zb, U=U24, u_format="f24")
         for l, (o, r, a) in zip(subs, outs):
             ar.attnres_fwd_merged(U[l], srcs[n], zb[l], rb, s_W[l], eps, out=o, rstd=r, alpha=a)
+        o, r, a = outs[-1]
+        ar.attnres_fwd_merged(U24[l24], srcs[n], zb[l24], rb, s_W[l24], eps, out=o, rstd=r, alpha=a)
 
     def inputs(k):
         wk = synth.Workload(f"graph_block_{k}", T=T, N=N, D=D, seed=40 + k)
@@ -275,9 +281,11 @@ def test_graph_capture_block_route_replays_match_eager():
         srcs = [src_k[i] for i in range(N)]
         r_rb, r_zb = ar.attnres_block_scores(srcs[:n], W_k, eps)  # eager, fresh buffers
         r_U = ar.attnres_block_sums(srcs[:n], r_zb)
+        r_U24 = ar.attnres_block_sums(srcs[:n], r_zb, u_format="f24")
         torch.cuda.synchronize()
         assert torch.equal(r_rb, rb) and torch.equal(r_zb, zb) and torch.equal(r_U, U), k
-        for l, (o, r, a) in zip(subs, outs):
-            e_o, e_r, e_a = ar.attnres_fwd_merged(r_U[l], srcs[n], r_zb[l], r_rb, W_k[l], eps)
+        assert torch.equal(r_U24, U24), k
+        for l, (o, r, a), Ue in zip(subs + (l24,), outs, (r_U,) * len(subs) + (r_U24,)):
+            e_o, e_r, e_a = ar.attnres_fwd_merged(Ue[l], srcs[n], r_zb[l], r_rb, W_k[l], eps)
             torch.cuda.synchronize()
             assert torch.equal(_bits(e_o), _bits(o)) and torch.equal(e_r, r) and torch.equal(e_a, a), (k, l)
