@@ -30,9 +30,10 @@ The C entry points, declared in ``include/attnres.h``:
                 forward from its slice of those scores.
     attnres_block_sums / attnres_fwd_merged: from those scores, the part of
                 every sub-layer's weighted sum that the shared sources
-                contribute (fp32, before the softmax normaliser), in one
-                pass; then each sub-layer's forward from its shared sum and
-                the partial sum alone.
+                contribute (summed in fp32, before the softmax normaliser;
+                stored as fp32 or in the 24-bit format), in one pass; then
+                each sub-layer's forward from its shared sum and the partial
+                sum alone.
 """
 from __future__ import annotations
 
