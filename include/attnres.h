@@ -24,7 +24,8 @@
  * only out, rstd and alpha (forward) and dsources, dw (backward).
  *
  * Conventions for every call
- *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float; the
+ *     block sums (attnres_block_sums) as void*, fp32 or 24-bit elements.
  *   - Layouts are row-major: stacked sources/dsources [N][T][D]
  *     (source-major), per-source rows with a pitch (see
  *     attnres_fwd_sources), out/dout [T][D], rstd/alpha [T][N]
