@@ -152,6 +152,7 @@ def test_header_constants_match_binding():
     assert _define("ATTNRES_MAX_SOURCES") == ar.MAX_SOURCES == 9
     assert _define("ATTNRES_MAX_D") == ar.MAX_D
     assert _define("ATTNRES_DW_PARTIALS") == ar.DW_PARTIALS
+    assert _define("ATTNRES_U_F32") == ar.U_F32 == 0 and _define("ATTNRES_U_F24") == ar.U_F24 == 1
     for name in ("SPLIT_MAX_D", "SPLIT_ANY_N_MAX_D", "SPLIT_MIN_N", "SPLIT_TOKENS", "SPLIT_RING", "SPLIT_CHUNK_SPANS",
                  "SPLIT_SPIN_DEFAULT"):
         assert _define("ATTNRES_" + name) == getattr(ar, name)
