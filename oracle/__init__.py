@@ -21,7 +21,10 @@ fp64 ``rms_norm`` and matmul and hand-derived constant-row cases, and the
 forward from given scores (``fwd_scored``) against the plain forward and the
 two-source sigmoid closed form; the block-batched shared sums (``block_sums``)
 and the forward from them (``fwd_merged``) against hand-worked sums, the plain
-forward, and the limits where one side of the softmax takes all the weight.
+forward, and the limits where one side of the softmax takes all the weight;
+the shared sums' 24-bit storage format (``round24``, ``decode24``) against
+hand-worked encodings (ties, carries, subnormals, overflow) and exact rational
+rounding.
 """
 from __future__ import annotations
 
@@ -49,6 +52,10 @@ class Oracle:
             f.argtypes = [i32, i64, i64, vp, vp, f64, vp, vp, vp]
             f.restype = None
         lib.oracle_add_bf16.argtypes = [i64, vp, vp, vp]
+        lib.oracle_round24.argtypes = [i64, vp, vp]
+        lib.oracle_round24.restype = None
+        lib.oracle_decode24.argtypes = [i64, vp, vp]
+        lib.oracle_decode24.restype = None
         lib.oracle_add_bf16.restype = None
         lib.oracle_block_scores.argtypes = [i32, i64, i64, i32, vp, vp, f64, vp, vp]
         lib.oracle_block_scores.restype = None
@@ -68,6 +75,23 @@ class Oracle:
         assert p_bits.shape == y_bits.shape
         out = np.empty_like(p_bits)
         self.lib.oracle_add_bf16(p_bits.size, _p(p_bits), _p(y_bits), _p(out))
+        return out
+
+    def round24(self, x: np.ndarray) -> np.ndarray:
+        """The 24-bit element format of the block sums: x (float32) rounded to
+        16 significant bits, ties to even, kept as the upper three bytes of
+        the fp32 pattern; returns uint8 with a trailing dimension of 3."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape + (3,), dtype=np.uint8)
+        self.lib.oracle_round24(x.size, _p(x), _p(out))
+        return out
+
+    def decode24(self, b: np.ndarray) -> np.ndarray:
+        """float32 values of 24-bit elements ([..., 3] uint8)."""
+        b = np.ascontiguousarray(b, dtype=np.uint8)
+        assert b.shape[-1] == 3
+        out = np.empty(b.shape[:-1], dtype=np.float32)
+        self.lib.oracle_decode24(out.size, _p(b), _p(out))
         return out
 
     def fwd_update(self, src_bits: np.ndarray, p_bits: np.ndarray, y_bits: np.ndarray, w: np.ndarray, eps: float):
@@ -256,6 +280,14 @@ def fwd_merged(U, p_bits, z_given, r_given, w, eps):
 
 def add_bf16(p_bits, y_bits):
     return default().add_bf16(p_bits, y_bits)
+
+
+def round24(x):
+    return default().round24(x)
+
+
+def decode24(b):
+    return default().decode24(b)
 
 
 def fwd_update(src_bits, p_bits, y_bits, w, eps):

@@ -392,3 +392,45 @@ static uint16_t f64_to_bf16_rne(double v) {
 void oracle_add_bf16(int64_t n, const uint16_t* p, const uint16_t* y, uint16_t* out) {
   for (int64_t k = 0; k < n; ++k) out[k] = f64_to_bf16_rne(bf16_to_f64(p[k]) + bf16_to_f64(y[k]));
 }
+
+/* The block sums' 24-bit element format (the library's ATTNRES_U_F24, a
+ * storage choice of the block-level route, not of the pages): a value rounded
+ * to 16 significant bits, nearest, ties to even, in the fp32 exponent range
+ * (below 2^-126 the quantum stays 2^-141, and values that round to 2^128
+ * become infinity), stored as the upper three bytes of the rounded value's
+ * fp32 bit pattern, least significant first.  The rounding is done on the
+ * value, as f64_to_bf16_rne does for bf16, not on the bit pattern. */
+void oracle_round24(int64_t n, const float* x, uint8_t* out) {
+  for (int64_t k = 0; k < n; ++k) {
+    const double v = (double)x[k];
+    float f;
+    if (v != v) {
+      f = x[k];
+    } else {
+      const double a = fabs(v);
+      double r = 0.0;
+      if (a != 0.0) {
+        int e;
+        const double m = frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1 */
+        int keep = 16;                 /* significant bits kept */
+        if (e - 1 < -126) keep -= -126 - (e - 1);
+        r = ldexp(nearbyint(ldexp(m, keep)), e - keep);
+      }
+      f = (float)(signbit(v) ? -r : r); /* exact; 2^128 becomes inf */
+    }
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    out[3 * k] = (uint8_t)(u >> 8);
+    out[3 * k + 1] = (uint8_t)(u >> 16);
+    out[3 * k + 2] = (uint8_t)(u >> 24);
+  }
+}
+
+/* The fp32 value of each 24-bit element: its three bytes as the upper bytes
+ * of an fp32 bit pattern whose low byte is zero. */
+void oracle_decode24(int64_t n, const uint8_t* in, float* out) {
+  for (int64_t k = 0; k < n; ++k) {
+    const uint32_t u = ((uint32_t)in[3 * k] << 8) | ((uint32_t)in[3 * k + 1] << 16) | ((uint32_t)in[3 * k + 2] << 24);
+    memcpy(&out[k], &u, 4);
+  }
+}

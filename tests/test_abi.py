@@ -564,20 +564,20 @@ def test_workspace_macro_matches_binding(tmp_path):
 
 
 def test_decode_u24_reads_the_24_bit_format():
-    """decode_u24 (host logic, CPU tensors here) returns the fp32 value whose
-    upper three bytes the element holds: exactly for values whose low byte is
-    zero, and within 2^-16 relative of the original for rounded values."""
+    """decode_u24 (host logic, CPU tensors here) reads the 24-bit elements as
+    the oracle's decode24 does, on every byte pattern of a random sample and
+    on the oracle's encodings of random values (within 2^-16 relative of the
+    values, infinity where they round past the binary32 range)."""
     import torch
+    import oracle
     rng = np.random.default_rng(3)
-    v = np.concatenate([rng.standard_normal(1000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 1000),
-                        np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -126, 3.0e38], dtype=np.float32)]).astype(np.float32)
-    b = v.view(np.uint32).astype(np.uint64)
-    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFFFF
-    by = np.stack([(r >> 8) & 0xFF, (r >> 16) & 0xFF, r >> 24], -1).astype(np.uint8)
-    d = ar.decode_u24(torch.from_numpy(by)).numpy()
-    assert np.array_equal(d.view(np.uint32), (r & 0xFFFFFF00).astype(np.uint32))
-    fin = np.isfinite(d)
-    assert fin.all()
+    raw = rng.integers(0, 256, (5000, 3)).astype(np.uint8)
+    assert np.array_equal(ar.decode_u24(torch.from_numpy(raw)).numpy().view(np.uint32),
+                          oracle.decode24(raw).view(np.uint32))
+    v = (rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000)).astype(np.float32)
+    enc = oracle.round24(v)
+    d = ar.decode_u24(torch.from_numpy(enc)).numpy()
+    assert np.array_equal(d.view(np.uint32), oracle.decode24(enc).view(np.uint32))
     assert np.all(np.abs(d.astype(np.float64) - v) <= 2.0 ** -16 * np.abs(v.astype(np.float64)))
     with pytest.raises(ValueError):
         ar.decode_u24(torch.zeros((4, 2), dtype=torch.uint8))

@@ -17,10 +17,11 @@ weight through the rescaled sum and the saved alpha.
 
 The 24-bit element format of U (each fp32 sum rounded to nearest even on a
 16-bit significand, three bytes kept): its bytes are checked bit for bit
-against that rounding of the fp32 sums, done here on the host from the
-definition; the merged forward on it bit for bit against the merged forward on
-the decoded values given as fp32; and the chain against the oracle within
-merged_out_bound plus the format's 2^-16 relative error on the shared part.
+against the oracle's encoding (oracle.round24, pinned by hand-worked cases and
+exact rational rounding) of the library's fp32 sums; the merged forward on it
+bit for bit against the merged forward on the decoded values given as fp32;
+and the chain against the oracle within merged_out_bound plus the format's
+2^-16 relative error on the shared part.
 """
 from __future__ import annotations
 
@@ -153,23 +154,14 @@ def test_merged_forward_f24_against_oracle(N, T, D):
         assert within_tolerance(e), e
 
 
-def _rne24_bytes(u32: np.ndarray) -> np.ndarray:
-    """The 24-bit format from its definition: the fp32 bit pattern plus 0x7F
-    plus bit 8 (round to nearest, ties to even, at bit 8), its upper three
-    bytes little-endian.  u32: uint32 bit patterns; returns [..., 3] uint8."""
-    b = u32.astype(np.uint64)
-    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFFFF
-    return np.stack([(r >> 8) & 0xFF, (r >> 16) & 0xFF, r >> 24], axis=-1).astype(np.uint8)
-
-
 @pytest.mark.parametrize("n,T,D,L,tmaj", [(8, 300, 7168, 24, False), (8, 130, 7168, 24, True), (9, 40, 7176, 33, True),
                                           (4, 257, 16384, 16, False), (1, 17, 64, 1, False), (3, 70, 1000, 5, True)],
                          ids=lambda v: str(v))
 def test_block_sums_f24_is_the_rounded_fp32(n, T, D, L, tmaj):
-    """U in the 24-bit format holds exactly the fp32 sums rounded as the format
-    defines (every byte), in both layouts; decode_u24 returns those values;
-    and the decoded sums lie within the fp32 bound plus the format's rounding
-    of the oracle's sums."""
+    """U in the 24-bit format holds exactly the oracle's encoding (oracle.round24)
+    of the library's own fp32 sums, every byte, in both layouts; decode_u24
+    reads them as the oracle's decode24 does; and the decoded sums lie within
+    the fp32 bound plus the format's rounding of the oracle's sums."""
     wl, bits = _sources(n, T, D, seed=4)
     W = _queries(D, L, 7)
     srcs = [to_dev_bf16(bits[i]) for i in range(n)]
@@ -179,13 +171,11 @@ def test_block_sums_f24_is_the_rounded_fp32(n, T, D, L, tmaj):
     Ub = ar.attnres_block_sums(srcs, z, token_major=tmaj, u_format="f24")
     torch.cuda.synchronize()
     assert Ub.dtype == torch.uint8 and Ub.shape == U32.shape + (3,)
-    want = _rne24_bytes(U32.cpu().numpy().view(np.uint32))
+    want = oracle.round24(U32.cpu().numpy())
     got = Ub.cpu().numpy()
     assert np.array_equal(got, want), f"{int((got != want).any(-1).sum())} elements differ"
     dec = ar.decode_u24(Ub)
-    wb = want.astype(np.uint32)
-    r = (wb[..., 0] << 8) | (wb[..., 1] << 16) | (wb[..., 2] << 24)
-    assert np.array_equal(dec.cpu().numpy().view(np.uint32), r)
+    assert np.array_equal(dec.cpu().numpy().view(np.uint32), oracle.decode24(want).view(np.uint32))
     Uo = oracle.block_sums(bits, z.cpu().double().numpy())
     Ur = torch.from_numpy(Uo).to(DEV)
     Ug = _u_rows(dec, tmaj).double()

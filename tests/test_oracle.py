@@ -482,8 +482,84 @@ def pin_fwd_merged(orc):
     return fails
 
 
+U24_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "u24_format.json")
+
+
+def _f32_value(bits: int) -> Fraction:
+    """Exact value of a finite binary32 bit pattern."""
+    sign = -1 if bits & 0x80000000 else 1
+    e, f = (bits >> 23) & 0xFF, bits & 0x7FFFFF
+    if e == 0:
+        return sign * Fraction(f, 1 << 23) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(f, 1 << 23)) * (Fraction(2) ** (e - 127))
+
+
+def _round16(v: Fraction):
+    """v rounded to 16 significant bits, nearest, ties to even, with the
+    quantum 2^-141 below 2^-126; None where it reaches 2^128 (infinity).
+    Worked on exact rationals from the rule, independently of the C route."""
+    a = abs(v)
+    if a == 0:
+        return Fraction(0)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    while Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 15)
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    k = lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
+    r = k * quantum
+    if r >= Fraction(2) ** 128:
+        return None
+    return r if v > 0 else -r
+
+
+def pin_u24_format(orc):
+    """The shared sums' 24-bit storage format: hand-worked encodings and
+    decodings, then exact rational rounding of random binary32 values
+    concentrated on ties, and exactness on values that already fit."""
+    fails = []
+    g = json.load(open(U24_GOLDEN))
+    xs = np.array([int(c["x"], 16) for c in g["round"]], dtype=np.uint32).view(np.float32)
+    got = orc.round24(xs)
+    for c, b in zip(g["round"], got):
+        if bytes(b.tolist()).hex().upper() != c["expect"]:
+            fails.append(f"u24 golden {c['name']}: got {bytes(b.tolist()).hex()} want {c['expect']}")
+    bs = np.array([list(bytes.fromhex(c["bytes"])) for c in g["decode"]], dtype=np.uint8)
+    dec = orc.decode24(bs).view(np.uint32)
+    for c, d in zip(g["decode"], dec.tolist()):
+        if d != int(c["expect"], 16):
+            fails.append(f"u24 decode golden {c['name']}: got {d:08X} want {c['expect']}")
+    rng = np.random.default_rng(23)
+    n = 3000
+    e = np.where(rng.random(n) < 0.1, rng.integers(0, 3, n), rng.integers(1, 255, n)).astype(np.uint32)
+    low = rng.choice(np.array([0x7F, 0x80, 0x81, 0x00, 0xFF], dtype=np.uint32), n)
+    low = np.where(rng.random(n) < 0.3, rng.integers(0, 256, n).astype(np.uint32), low)
+    pat = (rng.integers(0, 2, n).astype(np.uint32) << 31) | (e << 23) | (rng.integers(0, 1 << 15, n).astype(np.uint32) << 8) | low
+    x = pat.view(np.float32)
+    back = orc.decode24(orc.round24(x)).view(np.uint32)
+    for p_, b_ in zip(pat.tolist(), back.tolist()):
+        r = _round16(_f32_value(p_))
+        want = (0x7F800000 | (p_ & 0x80000000)) if r is None else None
+        if want is None:
+            want = int(np.array([float(r)], dtype=np.float32).view(np.uint32)[0])  # r has <= 16 bits: exact
+            if r == 0 and p_ & 0x80000000:
+                want = 0x80000000
+        if b_ != want:
+            fails.append(f"u24 rounding of {p_:08X}: got {b_:08X} want {want:08X}")
+            if len(fails) > 10:
+                break
+    fit = (pat & np.uint32(0xFFFFFF00)) & np.uint32(0xFF7FFFFF)  # zero low byte, finite exponents
+    if not np.array_equal(orc.decode24(orc.round24(fit.view(np.float32))).view(np.uint32), fit):
+        fails.append("u24: a value with 16 significant bits did not survive the round trip")
+    return fails
+
+
 PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update,
-        pin_block_scores, pin_fwd_scored, pin_block_sums, pin_fwd_merged]
+        pin_block_scores, pin_fwd_scored, pin_block_sums, pin_fwd_merged, pin_u24_format]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -563,6 +639,15 @@ MUTANTS = {
     "merged_alpha_shifted_by_given_max": ("alpha[t * N + i] = exp(zs[i] - top) / den;",
                                           "alpha[t * N + i] = exp(zs[i] - m) / den;"),
     "merged_shared_of_token_zero": ("shared * U[t * D + d]", "shared * U[d]"),
+    # the shared sums' 24-bit storage format
+    "u24_truncates": ("r = ldexp(nearbyint(ldexp(m, keep)), e - keep);", "r = ldexp(floor(ldexp(m, keep)), e - keep);"),
+    "u24_ties_away": ("r = ldexp(nearbyint(ldexp(m, keep)), e - keep);", "r = ldexp(round(ldexp(m, keep)), e - keep);"),
+    "u24_fifteen_bits": ("int keep = 16;", "int keep = 15;"),
+    "u24_no_subnormal_quantum": ("        if (e - 1 < -126) keep -= -126 - (e - 1);\n        r = ldexp",
+                                 "        r = ldexp"),
+    "u24_top_byte_wrong": ("out[3 * k + 2] = (uint8_t)(u >> 24);", "out[3 * k + 2] = (uint8_t)(u >> 16);"),
+    "u24_sign_dropped": ("f = (float)(signbit(v) ? -r : r);", "f = (float)r;"),
+    "u24_decode_shifted": ("((uint32_t)in[3 * k] << 8)", "((uint32_t)in[3 * k] << 0)"),
 }
 
 
