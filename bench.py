@@ -650,7 +650,9 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
     block-sums pass (the shared sources' part of every sub-layer's weighted
     sum, fp32 sub-layer-major and token-major, and in the 24-bit element
     format sub-layer-major) and L merged forwards that read only the shared
-    sum and the partial sum.  Median of `reps`
+    sum and the partial sum.  Then a model's block, where the partial sum
+    advances before every sub-layer: L plain forwards with the fused update
+    against block scores, 24-bit block sums and L merged forwards with it.  Median of `reps`
     whole-block timings, each preceded by a 512 MiB cache flush; per-call
     times from the same runs.  Device-side random inputs of the workload's
     scales (values do not change the timing)."""
@@ -697,9 +699,11 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
                 ev.record(l + 3, stream)
         return run
 
-    def timed(fn, last, marks):
+    def timed(fn, last, marks, prep=None):
         tot, parts = [], {m: [] for m in marks}
         for r in range(reps + 2):
+            if prep is not None:
+                prep()
             flush.zero_()
             fn()
             torch.cuda.synchronize()
@@ -724,6 +728,43 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
         del U
         U = None
         torch.cuda.empty_cache()
+    # A model's block: before each sub-layer the partial sum advances by the
+    # previous sub-layer's output, so the pair that matters is 24 plain
+    # forwards with the fused update against block scores + 24-bit block sums
+    # + 24 merged forwards with the fused update.  The partial sum is restored
+    # before each timed block, ahead of the flush.
+    y = (torch.randn((T, D), device=dev, generator=g) * 0.3).to(torch.bfloat16)
+    p0 = srcs[n].clone()
+    p = srcs[n].clone()
+    U = torch.empty((L, T, D, 3), dtype=torch.uint8, device=dev)
+
+    def restore():
+        p.copy_(p0)
+
+    def plain_update():
+        ev.record(0, stream)
+        for l in range(L):
+            ar.attnres_fwd_update(srcs[:n], p, y, W[l], 1e-6, out=out, rstd=rstd, alpha=alpha)
+            ev.record(l + 1, stream)
+
+    def merged_update():
+        ev.record(0, stream)
+        ar.attnres_block_scores(srcs[:n], W, 1e-6, rstd=rb, z=zb, workspace=ws)
+        ev.record(1, stream)
+        ar.attnres_block_sums(srcs[:n], zb, U=U, u_format="f24")
+        ev.record(2, stream)
+        for l in range(L):
+            ar.attnres_fwd_merged(U[l], p, zb[l], rb, W[l], 1e-6, delta=y, out=out, rstd=rstd, alpha=alpha)
+            ev.record(l + 3, stream)
+
+    pu_ms, _ = timed(plain_update, L, [(0, 1)], prep=restore)
+    mu_ms, mup = timed(merged_update, L + 2, [(1, 2), (2, L + 2)], prep=restore)
+    model_block = {"plain_update_block_ms": pu_ms, "merged_f24_update_block_ms": mu_ms,
+                   "vs_plain_update": pu_ms / mu_ms, "block_sums_ms": mup[(1, 2)],
+                   "merged_update_fwd_ms": mup[(2, L + 2)] / L}
+    del U, y, p0, p
+    U = None
+    torch.cuda.empty_cache()
     ev.close()
     scored_ms = (batched_ms - scores_ms) / L
     scores_bytes = T * n * (2 * D + 4) + L * T * n * 4 + 4 * L * D  # sources read; rstd, z written; W read
@@ -767,6 +808,7 @@ def block_batched(ar, torch, dev, T: int = 32768, n: int = 8, L: int = 24, D: in
     f_ms, u_ms = _median_ms(torch, flush, fused, 11), _median_ms(torch, flush, unfused, 11)
     rec["merged_update"] = {"fused_ms": f_ms, "fused_GBps": upd_bytes / f_ms / 1e6, "add_then_merged_ms": u_ms}
     del U, y, p
+    rec["model_block"] = model_block
     rec["reps"] = f"median of {reps}, 512 MiB flush before each block"
     del srcs, W, out, rstd, alpha, rb, zb, ws, flush
     torch.cuda.empty_cache()
