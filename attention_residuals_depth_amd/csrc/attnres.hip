@@ -2415,8 +2415,8 @@ hipError_t run_sums_vpt(hipStream_t st, const SrcRows& rows, const float* z, int
   const int64_t per_launch = (int64_t)(UINT32_MAX / (uint32_t)threads);
   for (int64_t t0 = 0; t0 < T; t0 += per_launch) {
     const int64_t n = T - t0 < per_launch ? T - t0 : per_launch;
-    hipLaunchKernelGGL((block_sums_kernel<NS, VPT, F24>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, rows, z, L, T,
-                       D, t0, U, ls, tp);
+    hipLaunchKernelGGL((block_sums_kernel<NS, VPT, F24>), dim3((unsigned)n), dim3((unsigned)threads), 0, st, rows, z,
+                       L, T, D, t0, U, ls, tp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2446,7 +2446,8 @@ attnres_status block_sums_impl(const uint16_t* const* srcs, int64_t pitch, const
   const bool f24 = u_format == ATTNRES_U_F24;
   if (!aligned(z, 4) || !aligned(U, f24 ? 4 : 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(pitch, T, D)) return ATTNRES_ERR_INVALID_ARGUMENT;
-  // U rows start on 16-byte boundaries and never overlap: sub-layer-major
+  // U rows start on 16-byte (fp32) or 4-byte (24-bit: 12-byte multiples from
+  // a 4-byte aligned base) boundaries and never overlap: sub-layer-major
   // (tp >= D, ls past the last token's row) or token-major (ls >= D, tp past
   // the last sub-layer's row); every offset stays far inside int64.
   if (ls < D || tp < D || ls % 4 != 0 || tp % 4 != 0) return ATTNRES_ERR_INVALID_ARGUMENT;
