@@ -980,12 +980,13 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = fmaf(e[i], f[i][c], acc[c]);
       // the wave's 64 x 32 bytes pass through its LDS stage so that each store
-      // writes one contiguous KiB with the streaming hint (lane j: bytes
-      // [16 j, 16 j + 16) and [1024 + 16 j, ...) of the wave's 2 KiB); the
-      // wave barriers order the stage's writes before other lanes' reads, and
-      // those reads before the next sub-layer's writes.  Two half-vector
-      // streaming stores per lane ran at 2.7 TB/s, the same with the default
-      // policy at 3.1, staged at 4.9 (T = 32768, n = 8, L = 24).
+      // writes one contiguous KiB (lane j: bytes [16 j, 16 j + 16) and
+      // [1024 + 16 j, ...) of the wave's 2 KiB); the wave barriers order the
+      // stage's writes before other lanes' reads, and those reads before the
+      // next sub-layer's writes.  Two half-vector streaming stores per lane
+      // ran at 2.7 TB/s, the same with the default policy at 3.1, staged at
+      // 4.9 with the streaming hint and 1.5-3% faster again with the default
+      // policy (T = 8192 and 32768, n = 8, L = 24, both element formats).
       // (24-bit elements: 24 bytes per lane, 1536 per wave, stored as two
       // runs of 768 bytes, 12 bytes per lane; 3D is a multiple of 12, so a
       // lane's 12 bytes are wholly inside the row or wholly past its end)
@@ -1007,16 +1008,16 @@ __global__ void __launch_bounds__(1024) block_sums_kernel(SrcRows src, const flo
         hi.x = s32[3 * kWave + 3 * lane]; hi.y = s32[3 * kWave + 3 * lane + 1]; hi.z = s32[3 * kWave + 3 * lane + 2];
         wave_sync();
         const uint32_t wb24 = (sl.off[k] >> 4) * 24u - 24u * (uint32_t)lane;  // the wave's first vector, bytes
-        __builtin_amdgcn_raw_buffer_store_b96(lo, ru, wb24 + 12u * (uint32_t)lane, 0, kAuxStreamStore);
-        __builtin_amdgcn_raw_buffer_store_b96(hi, ru, wb24 + 768u + 12u * (uint32_t)lane, 0, kAuxStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b96(lo, ru, wb24 + 12u * (uint32_t)lane, 0, kAuxDefault);
+        __builtin_amdgcn_raw_buffer_store_b96(hi, ru, wb24 + 768u + 12u * (uint32_t)lane, 0, kAuxDefault);
       } else {
         st[2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         st[2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         wave_sync();
         const float4 lo = st[lane], hi = st[kWave + lane];
         wave_sync();
-        bstore<kAuxStreamStore>(ru, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
-        bstore<kAuxStreamStore>(ru, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
+        bstore(ru, wbase + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, lo));
+        bstore(ru, wbase + 1024u + 16u * (uint32_t)lane, __builtin_bit_cast(uint4, hi));
       }
     }
   }
