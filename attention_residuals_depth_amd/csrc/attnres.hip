@@ -1211,6 +1211,40 @@ __global__ void __launch_bounds__(1024) fwd_merged_kernel(
 // (contiguous per-workgroup ranges measured 2-7% slower on MI355X: the HBM
 // accesses of 256 separate streams per source are less local).
 
+// Softmax backward, dz_i = alpha_i (da_i - s) with s = sum_j alpha_j da_j
+// (da_i = g.x_i), evaluated without cancellation.  When one source holds
+// nearly all the weight, s agrees with that source's da_i to within its
+// fp32 rounding, and da_i - s formed directly loses the whole difference
+// (alpha_m = 1 - 1e-10: the difference is 1e-10 of da_m, below an ulp) --
+// and with it that source's dz, which carries as much of dw as the other
+// sources' together.  With m the source of the largest weight (the first
+// such), e_j = da_j - da_m and s' = sum_j alpha_j e_j, the same quantity is
+// e_i - s' (the weights sum to 1), where no term cancels a much larger one.
+// The da_i are the token's totals, the same in every lane.
+// The weights are non-negative, so their bit patterns order like their
+// values: the search for m runs on the scalar unit (the weights and the
+// totals are wave-uniform), carrying da_m along instead of indexing by m.
+template <int N>
+__device__ __forceinline__ void softmax_bwd(const float (&al)[N], const float (&da)[N], float (&dz)[N]) {
+  uint32_t best = __builtin_bit_cast(uint32_t, al[0]);
+  float dam = da[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, al[i]);
+    const bool gt = b > best;  // strictly: the first of equal weights stays m
+    best = gt ? b : best;
+    dam = gt ? da[i] : dam;
+  }
+  float e[N], sp = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    e[i] = da[i] - dam;
+    sp = fmaf(al[i], e[i], sp);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) dz[i] = al[i] * (e[i] - sp);
+}
+
 struct BwdCtx {
   int64_t T;
   int32_t D;
@@ -1302,18 +1336,18 @@ __device__ __forceinline__ void bwd_token(uint4 (&x)[N][VPT], uint4 (&g)[VPT], f
     for (int i = 0; i < N; ++i) opaque(x[i][k]);
   }
 
-  // softmax backward: s = sum_j alpha_j da_j; dz_i = alpha_i (da_i - s)
-  float al[N], c1[N], kx[N];
-  float s = 0.f;
+  // softmax backward: dz_i = alpha_i (da_i - sum_j alpha_j da_j), da_i = part[i]
+  float al[N], c1[N], kx[N], da[N], dzv[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     al[i] = lane_value(sa, i);
-    s = fmaf(al[i], part[i], s);
+    da[i] = part[i];
   }
+  softmax_bwd<N>(al, da, dzv);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float rs = lane_value(sr, i);
-    const float dz = al[i] * (part[i] - s);
+    const float dz = dzv[i];
     const float z = rs * part[N + i];
     // dx_id = alpha_i g_d + c1 (w_d - kx x_id): c1 = dz rstd, kx = z rstd / D.
     // The bracket is formed first, so no intermediate carries rstd^2 (with
@@ -1827,19 +1861,18 @@ __global__ void __launch_bounds__(kSpThreads) bwd_split_kernel(SplitArgs a) {
 
   // softmax backward (every lane evaluates the N-value formulas, as the other kernels)
   // (the side's two waves hold the same token: these values are wave-uniform)
-  float al[N], c1[N], kx[N], da[N];
-  float s = 0.f;
+  float al[N], c1[N], kx[N], da[N], dzv[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     al[i] = lane_value(sa, i);
     da[i] = uniform(tot[side][i]);
-    s = fmaf(al[i], da[i], s);
   }
+  softmax_bwd<N>(al, da, dzv);
   const float inv_d = 1.0f / (float)D;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float rs = lane_value(sr, i);
-    const float dz = al[i] * (da[i] - s);
+    const float dz = dzv[i];
     const float z = rs * uniform(tot[side][N + i]);
     // dx_id = alpha_i g_d + c1 (w_d - kx x_id): the bracket is formed first, so
     // no intermediate carries rstd^2 (see the plain backward)

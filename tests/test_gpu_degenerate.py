@@ -9,7 +9,10 @@
   (dw, a sum over all tokens, is NaN on both sides).
 - Sources scaled by 2^+-50 (exact in bf16): mean squares of 1e-30 .. 1e30 stay
   inside the fp32 range the kernels accumulate in, so the results match the
-  oracle at the usual tolerances, also with eps = 0."""
+  oracle at the usual tolerances, also with eps = 0.
+- Nearly one-hot weights in every token of a small batch: dw then hinges on the
+  dominant source's dz, a difference of 1e-10 of its da, which the softmax
+  backward must not lose to cancellation."""
 from __future__ import annotations
 
 import numpy as np
@@ -108,3 +111,31 @@ def test_magnitudes_across_the_fp32_range(eps):
     if eps == 0.0:
         _, _, alpha_unscaled = oracle.fwd(base, wl.w(), 0.0)
         assert float(np.max(np.abs(gpu["alpha"] - alpha_unscaled))) <= TOL_ALPHA_ABS
+
+
+@pytest.mark.parametrize("name,N,T,D,eps,seed", [("onehot82", 9, 8, 7168, 1e-6, 82), ("fuzz651", 3, 5, 12288, 0.0, 651)],
+                         ids=["split_backward_N9", "one_token_backward_N3_D12288"])
+def test_backward_nearly_one_hot_softmax(name, N, T, D, eps, seed):
+    """Every token's weights nearly one-hot (the peaked workload's queries): the
+    dominant source's dz is alpha_m (da_m - s) with da_m - s about 1e-10 of
+    da_m, and it carries as much of dw as the other sources' dz together.
+    Formed directly in fp32 it vanished and dw came out 71% off; the kernels
+    form it from differences to the dominant source's da.  dw against the
+    oracle well inside the operator's 1e-2, and dsources within tolerance, on
+    the split backward (N = 9) and the one-token backward (D > 8192)."""
+    wl = synth.Workload(name, T=T, N=N, D=D, eps=eps, seed=seed, kind="depth", w_std=0.5)
+    src_h, w_h, dout_h = wl.sources(), wl.w(), wl.dout()
+    print(f"[one-hot] {name} N={N} T={T} D={D} eps={eps}", flush=True)
+    src = to_dev_bf16(src_h)
+    w = torch.from_numpy(w_h).to(DEV)
+    out, rstd, alpha = ar.attnres_fwd(src, w, eps)
+    dsrc, dw = ar.attnres_bwd(to_dev_bf16(dout_h), src, w, rstd, alpha)
+    torch.cuda.synchronize()
+    o_out, o_rstd, o_alpha = oracle.fwd(src_h, w_h, eps)
+    o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
+    assert float(np.min(np.max(o_alpha, axis=1))) > 1 - 1e-6  # the case is what it claims to be
+    e_dw = rel_l2(dw.cpu().double().numpy(), o_dw)
+    e_ds = rel_l2(bf16_dev_to_f64(dsrc), o_dsrc)
+    print(f"[one-hot]   dw rel-L2 {e_dw:.3e}, dsrc rel-L2 {e_ds:.3e}", flush=True)
+    assert e_dw <= 1e-3
+    assert e_ds <= TOL_DSRC_REL_L2
