@@ -187,9 +187,11 @@ def sums_bound(x, z) -> torch.Tensor:
     return 2.0 * b
 
 
-def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu) -> torch.Tensor:
+def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu, out_bits: int = 16) -> torch.Tensor:
     """Per-element bound on |dsrc_gpu - dsrc_ref| for the overwriting backward.
-    x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors."""
+    x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors.  out_bits: the
+    gradient's storage, 16 (bf16: half its ulp) or 32 (fp32: half an fp32
+    ulp of the result)."""
     N, n, D = x.shape
     u = U32
     r = r_ref.T[:, :, None]                   # [N][n][1]
@@ -225,7 +227,10 @@ def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu) -> torch
     b += x.abs() * (c1.abs() * e_k)
     b += g.abs()[None] * (dal + 2 * u * a.abs())
     b *= 2.0
-    b += 0.5 * bf16_ulp(torch.maximum(dsrc_ref.abs(), dsrc_gpu.abs()))
+    if out_bits == 16:
+        b += 0.5 * bf16_ulp(torch.maximum(dsrc_ref.abs(), dsrc_gpu.abs()))
+    else:
+        b += u * torch.maximum(dsrc_ref.abs(), dsrc_gpu.abs())
     return b
 
 

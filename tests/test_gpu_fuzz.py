@@ -17,8 +17,8 @@ import torch
 import attention_residuals_depth_amd as ar
 import oracle
 import synth
-from parity import (DEV, TOL_ALPHA_ABS, TOL_DSRC_REL_L2, TOL_DW_REL_L2, TOL_OUT_REL_L2, TOL_RSTD_REL,
-                    bf16_dev_to_f64, rel_l2, to_dev_bf16)
+from parity import (DEV, TOL_ALPHA_ABS, TOL_DSRC_REL_L2, TOL_DW_REL_L2, TOL_OUT_REL_L2, TOL_RSTD_REL, U32, _t,
+                    bf16_dev_to_f64, dsrc_bound, rel_l2, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def _zeros_like_layout(views, dtype=None):
     return out
 
 
-@pytest.mark.parametrize("seed", range(96))
+@pytest.mark.parametrize("seed", list(range(96)) + [651, 737, 753, 755, 994])  # + cases found by wider sweeps
 def test_random_configuration(seed):
     rng = np.random.default_rng(1000 + seed)
     N = int(rng.integers(1, 10))
@@ -117,7 +117,19 @@ def test_random_configuration(seed):
         torch.cuda.synchronize()
         got = np.stack([g.double().cpu().numpy() for g in grads])
         expect = o_dsrc if prior is None else np.stack([p.double().cpu().numpy() for p in prior]) + o_dsrc
-        assert rel_l2(got, expect) <= 1e-5  # fp32 gradients: no bf16 rounding
+        # fp32 gradients: no bf16 rounding, so each element within the bound of
+        # the kernel's fp32 arithmetic (the accumulating mode adds one rounding
+        # of the sum); the whole tensor far inside the operator's 1e-2
+        xs, gs = _t(src_h, DEV), _t(dout_h, DEV)
+        bd = dsrc_bound(xs, gs, _t(w_h, DEV), _t(o_rstd, DEV), rstd.double(), _t(o_alpha, DEV),
+                        alpha.double(), _t(o_dsrc, DEV), _t(got, DEV) - (0 if prior is None else _t(expect - o_dsrc, DEV)),
+                        out_bits=32)
+        if prior is not None:
+            bd = bd + U32 * _t(np.abs(expect), DEV)
+        ratio = float(((_t(got, DEV) - _t(expect, DEV)).abs() / bd).max())
+        print(f"[fuzz]   fp32 gradients: max err/bound {ratio:.3e}, rel-L2 {rel_l2(got, expect):.3e}", flush=True)
+        assert ratio <= 1.0, ratio
+        assert rel_l2(got, expect) <= 1e-4
         if np.linalg.norm(o_dw) > 0:
             assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
     if mode in ("plain", "accumulate"):
