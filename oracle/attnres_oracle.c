@@ -24,6 +24,7 @@
  *   da_i  = sum_d g_d x_id
  *   s     = sum_i alpha_i da_i
  *   dz_i  = alpha_i (da_i - s)                     softmax Jacobian
+ *         = alpha_i sum_j alpha_j (da_i - da_j)    (the weights sum to 1)
  *   dx_id = alpha_i g_d + dz_i r_i (w_d - z_i r_i x_id / D)
  *   dw_d  = sum over tokens and sources of dz_i r_i x_id
  *
@@ -80,9 +81,14 @@ static void token_backward(int N, int64_t D, const double* const* x, const doubl
     for (int64_t d = 0; d < D; ++d) acc += g[d] * x[i][d];
     da[i] = acc;
   }
-  double s = 0.0;
-  for (int i = 0; i < N; ++i) s += alpha[i] * da[i];
-  for (int i = 0; i < N; ++i) dz[i] = alpha[i] * (da[i] - s);
+  /* the softmax Jacobian in its second form above: when one weight is within
+   * a rounding of 1, da_i - s for that source lies below the rounding of da_i
+   * and the first form returns 0 for it, while this one keeps its value */
+  for (int i = 0; i < N; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < N; ++j) acc += alpha[j] * (da[i] - da[j]);
+    dz[i] = alpha[i] * acc;
+  }
   for (int i = 0; i < N; ++i)
     for (int64_t d = 0; d < D; ++d)
       dx[i][d] = alpha[i] * g[d] + dz[i] * r[i] * (w[d] - z[i] * r[i] * x[i][d] / (double)D);

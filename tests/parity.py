@@ -208,13 +208,14 @@ def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu, out_bits
     del wxt
     s = (a * da).sum(0, keepdim=True)
     e_s = (dal * da.abs() + a * e_da + N * u * a * da.abs()).sum(0, keepdim=True)
-    dz = a * (da - s)
+    dms = (a[None] * (da[:, None] - da[None])).sum(1)  # da_i - s, formed without cancellation
+    dz = a * dms
     # the kernels form da_i - s as e_i - sum_j a_j e_j with e_j = da_j - da_m
     # (m: the source of the largest weight), which adds the error of da_m and
     # the roundings of the e_j, at most (N + 2) u max_j |da_j|, to each term
     da_max = da.abs().max(0, keepdim=True).values
     e_m = e_da.max(0, keepdim=True).values + (N + 2) * u * da_max
-    e_dz = dal * (da - s).abs() + a * (e_da + e_s + e_m) + 2 * u * dz.abs()
+    e_dz = dal * dms.abs() + a * (e_da + e_s + e_m) + 2 * u * dz.abs()
     c1 = dz * r
     e_c1 = e_dz * r + dz.abs() * dr + u * c1.abs()
     z = r * wx

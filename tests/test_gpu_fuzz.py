@@ -59,7 +59,7 @@ def _zeros_like_layout(views, dtype=None):
     return out
 
 
-@pytest.mark.parametrize("seed", list(range(96)) + [651, 737, 753, 755, 994])  # + cases found by wider sweeps
+@pytest.mark.parametrize("seed", list(range(96)) + [651, 737, 753, 755, 994, 1902, 3052])  # + wider sweeps' finds
 def test_random_configuration(seed):
     rng = np.random.default_rng(1000 + seed)
     N = int(rng.integers(1, 10))

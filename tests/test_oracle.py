@@ -482,6 +482,31 @@ def pin_fwd_merged(orc):
     return fails
 
 
+def pin_softmax_bwd_one_hot(orc):
+    """A token whose weights are one-hot to within fp64 rounding.  Two sources,
+    D = 2, eps = 0: x_0 = (1, 0), x_1 = (0, 2) normalise to (sqrt 2, 0) and
+    (0, sqrt 2); with w = (0, 100 / sqrt 2) the scores are 0 and 100, so
+    alpha_0 = 1 / (1 + e^100) (3.7e-44) and alpha_1 = 1 - alpha_0 (1.0 in
+    fp64).  With g = (3, 1), da = (3, 2), and the softmax Jacobian gives
+    dz_0 = alpha_0 alpha_1 (da_0 - da_1) = -dz_1, so
+    dw = sum_i dz_i r_i x_i = sqrt 2 alpha_0 alpha_1 (1, -1): the dominant
+    source's dz must not vanish although da_1 - s is far below da_1's
+    rounding."""
+    fails = []
+    x = np.array([[[1.0, 0.0]], [[0.0, 2.0]]])
+    w = np.array([0.0, 100.0 / math.sqrt(2.0)])
+    g = np.array([[3.0, 1.0]])
+    _, _, alpha = orc.fwd_f64(x, w, 0.0)
+    _, dw = orc.bwd_f64(x, w, 0.0, g)
+    a0 = 1.0 / (1.0 + math.exp(100.0))
+    want = math.sqrt(2.0) * a0 * (1.0 - a0) * np.array([1.0, -1.0])
+    if not (abs(alpha[0, 0] - a0) <= 1e-12 * a0 and alpha[0, 1] == 1.0):
+        fails.append(f"one-hot weights: {alpha}")
+    if not np.allclose(dw, want, rtol=1e-12, atol=0.0):
+        fails.append(f"one-hot softmax backward: dw {dw} want {want}")
+    return fails
+
+
 U24_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "u24_format.json")
 
 
@@ -559,7 +584,7 @@ def pin_u24_format(orc):
 
 
 PINS = [pin_golden, pin_torch_route, pin_finite_differences, pin_invariants, pin_bf16_entry, pin_partial_sum_update,
-        pin_block_scores, pin_fwd_scored, pin_block_sums, pin_fwd_merged, pin_u24_format]
+        pin_block_scores, pin_fwd_scored, pin_block_sums, pin_fwd_merged, pin_u24_format, pin_softmax_bwd_one_hot]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -579,7 +604,7 @@ MUTANTS = {
     "score_unnormalised": ("dot += w[d] * (r[i] * x[i][d]);", "dot += w[d] * x[i][d];"),
     "no_max_subtraction": ("alpha[i] = exp(z[i] - m) / den;", "alpha[i] = exp(z[i]) / den * exp(-m);"),
     "values_normalised": ("acc += alpha[i] * x[i][d];", "acc += alpha[i] * r[i] * x[i][d];"),
-    "softmax_bwd_sign": ("dz[i] = alpha[i] * (da[i] - s);", "dz[i] = alpha[i] * (s - da[i]);"),
+    "softmax_bwd_sign": ("acc += alpha[j] * (da[i] - da[j]);", "acc += alpha[j] * (da[j] - da[i]);"),
     "direct_term_dropped": ("dx[i][d] = alpha[i] * g[d] + dz[i]", "dx[i][d] = dz[i]"),
     "rstd_term_dropped": ("(w[d] - z[i] * r[i] * x[i][d] / (double)D)", "(w[d])"),
     "dw_missing_rstd": ("dw[d] += dz[i] * r[i] * x[i][d];", "dw[d] += dz[i] * x[i][d];"),
@@ -597,8 +622,9 @@ MUTANTS = {
                                 "for (int i = 1; i < N; ++i) den += exp(z[i] - m);"),
     "weighted_sum_skips_first": ("for (int i = 0; i < N; ++i) acc += alpha[i] * x[i][d];",
                                  "for (int i = 1; i < N; ++i) acc += alpha[i] * x[i][d];"),
-    "softmax_bwd_unweighted_mean": ("for (int i = 0; i < N; ++i) s += alpha[i] * da[i];",
-                                    "for (int i = 0; i < N; ++i) s += da[i] / N;"),
+    "softmax_bwd_unweighted_mean": ("acc += alpha[j] * (da[i] - da[j]);", "acc += (da[i] - da[j]) / N;"),
+    "softmax_jacobian_first_form": ("for (int j = 0; j < N; ++j) acc += alpha[j] * (da[i] - da[j]);\n    dz[i] = alpha[i] * acc;",
+                                    "for (int j = 0; j < N; ++j) acc += alpha[j] * da[j];\n    dz[i] = alpha[i] * (da[i] - acc);"),
     "mean_abs_not_square": ("for (int64_t d = 0; d < D; ++d) ss += x[i][d] * x[i][d];",
                             "for (int64_t d = 0; d < D; ++d) ss += fabs(x[i][d]);"),
     "dw_drops_last_chunk": ("for (int64_t c = 0; c < nchunk; ++c)\n    for (int64_t d = 0; d < D; ++d) dw[d] += part",
