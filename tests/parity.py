@@ -187,11 +187,10 @@ def sums_bound(x, z) -> torch.Tensor:
     return 2.0 * b
 
 
-def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu, out_bits: int = 16) -> torch.Tensor:
-    """Per-element bound on |dsrc_gpu - dsrc_ref| for the overwriting backward.
-    x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors.  out_bits: the
-    gradient's storage, 16 (bf16: half its ulp) or 32 (fp32: half an fp32
-    ulp of the result)."""
+def _bwd_coefficients(x, g, w, r_ref, r_gpu, a_ref, a_gpu):
+    """The backward's per-token coefficients and bounds on their errors, from
+    the reference and the GPU's saved rstd and alpha (their difference covers
+    the saved state's own fp32 rounding and underflow)."""
     N, n, D = x.shape
     u = U32
     r = r_ref.T[:, :, None]                   # [N][n][1]
@@ -222,6 +221,28 @@ def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu, out_bits
     e_z = dr * wx.abs() + r * e_wx + u * z.abs()
     k = z * r / D
     e_k = (e_z * r + z.abs() * dr) / D + 2 * u * k.abs()
+    return dict(u=u, N=N, n=n, D=D, a=a, dal=dal, c1=c1, e_c1=e_c1, k=k, e_k=e_k)
+
+
+def dw_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu) -> torch.Tensor:
+    """Per-element bound on |dw_gpu - dw_ref|: dw = sum over tokens and sources
+    of c1 x (c1 = dz rstd), each term off by at most e_c1 |x| plus its own
+    rounding, and the fp32 sums over the n N terms add n N u sum |c1 x|;
+    doubled.  x [N][n][D] and the rest as dsrc_bound; float64 tensors."""
+    c = _bwd_coefficients(x, g, w, r_ref, r_gpu, a_ref, a_gpu)
+    ax = x.abs()
+    cx = (c["c1"].abs() * ax).sum((0, 1))
+    b = (c["e_c1"] * ax).sum((0, 1)) + (1 + c["N"] * c["n"]) * c["u"] * cx
+    return 2.0 * b
+
+
+def dsrc_bound(x, g, w, r_ref, r_gpu, a_ref, a_gpu, dsrc_ref, dsrc_gpu, out_bits: int = 16) -> torch.Tensor:
+    """Per-element bound on |dsrc_gpu - dsrc_ref| for the overwriting backward.
+    x [N][n][D], g [n][D], w [D], r/a [n][N]; float64 tensors.  out_bits: the
+    gradient's storage, 16 (bf16: half its ulp) or 32 (fp32: half an fp32
+    ulp of the result)."""
+    c = _bwd_coefficients(x, g, w, r_ref, r_gpu, a_ref, a_gpu)
+    u, a, dal, c1, e_c1, k, e_k = c["u"], c["a"], c["dal"], c["c1"], c["e_c1"], c["k"], c["e_k"]
     # per element: 2 (|da| |g| + u |a g| + e_c1 |inner| + |c1| (e_k |x| + u |inner|) + u (|a g| + |c1 inner|))
     inner = (w[None, None, :] - k * x).abs_()
     b = inner * (e_c1 + 2 * u * c1.abs())

@@ -18,7 +18,7 @@ import attention_residuals_depth_amd as ar
 import oracle
 import synth
 from parity import (DEV, TOL_ALPHA_ABS, TOL_DSRC_REL_L2, TOL_DW_REL_L2, TOL_OUT_REL_L2, TOL_RSTD_REL, U32, _t,
-                    bf16_dev_to_f64, dsrc_bound, rel_l2, to_dev_bf16)
+                    bf16_dev_to_f64, dsrc_bound, dw_bound, rel_l2, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,25 @@ def _place(src: torch.Tensor, layout: str, rng):
     return [buf[i, :, :D] for i in range(N)]
 
 
+def _dw_ok(dw, o_dw, src_h, dout_h, w_h, o_rstd, rstd, o_alpha, alpha) -> bool:
+    """dw within the operator's relative 1e-2 of the oracle's (near zero where
+    the oracle's is zero); or, where the
+    derived bound (parity.dw_bound) is itself at least 1e-2 of the oracle's dw
+    -- every term of dw rests on weights that the saved fp32 alpha rounds or
+    flushes to zero (a token one-hot beyond fp32's range) -- every element
+    within that bound."""
+    g = dw.cpu().double().numpy()
+    if np.linalg.norm(o_dw) == 0:
+        return float(np.max(np.abs(g), initial=0.0)) <= 1e-6
+    if rel_l2(g, o_dw) <= TOL_DW_REL_L2:
+        return True
+    b = dw_bound(_t(src_h, DEV), _t(dout_h, DEV), _t(w_h, DEV), _t(o_rstd, DEV), rstd.double(), _t(o_alpha, DEV),
+                 alpha.double()).cpu().numpy()
+    print(f"[fuzz]   dw: rel-L2 {rel_l2(g, o_dw):.3e}; |bound| / |dw| {np.linalg.norm(b) / np.linalg.norm(o_dw):.3e}, "
+          f"max err/bound {float(np.max(np.abs(g - o_dw) / np.maximum(b, 1e-300))):.3e}", flush=True)
+    return bool(np.linalg.norm(b) >= TOL_DW_REL_L2 * np.linalg.norm(o_dw) and np.all(np.abs(g - o_dw) <= b))
+
+
 def _zeros_like_layout(views, dtype=None):
     """Zero gradients in the layout of the source views (same row pitch), in
     the sources' dtype or the given one."""
@@ -59,7 +78,7 @@ def _zeros_like_layout(views, dtype=None):
     return out
 
 
-@pytest.mark.parametrize("seed", list(range(96)) + [651, 737, 753, 755, 994, 1902, 3052])  # + wider sweeps' finds
+@pytest.mark.parametrize("seed", list(range(96)) + [651, 737, 753, 755, 994, 1902, 3052, 3699, 4057])  # + wider sweeps' finds
 def test_random_configuration(seed):
     rng = np.random.default_rng(1000 + seed)
     N = int(rng.integers(1, 10))
@@ -130,8 +149,7 @@ def test_random_configuration(seed):
         print(f"[fuzz]   fp32 gradients: max err/bound {ratio:.3e}, rel-L2 {rel_l2(got, expect):.3e}", flush=True)
         assert ratio <= 1.0, ratio
         assert rel_l2(got, expect) <= 1e-4
-        if np.linalg.norm(o_dw) > 0:
-            assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
+        assert _dw_ok(dw, o_dw, src_h, dout_h, w_h, o_rstd, rstd, o_alpha, alpha)
     if mode in ("plain", "accumulate"):
         o_dsrc, o_dw = oracle.bwd(src_h, w_h, eps, dout_h)
         if layout == "stacked":
@@ -153,10 +171,7 @@ def test_random_configuration(seed):
             expect = o_dsrc if prior_h is None else oracle.bf16_to_f64(prior_h) + o_dsrc
         torch.cuda.synchronize()
         assert rel_l2(got, expect) <= TOL_DSRC_REL_L2
-        if np.linalg.norm(o_dw) > 0:
-            assert rel_l2(dw.cpu().double().numpy(), o_dw) <= TOL_DW_REL_L2
-        else:
-            assert float(np.max(np.abs(dw.cpu().double().numpy()))) <= 1e-6
+        assert _dw_ok(dw, o_dw, src_h, dout_h, w_h, o_rstd, rstd, o_alpha, alpha)
 
 
 @pytest.mark.parametrize("seed", range(32))
