@@ -684,6 +684,27 @@ constexpr int kBsTiles = ATTNRES_BS_TILES;        // 16-row tiles per wave
 constexpr int kBsWaveRows = kBsTiles * 16;        // 64
 constexpr int kBsRows = kBsWaves * kBsWaveRows;   // 256 tokens per workgroup
 constexpr int kBsChunk = 4;                       // k-steps per fresh accumulator (even: see the loop)
+// A operand staged through LDS (the default): a wave's global loads read 8
+// rows x 128 bytes each -- whole lines -- into registers, the wave writes
+// them to its own LDS slots, and the MFMA operands (16 rows x 16 bytes per
+// lane group) are read back from there.  Loaded straight into the operand
+// layout, each load instruction touches 16 rows x 64 bytes: half lines.
+#ifndef ATTNRES_BS_LDS
+#define ATTNRES_BS_LDS 1
+#endif
+// the staged loads consume whole lines, so they carry the streaming hint
+// (0.85 against 0.91 ms with the default policy at T = 32768, n = 8, L = 24)
+#ifndef ATTNRES_BS_LDS_AUX
+#define ATTNRES_BS_LDS_AUX 2
+#endif
+// two waves per SIMD (<= 256 registers) keep a second wave's loads in flight
+// while one computes
+#ifndef ATTNRES_BS_WAVES_PER_EU
+#define ATTNRES_BS_WAVES_PER_EU __attribute__((amdgpu_waves_per_eu(2)))
+#endif
+constexpr int kBsStageSteps = 2;                        // k-steps per stage: 64 channels, 128 bytes per row
+constexpr int kBsStageLoads = kBsWaveRows * 8 / kWave;  // 16-byte loads per lane per stage (8 rows per load)
+constexpr int kBsLdsPitch = 9;                          // uint4 slots per staged row: 8 + 1 to spread the banks
 
 __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restrict__ W, int32_t L, int32_t D,
                                                             int32_t Lpad, int32_t Dpad, uint16_t* __restrict__ Wp) {
@@ -709,15 +730,16 @@ __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restr
   Wp[(base + 2 * ctl * kWave) * 8 + e] = __builtin_bit_cast(uint16_t, lo);
 }
 
-// Loads of one k-step: this lane's 16 bytes of each of its four rows (A) and
-// of each query part of each column tile (B).
+// Loads of one k-step without the LDS stage (ATTNRES_BS_LDS = 0): this lane's
+// 16 bytes of each of its four rows (A) and of each query part of each column
+// tile (B).
 template <int CT>
 __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3], __amdgpu_buffer_rsrc_t ra,
                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&roff)[kBsTiles], int s, int q,
                                         int r, int32_t D, int32_t Lpad) {
   const int ch = 32 * s + 8 * q;  // this lane's first channel
   const uint32_t kb = (uint32_t)ch * 2u;
-  // default policy: a k-step reads 64 of a row's 128-byte line, and the L2
+  // default policy here: a k-step reads 64 of a row's 128-byte line, and the L2
   // keeps the line for the next k-step; with the streaming hint it was often
   // gone by then and fetched again (1.67x the algorithmic bytes, 1.50 against
   // 1.37 ms at T = 32768, n = 8, L = 24)
@@ -726,6 +748,18 @@ __device__ __forceinline__ void bs_load(uint4 (&a)[kBsTiles], uint4 (&b)[CT][3],
   // the parts in the B operand's lane order (split_queries_kernel); column
   // tiles past Lpad (CT > Lpad / 16) read whatever follows, or zeros past the
   // end, and their scores are never stored
+  const int ctl = Lpad / 16;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      b[c][p] = bload(rb, (uint32_t)((((s * 3 + p) * ctl + c) * kWave + q * 16 + r) * 16));
+}
+
+// The B operands of one k-step (the A operands come from LDS).
+template <int CT>
+__device__ __forceinline__ void bs_load_b(uint4 (&b)[CT][3], __amdgpu_buffer_rsrc_t rb, int s, int q, int r,
+                                          int32_t Lpad) {
   const int ctl = Lpad / 16;
 #pragma unroll
   for (int c = 0; c < CT; ++c)
@@ -768,11 +802,11 @@ __device__ __forceinline__ void bs_step(const uint4 (&a)[kBsTiles], const uint4 
 // of squares, and z = rstd * dot is formed in fp64 and rounded once.  With
 // chunks of 16 k-steps and one accumulator the scores of a peaked block were
 // off by up to ~5e-5 (a few ulps), enough to move a weight by 1e-5.
-template <int CT>  // query column tiles: L <= 16 * CT
-__global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t T, int32_t D, float eps, int32_t n,
-                                                           const uint16_t* __restrict__ Wp, int32_t L, int32_t Lpad,
-                                                           int32_t Dpad, int64_t wg_per_source,
-                                                           float* __restrict__ rstd_out, float* __restrict__ z_out) {
+template <int CT, bool AHEAD>  // query column tiles: L <= 16 * CT; AHEAD: see the stage loop
+__device__ __forceinline__ void block_scores_body(const SrcRows& src, int64_t T, int32_t D, float eps, int32_t n,
+                                                  const uint16_t* __restrict__ Wp, int32_t L, int32_t Lpad,
+                                                  int32_t Dpad, int64_t wg_per_source, float* __restrict__ rstd_out,
+                                                  float* __restrict__ z_out) {
   const int wave = wave_id(), lane = lane_id();
   const int r = lane & 15, q = lane >> 4;
   const int i = (int)(blockIdx.x / wg_per_source);
@@ -818,13 +852,67 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
       }
     }
   };
-  // One register set per k-step, loaded right before its matrix ops (the
-  // default): with the B operands in lane order this measured 3% faster than
+  // The LDS-staged loop is the default: 0.81 against 0.99-1.02 ms for the
+  // operands loaded straight into registers at T = 32768, n = 8, L = 24 (and
+  // 0.71 against 0.94-0.98 at L = 16).  Of the direct loops, one register set
+  // per k-step, loaded right before its matrix ops, measured 3% faster than
   // two sets alternating (the loads of step s + 1 in flight while step s runs,
   // ATTNRES_BS_PREFETCH = 1), whose extra registers cost more than the
   // overlap gained; the other waves of the CU cover the load latency.
   const int S = Dpad / 32;
-#if !ATTNRES_BS_PREFETCH
+#if ATTNRES_BS_LDS
+  // this wave's slots: row j of the wave at [j * kBsLdsPitch, + 8); only this
+  // wave touches them, so wave-level ordering suffices (no workgroup barrier)
+  __shared__ uint4 stage_lds[kBsWaves][kBsWaveRows * kBsLdsPitch];
+  uint4* const my = stage_lds[wave];
+  // load k of a stage reads row 8 k + lane / 8 of the wave, bytes
+  // 16 (lane % 8) .. + 15 of the stage's 128 (channels 64 g + 8 (lane % 8) ..)
+  const int srow = lane >> 3, scol = lane & 7;
+  const uint32_t sbase = (uint32_t)(srow * pitch_b + scol * 16);
+  const int G = (S + kBsStageSteps - 1) / kBsStageSteps;
+  uint4 stg[kBsStageLoads];
+  auto stage_load = [&](int g) {
+    const bool in = 64 * g + 8 * scol < D;
+#pragma unroll
+    for (int k = 0; k < kBsStageLoads; ++k)
+      stg[k] = bload<ATTNRES_BS_LDS_AUX>(ra, in ? sbase + (uint32_t)(8 * k * pitch_b) + (uint32_t)(128 * g) : 0xFFFFFFF0u);
+  };
+  stage_load(0);
+  for (int g = 0; g < G; ++g) {
+    wave_sync();  // every lane's reads of the previous stage are done
+#pragma unroll
+    for (int k = 0; k < kBsStageLoads; ++k) my[(8 * k + srow) * kBsLdsPitch + scol] = stg[k];
+    wave_sync();  // the stage is in LDS for every lane
+    // AHEAD: the B operands of both k-steps go out before the next stage's
+    // loads; the wait counts are in order, so the k-steps then wait for their
+    // own loads only and the stage loads have both k-steps to arrive (0.81
+    // against 0.84-0.87 ms at T = 32768, n = 8, L = 24).  Otherwise (the
+    // four-tile kernel, where the extra registers cost more: 1.42 against
+    // 1.30 ms at L = 48) they go out behind the first k-step's B operands.
+    uint4 b[AHEAD ? kBsStageSteps : 1][CT][3];
+    if constexpr (AHEAD) {
+#pragma unroll
+      for (int j = 0; j < kBsStageSteps; ++j)
+        if (g * kBsStageSteps + j < S) bs_load_b<CT>(b[j], rb, g * kBsStageSteps + j, q, r, Lpad);
+      if (g + 1 < G) stage_load(g + 1);
+    }
+#pragma unroll
+    for (int j = 0; j < kBsStageSteps; ++j) {
+      const int s = g * kBsStageSteps + j;
+      if (s >= S) break;
+      uint4 a[kBsTiles];
+      if constexpr (!AHEAD) {
+        bs_load_b<CT>(b[0], rb, s, q, r, Lpad);
+        if (j == 0 && g + 1 < G) stage_load(g + 1);
+      }
+      const uint4(&bj)[CT][3] = b[AHEAD ? j : 0];
+#pragma unroll
+      for (int m = 0; m < kBsTiles; ++m) a[m] = my[(16 * m + r) * kBsLdsPitch + 4 * j + q];  // channels 32 s + 8 q ..
+      bs_step<CT, SEP>(a, bj, acc, acch, ss_acc);
+      if (s % kBsChunk == kBsChunk - 1 || s + 1 >= S) fold();
+    }
+  }
+#elif !ATTNRES_BS_PREFETCH
   for (int s = 0; s < S; ++s) {
     uint4 a[kBsTiles], b[CT][3];
     bs_load<CT>(a, b, ra, rb, roff, s, q, r, D, Lpad);
@@ -866,6 +954,24 @@ __global__ void __launch_bounds__(256) block_scores_kernel(SrcRows src, int64_t 
       }
     }
   }
+}
+
+// Up to 32 queries (one or two column tiles) at two waves per SIMD.
+template <int CT>
+__global__ void __launch_bounds__(256) ATTNRES_BS_WAVES_PER_EU
+    block_scores_kernel(SrcRows src, int64_t T, int32_t D, float eps, int32_t n, const uint16_t* __restrict__ Wp,
+                        int32_t L, int32_t Lpad, int32_t Dpad, int64_t wg_per_source, float* __restrict__ rstd_out,
+                        float* __restrict__ z_out) {
+  block_scores_body<CT, true>(src, T, D, eps, n, Wp, L, Lpad, Dpad, wg_per_source, rstd_out, z_out);
+}
+
+// Four column tiles (33-64 queries): held to 256 registers they spill, so
+// this one runs at whatever occupancy its registers allow.
+__global__ void __launch_bounds__(256)
+    block_scores_kernel_wide(SrcRows src, int64_t T, int32_t D, float eps, int32_t n, const uint16_t* __restrict__ Wp,
+                             int32_t L, int32_t Lpad, int32_t Dpad, int64_t wg_per_source, float* __restrict__ rstd_out,
+                             float* __restrict__ z_out) {
+  block_scores_body<4, false>(src, T, D, eps, n, Wp, L, Lpad, Dpad, wg_per_source, rstd_out, z_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -2429,7 +2535,7 @@ attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, con
     hipLaunchKernelGGL(block_scores_kernel<2>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
                        wg_per_source, rstd, z);
   else
-    hipLaunchKernelGGL(block_scores_kernel<4>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
+    hipLaunchKernelGGL(block_scores_kernel_wide, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
                        wg_per_source, rstd, z);
   return hipGetLastError() == hipSuccess ? ATTNRES_OK : ATTNRES_ERR_HIP;
 }
