@@ -809,8 +809,16 @@ __device__ __forceinline__ void block_scores_body(const SrcRows& src, int64_t T,
                                                   float* __restrict__ z_out) {
   const int wave = wave_id(), lane = lane_id();
   const int r = lane & 15, q = lane >> 4;
-  const int i = (int)(blockIdx.x / wg_per_source);
-  const int64_t tw = (int64_t)(blockIdx.x % wg_per_source) * kBsRows + wave * kBsWaveRows;  // wave's first token
+  // workgroup b runs on XCD b % 8 (round-robin dispatch): the n workgroups of
+  // one token group share b % 8 and follow each other, so that XCD's L2 can
+  // merge their 4-byte score stores, which interleave at a stride of n floats
+  // ([L][T][n]), before the lines go to memory; the grid has whole rounds
+  // of 8 token groups, and groups past the last one return at once
+  const int64_t bx = blockIdx.x, kx = bx / 8;
+  const int i = (int)(kx % n);
+  const int64_t tg = bx % 8 + 8 * (kx / n);
+  if (tg >= wg_per_source) return;
+  const int64_t tw = tg * kBsRows + wave * kBsWaveRows;  // wave's first token
   if (tw >= T) return;  // no barrier in this kernel
   const int64_t rows = T - tw < kBsWaveRows ? T - tw : kBsWaveRows;
   const int64_t pitch_b = src.pitch * 2;
@@ -2502,7 +2510,8 @@ attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, con
   if (workspace == nullptr || workspace_bytes < need) return ATTNRES_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return ATTNRES_ERR_INVALID_ARGUMENT;
   const int64_t wg_per_source = (T + kBsRows - 1) / kBsRows;
-  if (wg_per_source * n > (int64_t)UINT32_MAX / 256) return ATTNRES_ERR_INVALID_ARGUMENT;
+  const int64_t bs_groups = (wg_per_source + 7) / 8 * 8;  // token groups in whole rounds of the 8 XCDs
+  if (bs_groups * n > (int64_t)UINT32_MAX / 256) return ATTNRES_ERR_INVALID_ARGUMENT;
   Range ins[ATTNRES_MAX_SOURCES + 1];
   SrcRows rows{};
   rows.pitch = pitch;
@@ -2527,7 +2536,7 @@ attnres_status block_scores_impl(const uint16_t* const* srcs, int64_t pitch, con
   hipLaunchKernelGGL(split_queries_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, W, L, D, Lpad, Dpad,
                      Wp);
   if (hipGetLastError() != hipSuccess) return ATTNRES_ERR_HIP;
-  const dim3 grid((unsigned)(wg_per_source * n)), block(kBsWaves * kWave);
+  const dim3 grid((unsigned)(bs_groups * n)), block(kBsWaves * kWave);
   if (Lpad <= 16)
     hipLaunchKernelGGL(block_scores_kernel<1>, grid, block, 0, st, rows, T, D, eps, n, Wp, L, Lpad, Dpad,
                        wg_per_source, rstd, z);
